@@ -1,0 +1,159 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) Native Sparse Attention forward.
+ *
+ * The operation (sources cited by page and section):
+ *   [P1] "Zhang Xiaojun Business Interviews #94" transcript (bidclub.ai),
+ *        s4 "Inside Native Sparse Attention", s5 "Hardware Makes Sparsity
+ *        Work", s6 "Why Sparse Attention Wins", s7 "Kimi Simplifies The
+ *        Sparse Route";
+ *   [P5] LateTalk #103 notes (zjai.club), close reading s12-s13.
+ *
+ * For every query token and head the output is a gated sum of three
+ * attention branches over the causal past ([P1] s4):
+ *   - compressed: softmax attention over one mean summary per complete KV
+ *     block (summaries of blocks that end after the query are masked);
+ *   - selected:   one softmax over all tokens (up to the query) of the
+ *     top_k blocks chosen for the token's KV group -- the group's heads add
+ *     up their compressed-branch probabilities so that they all pick the
+ *     same blocks;
+ *   - window:     softmax over the last `window` positions.
+ * MoBA ([P1] s7, [P5] s13) is the special case of one head per KV group,
+ * block means as block keys, the current block always chosen, and the
+ * selected branch alone.  Decoding ([P1] s6) is q_len = 1 with a long cache.
+ *
+ * Conventions shared by every call
+ *   Positions: the q_len queries sit at absolute positions
+ *     kv_len - q_len .. kv_len - 1 of their sequence (prefill: q_len == kv_len).
+ *   Heads: H = n_kv_groups * heads_per_group; head h uses KV group
+ *     h / heads_per_group.
+ *   Layouts (row-major, last dimension contiguous, every base pointer
+ *   16-byte aligned, all device memory unless stated):
+ *     q      [B, q_len, H, d_qk]          k     [B, kv_len, G, d_qk]
+ *     v      [B, kv_len, G, d_v]          gates [B, q_len, H, 3] (cmp, slc, win)
+ *     k_cmp  [B, nb, G, d_qk]             v_cmp [B, nb, G, d_v]   nb = kv_len / block
+ *     idx    int32 [B, q_len, G, top_k]   ascending block ids, padded with -1
+ *     out    [B, q_len, H, d_v]
+ *   Element type: dtype (NSA_BF16 or NSA_F32) for q, k, v, gates, k_cmp,
+ *     v_cmp and out (out is fp32 when NSA_F_OUT_F32 is set).  Arithmetic is
+ *     fp32 (bf16 inputs feed bf16 matrix cores with fp32 accumulation).
+ *   Ownership: the caller allocates and owns every buffer, including the
+ *     workspace (size from nsa_workspace_bytes).  The library allocates and
+ *     frees nothing, keeps no pointer after a call returns, and never
+ *     synchronises: work is queued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and results are ready when that stream reaches them.
+ *   Errors: arguments are validated before anything is queued; on any error
+ *     nothing is launched and no output is written.  NSA_ERR_HIP reports a
+ *     failed launch (hipGetLastError), in which case outputs are undefined.
+ *   Thread safety: calls hold no global state and may come from several
+ *     threads; calls sharing a workspace must be ordered on one stream.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSA_OK = 0,
+  NSA_ERR_INVALID_ARG = 1,  /* NULL/misaligned pointer, inconsistent sizes or flags */
+  NSA_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle (limits below) */
+  NSA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than nsa_workspace_bytes */
+  NSA_ERR_HIP = 4           /* a kernel launch failed */
+} nsa_status;
+
+enum { NSA_BF16 = 0, NSA_F32 = 1 };
+
+enum {
+  NSA_F_FORCE_FIRST = 1u,    /* block 0 is always chosen (attention-sink rationale, [P1] s4) */
+  NSA_F_FORCE_CURRENT = 2u,  /* the query's own block is always chosen ([P5] s13) */
+  NSA_F_CMP = 4u,            /* compressed branch enters the output */
+  NSA_F_SLC = 8u,            /* selected branch enters the output */
+  NSA_F_WIN = 16u,           /* window branch enters the output */
+  NSA_F_GATE_LOGITS = 32u,   /* gates hold logits; the kernel applies a sigmoid */
+  NSA_F_OUT_F32 = 64u        /* out is fp32 whatever dtype is */
+};
+
+/*
+ * Problem description.  Limits (NSA_ERR_UNSUPPORTED outside them):
+ *   1 <= heads_per_group <= 16; 1 <= d_qk, d_v <= 256; 1 <= block <= 4096;
+ *   top_k <= 64 and top_k * block <= 16384; window <= 16384;
+ *   nb = kv_len / block <= 16384.
+ * Invalid (NSA_ERR_INVALID_ARG): batch, q_len, n_kv_groups < 1;
+ *   kv_len < q_len; top_k smaller than the number of forced blocks;
+ *   window < 0; scale < 0; dtype unknown; flags outside NSA_F_*.
+ */
+typedef struct {
+  int32_t batch, q_len, kv_len;
+  int32_t n_kv_groups, heads_per_group;
+  int32_t d_qk, d_v;
+  int32_t block, top_k, window;
+  uint32_t flags;          /* NSA_F_* */
+  int32_t dtype;           /* NSA_BF16 or NSA_F32 */
+  float scale;             /* softmax scale; 0 means 1/sqrt(d_qk) */
+  const void* k_cmp;       /* nsa_forward: precomputed block summaries (e.g. a  */
+  const void* v_cmp;       /* decode cache) or NULL to compute them in workspace */
+  void* workspace;         /* device scratch owned by the caller */
+  size_t workspace_bytes;
+  void* stream;            /* hipStream_t */
+} nsa_params;
+
+/*
+ * Block compression ([P1] s4, s7): k_cmp[b, j, g, :] is the mean of the
+ * `block` keys of block j (j < nb), v_cmp likewise.  The sum is taken in
+ * fp64 in token order, divided by `block` and rounded once (to nearest,
+ * ties to even) to dtype, so results are reproducible bit for bit.
+ * Reads k, v; writes k_cmp, v_cmp.  Uses no workspace.
+ */
+nsa_status nsa_compress(const void* k, const void* v, void* k_cmp, void* v_cmp,
+                        const nsa_params* params);
+
+/*
+ * Block selection ([P1] s4 compressed branch + group-summed importance;
+ * [P1] s7 and [P5] s13 for MoBA).  For query token t at position p and
+ * group g: each head's softmax over the summaries of the complete blocks
+ * j with (j + 1) * block <= p + 1, added up over the group's heads, is the
+ * importance of block j.  Forced blocks (flags) come first; the remaining
+ * top_k slots take the visible blocks with the highest importance (ties to
+ * the lower block id).  idx[b, t, g, :] lists the chosen blocks ascending,
+ * padded with -1.  score_or_null (fp32, same shape) receives each listed
+ * block's importance, +inf for forced blocks and -inf for padding.
+ * Reads q and k_cmp (params->k_cmp is ignored here); may use the workspace.
+ */
+nsa_status nsa_select_topk(const void* q, const void* k_cmp, int32_t* idx,
+                           float* score_or_null, const nsa_params* params);
+
+/*
+ * Selected branch alone ([P1] s4, s5): for each token and head, one softmax
+ * over every position s <= p of the blocks listed in idx (entries < 0 are
+ * skipped; entries must be distinct and begin at or before p), written to
+ * out (no gate).  lse_or_null (fp32 [B, q_len, H]) receives the natural-log
+ * sum of the exponentiated scaled logits (-inf for an empty set, whose
+ * output is 0).  May use the workspace.
+ */
+nsa_status nsa_sparse_attn(const void* q, const void* k, const void* v, const int32_t* idx,
+                           void* out, float* lse_or_null, const nsa_params* params);
+
+/*
+ * The whole forward ([P1] s4): summaries (taken from params->k_cmp/v_cmp
+ * when both are given, else computed into the workspace), selection, the
+ * branches enabled by flags, and out = sum over enabled branches of
+ * gate * branch output.  gates may be NULL only when exactly one branch is
+ * enabled (its weight is then 1).  Needs the workspace.
+ */
+nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates,
+                       const nsa_params* params, void* out);
+
+/* Workspace bytes that any call above needs for these params (0 if none). */
+size_t nsa_workspace_bytes(const nsa_params* params);
+
+/* Static description of a status code. */
+const char* nsa_status_str(nsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NSA_H */

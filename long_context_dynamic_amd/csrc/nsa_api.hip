@@ -1,0 +1,119 @@
+// nsa_api.hip -- the C ABI declared in include/nsa.h: argument validation
+// (before anything is queued), workspace planning and kernel dispatch.
+#include <math.h>
+#include <string.h>
+
+#include "nsa_internal.h"
+#include "nsa_paths.h"
+
+using nsa::Prob;
+
+namespace {
+
+constexpr uint32_t kAllFlags = NSA_F_FORCE_FIRST | NSA_F_FORCE_CURRENT | NSA_F_CMP | NSA_F_SLC |
+                               NSA_F_WIN | NSA_F_GATE_LOGITS | NSA_F_OUT_F32;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+nsa_status describe(const nsa_params* p, Prob* P) {
+  if (!p) return NSA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->q_len < 1 || p->kv_len < p->q_len || p->n_kv_groups < 1 ||
+      p->heads_per_group < 1 || p->d_qk < 1 || p->d_v < 1 || p->block < 1 || p->top_k < 0 ||
+      p->window < 0 || (p->flags & ~kAllFlags) || (p->dtype != NSA_BF16 && p->dtype != NSA_F32) ||
+      !(p->scale >= 0.f) || isinf(p->scale))
+    return NSA_ERR_INVALID_ARG;
+  const int n_forced = ((p->flags & NSA_F_FORCE_FIRST) ? 1 : 0) + ((p->flags & NSA_F_FORCE_CURRENT) ? 1 : 0);
+  if (p->top_k < n_forced) return NSA_ERR_INVALID_ARG;
+  const int64_t nb = (int64_t)p->kv_len / p->block;
+  if (p->heads_per_group > 16 || p->d_qk > 256 || p->d_v > 256 || p->block > 4096 || p->top_k > 64 ||
+      (int64_t)p->top_k * p->block > 16384 || p->window > 16384 || nb > 16384)
+    return NSA_ERR_UNSUPPORTED;
+  P->B = p->batch; P->T = p->q_len; P->L = p->kv_len;
+  P->G = p->n_kv_groups; P->hpg = p->heads_per_group; P->H = P->G * P->hpg;
+  P->dq = p->d_qk; P->dv = p->d_v; P->bs = p->block; P->n = p->top_k; P->w = p->window; P->nb = nb;
+  P->flags = p->flags; P->dtype = p->dtype;
+  P->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d_qk));
+  // element counts must fit the grid: one workgroup per (b, t, g) and per (b, j, g)
+  if (P->B * P->T * P->G >= ((int64_t)1 << 31) || P->B * P->nb * P->G >= ((int64_t)1 << 31))
+    return NSA_ERR_UNSUPPORTED;
+  return NSA_OK;
+}
+
+int n_branches(uint32_t f) {
+  return ((f & NSA_F_CMP) ? 1 : 0) + ((f & NSA_F_SLC) ? 1 : 0) + ((f & NSA_F_WIN) ? 1 : 0);
+}
+
+nsa_status hip_status(hipError_t e) { return e == hipSuccess ? NSA_OK : NSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_status_str(nsa_status s) {
+  switch (s) {
+    case NSA_OK: return "ok";
+    case NSA_ERR_INVALID_ARG: return "invalid argument";
+    case NSA_ERR_UNSUPPORTED: return "unsupported problem shape";
+    case NSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case NSA_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+size_t nsa_workspace_bytes(const nsa_params* p) {
+  Prob P;
+  if (describe(p, &P) != NSA_OK) return 0;
+  return nsa::workspace_bytes_max(P, p->k_cmp != nullptr && p->v_cmp != nullptr);
+}
+
+nsa_status nsa_compress(const void* k, const void* v, void* k_cmp, void* v_cmp, const nsa_params* p) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  if (!ptr_ok(k) || !ptr_ok(v) || !ptr_ok(k_cmp) || !ptr_ok(v_cmp)) return NSA_ERR_INVALID_ARG;
+  return hip_status(nsa::launch_pool(P, k, v, k_cmp, v_cmp, (hipStream_t)p->stream));
+}
+
+nsa_status nsa_select_topk(const void* q, const void* k_cmp, int32_t* idx, float* score, const nsa_params* p) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  if (!ptr_ok(q) || !ptr_ok(k_cmp) || !ptr_ok(idx) || !opt_ok(score)) return NSA_ERR_INVALID_ARG;
+  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Select, true);
+  if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
+  return hip_status(nsa::run_select(P, q, k_cmp, idx, score, ws, p->workspace, (hipStream_t)p->stream));
+}
+
+nsa_status nsa_sparse_attn(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
+                           float* lse, const nsa_params* p) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(out) || !opt_ok(lse))
+    return NSA_ERR_INVALID_ARG;
+  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::SparseAttn, true);
+  if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
+  return hip_status(nsa::run_sparse_attn(P, q, k, v, idx, out, lse, ws, p->workspace, (hipStream_t)p->stream));
+}
+
+nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates, const nsa_params* p,
+                       void* out) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  const int nbr = n_branches(P.flags);
+  if (nbr == 0 || (gates == nullptr && nbr > 1)) return NSA_ERR_INVALID_ARG;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out) || !opt_ok(gates)) return NSA_ERR_INVALID_ARG;
+  if ((p->k_cmp == nullptr) != (p->v_cmp == nullptr) || !opt_ok(p->k_cmp) || !opt_ok(p->v_cmp))
+    return NSA_ERR_INVALID_ARG;
+  const bool have_cmp = p->k_cmp != nullptr;
+  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Forward, have_cmp);
+  if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
+  return hip_status(nsa::run_forward(P, q, k, v, gates, have_cmp ? p->k_cmp : nullptr,
+                                     have_cmp ? p->v_cmp : nullptr, out, ws, p->workspace,
+                                     (hipStream_t)p->stream));
+}
+
+}  // extern "C"

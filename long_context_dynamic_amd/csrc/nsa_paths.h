@@ -1,0 +1,32 @@
+// nsa_paths.h -- workspace planning and the choice between the any-shape
+// path and the matrix-core paths (internal).
+#pragma once
+
+#include "nsa_internal.h"
+
+namespace nsa {
+
+// Byte offsets into the caller's workspace (each 256-byte aligned); a field
+// is meaningful only when the chosen path uses it.
+struct Workspace {
+  size_t total = 0;
+  size_t kc = 0, vc = 0;  // block summaries, when the caller gives none
+  size_t idx = 0;         // int32 [B, T, G, top_k]
+  size_t ocmp = 0;        // fp32 [B, T, H, d_v] compressed-branch output
+};
+
+enum class Call { Select, SparseAttn, Forward };
+
+Workspace plan_workspace(const Prob& P, Call call, bool have_cmp);
+// The largest need over every call (what nsa_workspace_bytes reports).
+size_t workspace_bytes_max(const Prob& P, bool have_cmp);
+
+hipError_t run_select(const Prob& P, const void* q, const void* kc, int32_t* idx, float* score,
+                      const Workspace& ws, void* base, hipStream_t s);
+hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const void* v, const int32_t* idx,
+                           void* out, float* lse, const Workspace& ws, void* base, hipStream_t s);
+hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
+                       const void* kc_given, const void* vc_given, void* out, const Workspace& ws,
+                       void* base, hipStream_t s);
+
+}  // namespace nsa

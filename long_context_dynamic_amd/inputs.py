@@ -1,22 +1,32 @@
 """Seeded synthetic inputs (no attention arithmetic here).
 
-Recipe, per batch element b (its own stream, so sequences can be generated
-one at a time): numpy ``Generator(PCG64(SeedSequence(seed).spawn(B)[b]))``
-draws, in this order,
+Recipe.  For batch element b, ``seq = SeedSequence(seed).spawn(B)[b]`` and
+``seq.spawn(4)`` gives one stream per tensor (q, k, v, gates).  Each tensor
+is drawn in chunks of CHUNK tokens; chunk c uses the c-th child of its
+tensor's stream, ``Generator(PCG64(child))``, so chunks can be filled in
+parallel and a shorter problem is a prefix of a longer one.  Values:
 
     q       ~ N(0, 1)       [T, H, d_qk]
-    k       ~ N(0, 1)       [L, G, d_qk]
-    offset  ~ N(0, std^2)   [ceil(L / block), G, d_qk], added to every key of its block
+    k       ~ N(0, 1)       [L, G, d_qk], plus a per-block offset
+    offset  ~ N(0, std^2)   [ceil(L / block), G, d_qk] (std = key_offset_std),
+                            drawn first from the k stream's last child and
+                            added to every key of its block
     v       ~ N(0, 1)       [L, G, d_v]
     gates   ~ U(0, 1)       [T, H, 3]
 
-all in float32, then stored as float32 or rounded to bf16 (nearest, ties to
+all float32, then stored as float32 or rounded to bf16 (nearest, ties to
 even).  The per-block key offset gives blocks distinct summaries, so the
 top-k choice is not a coin toss.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
+
+CHUNK = 4096
+_OFFSET_CHILD = 1 << 20  # child index reserved for the key offsets
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -24,7 +34,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     out = np.empty(u.shape, dtype=np.uint16)
     flat_u, flat_o = u.reshape(-1), out.reshape(-1)
-    step = 1 << 24
+    step = 1 << 22
     for s in range(0, flat_u.size, step):
         c = flat_u[s:s + step]
         flat_o[s:s + step] = ((c + np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1)))
@@ -37,46 +47,67 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
     return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _store(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+def _workers() -> int:
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
 
 
-def sequence_rng(prob: dict, b: int) -> np.random.Generator:
-    seq = np.random.SeedSequence(int(prob.get("seed", 0))).spawn(int(prob["batch"]))[b]
-    return np.random.Generator(np.random.PCG64(seq))
+def _child(ss: np.random.SeedSequence, c: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(ss.entropy, spawn_key=ss.spawn_key + (c,))))
 
 
-def generate_sequence(prob: dict, b: int, want=("q", "k", "v", "gates")) -> dict:
+def _fill(out: np.ndarray, ss, rows: int, width_shape, dtype: str, kind: str, pool, offset=None, bs=1):
+    """Fill out[rows, *width_shape] chunk by chunk."""
+    def one(c):
+        lo, hi = c * CHUNK, min(rows, (c + 1) * CHUNK)
+        g = _child(ss, c)
+        shape = (hi - lo,) + tuple(width_shape)
+        x = g.standard_normal(shape, dtype=np.float32) if kind == "normal" else g.random(shape, dtype=np.float32)
+        if offset is not None:
+            blk = np.arange(lo, hi) // bs
+            x += offset[blk]
+        out[lo:hi] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    list(pool.map(one, range(-(-rows // CHUNK))))
+
+
+def generate_sequence(prob: dict, b: int, want=("q", "k", "v", "gates"), pool=None) -> dict:
     """Inputs of batch element b, each with a leading batch dimension of 1."""
-    rng = sequence_rng(prob, b)
     T, L = prob["q_len"], prob["kv_len"]
     G, hpg = prob["n_groups"], prob["heads_per_group"]
     H, dq, dv, bs = G * hpg, prob["d_qk"], prob["d_v"], prob["block"]
     dt = prob["dtype"]
-    out = {}
-    q = rng.standard_normal((T, H, dq), dtype=np.float32)
-    if "q" in want:
-        out["q"] = _store(q, dt)[None]
-    del q
-    k = rng.standard_normal((L, G, dq), dtype=np.float32)
-    nbk = -(-L // bs)
-    offset = rng.standard_normal((nbk, G, dq), dtype=np.float32) * np.float32(prob.get("key_offset_std", 0.5))
-    for j in range(nbk):
-        k[j * bs:(j + 1) * bs] += offset[j]
-    if "k" in want:
-        out["k"] = _store(k, dt)[None]
-    del k
-    v = rng.standard_normal((L, G, dv), dtype=np.float32)
-    if "v" in want:
-        out["v"] = _store(v, dt)[None]
-    del v
-    gates = rng.random((T, H, 3), dtype=np.float32)
-    if "gates" in want:
-        out["gates"] = _store(gates, dt)[None]
-    return out
+    st = np.uint16 if dt == "bf16" else np.float32
+    seq = np.random.SeedSequence(int(prob.get("seed", 0))).spawn(int(prob["batch"]))[b]
+    s_q, s_k, s_v, s_g = seq.spawn(4)
+    own = pool is None
+    pool = pool or cf.ThreadPoolExecutor(_workers())
+    try:
+        out = {}
+        if "q" in want:
+            out["q"] = np.empty((1, T, H, dq), st)
+            _fill(out["q"][0], s_q, T, (H, dq), dt, "normal", pool)
+        if "k" in want:
+            nbk = -(-L // bs)
+            offset = _child(s_k, _OFFSET_CHILD).standard_normal((nbk, G, dq), dtype=np.float32)
+            offset *= np.float32(prob.get("key_offset_std", 0.5))
+            out["k"] = np.empty((1, L, G, dq), st)
+            _fill(out["k"][0], s_k, L, (G, dq), dt, "normal", pool, offset=offset, bs=bs)
+        if "v" in want:
+            out["v"] = np.empty((1, L, G, dv), st)
+            _fill(out["v"][0], s_v, L, (G, dv), dt, "normal", pool)
+        if "gates" in want:
+            out["gates"] = np.empty((1, T, H, 3), st)
+            _fill(out["gates"][0], s_g, T, (H, 3), dt, "uniform", pool)
+        return out
+    finally:
+        if own:
+            pool.shutdown()
 
 
 def generate(prob: dict, want=("q", "k", "v", "gates")) -> dict:
     """Inputs for every batch element, concatenated along the batch axis."""
-    parts = [generate_sequence(prob, b, want) for b in range(prob["batch"])]
+    with cf.ThreadPoolExecutor(_workers()) as pool:
+        parts = [generate_sequence(prob, b, want, pool) for b in range(prob["batch"])]
+    if len(parts) == 1:
+        return parts[0]
     return {name: np.concatenate([p[name] for p in parts], axis=0) for name in parts[0]}

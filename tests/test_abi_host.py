@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every call include/nsa.h declares, and rejects bad arguments synchronously,
+before anything is queued (fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_dynamic_amd import nsa, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+class _NoStream:
+    cuda_stream = 0
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\**\s*(nsa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
+              "nsa_workspace_bytes", "nsa_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nsa.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = nsa.lib()
+    seen = {lib.nsa_status_str(c).decode() for c in range(5)}
+    assert len(seen) == 5
+    assert lib.nsa_status_str(99).decode() == "unknown status"
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation
+
+
+def _p(prob, **kw):
+    p = nsa.params(prob, stream=_NoStream, **{k: v for k, v in kw.items() if k in ("flags",)})
+    for k, v in kw.items():
+        if k != "flags":
+            setattr(p, k, v)
+    return p
+
+
+def _forward(p, gates=FAKE, q=FAKE, out=FAKE):
+    return nsa.lib().nsa_forward(q, FAKE, FAKE, gates, ctypes.byref(p), out)
+
+
+BASE = workloads.get("nsa_prefill_8k", q_len=256, kv_len=256)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 1), ("q_len", 0, 1), ("kv_len", 100, 1), ("n_kv_groups", 0, 1),
+    ("heads_per_group", 0, 1), ("heads_per_group", 17, 2), ("d_qk", 0, 1), ("d_qk", 300, 2),
+    ("d_v", 257, 2), ("block", 0, 1), ("block", 8192, 2), ("top_k", -1, 1), ("top_k", 1, 1),
+    ("top_k", 65, 2), ("window", -1, 1), ("window", 20000, 2), ("dtype", 7, 1), ("flags", 1 << 9, 1),
+    ("scale", -1.0, 1), ("scale", float("inf"), 1), ("scale", float("nan"), 1),
+])
+def test_bad_params_are_rejected_before_launch(field, value, code):
+    p = _p(BASE)
+    setattr(p, field, value)
+    assert _forward(p) == code
+    assert nsa.lib().nsa_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_pointer_and_flag_errors():
+    lib = nsa.lib()
+    p = _p(BASE)
+    assert _forward(p, q=0) == 1                        # NULL q
+    assert _forward(p, q=FAKE + 2) == 1                 # misaligned q
+    assert _forward(p, gates=0) == 1                    # three branches need gates
+    p0 = _p(BASE, flags=0)
+    assert _forward(p0) == 1                            # no branch at all
+    p1 = _p(BASE)
+    p1.k_cmp = FAKE                                     # summaries: both or neither
+    assert _forward(p1) == 1
+    p2 = _p(BASE)
+    p2.workspace, p2.workspace_bytes = FAKE, 16         # too small
+    assert _forward(p2) == 3
+    p3 = _p(BASE)
+    assert _forward(p3) == 3                            # none given
+    assert lib.nsa_compress(FAKE, FAKE, 0, FAKE, ctypes.byref(p)) == 1
+    assert lib.nsa_select_topk(FAKE, FAKE, FAKE + 4, 0, ctypes.byref(p)) == 1
+    assert lib.nsa_sparse_attn(FAKE, FAKE, FAKE, FAKE, 0, 0, ctypes.byref(p)) == 1
+    assert lib.nsa_compress(FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_workspace_sizes():
+    for name in workloads.WORKLOADS:
+        prob = workloads.get(name)
+        need = nsa.workspace_bytes(prob)
+        assert need > 0, name
+        assert need % 256 == 0
+    # a caller-provided summary cache needs less room than computing it
+    dec = workloads.get("nsa_decode_64x64k")
+    assert nsa.workspace_bytes(dec, have_cmp=True) < nsa.workspace_bytes(dec)

@@ -1,0 +1,178 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs.  Pooling is bit-exact; selections match outside the near-tie band
+(oracle's r-th / (r+1)-th importance gap under 1e-4 relative); outputs are
+compared with oracle attention evaluated on the GPU's own selection, to
+max |err| <= 2e-2 (bf16) or 1e-4 (fp32).
+
+Cases: each named workload, once at a reduced size the oracle finishes in
+seconds (several tiles and a ragged tail) checked on every row, and once at
+its full size checked on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_dynamic_amd import inputs, nsa, workloads
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+# (workload, overrides, rows to check: None = all rows, int = sample size)
+CASES = [
+    ("nsa_tiny_fp32", {}, None),
+    ("nsa_tiny_fp32", dict(q_len=700, kv_len=1000, window=100), None),
+    ("nsa_prefill_8k", dict(q_len=1000, kv_len=1000), None),
+    ("nsa_prefill_8k", dict(q_len=333, kv_len=1100, gate_logits=1), None),
+    ("nsa_prefill_8k", {}, 48),
+    ("nsa_prefill_64k", {}, 20),
+    ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
+    ("moba_32k", {}, 24),
+    ("nsa_decode_64x64k", dict(batch=6, kv_len=4096 + 17), None),
+]
+
+
+def _ids():
+    return [f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items()) or 'full'}" for n, o, _ in CASES]
+
+
+_cache = {}
+
+
+def _case(i):
+    """Inputs, device tensors and the oracle's selection for CASES[i] (cached per case)."""
+    if i in _cache:
+        return _cache[i]
+    _cache.clear()
+    torch.cuda.empty_cache()
+    name, over, nrows = CASES[i]
+    prob = workloads.get(name, **over)
+    print(f"[case] {name} {over}", flush=True)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    rows = (np.arange(prob["batch"] * prob["q_len"]) if nrows is None
+            else U.sample_rows(prob, nrows, seed=i))
+    kc, vc = oracle.pool(prob, x["k"], x["v"])
+    idx, imp, ocmp = oracle.select(prob, x["q"], kc, vc, rows=rows, want_cmp=bool(prob["use_cmp"]))
+    _cache[i] = (prob, x, t, rows, (kc, vc, idx, imp, ocmp))
+    return _cache[i]
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=_ids())
+def test_compress_is_bit_exact(i):
+    prob, x, t, rows, (kc, vc, *_) = _case(i)
+    gkc, gvc = nsa.compress(prob, t["k"], t["v"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(nsa.to_host_bits(gkc), kc)
+    np.testing.assert_array_equal(nsa.to_host_bits(gvc), vc)
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=_ids())
+def test_select_topk(i):
+    prob, x, t, rows, (kc, vc, idx, imp, _) = _case(i)
+    gkc = nsa.to_device(kc, prob)
+    gidx, gscore = nsa.select_topk(prob, t["q"], gkc)
+    torch.cuda.synchronize()
+    got = U.gather_rows(gidx.cpu().numpy(), prob, rows)
+    band = U.check_selection(prob, rows, got, idx, imp)
+    print(f"rows={len(rows)} groups={prob['n_groups']} tie-band pairs={band}")
+    # scores: importance of each chosen block, +inf forced, -inf padding
+    sc = U.gather_rows(gscore.cpu().numpy(), prob, rows)
+    T, bs = prob["q_len"], prob["block"]
+    for ri, r in enumerate(rows):
+        p = prob["kv_len"] - T + int(r) % T
+        F = U.forced_set(prob, p)
+        for g in range(prob["n_groups"]):
+            for slot, j in enumerate(got[ri, g]):
+                s = sc[ri, g, slot]
+                if j < 0:
+                    assert s == -np.inf
+                elif j in F:
+                    assert s == np.inf
+                else:
+                    assert abs(s - imp[ri, g, j]) <= 1e-5 + 1e-4 * imp[ri, g, j], (r, g, j, s, imp[ri, g, j])
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=_ids())
+def test_sparse_attn_on_given_selection(i):
+    prob, x, t, rows, (kc, vc, idx, imp, _) = _case(i)
+    # run on the oracle's own selection, every row filled in
+    full_idx = np.full((prob["batch"] * prob["q_len"], prob["n_groups"], prob["top_k"]), -1, np.int32)
+    full_idx[rows] = idx
+    sel_rows = rows
+    gidx = torch.from_numpy(full_idx.reshape(prob["batch"], prob["q_len"], prob["n_groups"], -1)).cuda()
+    out, lse = nsa.sparse_attn(prob, t["q"], t["k"], t["v"], gidx, out_f32=True)
+    torch.cuda.synchronize()
+    oprob = dict(prob, use_cmp=0, use_slc=1, use_win=0)
+    _, want, _ = oracle.attend(oprob, x["q"], x["k"], x["v"], None, idx, None, rows=sel_rows)
+    got = U.gather_rows(out.cpu().numpy().astype(np.float64), prob, sel_rows)
+    err = np.abs(got - want).max()
+    print(f"max |o_slc - oracle| = {err:.3e}")
+    assert err <= U.TOL[prob["dtype"]]
+    assert np.all(np.isfinite(U.gather_rows(lse.cpu().numpy(), prob, sel_rows)))
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+@pytest.mark.parametrize("i", range(len(CASES)), ids=_ids())
+def test_forward(i, out_f32):
+    prob, x, t, rows, (kc, vc, idx, imp, ocmp) = _case(i)
+    gkc = nsa.to_device(kc, prob)
+    gidx, _ = nsa.select_topk(prob, t["q"], gkc, want_score=False)
+    gates = t["gates"] if (prob["use_cmp"] + prob["use_slc"] + prob["use_win"]) > 1 else None
+    out = torch.full((prob["batch"], prob["q_len"], workloads.n_heads(prob), prob["d_v"]), float("nan"),
+                     dtype=torch.float32 if out_f32 else nsa.torch_dtype(prob), device="cuda")
+    nsa.forward(prob, t["q"], t["k"], t["v"], gates, out=out, out_f32=out_f32)
+    torch.cuda.synchronize()
+    gsel = U.gather_rows(gidx.cpu().numpy(), prob, rows)
+    U.check_selection(prob, rows, gsel, idx, imp)
+    want, _, _ = oracle.attend(prob, x["q"], x["k"], x["v"], x["gates"] if gates is not None else None,
+                               gsel, ocmp if prob["use_cmp"] else None, rows=rows)
+    got = U.gather_rows(U.widen_out(out, prob), prob, rows)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - want)
+    tol = U.out_tolerance(prob, want, out_f32)
+    print(f"max |out - oracle| = {err.max():.3e} (worst err - tol {np.max(err - tol):.3e})")
+    assert np.all(err <= tol)
+    assert not torch.isnan(out).any().item()  # every element written
+
+
+def test_forward_is_deterministic():
+    prob = workloads.get("nsa_prefill_8k", q_len=2048, kv_len=2048)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    a = nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"])
+    b = nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_with_given_summary_cache_matches_internal():
+    prob = workloads.get("nsa_decode_64x64k", batch=3, kv_len=3000)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    kc, vc = nsa.compress(prob, t["k"], t["v"])
+    a = nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"], k_cmp=kc, v_cmp=vc, out_f32=True)
+    b = nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"], out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_all_blocks_selected_equals_dense_causal_attention():
+    # top-k covering every block turns the selected branch into full attention
+    prob = workloads.get("nsa_prefill_8k", q_len=640, kv_len=640, top_k=16, use_cmp=0, use_win=0)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    out = nsa.forward(prob, t["q"], t["k"], t["v"], None, out_f32=True)
+    torch.cuda.synchronize()
+    q = inputs.bf16_bits_to_f32(x["q"][0]).astype(np.float64)
+    k = inputs.bf16_bits_to_f32(x["k"][0]).astype(np.float64)
+    v = inputs.bf16_bits_to_f32(x["v"][0]).astype(np.float64)
+    got = out.cpu().numpy()[0]
+    T = 640
+    mask = np.tril(np.ones((T, T), bool))
+    for h in (0, 17, 63):
+        g = h // 16
+        s = q[:, h] @ k[:, g].T / np.sqrt(192)
+        s[~mask] = -np.inf
+        pr = np.exp(s - s.max(1, keepdims=True))
+        pr /= pr.sum(1, keepdims=True)
+        assert np.abs(got[:, h] - pr @ v[:, g]).max() <= 2e-2
