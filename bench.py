@@ -1,0 +1,245 @@
+"""Benchmark of the NSA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+One step is one nsa_forward (pooling, selection, all three branches, gates)
+over the 64k-token prefill workload (B=1, T=65536, 4 KV groups x 16 heads,
+d_qk 192, d_v 128, block 64, top-16, window 512) with inputs resident in
+HBM.  Prints ONE JSON line: tokens/s, per-kernel times from HIP events
+recorded on the library's stream, the roofline of the dominant kernel, the
+batched-decode measurement (64 x 65536-token caches, % of HBM peak) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "NSA fwd tokens/s + % bf16 MFMA peak (64k prefill); decode % HBM peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- counts --
+
+def positions(prob):
+    return prob["kv_len"] - prob["q_len"] + np.arange(prob["q_len"], dtype=np.int64)
+
+
+def algorithmic_flops(prob):
+    """Per-branch algorithmic FLOPs of one forward: 2 per multiply-add, over
+    exactly the keys each branch attends to (masked work not counted)."""
+    p = positions(prob)
+    bs, n, w = prob["block"], prob["top_k"], prob["window"]
+    H, dq, dv = prob["n_groups"] * prob["heads_per_group"], prob["d_qk"], prob["d_v"]
+    per_key = 2.0 * (dq + dv) * H * prob["batch"]
+    nvis = np.minimum((p + 1) // bs, prob["kv_len"] // bs)
+    cur = p // bs
+    first, current = bool(prob["force_first"]), bool(prob["force_current"])
+    n_forced = np.full_like(p, int(first) + int(current))
+    if first and current:
+        n_forced[cur == 0] = 1
+    forced_visible = (int(first) * (nvis >= 1)) + (int(current) * (cur < nvis))
+    if first and current:
+        forced_visible = np.where(cur == 0, (nvis >= 1).astype(np.int64), forced_visible)
+    chosen = n_forced + np.minimum(n - n_forced, nvis - forced_visible)
+    cur_in = np.full(p.shape, current) | ((cur == 0) & first)
+    sel_keys = bs * chosen - np.where(cur_in, bs - (p % bs + 1), 0)
+    win_keys = np.minimum(w, p + 1) if (prob["use_win"] and w > 0) else np.zeros_like(p)
+    return {
+        "cmp": per_key * float(nvis.sum()) if prob["use_cmp"] else 0.0,
+        "slc": per_key * float(sel_keys.sum()),
+        "win": per_key * float(win_keys.sum()),
+    }
+
+
+# ---------------------------------------------------------------- prefill --
+
+def run_prefill(args, torch, nsa, workloads, inputs):
+    prob = workloads.get(args.workload)
+    log(f"workload {args.workload}: generating inputs")
+    t0 = time.time()
+    x = inputs.generate(prob)
+    log(f"inputs ready in {time.time() - t0:.1f}s; uploading")
+    t = {k: nsa.to_device(a, prob) for k, a in x.items()}
+    ws = nsa.alloc_workspace(prob)
+    out = torch.empty((1, prob["q_len"], workloads.n_heads(prob), prob["d_v"]), dtype=torch.bfloat16, device="cuda")
+    phases = nsa.forward_phases(prob)
+    K, W = args.steps, args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
+    for i in range(W):
+        nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"warmup done ({W} steps); timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"], out=out, workspace=ws, events=ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_phase = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                 for j, name in enumerate(phases)}
+    return prob, x, wall / K * 1e3, per_phase
+
+
+def prefill_roofline(prob, per_phase):
+    fl = algorithmic_flops(prob)
+    kernel_flops = {"selected": fl["slc"], "cmp_select_window": fl["cmp"] + fl["win"]}
+    dominant = max((k for k in per_phase if k in kernel_flops), key=lambda k: per_phase[k])
+    ms = per_phase[dominant]
+    achieved = kernel_flops[dominant] / (ms * 1e-3) / 1e12
+    roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "algorithmic_flop_per_launch": kernel_flops[dominant]}
+    return roof, fl
+
+
+# ----------------------------------------------------------------- decode --
+
+def run_decode(args, torch, nsa, workloads, inputs):
+    import concurrent.futures as cf
+    prob = workloads.get("nsa_decode_64x64k")
+    B, L, G, dq, dv = prob["batch"], prob["kv_len"], prob["n_groups"], prob["d_qk"], prob["d_v"]
+    H = workloads.n_heads(prob)
+    log("decode: generating 64 x 65536-token caches")
+    t0 = time.time()
+    dev = {"q": torch.empty((B, 1, H, dq), dtype=torch.bfloat16, device="cuda"),
+           "k": torch.empty((B, L, G, dq), dtype=torch.bfloat16, device="cuda"),
+           "v": torch.empty((B, L, G, dv), dtype=torch.bfloat16, device="cuda"),
+           "gates": torch.empty((B, 1, H, 3), dtype=torch.bfloat16, device="cuda")}
+    with cf.ThreadPoolExecutor(16) as pool:
+        for b in range(B):
+            xs = inputs.generate_sequence(prob, b, pool=pool)
+            for name, arr in xs.items():
+                dev[name][b:b + 1].copy_(nsa.to_device(arr, prob))
+    torch.cuda.synchronize()
+    log(f"decode inputs ready in {time.time() - t0:.1f}s")
+    kc, vc = nsa.compress(prob, dev["k"], dev["v"])
+    ws = nsa.alloc_workspace(prob, have_cmp=True)
+    out = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device="cuda")
+    idx, _ = nsa.select_topk(prob, dev["q"], kc, want_score=False)
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    phases = nsa.forward_phases(prob, have_cmp=True)
+    K = max(args.steps, 10)
+    times = []
+    per_phase = {n: [] for n in phases}
+    for i in range(args.warmup + K):
+        flush.fill_(i & 0xFF)  # evict the 256 MB last-level cache between steps
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        nsa.forward(prob, dev["q"], dev["k"], dev["v"], dev["gates"], out=out, k_cmp=kc, v_cmp=vc,
+                    workspace=ws, events=evs)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(evs[0].elapsed_time(evs[-1]))
+            for j, n in enumerate(phases):
+                per_phase[n].append(evs[j].elapsed_time(evs[j + 1]))
+    ms = float(np.median(times))
+    # algorithmic bytes: summaries, the union of selected and window blocks, q, gates, out
+    sel = idx.cpu().numpy()[:, 0]  # [B, G, n]
+    p = L - 1
+    win_blocks = set(range(max(0, p - prob["window"] + 1) // 64, p // 64 + 1))
+    nblk = sum(len(set(int(j) for j in sel[b, g] if j >= 0) | win_blocks) for b in range(B) for g in range(G))
+    nb = L // 64
+    byts = (B * G * nb * (dq + dv) * 2 + nblk * 64 * (dq + dv) * 2 + B * H * (dq + 3 + dv) * 2)
+    achieved = byts / (ms * 1e-3) / 1e9
+    return {"workload": "nsa_decode_64x64k", "batch": B, "kv_len": L, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "phases_ms": {n: round(float(np.median(v)), 4) for n, v in per_phase.items()},
+            "roofline": {"kernel": "whole decode step", "bound": "hbm", "achieved": round(achieved, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "traffic": None, "algorithmic_bytes_per_step": int(byts)},
+            "timing": "median of per-step HIP-event times; 512 MiB cache flush between steps"}
+
+
+# -------------------------------------------------------------- cpu oracle --
+
+def run_cpu_baseline(prob, x, target_s=15.0):
+    import oracle
+    T = prob["q_len"]
+    t0 = time.perf_counter()
+    kc, vc = oracle.pool(prob, x["k"], x["v"])
+    t_pool = time.perf_counter() - t0
+
+    def timed(rows):
+        s = time.perf_counter()
+        idx, _, ocmp = oracle.select(prob, x["q"], kc, vc, rows=rows, want_imp=False)
+        oracle.attend(prob, x["q"], x["k"], x["v"], x["gates"], idx, ocmp, rows=rows)
+        return time.perf_counter() - s
+
+    probe = np.linspace(0, T - 1, 16).astype(np.int64)
+    t_probe = timed(probe)
+    n = int(np.clip(target_s / max(t_probe / len(probe), 1e-6), 16, T))
+    rows = np.linspace(0, T - 1, n).astype(np.int64)
+    t_rows = timed(rows)
+    secs = t_rows + t_pool * n / T
+    return {"value": round(n / secs, 2), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} query rows evenly spaced over the {T}-token sequence (all 64 heads each); "
+                      f"pooling of the whole sequence ({t_pool:.2f}s) prorated by {n}/{T}",
+            "seconds": round(t_rows + t_pool, 2)}
+
+
+# ------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="nsa_prefill_64k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path runs on a single "
+              "MI355X and its multi-GPU sharding is a design note, not a measured mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_dynamic_amd import inputs, nsa, workloads
+    torch.cuda.set_device(0)
+    nsa.lib()
+
+    prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs)
+    roof, fl = prefill_roofline(prob, per_phase)
+    f_tot = fl["cmp"] + fl["slc"] + fl["win"]
+    tokens = prob["batch"] * prob["q_len"]
+    rec = {
+        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64: q,k,v ~ N(0,1), per-block key offset N(0,0.5^2), gates ~ U(0,1))",
+        "config": {"workload": args.workload, "batch": prob["batch"], "seq_len": prob["q_len"],
+                   "kv_groups": prob["n_groups"], "heads_per_group": prob["heads_per_group"],
+                   "d_qk": prob["d_qk"], "d_v": prob["d_v"], "block": prob["block"], "top_k": prob["top_k"],
+                   "window": prob["window"]},
+        "phases_ms": {k: round(v, 4) for k, v in per_phase.items()},
+        "algorithmic_tflop": {k: round(v / 1e12, 4) for k, v in fl.items()},
+        "forward_mfma_frac": round(f_tot / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+    }
+    log(f"prefill: {ms:.3f} ms/step, phases {rec['phases_ms']}")
+    if not args.no_decode:
+        del x
+        torch.cuda.empty_cache()
+        rec["decode"] = run_decode(args, torch, nsa, workloads, inputs)
+        log(f"decode: {rec['decode']['ms_per_step']} ms/step")
+        x = inputs.generate(prob)
+    if not args.no_cpu:
+        log("cpu baseline: timing the oracle on a sample")
+        rec["cpu_baseline"] = run_cpu_baseline(prob, x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

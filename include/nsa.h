@@ -99,6 +99,12 @@ typedef struct {
   void* workspace;         /* device scratch owned by the caller */
   size_t workspace_bytes;
   void* stream;            /* hipStream_t */
+  /* Optional timing hook (NULL = none): n_phase_events hipEvent_t handles
+   * owned by the caller.  nsa_forward records phase_events[0] on `stream`
+   * before its first kernel and phase_events[i + 1] after its i-th kernel
+   * (as far as events are given); nsa_forward_phases names the kernels. */
+  void* const* phase_events;
+  int32_t n_phase_events;
 } nsa_params;
 
 /*
@@ -146,6 +152,10 @@ nsa_status nsa_sparse_attn(const void* q, const void* k, const void* v, const in
  */
 nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates,
                        const nsa_params* params, void* out);
+
+/* Number of kernels nsa_forward launches for these params (0 if they are
+ * invalid); names[i] (i < max_names) receives a static name of kernel i. */
+int32_t nsa_forward_phases(const nsa_params* params, const char** names, int32_t max_names);
 
 /* Workspace bytes that any call above needs for these params (0 if none). */
 size_t nsa_workspace_bytes(const nsa_params* params);

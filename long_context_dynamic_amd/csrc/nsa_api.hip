@@ -111,9 +111,20 @@ nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* 
   const bool have_cmp = p->k_cmp != nullptr;
   const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Forward, have_cmp);
   if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
+  if (p->n_phase_events < 0 || (p->n_phase_events > 0 && !p->phase_events)) return NSA_ERR_INVALID_ARG;
+  nsa::Phases ph;
+  ph.ev = p->phase_events;
+  ph.n = p->phase_events ? p->n_phase_events : 0;
   return hip_status(nsa::run_forward(P, q, k, v, gates, have_cmp ? p->k_cmp : nullptr,
                                      have_cmp ? p->v_cmp : nullptr, out, ws, p->workspace,
-                                     (hipStream_t)p->stream));
+                                     (hipStream_t)p->stream, ph));
+}
+
+int32_t nsa_forward_phases(const nsa_params* p, const char** names, int32_t max_names) {
+  Prob P;
+  if (describe(p, &P) != NSA_OK) return 0;
+  const bool have_cmp = p->k_cmp != nullptr && p->v_cmp != nullptr;
+  return nsa::forward_phase_names(P, have_cmp, names, names ? max_names : 0);
 }
 
 }  // extern "C"

@@ -1,0 +1,55 @@
+// nsa_mfma.h -- gfx950 matrix-core building blocks for the NSA kernels.
+//
+// v_mfma_f32_16x16x32_bf16 (one wave, D = A * B + C, A 16x32, B 32x16):
+//   A: lane l holds A[l % 16][8 * (l / 16) + s], s = 0..7
+//   B: lane l holds B[8 * (l / 16) + s][l % 16]
+//   D: lane l holds D[4 * (l / 16) + r][l % 16], r = 0..3
+// The 32-long contraction index only has to be the same bijection for A and
+// B, so the kernels are free to assign any 32 keys (or dims) to the slots.
+#pragma once
+
+#include "nsa_internal.h"
+
+namespace nsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 contiguous bytes (8 bf16) from global or LDS memory.
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
+}
+// Two 8-byte halves (4 bf16 each) into one operand.
+__device__ __forceinline__ bf16x8 ld4x2(const uint16_t* lo, const uint16_t* hi) {
+  u32x2 a = *(const u32x2*)lo;
+  u32x2 b = *(const u32x2*)hi;
+  u32x4 r = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ float xor_max16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float xor_sum16_32(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace nsa

@@ -13,7 +13,25 @@ struct Workspace {
   size_t kc = 0, vc = 0;  // block summaries, when the caller gives none
   size_t idx = 0;         // int32 [B, T, G, top_k]
   size_t ocmp = 0;        // fp32 [B, T, H, d_v] compressed-branch output
+  size_t vT = 0;          // values, key-contiguous [B, G, d_v, round_up(L, 64)]
+  size_t vcT = 0;         // value summaries, block-contiguous [B, G, d_v, round_up(nb, 64)]
+  size_t acc = 0;         // fp32 [B, T, H, d_v] gated compressed + window sum
 };
+
+// Records an event before the first and after every launch (timing hook).
+struct Phases {
+  void* const* ev = nullptr;
+  int n = 0, i = 0;
+  hipStream_t s = nullptr;
+  hipError_t err = hipSuccess;
+  void mark() {
+    if (ev && i < n && err == hipSuccess) err = hipEventRecord((hipEvent_t)ev[i], s);
+    ++i;
+  }
+};
+
+// Names of the kernels run_forward launches, in order; returns the count.
+int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int max_names);
 
 enum class Call { Select, SparseAttn, Forward };
 
@@ -27,6 +45,6 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
                            void* out, float* lse, const Workspace& ws, void* base, hipStream_t s);
 hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
                        const void* kc_given, const void* vc_given, void* out, const Workspace& ws,
-                       void* base, hipStream_t s);
+                       void* base, hipStream_t s, Phases& ph);
 
 }  // namespace nsa

@@ -1,13 +1,25 @@
-// nsa_paths.hip -- workspace planning and dispatch of the forward pass.
+// nsa_paths.hip -- workspace planning and dispatch: the matrix-core kernels
+// for the shapes they take (bf16, 16 heads per group, 64-token blocks), the
+// any-shape kernels otherwise.
 #include "nsa_paths.h"
+#include "nsa_prefill.h"
 
 namespace nsa {
 namespace {
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t elem_bytes(const Prob& P) { return P.bf16() ? 2 : 4; }
+int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 
 template <typename T> T* at(void* base, size_t off) { return (T*)((char*)base + off); }
+
+PfArgs pf_args(const Prob& P) {
+  PfArgs a = {};
+  a.B = P.B; a.T = P.T; a.L = P.L; a.G = P.G; a.H = P.H; a.nb = P.nb;
+  a.nbp = pad64(P.nb); a.Lp = pad64(P.L); a.n = P.n; a.w = P.w;
+  a.flags = P.flags; a.scale = P.scale;
+  return a;
+}
 
 }  // namespace
 
@@ -15,13 +27,25 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
   Workspace w;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
-  if (call != Call::Forward) return w;  // the any-shape select/attend kernels need none
+  const bool fast = prefill_fast_ok(P);
+  if (call == Call::Select) return w;  // reads the caller's summaries directly
+  if (call == Call::SparseAttn) {
+    if (fast) w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+    w.total = off;
+    return w;
+  }
   if (!have_cmp) {
     w.kc = take((size_t)(P.B * P.nb * P.G * P.dq) * elem_bytes(P));
     w.vc = take((size_t)(P.B * P.nb * P.G * P.dv) * elem_bytes(P));
   }
   w.idx = take((size_t)(P.B * P.T * P.G * P.n) * sizeof(int32_t));
-  if (P.has(NSA_F_CMP)) w.ocmp = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
+  if (fast) {
+    w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+    w.vcT = take((size_t)(P.B * P.G * P.dv * pad64(P.nb)) * 2);
+    w.acc = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
+  } else if (P.has(NSA_F_CMP)) {
+    w.ocmp = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
+  }
   w.total = off;
   return w;
 }
@@ -35,33 +59,101 @@ size_t workspace_bytes_max(const Prob& P, bool have_cmp) {
   return m;
 }
 
+int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int max_names) {
+  const char* list[8];
+  int n = 0;
+  if (!have_cmp) list[n++] = "pool";
+  if (prefill_fast_ok(P)) {
+    list[n++] = "transpose_vc";
+    list[n++] = "transpose_v";
+    list[n++] = "cmp_select_window";
+    list[n++] = "selected";
+  } else {
+    list[n++] = "select_generic";
+    list[n++] = "attend_generic";
+  }
+  for (int i = 0; i < n && i < max_names; ++i) names[i] = list[i];
+  return n;
+}
+
 hipError_t run_select(const Prob& P, const void* q, const void* kc, int32_t* idx, float* score,
                       const Workspace&, void*, hipStream_t s) {
+  if (prefill_fast_ok(P)) {
+    PfArgs a = pf_args(P);
+    a.q = (const uint16_t*)q;
+    a.kc = (const uint16_t*)kc;
+    a.idx = idx;
+    a.score = score;
+    return launch_cmpwin(P, a, false, s);
+  }
   return launch_select_generic(P, q, kc, nullptr, idx, score, nullptr, s);
 }
 
 hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const void* v, const int32_t* idx,
-                           void* out, float* lse, const Workspace&, void*, hipStream_t s) {
+                           void* out, float* lse, const Workspace& ws, void* base, hipStream_t s) {
   Prob S = P;
   S.flags = NSA_F_SLC | (P.flags & NSA_F_OUT_F32);
+  if (prefill_fast_ok(P)) {
+    PfArgs a = pf_args(S);
+    uint16_t* vT = at<uint16_t>(base, ws.vT);
+    hipError_t e = launch_transpose(v, vT, P.B, P.L, a.Lp, P.G, (int)P.dv, s);
+    if (e != hipSuccess) return e;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.vT = vT;
+    a.idx = (int32_t*)idx;
+    a.out = out;
+    a.lse = lse;
+    return launch_sel(P, a, false, P.has(NSA_F_OUT_F32), s);
+  }
   return launch_attend_generic(S, q, k, v, nullptr, idx, nullptr, out, lse, P.has(NSA_F_OUT_F32), s);
 }
 
 hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
                        const void* kc_given, const void* vc_given, void* out, const Workspace& ws,
-                       void* base, hipStream_t s) {
+                       void* base, hipStream_t s, Phases& ph) {
   const void* kc = kc_given;
   const void* vc = vc_given;
   hipError_t e;
+  ph.s = s;
+  ph.mark();
   if (!kc) {
     kc = at<char>(base, ws.kc);
     vc = at<char>(base, ws.vc);
     if ((e = launch_pool(P, k, v, (void*)kc, (void*)vc, s)) != hipSuccess) return e;
+    ph.mark();
   }
   int32_t* idx = at<int32_t>(base, ws.idx);
+  if (prefill_fast_ok(P)) {
+    PfArgs a = pf_args(P);
+    uint16_t* vT = at<uint16_t>(base, ws.vT);
+    uint16_t* vcT = at<uint16_t>(base, ws.vcT);
+    if ((e = launch_transpose(vc, vcT, P.B, P.nb, a.nbp, P.G, (int)P.dv, s)) != hipSuccess) return e;
+    ph.mark();
+    if ((e = launch_transpose(v, vT, P.B, P.L, a.Lp, P.G, (int)P.dv, s)) != hipSuccess) return e;
+    ph.mark();
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.vT = vT;
+    a.kc = (const uint16_t*)kc;
+    a.vcT = vcT;
+    a.gates = (const uint16_t*)gates;
+    a.acc = at<float>(base, ws.acc);
+    a.idx = idx;
+    a.out = out;
+    if ((e = launch_cmpwin(P, a, true, s)) != hipSuccess) return e;
+    ph.mark();
+    if ((e = launch_sel(P, a, true, P.has(NSA_F_OUT_F32), s)) != hipSuccess) return e;
+    ph.mark();
+    return ph.err;
+  }
   float* ocmp = P.has(NSA_F_CMP) ? at<float>(base, ws.ocmp) : nullptr;
   if ((e = launch_select_generic(P, q, kc, vc, idx, nullptr, ocmp, s)) != hipSuccess) return e;
-  return launch_attend_generic(P, q, k, v, gates, idx, ocmp, out, nullptr, P.has(NSA_F_OUT_F32), s);
+  ph.mark();
+  if ((e = launch_attend_generic(P, q, k, v, gates, idx, ocmp, out, nullptr, P.has(NSA_F_OUT_F32), s)) != hipSuccess)
+    return e;
+  ph.mark();
+  return ph.err;
 }
 
 }  // namespace nsa

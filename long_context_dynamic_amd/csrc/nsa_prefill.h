@@ -1,0 +1,37 @@
+// nsa_prefill.h -- arguments and launchers of the matrix-core NSA kernels
+// (internal).
+#pragma once
+
+#include "nsa_internal.h"
+
+namespace nsa {
+
+struct PfArgs {
+  const uint16_t* q;      // [B, T, H, DQ]
+  const uint16_t* k;      // [B, L, G, DQ]
+  const uint16_t* vT;     // [B, G, DV, Lp]   values, key-contiguous
+  const uint16_t* kc;     // [B, nb, G, DQ]   block summaries
+  const uint16_t* vcT;    // [B, G, DV, nbp]  value summaries, block-contiguous
+  const uint16_t* gates;  // [B, T, H, 3] or NULL
+  float* acc;             // [B, T, H, DV]    gated compressed + window partial sum
+  int32_t* idx;           // [B, T, G, n]
+  float* score;           // [B, T, G, n] or NULL
+  void* out;              // [B, T, H, DV]
+  float* lse;             // [B, T, H] or NULL
+  int64_t B, T, L, G, H, nb, nbp, Lp, n, w;
+  uint32_t flags;
+  float scale;
+};
+
+// True when the matrix-core kernels take this shape: bf16, 16 heads per
+// group, 64-token blocks, d_qk in {64,128,192}, d_v in {64,128}, nb <= 2048.
+bool prefill_fast_ok(const Prob& P);
+
+hipError_t launch_transpose(const void* src, void* dst, int64_t B, int64_t N, int64_t Np, int64_t G, int D,
+                            hipStream_t s);
+// fwd: compressed + window + selection + gated partial (acc); else selection only.
+hipError_t launch_cmpwin(const Prob& P, const PfArgs& a, bool fwd, hipStream_t s);
+// fwd: out = acc + gate * selected branch; else out = selected branch (+ lse).
+hipError_t launch_sel(const Prob& P, const PfArgs& a, bool fwd, bool out_f32, hipStream_t s);
+
+}  // namespace nsa

@@ -20,7 +20,7 @@ STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "N
           4: "NSA_ERR_HIP"}
 
 EXPORTS = ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
-           "nsa_workspace_bytes", "nsa_status_str")
+           "nsa_forward_phases", "nsa_workspace_bytes", "nsa_status_str")
 
 
 class NsaError(RuntimeError):
@@ -39,6 +39,7 @@ class Params(ctypes.Structure):
         ("k_cmp", ctypes.c_void_p), ("v_cmp", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_phase_events", ctypes.c_int32),
     ]
 
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_forward.argtypes = [vp, vp, vp, vp, P, vp]
         L.nsa_workspace_bytes.argtypes = [P]
         L.nsa_workspace_bytes.restype = ctypes.c_size_t
+        L.nsa_forward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
+        L.nsa_forward_phases.restype = ctypes.c_int32
         L.nsa_status_str.argtypes = [ctypes.c_int]
         L.nsa_status_str.restype = ctypes.c_char_p
         for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward"):
@@ -198,8 +201,17 @@ def sparse_attn(prob: dict, q, k, v, idx, out=None, lse=None, want_lse=True, out
     return out, lse
 
 
+def forward_phases(prob: dict, have_cmp: bool = False) -> list:
+    """Names of the kernels nsa_forward launches for this problem, in order."""
+    p = params(prob, stream=_NoStream)
+    p.k_cmp = p.v_cmp = (16 if have_cmp else None)
+    names = (ctypes.c_char_p * 16)()
+    n = lib().nsa_forward_phases(ctypes.byref(p), names, 16)
+    return [names[i].decode() for i in range(min(n, 16))]
+
+
 def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f32=False,
-            workspace=None, stream=None):
+            workspace=None, stream=None, events=None):
     s, dt = _shapes(prob), torch_dtype(prob)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check(t, s[name], dt, name)
@@ -214,6 +226,12 @@ def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f3
     if workspace is None:
         workspace = alloc_workspace(prob, k_cmp is not None, q.device)
     p = params(prob, out_f32=out_f32, k_cmp=k_cmp, v_cmp=v_cmp, workspace=workspace, stream=stream)
+    if events is not None:  # torch.cuda.Event list: recorded around each kernel
+        for e in events:
+            if not e.cuda_event:  # torch creates the HIP event on first record
+                e.record()
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        p.phase_events, p.n_phase_events = handles, len(events)
     _call("nsa_forward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), ctypes.byref(p),
           out.data_ptr())
     return out
