@@ -131,7 +131,7 @@ def run_decode(args, torch, nsa, workloads, inputs):
     idx, _ = nsa.select_topk(prob, dev["q"], kc, want_score=False)
     flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
     phases = nsa.forward_phases(prob, have_cmp=True)
-    K = max(args.steps, 10)
+    K = args.steps if args.only else max(args.steps, 10)
     times = []
     per_phase = {n: [] for n in phases}
     for i in range(args.warmup + K):
@@ -189,6 +189,27 @@ def run_cpu_baseline(prob, x, target_s=15.0):
             "seconds": round(t_rows + t_pool, 2)}
 
 
+# ------------------------------------------------------- profiling legs --
+
+def run_only(args, torch, nsa, workloads, inputs):
+    """One leg for a profiler: prefill or decode steps, or a plain 1 GiB
+    device copy whose byte counters calibrate the others'."""
+    if args.only == "copy":
+        a = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied 1 GiB x {args.steps}")
+    elif args.only == "prefill":
+        args.steps, args.warmup = max(1, args.steps), args.warmup
+        _, _, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs)
+        log(f"prefill {ms:.3f} ms/step {per_phase}")
+    else:
+        rec = run_decode(args, torch, nsa, workloads, inputs)
+        log(f"decode {rec['ms_per_step']} ms/step {rec['phases_ms']}")
+
+
 # ------------------------------------------------------------------- main --
 
 def main():
@@ -199,6 +220,8 @@ def main():
     ap.add_argument("--workload", default="nsa_prefill_64k")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path runs on a single "
@@ -209,6 +232,9 @@ def main():
     from long_context_dynamic_amd import inputs, nsa, workloads
     torch.cuda.set_device(0)
     nsa.lib()
+    if args.only:
+        run_only(args, torch, nsa, workloads, inputs)
+        return
 
     prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs)
     roof, fl = prefill_roofline(prob, per_phase)

@@ -1,0 +1,470 @@
+// k_decode.hip -- NSA forward for a few query tokens against a long cache
+// (decoding, [P1] s6: memory-bound, time set by the KV bytes read, which the
+// group-shared selection keeps small).  Same arithmetic as the prefill path,
+// reorganised so that many waves stream the cache at once:
+//
+//   k_dec_cmp     one wave per (row, group, 2 tiles of 64 block summaries):
+//                 compressed-branch logits (kept in zbuf for the importance)
+//                 and a partial softmax-weighted sum of the value summaries.
+//   k_dec_select  one workgroup per (row, group): per-head softmax statistics
+//                 from the partials, group importance, top-k (one wave).
+//   k_dec_attn    one wave per (row, group, slice of the key blocks): the
+//                 selected blocks (4 per wave) and the window blocks, each
+//                 with its own online softmax.
+//   k_dec_merge   one workgroup per (row, group): log-sum-exp merge of each
+//                 branch's partials, gates, output.
+// Every streaming wave runs the same tile loop: K fragments straight from
+// global memory into matrix-op registers, the V tile through LDS (read back
+// transposed), the next tile's reads issued before the current softmax, and
+// a partial record (max, sum, unnormalised output) at the end.
+// A row is one (batch, query) pair at position p = kv_len - q_len + t.
+#include <math.h>
+
+#include <type_traits>
+
+#include "nsa_decode.h"
+#include "nsa_mfma.h"
+
+namespace nsa {
+namespace {
+
+constexpr int MAX_NB_LANE = 32;  // nb <= 2048
+constexpr int SLOTS_PER_WAVE = 4;      // selected blocks per streaming wave
+constexpr int TILES_PER_CMP_WAVE = 2;  // 64-summary tiles per compressed-branch wave
+
+__device__ __forceinline__ float dgate(const DecArgs& a, int64_t hrow, int branch) {
+  if (!a.gates) return 1.f;
+  float x = bf16_to_f32(a.gates[hrow * 3 + branch]);
+  return (a.flags & NSA_F_GATE_LOGITS) ? sigmoid(x) : x;
+}
+
+__device__ __forceinline__ bool dbetter(float v, int j, float bv, int bj) {
+  return v > bv || (v == bv && j < bj);
+}
+
+// ---------------------------------------------------------------------------
+// Partial record of one wave: [16 heads][DV] unnormalised outputs, then
+// [16] maxima (log2 units) and [16] sums.
+template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
+
+// Stream 64-row tiles `tiles[0..nt)` of K [B, N, G, DQ] / V [B, N, G, DV] for
+// one (b, g) and the 16 heads in qf; keep rows where ok(row).  Writes scaled
+// logits to zrow[h * zstride + row] when zrow is given.  Ends by writing the
+// wave's partial record.  WITH_V = false: softmax statistics only, V is never
+// read (its output part of the record is left as zeros).
+template <int DQ, int DV, bool WITH_V, typename Ok>
+__device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* V, int64_t N, int64_t b, int64_t g,
+                                             int64_t G, const int* tiles, int nt, Ok ok, const bf16x8 (&qf)[DQ / 32],
+                                             float c, uint16_t* myv, float* zrow, int64_t zstride, float* rec) {
+  constexpr int VS = DV + 8;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[DV / 16];
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 kf[4][DQ / 32];
+  u32x4 vreg[DV / 8];
+  auto load_k = [&](int i) {
+    const int64_t kb = (int64_t)tiles[i] * 64;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      int64_t r = kb + 16 * mt + lr;
+      if (r > N - 1) r = N - 1;
+      const uint16_t* kr = K + ((b * N + r) * G + g) * DQ + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < DQ / 32; ++ks) kf[mt][ks] = ld8(kr + 32 * ks);
+    }
+  };
+  auto load_v = [&](int i) {
+    const int64_t kb = (int64_t)tiles[i] * 64;
+#pragma unroll
+    for (int q = 0; q < DV / 8; ++q) {
+      const int cidx = lane + 64 * q;  // 64 rows x DV/8 chunks
+      const int r = cidx / (DV / 8), c8 = cidx % (DV / 8);
+      int64_t row = kb + r;
+      if (row > N - 1) row = N - 1;
+      vreg[q] = *(const u32x4*)(V + ((b * N + row) * G + g) * DV + 8 * c8);
+    }
+  };
+  if (nt > 0) {
+    load_k(0);
+    if (WITH_V) load_v(0);
+  }
+  // the next tile's reads are issued as soon as this tile's registers are
+  // free; the last tile is peeled so no tile is read twice
+  auto tile = [&](int i, auto prefetch) {
+    constexpr bool PF = decltype(prefetch)::value;
+    const int64_t kb = (int64_t)tiles[i] * 64;
+    f32x4 s[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DQ / 32; ++ks) s[mt] = mfma16(kf[mt][ks], qf[ks], s[mt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (PF) load_k(i + 1);
+    if (WITH_V) {
+#pragma unroll
+      for (int q = 0; q < DV / 8; ++q) {
+        const int cidx = lane + 64 * q;
+        const int r = cidx / (DV / 8), c8 = cidx % (DV / 8);
+        *(u32x4*)(myv + r * VS + 8 * c8) = vreg[q];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (PF) load_v(i + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // s[mt][r]: row kb + 16*mt + 4*lg + r, head lr
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = kb + 16 * mt + 4 * lg + r;
+        if (!ok(row)) s[mt][r] = -INFINITY;
+        else if (zrow) zrow[lr * zstride + row] = s[mt][r] * c;
+        tmax = fmaxf(tmax, s[mt][r]);
+      }
+    tmax = xor_max16_32(tmax);
+    const float mnew = fmaxf(m, tmax);
+    const float alpha = mnew == -INFINITY ? 1.f : exp2f((m - mnew) * c);
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = mnew == -INFINITY ? 0.f : exp2f((s[mt][r] - mnew) * c);
+        s[mt][r] = pv;
+        rs += pv;
+      }
+    rs = xor_sum16_32(rs);
+    l = l * alpha + rs;
+    m = mnew;
+    if (!WITH_V) return;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const bf16x8 p0 = pack8(s[0], s[1]);
+    const bf16x8 p1 = pack8(s[2], s[3]);
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      const int d = 16 * dt + lr;
+      bf16x8 va, vb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        va[e] = __builtin_bit_cast(__bf16, myv[(4 * lg + e) * VS + d]);
+        va[4 + e] = __builtin_bit_cast(__bf16, myv[(16 + 4 * lg + e) * VS + d]);
+        vb[e] = __builtin_bit_cast(__bf16, myv[(32 + 4 * lg + e) * VS + d]);
+        vb[4 + e] = __builtin_bit_cast(__bf16, myv[(48 + 4 * lg + e) * VS + d]);
+      }
+      o[dt] = mfma16(va, p0, o[dt] * alpha);
+      o[dt] = mfma16(vb, p1, o[dt]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  };
+  for (int i = 0; i + 1 < nt; ++i) tile(i, std::true_type{});
+  if (nt > 0) tile(nt - 1, std::false_type{});
+  // o^T: lane holds d = 16*dt + 4*lg + r of head lr
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(rec + lr * DV + 16 * dt + 4 * lg) = o[dt];
+  if (lg == 0) {
+    rec[16 * DV + lr] = m == -INFINITY ? -INFINITY : m * c;
+    rec[16 * DV + 16 + lr] = l;
+  }
+}
+
+template <int DQ>
+__device__ __forceinline__ void load_q(const DecArgs& a, int64_t row, int64_t g, bf16x8 (&qf)[DQ / 32]) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const uint16_t* qr = a.q + (row * a.H + g * 16 + lr) * DQ + 8 * lg;
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+}
+
+// ---------------------------------------------------------------------------
+template <int DQ, int DV, bool WITH_V>
+__global__ void __launch_bounds__(256) k_dec_cmp(DecArgs a) {
+  __shared__ __align__(16) uint16_t vt[4][64 * (DV + 8)];
+  const int wave = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row, g, cmp wave)
+  if (item >= a.R * a.G * a.n_cmp_waves) return;
+  const int64_t cw = item % a.n_cmp_waves;
+  const int64_t g = (item / a.n_cmp_waves) % a.G;
+  const int64_t row = item / (a.n_cmp_waves * a.G);
+  const int64_t b = row / a.T, t = row % a.T;
+  const int64_t p = a.L - a.T + t;
+  int64_t nvis = (p + 1) / 64;
+  if (nvis > a.nb) nvis = a.nb;
+  int tiles[TILES_PER_CMP_WAVE];
+  int nt = 0;
+  for (int i = 0; i < TILES_PER_CMP_WAVE; ++i) {
+    const int64_t jt = cw * TILES_PER_CMP_WAVE + i;
+    if (jt * 64 < nvis) tiles[nt++] = (int)jt;
+  }
+  bf16x8 qf[DQ / 32];
+  load_q<DQ>(a, row, g, qf);
+  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
+  float* rec = a.part + ((row * a.G + g) * nwaves + cw) * part_floats<DV>();
+  float* zrow = a.zbuf + (row * a.G + g) * 16 * a.nbp;
+  stream_tiles<DQ, DV, WITH_V>(a.kc, a.vc, a.nb, b, g, a.G, tiles, nt, [&](int64_t j) { return j < nvis; }, qf,
+                               a.scale * kLog2e, vt[wave], zrow, a.nbp, rec);
+}
+
+template <int DQ, int DV>
+__global__ void __launch_bounds__(256) k_dec_attn(DecArgs a) {
+  __shared__ __align__(16) uint16_t vt[4][64 * (DV + 8)];
+  const int wave = threadIdx.x >> 6;
+  const int64_t nsw = a.n_sel_waves + a.n_win_waves;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row, g, wave slot)
+  if (item >= a.R * a.G * nsw) return;
+  const int64_t ws = item % nsw;
+  const int64_t g = (item / nsw) % a.G;
+  const int64_t row = item / (nsw * a.G);
+  const int64_t b = row / a.T, t = row % a.T;
+  const int64_t p = a.L - a.T + t;
+  const bool is_win = ws >= a.n_sel_waves;
+  int tiles[SLOTS_PER_WAVE + 1];
+  int nt = 0;
+  int64_t lo = 0;
+  if (!is_win) {
+    if (a.flags & NSA_F_SLC) {
+      for (int i = 0; i < SLOTS_PER_WAVE; ++i) {
+        const int64_t slot = ws * SLOTS_PER_WAVE + i;
+        const int j = slot < a.n ? a.idx[(row * a.G + g) * a.n + slot] : -1;
+        if (j >= 0 && (int64_t)j * 64 <= p) tiles[nt++] = j;
+      }
+    }
+  } else if ((a.flags & NSA_F_WIN) && a.w > 0) {
+    lo = p - a.w + 1;
+    if (lo < 0) lo = 0;
+    const int64_t kb0 = lo / 64, kb1 = p / 64;
+    const int64_t per = (kb1 - kb0 + a.n_win_waves) / a.n_win_waves;
+    const int64_t first = kb0 + (ws - a.n_sel_waves) * per;
+    for (int64_t j = first; j <= kb1 && j < first + per && nt < SLOTS_PER_WAVE + 1; ++j) tiles[nt++] = (int)j;
+  }
+  bf16x8 qf[DQ / 32];
+  load_q<DQ>(a, row, g, qf);
+  const int64_t nwaves = a.n_cmp_waves + nsw;
+  float* rec = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves + ws) * part_floats<DV>();
+  const float c = a.scale * kLog2e;
+  if (!is_win)
+    stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, tiles, nt, [&](int64_t s) { return s <= p; }, qf, c,
+                               vt[wave], nullptr, 0, rec);
+  else
+    stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, tiles, nt, [&](int64_t s) { return s <= p && s >= lo; }, qf,
+                               c, vt[wave], nullptr, 0, rec);
+}
+
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
+  __shared__ float imp[64 * MAX_NB_LANE];
+  __shared__ float sM[16], sL[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t g = blockIdx.x % a.G;
+  const int64_t row = blockIdx.x / a.G;
+  const int64_t t = row % a.T;
+  const int64_t p = a.L - a.T + t;
+  int64_t nvis = (p + 1) / 64;
+  if (nvis > a.nb) nvis = a.nb;
+  const float* z = a.zbuf + (row * a.G + g) * 16 * a.nbp;
+  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
+  const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
+  // per-head softmax statistics from the compressed-branch partials
+  if (tid < 16) {
+    float M = -INFINITY;
+    for (int64_t w = 0; w < a.n_cmp_waves; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + tid]);
+    float L = 0.f;
+    for (int64_t w = 0; w < a.n_cmp_waves; ++w) {
+      const float mw = base[w * part_floats<DV>() + 16 * DV + tid];
+      if (mw != -INFINITY) L = fmaf(exp2f(mw - M), base[w * part_floats<DV>() + 16 * DV + 16 + tid], L);
+    }
+    sM[tid] = M;
+    sL[tid] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  for (int64_t j = tid; j < nvis; j += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < 16; ++h) s += exp2f(z[h * a.nbp + j] - sM[h]) * sL[h];
+    imp[j] = s;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t cur = p / 64;
+  int forced[2];
+  int nf = 0;
+  if (a.flags & NSA_F_FORCE_FIRST) forced[nf++] = 0;
+  if ((a.flags & NSA_F_FORCE_CURRENT) && !((a.flags & NSA_F_FORCE_FIRST) && cur == 0)) forced[nf++] = (int)cur;
+  float vals[MAX_NB_LANE];
+#pragma unroll
+  for (int i = 0; i < MAX_NB_LANE; ++i) {
+    const int64_t j = lane + 64 * i;
+    vals[i] = j < nvis ? imp[j] : -1.f;
+  }
+  int ncand = (int)nvis;
+  for (int f = 0; f < nf; ++f) {
+    if (forced[f] < nvis) {
+      --ncand;
+#pragma unroll
+      for (int i = 0; i < MAX_NB_LANE; ++i)
+        if (lane + 64 * i == forced[f]) vals[i] = -1.f;
+    }
+  }
+  const int r_take = ((int)a.n - nf) < ncand ? ((int)a.n - nf) : ncand;
+  int cj = -1;
+  float cs = -INFINITY;
+  for (int f = 0; f < nf; ++f)
+    if (lane == f) { cj = forced[f]; cs = INFINITY; }
+  for (int round = 0; round < r_take; ++round) {
+    float bv = -1.f;
+    int bj = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < MAX_NB_LANE; ++i)
+      if (vals[i] > bv) { bv = vals[i]; bj = lane + 64 * i; }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oj = __shfl_xor(bj, off, 64);
+      if (dbetter(ov, oj, bv, bj)) { bv = ov; bj = oj; }
+    }
+#pragma unroll
+    for (int i = 0; i < MAX_NB_LANE; ++i)
+      if (lane + 64 * i == bj) vals[i] = -1.f;
+    if (lane == nf + round) { cj = bj; cs = bv; }
+  }
+  const int cnt = nf + r_take;
+  int rank = 0;
+  for (int k2 = 0; k2 < cnt; ++k2) rank += (__shfl(cj, k2, 64) < cj) ? 1 : 0;
+  int32_t* orow = a.idx + (row * a.G + g) * a.n;
+  float* srow = a.score ? a.score + (row * a.G + g) * a.n : nullptr;
+  if (lane < cnt) {
+    orow[rank] = cj;
+    if (srow) srow[rank] = cs;
+  } else if (lane < a.n) {
+    orow[lane] = -1;
+    if (srow) srow[lane] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of each branch's partial records, gates, output.  With
+// gates == NULL every enabled branch has weight 1; lse (selected branch only,
+// natural log) is written when given.
+template <int DV, typename TO>
+__global__ void __launch_bounds__(256) k_dec_merge(DecArgs a) {
+  constexpr int MAXW = 32;
+  __shared__ float coef[16][MAXW];  // weight of each partial in its branch's merge
+  __shared__ float slse[16];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x % a.G;
+  const int64_t row = blockIdx.x / a.G;
+  const int nc = (int)a.n_cmp_waves, ns = (int)a.n_sel_waves, nwaves = nc + ns + (int)a.n_win_waves;
+  const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
+  if (tid < 48) {
+    const int h = tid & 15, br = tid >> 4;  // 0 cmp, 1 sel, 2 win
+    const int w0 = br == 0 ? 0 : (br == 1 ? nc : nc + ns), w1 = br == 0 ? nc : (br == 1 ? nc + ns : nwaves);
+    float M = -INFINITY;
+    for (int w = w0; w < w1; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + h]);
+    float den = 0.f;
+    for (int w = w0; w < w1; ++w) {
+      const float mw = base[w * part_floats<DV>() + 16 * DV + h];
+      const float sc = (M == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      coef[h][w] = sc;
+      den = fmaf(sc, base[w * part_floats<DV>() + 16 * DV + 16 + h], den);
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int w = w0; w < w1; ++w) coef[h][w] *= inv;
+    if (br == 1) slse[h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+  }
+  __syncthreads();
+  const bool use_cmp = a.flags & NSA_F_CMP, use_slc = a.flags & NSA_F_SLC;
+  const bool use_win = (a.flags & NSA_F_WIN) && a.w > 0;
+  for (int item = tid; item < 16 * DV / 4; item += 256) {
+    const int h = item / (DV / 4), d = 4 * (item % (DV / 4));
+    f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int w = 0; w < nwaves; ++w) {
+      const f32x4 v = *(const f32x4*)(base + w * part_floats<DV>() + h * DV + d);
+      br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v * coef[h][w];
+    }
+    const int64_t hrow = row * a.H + g * 16 + h;
+    f32x4 out = {0.f, 0.f, 0.f, 0.f};
+    if (use_cmp) out += br[0] * dgate(a, hrow, 0);
+    if (use_slc) out += br[1] * dgate(a, hrow, 1);
+    if (use_win) out += br[2] * dgate(a, hrow, 2);
+    if (sizeof(TO) == 2) {
+      u32x2 wv = {(uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16),
+                  (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16)};
+      *(u32x2*)((uint16_t*)a.out + hrow * DV + d) = wv;
+    } else {
+      *(f32x4*)((float*)a.out + hrow * DV + d) = out;
+    }
+  }
+  if (a.lse && tid < 16) a.lse[row * a.H + g * 16 + tid] = slse[tid];
+}
+
+// mode: 0 selection only, 1 whole forward, 2 selected branch on a given idx
+template <int DQ, int DV>
+hipError_t run_t(const DecArgs& a, int mode, bool out_f32, hipStream_t s, Phases* ph) {
+  const int64_t nsw = a.n_sel_waves + a.n_win_waves;
+  if (mode != 2) {
+    // selection only: the value summaries are not an input (and not read)
+    const unsigned gc = (unsigned)((a.R * a.G * a.n_cmp_waves + 3) / 4);
+    if (mode == 0) k_dec_cmp<DQ, DV, false><<<gc, 256, 0, s>>>(a);
+    else k_dec_cmp<DQ, DV, true><<<gc, 256, 0, s>>>(a);
+    if (ph) ph->mark();
+    k_dec_select<DV><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+    if (ph) ph->mark();
+    if (mode == 0) return hipGetLastError();
+  }
+  k_dec_attn<DQ, DV><<<(unsigned)((a.R * a.G * nsw + 3) / 4), 256, 0, s>>>(a);
+  if (ph) ph->mark();
+  if (out_f32) k_dec_merge<DV, float><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+  else k_dec_merge<DV, uint16_t><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+  if (ph) ph->mark();
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void decode_layout(const Prob& P, int64_t* n_cmp_waves, int64_t* n_sel_waves, int64_t* n_win_waves) {
+  const int64_t nbp = (P.nb + 63) / 64 * 64;
+  *n_cmp_waves = (nbp / 64 + TILES_PER_CMP_WAVE - 1) / TILES_PER_CMP_WAVE;
+  if (*n_cmp_waves < 1) *n_cmp_waves = 1;
+  *n_sel_waves = (P.n + SLOTS_PER_WAVE - 1) / SLOTS_PER_WAVE;
+  // window blocks: at most ceil(w / 64) + 1, spread over waves of <= SLOTS_PER_WAVE + 1 blocks
+  const int64_t wblocks = P.w > 0 ? (P.w + 63) / 64 + 1 : 0;
+  *n_win_waves = wblocks > 0 ? (wblocks + SLOTS_PER_WAVE) / (SLOTS_PER_WAVE + 1) : 1;
+}
+
+bool decode_ok(const Prob& P) {
+  const int64_t nbp = (P.nb + 63) / 64 * 64;
+  if (!(P.bf16() && P.hpg == 16 && P.bs == 64 && P.T <= 8 && (P.dq == 64 || P.dq == 128 || P.dq == 192) &&
+        (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE && P.n <= 32 && P.n >= 1))
+    return false;
+  int64_t nc, ns, nw;
+  decode_layout(P, &nc, &ns, &nw);
+  return nc + ns + nw <= 32;  // partial records one merge workgroup weighs
+}
+
+size_t decode_part_bytes(const Prob& P) {
+  int64_t nc, ns, nw;
+  decode_layout(P, &nc, &ns, &nw);
+  return (size_t)(P.B * P.T * P.G * (nc + ns + nw) * (16 * P.dv + 32)) * sizeof(float);
+}
+
+hipError_t launch_decode(const Prob& P, DecArgs a, int mode, bool out_f32, hipStream_t s, Phases* ph) {
+  decode_layout(P, &a.n_cmp_waves, &a.n_sel_waves, &a.n_win_waves);
+#define CALL_DEC(DQ, DV) run_t<DQ, DV>(a, mode, out_f32, s, ph)
+  if (P.dq == 192 && P.dv == 128) return CALL_DEC(192, 128);
+  if (P.dq == 128 && P.dv == 128) return CALL_DEC(128, 128);
+  if (P.dq == 64 && P.dv == 64) return CALL_DEC(64, 64);
+  if (P.dq == 192 && P.dv == 64) return CALL_DEC(192, 64);
+  if (P.dq == 128 && P.dv == 64) return CALL_DEC(128, 64);
+  if (P.dq == 64 && P.dv == 128) return CALL_DEC(64, 128);
+#undef CALL_DEC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nsa

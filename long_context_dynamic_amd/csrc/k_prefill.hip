@@ -2,9 +2,12 @@
 // query heads and 64-token blocks ([P1] s4 three branches; [P1] s5 the group's
 // heads stacked as the matrix M dimension instead of a block of queries).
 //
-//   k_transpose  V [B, N, G, D] -> V^T [B, G, D, Np] (key-contiguous rows,
-//                zero padded to Np = round_up(N, 64)); makes every P.V operand
-//                one contiguous load.
+//   k_transpose  V [B, N, G, D] -> block-tiled V^T [B, G, Np / 64, D, 64]
+//                (each 64-key tile one contiguous D x 64 chunk, zero padded to
+//                Np = round_up(N, 64)); makes every P.V operand one contiguous
+//                load and every tile one contiguous read.
+//   k_group_major  K [B, L, G, D] -> [B, G, L, D]: each 64-key block of one
+//                group becomes one contiguous 64 x D chunk.
 //   k_cmpwin     one workgroup per (8-token query tile, KV group), one wave
 //                per token: compressed branch (online softmax over the block
 //                summaries), group importance (second pass, each head's
@@ -59,35 +62,77 @@ __global__ void __launch_bounds__(256) k_transpose(const uint16_t* __restrict__ 
     for (int i = 0; i < 8; ++i) w[i] = tile[8 * k8 + i][d];
     u32x4 val = {(uint32_t)w[0] | ((uint32_t)w[1] << 16), (uint32_t)w[2] | ((uint32_t)w[3] << 16),
                  (uint32_t)w[4] | ((uint32_t)w[5] << 16), (uint32_t)w[6] | ((uint32_t)w[7] << 16)};
-    *(u32x4*)(dst + ((b * G + g) * D + d) * Np + n0 + 8 * k8) = val;
+    *(u32x4*)(dst + (((b * G + g) * ntile + tix) * D + d) * 64 + 8 * k8) = val;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_group_major(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     int64_t L, int64_t G, int D) {
+  // one workgroup per (b, 64-row slab); rows of all groups are read once
+  const int64_t nslab = (L + 63) / 64;
+  const int64_t b = blockIdx.x / nslab, s0 = (blockIdx.x % nslab) * 64;
+  const int chunks = D / 8;
+  for (int64_t c = threadIdx.x; c < 64 * G * chunks; c += 256) {
+    const int64_t r = c / (G * chunks), g = (c / chunks) % G, c8 = c % chunks;
+    if (s0 + r >= L) continue;
+    const u32x4 val = *(const u32x4*)(src + ((b * L + s0 + r) * G + g) * D + 8 * c8);
+    *(u32x4*)(dst + ((b * G + g) * L + s0 + r) * D + 8 * c8) = val;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Stage rows [row0, row0 + 64) of a [B, Nrows, G, DQ] tensor (rows clamped to
-// Nrows - 1) into LDS with a padded row stride.
-template <int DQ>
-__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* src, int64_t b, int64_t g, int64_t G,
-                                           int64_t Nrows, int64_t row0) {
-  constexpr int KS = DQ + 8, C = DQ / 8;
-  for (int c = threadIdx.x; c < 64 * C; c += blockDim.x) {
-    const int r = c / C, c8 = c % C;
-    int64_t row = row0 + r;
-    if (row > Nrows - 1) row = Nrows - 1;
-    *(u32x4*)(lds + r * KS + 8 * c8) = *(const u32x4*)(src + ((b * Nrows + row) * G + g) * DQ + 8 * c8);
-  }
-}
+// Register-prefetching tile stager: load() issues the global reads of one
+// 64-key tile (K rows [row0, row0 + 64) of a [B, Nrows, G, DQ] tensor, rows
+// clamped to Nrows - 1, and optionally V^T columns [col0, col0 + 64) of a
+// [B, G, DV, Np] tensor) into registers; store() writes them to LDS.  The
+// next tile's reads are in flight while the current tile is computed on.
+template <int DQ, int DV, int NT>
+struct Stager {
+  static constexpr int KS = DQ + 8, VS = 64 + 8;
+  static constexpr int KC = 64 * DQ / 8, VC = DV * 8;
+  static constexpr int KPT = (KC + NT - 1) / NT, VPT = (VC + NT - 1) / NT;
+  u32x4 kr[KPT], vr[VPT];
 
-// Stage columns [col0, col0 + 64) of a transposed [B, G, DV, Np] tensor.
-template <int DV>
-__device__ __forceinline__ void stage_cols(uint16_t* lds, const uint16_t* srcT, int64_t b, int64_t g, int64_t G,
-                                           int64_t Np, int64_t col0) {
-  constexpr int VS = 64 + 8;
-  for (int c = threadIdx.x; c < DV * 8; c += blockDim.x) {
-    const int d = c / 8, c8 = c % 8;
-    *(u32x4*)(lds + d * VS + 8 * c8) = *(const u32x4*)(srcT + ((b * G + g) * DV + d) * Np + col0 + 8 * c8);
+  // rows: [B, Nrows, G, DQ], or [B, G, Nrows, DQ] when group_major;
+  // colsT: block-tiled [B, G, Np / 64, DV, 64]
+  __device__ __forceinline__ void load(const uint16_t* rows, int64_t Nrows, int64_t row0, bool group_major,
+                                       const uint16_t* colsT, int64_t Np, int64_t col0, int64_t b, int64_t g,
+                                       int64_t G, bool with_v) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (KC % NT == 0 || c < KC) {
+        const int r = c / (DQ / 8), c8 = c % (DQ / 8);
+        int64_t row = row0 + r;
+        if (row > Nrows - 1) row = Nrows - 1;
+        const int64_t off = group_major ? ((b * G + g) * Nrows + row) * DQ : ((b * Nrows + row) * G + g) * DQ;
+        kr[i] = *(const u32x4*)(rows + off + 8 * c8);
+      }
+    }
+    if (with_v) {
+      const uint16_t* tile = colsT + ((b * G + g) * (Np / 64) + col0 / 64) * DV * 64;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (VC % NT == 0 || c < VC) vr[i] = *(const u32x4*)(tile + 8 * c);
+      }
+    }
   }
-}
+  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, bool with_v) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (KC % NT == 0 || c < KC) *(u32x4*)(kt + (c / (DQ / 8)) * KS + 8 * (c % (DQ / 8))) = kr[i];
+    }
+    if (with_v) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (VC % NT == 0 || c < VC) *(u32x4*)(vt + (c / 8) * VS + 8 * (c % 8)) = vr[i];
+      }
+    }
+  }
+};
 
 // One 64-key online-softmax step for one token (16 heads) of one wave.
 // s[mt] holds S^T for keys 16*mt + 4*lg + r (raw dot products, masked ones
@@ -190,11 +235,14 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   f32x4 o[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t jt = 0; jt * 64 < nvis_max; ++jt) {
+  Stager<DQ, DV, TQ * 64> st;
+  const int64_t ntile_cmp = (nvis_max + 63) / 64;
+  if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, false, a.vcT, a.nbp, 0, b, g, a.G, use_cmp);
+  for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
-    stage_rows<DQ>(kt, a.kc, b, g, a.G, a.nb, jt * 64);
-    if (use_cmp) stage_cols<DV>(vt, a.vcT, b, g, a.G, a.nbp, jt * 64);
+    st.store(kt, vt, use_cmp);
     __syncthreads();
+    if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, false, a.vcT, a.nbp, (jt + 1) * 64, b, g, a.G, use_cmp);
     if (jt * 64 < nvis) {
       f32x4 s[4];
       qk_tile_T<DQ>(kt, qf, s, lr, lg);
@@ -224,10 +272,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     ih[r] = __shfl(inv_l, 4 * lg + r, 64);
   }
   float* my_imp = imp + (int64_t)wave * a.nbp;
-  for (int64_t jt = 0; jt * 64 < nvis_max; ++jt) {
+  if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, false, nullptr, 0, 0, b, g, a.G, false);
+  for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
-    stage_rows<DQ>(kt, a.kc, b, g, a.G, a.nb, jt * 64);
+    st.store(kt, vt, false);
     __syncthreads();
+    if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, false, nullptr, 0, 0, b, g, a.G, false);
     if (jt * 64 < nvis) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -312,11 +362,13 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     int64_t lo = p_first - a.w + 1;
     if (lo < 0) lo = 0;
-    for (int64_t kb = lo / 64; kb <= p_last / 64; ++kb) {
+    const int64_t kb0 = lo / 64, kb1 = p_last / 64;
+    st.load(a.kG, a.L, kb0 * 64, true, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
+    for (int64_t kb = kb0; kb <= kb1; ++kb) {
       __syncthreads();
-      stage_rows<DQ>(kt, a.k, b, g, a.G, a.L, kb * 64);
-      stage_cols<DV>(vt, a.vT, b, g, a.G, a.Lp, kb * 64);
+      st.store(kt, vt, true);
       __syncthreads();
+      if (kb + 1 <= kb1) st.load(a.kG, a.L, (kb + 1) * 64, true, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
       if (active && kb * 64 <= p && kb * 64 + 63 > p - a.w) {
         f32x4 s[4];
         qk_tile_T<DQ>(kt, qf, s, lr, lg);
@@ -344,17 +396,93 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
 
 // ---------------------------------------------------------------------------
 template <typename TO> __device__ __forceinline__ void store4(TO* p, f32x4 v);
-template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 v) { *(f32x4*)p = v; }
+// outputs are written once and never re-read here: non-temporal stores keep
+// them from evicting the K/V tiles that other tokens re-use
+template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 v) { __builtin_nontemporal_store(v, (f32x4*)p); }
 template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
   u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
              (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
-  *(u32x2*)p = w;
+  __builtin_nontemporal_store(w, (u32x2*)p);
+}
+
+// Fragments of one 32-key chunk of a selected block, in matrix-op layout.
+// The two 16-row S^T tiles hold the keys in an interleaved order, row i of
+// tile t <-> key kb + 8*(i/4) + 4*t + i%4, so that lane group lg ends up
+// with the probabilities of the 8 consecutive keys kb + 8*lg .. kb + 8*lg + 7:
+// each V^T operand (row d = 16*dt + lr) is then one 16-byte read.
+template <int DQ> struct KFrag { bf16x8 k0[DQ / 32], k1[DQ / 32]; };
+template <int DV> struct VFrag { bf16x8 v[DV / 16]; };
+
+// kr: buffer over this (b, g)'s group-major K rows [L, DQ]; rows past the
+// end read as zeros (those keys are masked).  kofs: lane byte offset
+// (8*lg dims).
+template <int DQ>
+__device__ __forceinline__ void load_k(KFrag<DQ>& f, __amdgpu_buffer_rsrc_t kr, uint32_t kofs, int64_t kb, int lr) {
+  const uint32_t i = 8 * (lr >> 2) + (lr & 3);
+  const uint32_t v0 = ((uint32_t)kb + i) * DQ * 2 + kofs;
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) {
+    f.k0[ks] = bld8(kr, v0, 64 * ks);
+    f.k1[ks] = bld8(kr, v0, 4 * DQ * 2 + 64 * ks);
+  }
+}
+
+// vr: buffer over this (b, g)'s tiled V^T [Lp/64, DV, 64]; vofs: lane byte
+// offset (row lr, keys 8*lg ..).
+template <int DV>
+__device__ __forceinline__ void load_v(VFrag<DV>& f, __amdgpu_buffer_rsrc_t vr, uint32_t vofs, int64_t kb) {
+  const uint32_t v0 = (((uint32_t)kb / 64) * DV * 64 + ((uint32_t)kb % 64)) * 2 + vofs;
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) f.v[dt] = bld8(vr, v0, 16 * dt * 64 * 2);
+}
+
+// S^T for the chunk's 32 keys (raw dot products), keys beyond p masked.
+template <int DQ>
+__device__ __forceinline__ void qk_chunk(const KFrag<DQ>& f, const bf16x8 (&qf)[DQ / 32], f32x4& s0, f32x4& s1,
+                                         int64_t kb, int64_t p, int lg) {
+  s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) {
+    s0 = mfma16(f.k0[ks], qf[ks], s0);
+    s1 = mfma16(f.k1[ks], qf[ks], s1);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (kb + 8 * lg + r > p) s0[r] = -INFINITY;
+    if (kb + 8 * lg + 4 + r > p) s1[r] = -INFINITY;
+  }
+}
+
+// Online-softmax update of one wave's token (16 heads) with the chunk.
+template <int DV>
+__device__ __forceinline__ void pv_chunk(const VFrag<DV>& f, f32x4 s0, f32x4 s1, f32x4 (&o)[DV / 16], float& m,
+                                         float& l, float c) {
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
+  tmax = xor_max16_32(tmax);
+  const float mnew = fmaxf(m, tmax);
+  const float alpha = exp2f((m - mnew) * c);
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s0[r] = exp2f((s0[r] - mnew) * c);
+    s1[r] = exp2f((s1[r] - mnew) * c);
+    rs += s0[r] + s1[r];
+  }
+  rs = xor_sum16_32(rs);
+  l = l * alpha + rs;
+  m = mnew;
+  const bf16x8 pf = pack8(s0, s1);
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = mfma16(f.v[dt], pf, o[dt] * alpha);
 }
 
 template <int DQ, int DV, bool FWD, typename TO>
 __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int64_t g = blockIdx.x % a.G;
+  const int64_t g = blockIdx.x % a.G;  // consecutive workgroups alternate groups: each XCD serves fixed groups
   const int64_t tg = (blockIdx.x / a.G) * 4 + wave;  // flat (b, t)
   if (tg >= a.B * a.T) return;
   const int64_t b = tg / a.T, t = tg % a.T;
@@ -367,61 +495,72 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
   {
     const uint16_t* qr = a.q + row * DQ + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+    for (int ks = 0; ks < DQ / 32; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qr + 32 * ks)));
   }
-  const int iv = lane < a.n ? a.idx[((b * a.T + t) * a.G + g) * a.n + lane] : -1;
   const bool use_slc = !FWD || (a.flags & NSA_F_SLC);
+  // chunk list: lane c describes chunk c = (slot c / 2, half c % 2); n <= 32
+  int64_t kbv = -1;
+  {
+    const int slot = lane >> 1;
+    const int j = slot < a.n ? a.idx[((b * a.T + t) * a.G + g) * a.n + slot] : -1;
+    const int64_t kb = (int64_t)j * 64 + 32 * (lane & 1);
+    if (use_slc && j >= 0 && kb <= p) kbv = kb;
+  }
+  uint64_t pending = __ballot(kbv >= 0);
+  const int nch = __popcll(pending);
 
   float m = -INFINITY, l = 0.f;
   f32x4 o[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* kg = a.k + g * DQ + 8 * lg;
-  const uint16_t* vg = a.vT + ((b * a.G + g) * DV + lr) * a.Lp + 4 * lg;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kG + (b * a.G + g) * a.L * DQ, (uint32_t)(a.L * DQ * 2));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.vT + (b * a.G + g) * a.Lp * DV, (uint32_t)(a.Lp * DV * 2));
+  const uint32_t kofs = 16 * lg, vofs = (lr * 64 + 8 * lg) * 2;
 
-  for (int slot = 0; use_slc && slot < a.n; ++slot) {
-    const int j = __shfl(iv, slot, 64);
-    if (j < 0) continue;
-    for (int half = 0; half < 2; ++half) {
-      const int64_t kb = (int64_t)j * 64 + 32 * half;
-      if (kb > p) break;
-      int64_t r0 = kb + lr, r1 = kb + 16 + lr;
-      if (r0 > a.L - 1) r0 = a.L - 1;
-      if (r1 > a.L - 1) r1 = a.L - 1;
-      const uint16_t* k0 = kg + (b * a.L + r0) * a.G * DQ;
-      const uint16_t* k1 = kg + (b * a.L + r1) * a.G * DQ;
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DQ / 32; ++ks) {
-        s0 = mfma16(ld8(k0 + 32 * ks), qf[ks], s0);
-        s1 = mfma16(ld8(k1 + 32 * ks), qf[ks], s1);
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (kb + 4 * lg + r > p) s0[r] = -INFINITY;
-        if (kb + 16 + 4 * lg + r > p) s1[r] = -INFINITY;
-        tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
-      }
-      tmax = xor_max16_32(tmax);
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = exp2f((m - mnew) * c);
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s0[r] = exp2f((s0[r] - mnew) * c);
-        s1[r] = exp2f((s1[r] - mnew) * c);
-        rs += s0[r] + s1[r];
-      }
-      rs = xor_sum16_32(rs);
-      l = l * alpha + rs;
-      m = mnew;
-      const bf16x8 pf = pack8(s0, s1);
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        const uint16_t* vr = vg + (int64_t)16 * dt * a.Lp + kb;
-        o[dt] = mfma16(ld4x2(vr, vr + 16), pf, o[dt] * alpha);
-      }
+  // next chunk's key base; once the list is exhausted the last one again, so
+  // that every prefetch below is unconditional (exact wait counts, no merge)
+  int64_t last_kb = 0;
+  auto next_kb = [&]() -> int64_t {
+    if (pending) {
+      const int pos = __ffsll((unsigned long long)pending) - 1;
+      pending &= pending - 1;
+      last_kb = __shfl(kbv, pos, 64);
+    }
+    return last_kb;
+  };
+  // software pipeline, split by operand: the next chunk's K reads are issued
+  // before this chunk's Q.K^T, its V reads before this chunk's softmax and
+  // P.V, so at most three fragment sets are live.  Every prefetch is
+  // unconditional (past the end it re-reads the last chunk, at most one
+  // extra chunk per token) so each step has exact wait counts.
+  KFrag<DQ> ka, kb2;
+  VFrag<DV> va, vb;
+  if (nch > 0) {
+    int64_t ca = next_kb();
+    load_k<DQ>(ka, kr, kofs, ca, lr);
+    load_v<DV>(va, vr, vofs, ca);
+    for (int ci = 0; ci < nch; ci += 2) {
+      f32x4 s0, s1;
+      const int64_t cb = next_kb();
+      load_k<DQ>(kb2, kr, kofs, cb, lr);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_chunk<DQ>(ka, qf, s0, s1, ca, p, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v<DV>(vb, vr, vofs, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_chunk<DV>(va, s0, s1, o, m, l, c);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ci + 1 >= nch) break;
+      ca = next_kb();
+      load_k<DQ>(ka, kr, kofs, ca, lr);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_chunk<DQ>(kb2, qf, s0, s1, cb, p, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v<DV>(va, vr, vofs, ca);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_chunk<DV>(vb, s0, s1, o, m, l, c);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -432,7 +571,8 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
     if (a.flags & NSA_F_SLC) g1 = gate_of(a, row, 1) * inv_l;
     const float* arow = a.acc + row * DV + 4 * lg;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) store4<TO>(orow + 16 * dt, *(const f32x4*)(arow + 16 * dt) + o[dt] * g1);
+    for (int dt = 0; dt < DV / 16; ++dt)
+      store4<TO>(orow + 16 * dt, __builtin_nontemporal_load((const f32x4*)(arow + 16 * dt)) + o[dt] * g1);
   } else {
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) store4<TO>(orow + 16 * dt, o[dt] * inv_l);
@@ -475,7 +615,14 @@ hipError_t launch_sel_t(const PfArgs& a, bool fwd, bool out_f32, hipStream_t s) 
 bool prefill_fast_ok(const Prob& P) {
   const int64_t nbp = (P.nb + 63) / 64 * 64;
   return P.bf16() && P.hpg == 16 && P.bs == 64 && (P.dq == 64 || P.dq == 128 || P.dq == 192) &&
-         (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE && P.n <= 64;
+         (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE && P.n <= 32;
+}
+
+hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, int64_t G, int D, hipStream_t s) {
+  const unsigned grid = (unsigned)(B * ((L + 63) / 64));
+  if (grid == 0) return hipSuccess;
+  k_group_major<<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, L, G, D);
+  return hipGetLastError();
 }
 
 hipError_t launch_transpose(const void* src, void* dst, int64_t B, int64_t N, int64_t Np, int64_t G, int D,

@@ -34,6 +34,16 @@ __device__ __forceinline__ bf16x8 ld4x2(const uint16_t* lo, const uint16_t* hi) 
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Buffer resource over [base, base + bytes): loads through it take a 32-bit
+// byte offset per lane and return zeros past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset voff + soff (soff uniform).
+__device__ __forceinline__ bf16x8 bld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   bf16x8 r;
   r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];

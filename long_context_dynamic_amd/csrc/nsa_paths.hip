@@ -2,6 +2,7 @@
 // for the shapes they take (bf16, 16 heads per group, 64-token blocks), the
 // any-shape kernels otherwise.
 #include "nsa_paths.h"
+#include "nsa_decode.h"
 #include "nsa_prefill.h"
 
 namespace nsa {
@@ -12,6 +13,13 @@ size_t elem_bytes(const Prob& P) { return P.bf16() ? 2 : 4; }
 int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 
 template <typename T> T* at(void* base, size_t off) { return (T*)((char*)base + off); }
+
+DecArgs dec_args(const Prob& P) {
+  DecArgs a = {};
+  a.B = P.B; a.T = P.T; a.R = P.B * P.T; a.L = P.L; a.G = P.G; a.H = P.H; a.nb = P.nb;
+  a.nbp = pad64(P.nb); a.n = P.n; a.w = P.w; a.flags = P.flags; a.scale = P.scale;
+  return a;
+}
 
 PfArgs pf_args(const Prob& P) {
   PfArgs a = {};
@@ -28,9 +36,23 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   const bool fast = prefill_fast_ok(P);
-  if (call == Call::Select) return w;  // reads the caller's summaries directly
+  const bool dec = decode_ok(P);
+  const size_t zbytes = (size_t)(P.B * P.T * P.G * 16 * pad64(P.nb)) * sizeof(float);
+  if (call == Call::Select) {  // reads the caller's summaries directly
+    if (dec) {
+      w.zbuf = take(zbytes);
+      w.part = take(decode_part_bytes(P));
+    }
+    w.total = off;
+    return w;
+  }
   if (call == Call::SparseAttn) {
-    if (fast) w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+    if (dec) {
+      w.part = take(decode_part_bytes(P));
+    } else if (fast) {
+      w.kG = take((size_t)(P.B * P.G * P.L * P.dq) * 2);
+      w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+    }
     w.total = off;
     return w;
   }
@@ -39,7 +61,11 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     w.vc = take((size_t)(P.B * P.nb * P.G * P.dv) * elem_bytes(P));
   }
   w.idx = take((size_t)(P.B * P.T * P.G * P.n) * sizeof(int32_t));
-  if (fast) {
+  if (dec) {
+    w.zbuf = take(zbytes);
+    w.part = take(decode_part_bytes(P));
+  } else if (fast) {
+    w.kG = take((size_t)(P.B * P.G * P.L * P.dq) * 2);
     w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
     w.vcT = take((size_t)(P.B * P.G * P.dv * pad64(P.nb)) * 2);
     w.acc = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
@@ -63,9 +89,15 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
   const char* list[8];
   int n = 0;
   if (!have_cmp) list[n++] = "pool";
-  if (prefill_fast_ok(P)) {
+  if (decode_ok(P)) {
+    list[n++] = "dec_cmp";
+    list[n++] = "dec_select";
+    list[n++] = "dec_attn";
+    list[n++] = "dec_merge";
+  } else if (prefill_fast_ok(P)) {
     list[n++] = "transpose_vc";
     list[n++] = "transpose_v";
+    list[n++] = "group_major_k";
     list[n++] = "cmp_select_window";
     list[n++] = "selected";
   } else {
@@ -77,7 +109,17 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
 }
 
 hipError_t run_select(const Prob& P, const void* q, const void* kc, int32_t* idx, float* score,
-                      const Workspace&, void*, hipStream_t s) {
+                      const Workspace& ws, void* base, hipStream_t s) {
+  if (decode_ok(P)) {
+    DecArgs a = dec_args(P);
+    a.q = (const uint16_t*)q;
+    a.kc = (const uint16_t*)kc;
+    a.zbuf = at<float>(base, ws.zbuf);
+    a.part = at<float>(base, ws.part);
+    a.idx = idx;
+    a.score = score;
+    return launch_decode(P, a, 0, false, s, nullptr);
+  }
   if (prefill_fast_ok(P)) {
     PfArgs a = pf_args(P);
     a.q = (const uint16_t*)q;
@@ -93,13 +135,27 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
                            void* out, float* lse, const Workspace& ws, void* base, hipStream_t s) {
   Prob S = P;
   S.flags = NSA_F_SLC | (P.flags & NSA_F_OUT_F32);
+  if (decode_ok(P)) {
+    DecArgs a = dec_args(S);
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.idx = (int32_t*)idx;
+    a.part = at<float>(base, ws.part);
+    a.out = out;
+    a.lse = lse;
+    return launch_decode(S, a, 2, P.has(NSA_F_OUT_F32), s, nullptr);
+  }
   if (prefill_fast_ok(P)) {
     PfArgs a = pf_args(S);
     uint16_t* vT = at<uint16_t>(base, ws.vT);
+    uint16_t* kG = at<uint16_t>(base, ws.kG);
     hipError_t e = launch_transpose(v, vT, P.B, P.L, a.Lp, P.G, (int)P.dv, s);
     if (e != hipSuccess) return e;
+    if ((e = launch_group_major(k, kG, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
+    a.kG = kG;
     a.vT = vT;
     a.idx = (int32_t*)idx;
     a.out = out;
@@ -124,6 +180,21 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     ph.mark();
   }
   int32_t* idx = at<int32_t>(base, ws.idx);
+  if (decode_ok(P)) {
+    DecArgs a = dec_args(P);
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.kc = (const uint16_t*)kc;
+    a.vc = (const uint16_t*)vc;
+    a.gates = (const uint16_t*)gates;
+    a.zbuf = at<float>(base, ws.zbuf);
+    a.idx = idx;
+    a.part = at<float>(base, ws.part);
+    a.out = out;
+    if ((e = launch_decode(P, a, 1, P.has(NSA_F_OUT_F32), s, &ph)) != hipSuccess) return e;
+    return ph.err;
+  }
   if (prefill_fast_ok(P)) {
     PfArgs a = pf_args(P);
     uint16_t* vT = at<uint16_t>(base, ws.vT);
@@ -132,8 +203,12 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     ph.mark();
     if ((e = launch_transpose(v, vT, P.B, P.L, a.Lp, P.G, (int)P.dv, s)) != hipSuccess) return e;
     ph.mark();
+    uint16_t* kG = at<uint16_t>(base, ws.kG);
+    if ((e = launch_group_major(k, kG, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
+    ph.mark();
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
+    a.kG = kG;
     a.vT = vT;
     a.kc = (const uint16_t*)kc;
     a.vcT = vcT;

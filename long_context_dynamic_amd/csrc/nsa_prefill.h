@@ -9,9 +9,10 @@ namespace nsa {
 struct PfArgs {
   const uint16_t* q;      // [B, T, H, DQ]
   const uint16_t* k;      // [B, L, G, DQ]
-  const uint16_t* vT;     // [B, G, DV, Lp]   values, key-contiguous
+  const uint16_t* kG;     // [B, G, L, DQ]    keys, group-major copy
+  const uint16_t* vT;     // [B, G, Lp / 64, DV, 64]  values, block-tiled and key-contiguous
   const uint16_t* kc;     // [B, nb, G, DQ]   block summaries
-  const uint16_t* vcT;    // [B, G, DV, nbp]  value summaries, block-contiguous
+  const uint16_t* vcT;    // [B, G, nbp / 64, DV, 64]  value summaries, tiled likewise
   const uint16_t* gates;  // [B, T, H, 3] or NULL
   float* acc;             // [B, T, H, DV]    gated compressed + window partial sum
   int32_t* idx;           // [B, T, G, n]
@@ -24,9 +25,10 @@ struct PfArgs {
 };
 
 // True when the matrix-core kernels take this shape: bf16, 16 heads per
-// group, 64-token blocks, d_qk in {64,128,192}, d_v in {64,128}, nb <= 2048.
+// group, 64-token blocks, d_qk in {64,128,192}, d_v in {64,128}, nb <= 2048, top_k <= 32.
 bool prefill_fast_ok(const Prob& P);
 
+hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, int64_t G, int D, hipStream_t s);
 hipError_t launch_transpose(const void* src, void* dst, int64_t B, int64_t N, int64_t Np, int64_t G, int D,
                             hipStream_t s);
 // fwd: compressed + window + selection + gated partial (acc); else selection only.

@@ -176,3 +176,40 @@ def test_all_blocks_selected_equals_dense_causal_attention():
         pr = np.exp(s - s.max(1, keepdims=True))
         pr /= pr.sum(1, keepdims=True)
         assert np.abs(got[:, h] - pr @ v[:, g]).max() <= 2e-2
+
+
+def test_decode_full_size_sampled_sequences():
+    """64 sequences x 65536-token caches (the batched-decode workload, same
+    launch as the benchmark); 4 sequences checked against the oracle."""
+    prob = workloads.get("nsa_decode_64x64k")
+    B, L, G, H = prob["batch"], prob["kv_len"], prob["n_groups"], workloads.n_heads(prob)
+    dq, dv = prob["d_qk"], prob["d_v"]
+    dev = {"q": torch.empty((B, 1, H, dq), dtype=torch.bfloat16, device="cuda"),
+           "k": torch.empty((B, L, G, dq), dtype=torch.bfloat16, device="cuda"),
+           "v": torch.empty((B, L, G, dv), dtype=torch.bfloat16, device="cuda"),
+           "gates": torch.empty((B, 1, H, 3), dtype=torch.bfloat16, device="cuda")}
+    check = [0, 21, 42, 63]
+    host = {}
+    for b in range(B):
+        xs = inputs.generate_sequence(prob, b)
+        for name, arr in xs.items():
+            dev[name][b:b + 1].copy_(nsa.to_device(arr, prob))
+        if b in check:
+            host[b] = xs
+    kc, vc = nsa.compress(prob, dev["k"], dev["v"])
+    out = nsa.forward(prob, dev["q"], dev["k"], dev["v"], dev["gates"], k_cmp=kc, v_cmp=vc)
+    gidx, _ = nsa.select_topk(prob, dev["q"], kc, want_score=False)
+    torch.cuda.synchronize()
+    one = dict(prob, batch=1)
+    for b in check:
+        xs = host[b]
+        okc, ovc = oracle.pool(one, xs["k"], xs["v"])
+        np.testing.assert_array_equal(nsa.to_host_bits(kc[b:b + 1]), okc)
+        idx, imp, ocmp = oracle.select(one, xs["q"], okc, ovc)
+        got_idx = gidx[b:b + 1].cpu().numpy().reshape(1, G, -1)
+        band = U.check_selection(one, [0], got_idx, idx, imp)
+        want, _, _ = oracle.attend(one, xs["q"], xs["k"], xs["v"], xs["gates"], got_idx, ocmp)
+        got = U.widen_out(out[b:b + 1], prob).reshape(1, H, dv)
+        err = np.abs(got - want)
+        print(f"seq {b}: max err {err.max():.3e}, tie-band groups {band}")
+        assert np.all(err <= U.out_tolerance(prob, want, False))
