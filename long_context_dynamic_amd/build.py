@@ -39,6 +39,9 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    warn = "\n".join(l for l in r.stderr.splitlines() if "warning:" in l and "packed-fp32-ops" not in l)
+    if warn:
+        print(f"{os.path.basename(src)}: {warn}", file=sys.stderr)
     return obj
 
 

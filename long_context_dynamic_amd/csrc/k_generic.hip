@@ -299,11 +299,11 @@ hipError_t launch_select_generic(const Prob& P, const void* q, const void* kc, c
   const unsigned grid = (unsigned)(P.B * P.T * P.G);
   if (P.bf16()) {
     auto kern = k_select_generic<uint16_t>;
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, kThreads, lds, s>>>((const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, idx, score, ocmp, a);
   } else {
     auto kern = k_select_generic<float>;
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, kThreads, lds, s>>>((const float*)q, (const float*)kc, (const float*)vc, idx, score, ocmp, a);
   }
   return hipGetLastError();
@@ -321,7 +321,7 @@ hipError_t launch_attend_generic(const Prob& P, const void* q, const void* k, co
 #define NSA_LAUNCH_ATTEND(TI, TO)                                                                    \
   do {                                                                                               \
     auto kern = k_attend_generic<TI, TO>;                                                            \
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);    \
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);    \
     kern<<<grid, kThreads, lds, s>>>((const TI*)q, (const TI*)k, (const TI*)v, (const TI*)gates, idx, \
                                      ocmp, (TO*)out, lse, a, cap);                                   \
   } while (0)

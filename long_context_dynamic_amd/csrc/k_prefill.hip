@@ -2,12 +2,16 @@
 // query heads and 64-token blocks ([P1] s4 three branches; [P1] s5 the group's
 // heads stacked as the matrix M dimension instead of a block of queries).
 //
-//   k_transpose  V [B, N, G, D] -> block-tiled V^T [B, G, Np / 64, D, 64]
-//                (each 64-key tile one contiguous D x 64 chunk, zero padded to
-//                Np = round_up(N, 64)); makes every P.V operand one contiguous
-//                load and every tile one contiguous read.
-//   k_group_major  K [B, L, G, D] -> [B, G, L, D]: each 64-key block of one
-//                group becomes one contiguous 64 x D chunk.
+//   k_transpose  V [B, N, G, D] -> tiled V^T [B, G, Np / 32, D, 32] (each
+//                32-key tile one contiguous D x 32 chunk, zero padded to
+//                Np = round_up(N, 64)): every P.V operand is one contiguous
+//                load, a 32-key step reads whole cache lines, a 64-key block
+//                is one contiguous 2 x D x 32 read.
+//   k_group_major  K [B, L, G, D] -> per group, 16-row groups with rows i and
+//                i + 8 interleaved every 32 dims ([B, G, Lp / 16, D / 32, 8, 2, 32],
+//                zero padded to Lp = round_up(L, 64)): a 64-key block is one
+//                contiguous read, and each matrix-op K load (16 rows x 32
+//                dims, the rows pairing i with i + 8) reads whole cache lines.
 //   k_cmpwin     one workgroup per (8-token query tile, KV group), one wave
 //                per token: compressed branch (online softmax over the block
 //                summaries), group importance (second pass, each head's
@@ -62,21 +66,28 @@ __global__ void __launch_bounds__(256) k_transpose(const uint16_t* __restrict__ 
     for (int i = 0; i < 8; ++i) w[i] = tile[8 * k8 + i][d];
     u32x4 val = {(uint32_t)w[0] | ((uint32_t)w[1] << 16), (uint32_t)w[2] | ((uint32_t)w[3] << 16),
                  (uint32_t)w[4] | ((uint32_t)w[5] << 16), (uint32_t)w[6] | ((uint32_t)w[7] << 16)};
-    *(u32x4*)(dst + (((b * G + g) * ntile + tix) * D + d) * 64 + 8 * k8) = val;
+    // keys 8*k8 .. 8*k8+7 of the 64-key tile: half k8 / 4 of it, 8*(k8 % 4) into the half
+    *(u32x4*)(dst + ((b * G + g) * ntile + tix) * D * 64 + (k8 / 4) * D * 32 + d * 32 + 8 * (k8 % 4)) = val;
   }
 }
 
+// Element offset of (row, d) inside one group's paired-row K image.
+__device__ __forceinline__ int64_t kp_offset(int64_t row, int64_t d, int D) {
+  const int64_t rg = row >> 4, w = row & 15;
+  return ((rg * (D / 32) + (d >> 5)) * 8 + (w & 7)) * 64 + (w >> 3) * 32 + (d & 31);
+}
+
 __global__ void __launch_bounds__(256) k_group_major(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                     int64_t L, int64_t G, int D) {
+                                                     int64_t L, int64_t Lp, int64_t G, int D) {
   // one workgroup per (b, 64-row slab); rows of all groups are read once
-  const int64_t nslab = (L + 63) / 64;
+  const int64_t nslab = Lp / 64;
   const int64_t b = blockIdx.x / nslab, s0 = (blockIdx.x % nslab) * 64;
   const int chunks = D / 8;
   for (int64_t c = threadIdx.x; c < 64 * G * chunks; c += 256) {
     const int64_t r = c / (G * chunks), g = (c / chunks) % G, c8 = c % chunks;
-    if (s0 + r >= L) continue;
-    const u32x4 val = *(const u32x4*)(src + ((b * L + s0 + r) * G + g) * D + 8 * c8);
-    *(u32x4*)(dst + ((b * G + g) * L + s0 + r) * D + 8 * c8) = val;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (s0 + r < L) val = *(const u32x4*)(src + ((b * L + s0 + r) * G + g) * D + 8 * c8);
+    *(u32x4*)(dst + (b * G + g) * Lp * D + kp_offset(s0 + r, 8 * c8, D)) = val;
   }
 }
 
@@ -93,8 +104,9 @@ struct Stager {
   static constexpr int KPT = (KC + NT - 1) / NT, VPT = (VC + NT - 1) / NT;
   u32x4 kr[KPT], vr[VPT];
 
-  // rows: [B, Nrows, G, DQ], or [B, G, Nrows, DQ] when group_major;
-  // colsT: block-tiled [B, G, Np / 64, DV, 64]
+  // rows: [B, Nrows, G, DQ], or with group_major one paired-row image of
+  // Nrows (a multiple of 64) rows per (b, g);
+  // colsT: tiled [B, G, Np / 32, DV, 32] (a 64-key tile = two 32-key halves)
   __device__ __forceinline__ void load(const uint16_t* rows, int64_t Nrows, int64_t row0, bool group_major,
                                        const uint16_t* colsT, int64_t Np, int64_t col0, int64_t b, int64_t g,
                                        int64_t G, bool with_v) {
@@ -102,11 +114,14 @@ struct Stager {
     for (int i = 0; i < KPT; ++i) {
       const int c = threadIdx.x + i * NT;
       if (KC % NT == 0 || c < KC) {
-        const int r = c / (DQ / 8), c8 = c % (DQ / 8);
-        int64_t row = row0 + r;
-        if (row > Nrows - 1) row = Nrows - 1;
-        const int64_t off = group_major ? ((b * G + g) * Nrows + row) * DQ : ((b * Nrows + row) * G + g) * DQ;
-        kr[i] = *(const u32x4*)(rows + off + 8 * c8);
+        if (group_major) {  // the tile is one contiguous run of the image
+          kr[i] = *(const u32x4*)(rows + ((b * G + g) * Nrows + row0) * DQ + 8 * c);
+        } else {
+          const int r = c / (DQ / 8), c8 = c % (DQ / 8);
+          int64_t row = row0 + r;
+          if (row > Nrows - 1) row = Nrows - 1;
+          kr[i] = *(const u32x4*)(rows + ((b * Nrows + row) * G + g) * DQ + 8 * c8);
+        }
       }
     }
     if (with_v) {
@@ -118,17 +133,30 @@ struct Stager {
       }
     }
   }
-  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, bool with_v) const {
+  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, bool with_v, bool group_major) const {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = threadIdx.x + i * NT;
-      if (KC % NT == 0 || c < KC) *(u32x4*)(kt + (c / (DQ / 8)) * KS + 8 * (c % (DQ / 8))) = kr[i];
+      if (KC % NT == 0 || c < KC) {
+        int r, d;
+        if (group_major) {  // chunk c of the paired-row image: back to (row, dim)
+          const int e = 8 * c, rg = e / (16 * DQ), rem = e % (16 * DQ);
+          const int ks = rem / 512, w8 = (rem % 512) / 64, h = (rem % 64) / 32;
+          r = 16 * rg + 8 * h + w8;
+          d = 32 * ks + (rem % 32);
+        } else {
+          r = c / (DQ / 8);
+          d = 8 * (c % (DQ / 8));
+        }
+        *(u32x4*)(kt + r * KS + d) = kr[i];
+      }
     }
     if (with_v) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        const int c = threadIdx.x + i * NT;
-        if (VC % NT == 0 || c < VC) *(u32x4*)(vt + (c / 8) * VS + 8 * (c % 8)) = vr[i];
+        const int c = threadIdx.x + i * NT;  // 16-byte chunk c: half c / (4 DV), row d, keys 8 * (c % 4)
+        const int h = c / (4 * DV), d = (c / 4) % DV, j8 = c % 4;
+        if (VC % NT == 0 || c < VC) *(u32x4*)(vt + d * VS + 32 * h + 8 * j8) = vr[i];
       }
     }
   }
@@ -240,7 +268,7 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, false, a.vcT, a.nbp, 0, b, g, a.G, use_cmp);
   for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
-    st.store(kt, vt, use_cmp);
+    st.store(kt, vt, use_cmp, false);
     __syncthreads();
     if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, false, a.vcT, a.nbp, (jt + 1) * 64, b, g, a.G, use_cmp);
     if (jt * 64 < nvis) {
@@ -275,7 +303,7 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, false, nullptr, 0, 0, b, g, a.G, false);
   for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
-    st.store(kt, vt, false);
+    st.store(kt, vt, false, false);
     __syncthreads();
     if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, false, nullptr, 0, 0, b, g, a.G, false);
     if (jt * 64 < nvis) {
@@ -363,12 +391,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     int64_t lo = p_first - a.w + 1;
     if (lo < 0) lo = 0;
     const int64_t kb0 = lo / 64, kb1 = p_last / 64;
-    st.load(a.kG, a.L, kb0 * 64, true, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
+    st.load(a.kG, a.Lp, kb0 * 64, true, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
     for (int64_t kb = kb0; kb <= kb1; ++kb) {
       __syncthreads();
-      st.store(kt, vt, true);
+      st.store(kt, vt, true, true);
       __syncthreads();
-      if (kb + 1 <= kb1) st.load(a.kG, a.L, (kb + 1) * 64, true, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
+      if (kb + 1 <= kb1) st.load(a.kG, a.Lp, (kb + 1) * 64, true, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
       if (active && kb * 64 <= p && kb * 64 + 63 > p - a.w) {
         f32x4 s[4];
         qk_tile_T<DQ>(kt, qf, s, lr, lg);
@@ -413,27 +441,31 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 
 template <int DQ> struct KFrag { bf16x8 k0[DQ / 32], k1[DQ / 32]; };
 template <int DV> struct VFrag { bf16x8 v[DV / 16]; };
 
-// kr: buffer over this (b, g)'s group-major K rows [L, DQ]; rows past the
-// end read as zeros (those keys are masked).  kofs: lane byte offset
-// (8*lg dims).
+constexpr uint32_t kPastEnd = 0x7fff0000u;  // byte offset beyond any buffer: reads return zeros
+
+// kr: buffer over this (b, g)'s paired-row K image (Lp rows); kofs: lane
+// byte offset of its 8 dims (8*lg).  The chunk's key order puts rows
+// w and w + 8 of each 16-row group in the same load, so each load reads
+// whole lines.
 template <int DQ>
 __device__ __forceinline__ void load_k(KFrag<DQ>& f, __amdgpu_buffer_rsrc_t kr, uint32_t kofs, int64_t kb, int lr) {
-  const uint32_t i = 8 * (lr >> 2) + (lr & 3);
-  const uint32_t v0 = ((uint32_t)kb + i) * DQ * 2 + kofs;
+  // tile-0 row of lane lr: kb + 8*(lr/4) + lr%4 = 16*(kb/16 + lr/8) + 8*((lr/4)%2) + lr%4
+  const uint32_t rg = (uint32_t)kb / 16 + (lr >> 3), h = (lr >> 2) & 1, w8 = lr & 3;
+  const uint32_t v0 = kb < 0 ? kPastEnd : ((rg * (DQ / 32) * 8 + w8) * 64 + h * 32) * 2 + kofs;
 #pragma unroll
   for (int ks = 0; ks < DQ / 32; ++ks) {
-    f.k0[ks] = bld8(kr, v0, 64 * ks);
-    f.k1[ks] = bld8(kr, v0, 4 * DQ * 2 + 64 * ks);
+    f.k0[ks] = bld8(kr, v0, ks * 8 * 64 * 2);
+    f.k1[ks] = bld8(kr, v0, ks * 8 * 64 * 2 + 4 * 64 * 2);  // tile 1: rows + 4 -> w8 + 4
   }
 }
 
-// vr: buffer over this (b, g)'s tiled V^T [Lp/64, DV, 64]; vofs: lane byte
-// offset (row lr, keys 8*lg ..).
+// vr: buffer over this (b, g)'s tiled V^T [Lp/32, DV, 32]; vofs: lane byte
+// offset (row lr, keys 8*lg ..).  kb is a multiple of 32.
 template <int DV>
 __device__ __forceinline__ void load_v(VFrag<DV>& f, __amdgpu_buffer_rsrc_t vr, uint32_t vofs, int64_t kb) {
-  const uint32_t v0 = (((uint32_t)kb / 64) * DV * 64 + ((uint32_t)kb % 64)) * 2 + vofs;
+  const uint32_t v0 = kb < 0 ? kPastEnd : ((uint32_t)kb / 32) * DV * 32 * 2 + vofs;
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) f.v[dt] = bld8(vr, v0, 16 * dt * 64 * 2);
+  for (int dt = 0; dt < DV / 16; ++dt) f.v[dt] = bld8(vr, v0, 16 * dt * 32 * 2);
 }
 
 // S^T for the chunk's 32 keys (raw dot products), keys beyond p masked.
@@ -514,52 +546,53 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
   f32x4 o[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kG + (b * a.G + g) * a.L * DQ, (uint32_t)(a.L * DQ * 2));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kG + (b * a.G + g) * a.Lp * DQ, (uint32_t)(a.Lp * DQ * 2));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.vT + (b * a.G + g) * a.Lp * DV, (uint32_t)(a.Lp * DV * 2));
-  const uint32_t kofs = 16 * lg, vofs = (lr * 64 + 8 * lg) * 2;
+  const uint32_t kofs = 16 * lg, vofs = (lr * 32 + 8 * lg) * 2;
 
-  // next chunk's key base; once the list is exhausted the last one again, so
-  // that every prefetch below is unconditional (exact wait counts, no merge)
-  int64_t last_kb = 0;
+  // next chunk's key base, -1 once the list is exhausted (its loads then
+  // fall past the end of the buffers: zeros, no memory traffic)
   auto next_kb = [&]() -> int64_t {
-    if (pending) {
-      const int pos = __ffsll((unsigned long long)pending) - 1;
-      pending &= pending - 1;
-      last_kb = __shfl(kbv, pos, 64);
-    }
-    return last_kb;
+    if (!pending) return -1;
+    const int pos = __ffsll((unsigned long long)pending) - 1;
+    pending &= pending - 1;
+    return __shfl(kbv, pos, 64);
   };
-  // software pipeline, split by operand: the next chunk's K reads are issued
-  // before this chunk's Q.K^T, its V reads before this chunk's softmax and
-  // P.V, so at most three fragment sets are live.  Every prefetch is
-  // unconditional (past the end it re-reads the last chunk, at most one
-  // extra chunk per token) so each step has exact wait counts.
-  KFrag<DQ> ka, kb2;
-  VFrag<DV> va, vb;
+  // three-deep software pipeline: while chunk i is computed, chunks i+1 and
+  // i+2 are in flight.  Unrolled by three so every buffer is a fixed set of
+  // registers and every step has exact wait counts.
+  KFrag<DQ> k0, k1, k2;
+  VFrag<DV> v0, v1, v2;
+  auto load = [&](KFrag<DQ>& kf, VFrag<DV>& vf, int64_t kb) {
+    load_k<DQ>(kf, kr, kofs, kb, lr);
+    load_v<DV>(vf, vr, vofs, kb);
+  };
+  auto step = [&](const KFrag<DQ>& kf, const VFrag<DV>& vf, int64_t kb) {
+    f32x4 s0, s1;
+    qk_chunk<DQ>(kf, qf, s0, s1, kb, p, lg);
+    pv_chunk<DV>(vf, s0, s1, o, m, l, c);
+  };
   if (nch > 0) {
-    int64_t ca = next_kb();
-    load_k<DQ>(ka, kr, kofs, ca, lr);
-    load_v<DV>(va, vr, vofs, ca);
-    for (int ci = 0; ci < nch; ci += 2) {
-      f32x4 s0, s1;
-      const int64_t cb = next_kb();
-      load_k<DQ>(kb2, kr, kofs, cb, lr);
+    int64_t c0 = next_kb(), c1 = next_kb(), c2;
+    load(k0, v0, c0);
+    load(k1, v1, c1);
+    for (int ci = 0; ci < nch; ci += 3) {
+      c2 = next_kb();
+      load(k2, v2, c2);
       __builtin_amdgcn_sched_barrier(0);
-      qk_chunk<DQ>(ka, qf, s0, s1, ca, p, lg);
-      __builtin_amdgcn_sched_barrier(0);
-      load_v<DV>(vb, vr, vofs, cb);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_chunk<DV>(va, s0, s1, o, m, l, c);
+      step(k0, v0, c0);
       __builtin_amdgcn_sched_barrier(0);
       if (ci + 1 >= nch) break;
-      ca = next_kb();
-      load_k<DQ>(ka, kr, kofs, ca, lr);
+      c0 = next_kb();
+      load(k0, v0, c0);
       __builtin_amdgcn_sched_barrier(0);
-      qk_chunk<DQ>(kb2, qf, s0, s1, cb, p, lg);
+      step(k1, v1, c1);
       __builtin_amdgcn_sched_barrier(0);
-      load_v<DV>(va, vr, vofs, ca);
+      if (ci + 2 >= nch) break;
+      c1 = next_kb();
+      load(k1, v1, c1);
       __builtin_amdgcn_sched_barrier(0);
-      pv_chunk<DV>(vb, s0, s1, o, m, l, c);
+      step(k2, v2, c2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -587,11 +620,11 @@ hipError_t launch_cmpwin_t(const PfArgs& a, bool fwd, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * a.G * ((a.T + TQ - 1) / TQ));
   if (fwd) {
     auto kern = k_cmpwin<DQ, DV, true>;
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, TQ * 64, lds, s>>>(a);
   } else {
     auto kern = k_cmpwin<DQ, DV, false>;
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kern<<<grid, TQ * 64, lds, s>>>(a);
   }
   return hipGetLastError();
@@ -619,9 +652,10 @@ bool prefill_fast_ok(const Prob& P) {
 }
 
 hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, int64_t G, int D, hipStream_t s) {
-  const unsigned grid = (unsigned)(B * ((L + 63) / 64));
+  const int64_t Lp = (L + 63) / 64 * 64;
+  const unsigned grid = (unsigned)(B * (Lp / 64));
   if (grid == 0) return hipSuccess;
-  k_group_major<<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, L, G, D);
+  k_group_major<<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, L, Lp, G, D);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     if (dec) {
       w.part = take(decode_part_bytes(P));
     } else if (fast) {
-      w.kG = take((size_t)(P.B * P.G * P.L * P.dq) * 2);
+      w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
       w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
     }
     w.total = off;
@@ -65,7 +65,7 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     w.zbuf = take(zbytes);
     w.part = take(decode_part_bytes(P));
   } else if (fast) {
-    w.kG = take((size_t)(P.B * P.G * P.L * P.dq) * 2);
+    w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
     w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
     w.vcT = take((size_t)(P.B * P.G * P.dv * pad64(P.nb)) * 2);
     w.acc = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));

@@ -9,10 +9,10 @@ namespace nsa {
 struct PfArgs {
   const uint16_t* q;      // [B, T, H, DQ]
   const uint16_t* k;      // [B, L, G, DQ]
-  const uint16_t* kG;     // [B, G, L, DQ]    keys, group-major copy
-  const uint16_t* vT;     // [B, G, Lp / 64, DV, 64]  values, block-tiled and key-contiguous
+  const uint16_t* kG;     // [B, G, Lp / 16, DQ / 32, 8, 2, 32] keys, per group, paired rows
+  const uint16_t* vT;     // [B, G, Lp / 32, DV, 32]  values, tiled and key-contiguous
   const uint16_t* kc;     // [B, nb, G, DQ]   block summaries
-  const uint16_t* vcT;    // [B, G, nbp / 64, DV, 64]  value summaries, tiled likewise
+  const uint16_t* vcT;    // [B, G, nbp / 32, DV, 32]  value summaries, tiled likewise
   const uint16_t* gates;  // [B, T, H, 3] or NULL
   float* acc;             // [B, T, H, DV]    gated compressed + window partial sum
   int32_t* idx;           // [B, T, G, n]
