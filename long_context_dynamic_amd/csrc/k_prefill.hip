@@ -164,33 +164,122 @@ struct Stager {
 
 // One 64-key online-softmax step for one token (16 heads) of one wave.
 // s[mt] holds S^T for keys 16*mt + 4*lg + r (raw dot products, masked ones
-// already -inf); updates (m, l) of head lr and rescales o.
+// already -inf); updates the stale maximum m (raw units, raised only by more
+// than 2^kStaleLog2 in probability), the sum l of head lr, and rescales o
+// when m moves.
 template <int DV>
 __device__ __forceinline__ void softmax_step(f32x4 (&s)[4], float& m, float& l, f32x4 (&o)[DV / 16], float c,
-                                             bool with_o) {
+                                             float stale, bool with_o) {
   float tmax = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[mt][r]);
+  for (int mt = 0; mt < 4; ++mt) tmax = fmaxf(tmax, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
   tmax = xor_max16_32(tmax);
-  const float mnew = fmaxf(m, tmax);
-  const float alpha = exp2f((m - mnew) * c);
+  const bool raise = tmax > m + stale;
+  if (__ballot(raise)) {
+    const float mnew = raise ? tmax : m;
+    const float alpha = fast_exp2((m - mnew) * c);
+    l *= alpha;
+    if (with_o) {
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
+    }
+    m = mnew;
+  }
+  const float mc = m * c;
   float rs = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pv = exp2f((s[mt][r] - mnew) * c);
+      const float pv = fast_exp2(fmaf(s[mt][r], c, -mc));
       s[mt][r] = pv;
       rs += pv;
     }
-  rs = xor_sum16_32(rs);
-  l = l * alpha + rs;
-  m = mnew;
-  if (with_o) {
+  l += xor_sum16_32(rs);
+}
+
+// Keys (rows of an S^T tile) at or beyond `limit` relative to the tile
+// start are masked: s[mt][r] is key 16*mt + 4*lg + r.
+__device__ __forceinline__ void mask_from(f32x4 (&s)[4], int limit, int lg) {
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (16 * mt + 4 * lg + r >= limit) s[mt][r] = -INFINITY;
+}
+// ... and keys below `first`.
+__device__ __forceinline__ void mask_below(f32x4 (&s)[4], int first, int lg) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (16 * mt + 4 * lg + r < first) s[mt][r] = -INFINITY;
+}
+
+// Top-k of one token's block importances imp[0 .. nvis) (one wave): forced
+// blocks first, then r rounds; in each the wave finds the largest remaining
+// value (lowest block id on ties) with two cross-lane reductions, and only
+// the winning lane rescans its own candidates.  Writes the sorted list.
+template <int NBL>
+__device__ __forceinline__ void topk_row(const float* imp, int64_t nvis, int64_t cur, uint32_t flags, int n,
+                                         int32_t* orow, float* srow) {
+  const int lane = threadIdx.x & 63;
+  int forced[2];
+  int nf = 0;
+  if (flags & NSA_F_FORCE_FIRST) forced[nf++] = 0;
+  if ((flags & NSA_F_FORCE_CURRENT) && !((flags & NSA_F_FORCE_FIRST) && cur == 0)) forced[nf++] = (int)cur;
+  float vals[NBL];
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int64_t j = lane + 64 * i;
+    vals[i] = j < nvis ? imp[j] : -1.f;
+  }
+  int ncand = (int)nvis;
+  for (int f = 0; f < nf; ++f) {
+    if (forced[f] < nvis) {
+      --ncand;
+      if (lane == (forced[f] & 63)) {
+#pragma unroll
+        for (int i = 0; i < NBL; ++i)
+          if (i == (forced[f] >> 6)) vals[i] = -1.f;
+      }
+    }
+  }
+  const int r_take = (n - nf) < ncand ? (n - nf) : ncand;
+  int cj = -1;
+  float cs = -INFINITY;
+  for (int f = 0; f < nf; ++f)
+    if (lane == f) { cj = forced[f]; cs = INFINITY; }
+  // this lane's best remaining candidate (first index wins ties)
+  float bv = -1.f;
+  int bi = 0;
+#pragma unroll
+  for (int i = 0; i < NBL; ++i)
+    if (vals[i] > bv) { bv = vals[i]; bi = i; }
+  for (int round = 0; round < r_take; ++round) {
+    const float M = wave_allmax(bv);
+    const int J = wave_allmin_u(bv == M ? lane + 64 * bi : 0x7fffffff);
+    if (lane == nf + round) { cj = J; cs = M; }
+    if (lane == (J & 63)) {
+#pragma unroll
+      for (int i = 0; i < NBL; ++i)
+        if (i == (J >> 6)) vals[i] = -1.f;
+      bv = -1.f;
+      bi = 0;
+#pragma unroll
+      for (int i = 0; i < NBL; ++i)
+        if (vals[i] > bv) { bv = vals[i]; bi = i; }
+    }
+  }
+  const int cnt = nf + r_take;
+  int rank = 0;
+  for (int k2 = 0; k2 < cnt; ++k2) rank += (__shfl(cj, k2, 64) < cj) ? 1 : 0;
+  if (lane < cnt) {
+    orow[rank] = cj;
+    if (srow) srow[rank] = cs;
+  } else if (lane < n) {
+    orow[lane] = -1;
+    if (srow) srow[lane] = -INFINITY;
   }
 }
 
@@ -246,6 +335,7 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   int64_t nvis_max = (p_last + 1) / 64;
   if (nvis_max > a.nb) nvis_max = a.nb;
   const float c = a.scale * kLog2e;
+  const float stale = kStaleLog2 / c;
   const int64_t h = g * 16 + lr;
   const int64_t row = (b * a.T + (active ? t : t_last)) * a.H + h;
   const bool use_cmp = FWD && (a.flags & NSA_F_CMP);
@@ -274,12 +364,8 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     if (jt * 64 < nvis) {
       f32x4 s[4];
       qk_tile_T<DQ>(kt, qf, s, lr, lg);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (jt * 64 + 16 * mt + 4 * lg + r >= nvis) s[mt][r] = -INFINITY;
-      softmax_step<DV>(s, m, l, o, c, use_cmp);
+      if (jt * 64 + 64 > nvis) mask_from(s, (int)(nvis - jt * 64), lg);
+      softmax_step<DV>(s, m, l, o, c, stale, use_cmp);
       if (use_cmp) pv_tile<DV>(vt, s, o, lr, lg);
     }
   }
@@ -293,10 +379,10 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   }
 
   // ---- pass 2: importance of each visible block, summed over the heads ----
-  float mh[4], ih[4];
+  float mh[4], ih[4];  // per head 4*lg + r: m * c and 1 / l
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    mh[r] = __shfl(m, 4 * lg + r, 64);
+    mh[r] = __shfl(m * c, 4 * lg + r, 64);
     ih[r] = __shfl(inv_l, 4 * lg + r, 64);
   }
   float* my_imp = imp + (int64_t)wave * a.nbp;
@@ -314,7 +400,7 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
         for (int ks = 0; ks < DQ / 32; ++ks) s = mfma16(qf[ks], ld8(kt + (16 * nt + lr) * KS + 8 * lg + 32 * ks), s);
         float v = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v += exp2f((s[r] - mh[r]) * c) * ih[r];
+        for (int r = 0; r < 4; ++r) v = fmaf(fast_exp2(fmaf(s[r], c, -mh[r])), ih[r], v);
         v = xor_sum16_32(v);
         const int64_t blk = jt * 64 + 16 * nt + lr;
         if (lg == 0 && blk < nvis) my_imp[blk] = v;
@@ -323,62 +409,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   }
   __syncthreads();
 
-  // ---- top-k of this token's row (one wave, registers + wave reductions) ----
+  // ---- top-k of this token's row (one wave) ----
   if (active) {
-    const int64_t cur = p / 64;
-    int forced[2];
-    int nf = 0;
-    if (a.flags & NSA_F_FORCE_FIRST) forced[nf++] = 0;
-    if ((a.flags & NSA_F_FORCE_CURRENT) && !((a.flags & NSA_F_FORCE_FIRST) && cur == 0)) forced[nf++] = (int)cur;
-    float vals[MAX_NB_LANE];
-#pragma unroll
-    for (int i = 0; i < MAX_NB_LANE; ++i) {
-      const int64_t j = lane + 64 * i;
-      vals[i] = j < nvis ? my_imp[j] : -1.f;
-    }
-    int ncand = (int)nvis;
-    for (int f = 0; f < nf; ++f) {
-      if (forced[f] < nvis) {
-        --ncand;
-#pragma unroll
-        for (int i = 0; i < MAX_NB_LANE; ++i)
-          if (lane + 64 * i == forced[f]) vals[i] = -1.f;
-      }
-    }
-    const int r_take = ((int)a.n - nf) < ncand ? ((int)a.n - nf) : ncand;
-    int cj = -1;
-    float cs = -INFINITY;
-    for (int f = 0; f < nf; ++f)
-      if (lane == f) { cj = forced[f]; cs = INFINITY; }
-    for (int round = 0; round < r_take; ++round) {
-      float bv = -1.f;
-      int bj = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < MAX_NB_LANE; ++i)
-        if (vals[i] > bv) { bv = vals[i]; bj = lane + 64 * i; }  // ascending j: first max wins
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oj = __shfl_xor(bj, off, 64);
-        if (better(ov, oj, bv, bj)) { bv = ov; bj = oj; }
-      }
-#pragma unroll
-      for (int i = 0; i < MAX_NB_LANE; ++i)
-        if (lane + 64 * i == bj) vals[i] = -1.f;
-      if (lane == nf + round) { cj = bj; cs = bv; }
-    }
-    const int cnt = nf + r_take;
-    int rank = 0;
-    for (int k2 = 0; k2 < cnt; ++k2) rank += (__shfl(cj, k2, 64) < cj) ? 1 : 0;
     int32_t* orow = a.idx + ((b * a.T + t) * a.G + g) * a.n;
     float* srow = a.score ? a.score + ((b * a.T + t) * a.G + g) * a.n : nullptr;
-    if (lane < cnt) {
-      orow[rank] = cj;
-      if (srow) srow[rank] = cs;
-    } else if (lane < a.n) {
-      orow[lane] = -1;
-      if (srow) srow[lane] = -INFINITY;
-    }
+    if (a.nbp <= 1024) topk_row<16>(my_imp, nvis, p / 64, a.flags, (int)a.n, orow, srow);
+    else topk_row<MAX_NB_LANE>(my_imp, nvis, p / 64, a.flags, (int)a.n, orow, srow);
   }
 
   if (!FWD) return;
@@ -400,14 +436,9 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
       if (active && kb * 64 <= p && kb * 64 + 63 > p - a.w) {
         f32x4 s[4];
         qk_tile_T<DQ>(kt, qf, s, lr, lg);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t key = kb * 64 + 16 * mt + 4 * lg + r;
-            if (key > p || key <= p - a.w) s[mt][r] = -INFINITY;
-          }
-        softmax_step<DV>(s, m2, l2, o, c, true);
+        if (kb * 64 + 63 > p) mask_from(s, (int)(p + 1 - kb * 64), lg);
+        if (kb * 64 <= p - a.w) mask_below(s, (int)(p - a.w + 1 - kb * 64), lg);
+        softmax_step<DV>(s, m2, l2, o, c, stale, true);
         pv_tile<DV>(vt, s, o, lr, lg);
       }
     }
@@ -468,10 +499,9 @@ __device__ __forceinline__ void load_v(VFrag<DV>& f, __amdgpu_buffer_rsrc_t vr, 
   for (int dt = 0; dt < DV / 16; ++dt) f.v[dt] = bld8(vr, v0, 16 * dt * 32 * 2);
 }
 
-// S^T for the chunk's 32 keys (raw dot products), keys beyond p masked.
+// S^T for the chunk's 32 keys (raw dot products).
 template <int DQ>
-__device__ __forceinline__ void qk_chunk(const KFrag<DQ>& f, const bf16x8 (&qf)[DQ / 32], f32x4& s0, f32x4& s1,
-                                         int64_t kb, int64_t p, int lg) {
+__device__ __forceinline__ void qk_chunk(const KFrag<DQ>& f, const bf16x8 (&qf)[DQ / 32], f32x4& s0, f32x4& s1) {
   s0 = f32x4{0.f, 0.f, 0.f, 0.f};
   s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -479,36 +509,47 @@ __device__ __forceinline__ void qk_chunk(const KFrag<DQ>& f, const bf16x8 (&qf)[
     s0 = mfma16(f.k0[ks], qf[ks], s0);
     s1 = mfma16(f.k1[ks], qf[ks], s1);
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (kb + 8 * lg + r > p) s0[r] = -INFINITY;
-    if (kb + 8 * lg + 4 + r > p) s1[r] = -INFINITY;
-  }
 }
 
-// Online-softmax update of one wave's token (16 heads) with the chunk.
+// Online-softmax update of one wave's token (16 heads, head lr per lane)
+// with a chunk whose keys start at kb; keys beyond p are masked (only the
+// query's own block can have any).  m is a stale maximum in raw dot units:
+// it is raised only when a score exceeds it by more than 2^kStaleLog2 in
+// probability, and only then are l and o rescaled.
 template <int DV>
 __device__ __forceinline__ void pv_chunk(const VFrag<DV>& f, f32x4 s0, f32x4 s1, f32x4 (&o)[DV / 16], float& m,
-                                         float& l, float c) {
-  float tmax = -INFINITY;
+                                         float& l, float c, float stale, int64_t kb, int64_t p, int lg) {
+  if (kb + 31 > p) {
+    const int rel = (int)(p - kb);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 4; ++r) {
+      if (8 * lg + r > rel) s0[r] = -INFINITY;
+      if (8 * lg + 4 + r > rel) s1[r] = -INFINITY;
+    }
+  }
+  float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
   tmax = xor_max16_32(tmax);
-  const float mnew = fmaxf(m, tmax);
-  const float alpha = exp2f((m - mnew) * c);
+  const bool raise = tmax > m + stale;
+  if (__ballot(raise)) {
+    const float mnew = raise ? tmax : m;
+    const float alpha = fast_exp2((m - mnew) * c);
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
+    m = mnew;
+  }
+  const float mc = m * c;
   float rs = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s0[r] = exp2f((s0[r] - mnew) * c);
-    s1[r] = exp2f((s1[r] - mnew) * c);
+    s0[r] = fast_exp2(fmaf(s0[r], c, -mc));
+    s1[r] = fast_exp2(fmaf(s1[r], c, -mc));
     rs += s0[r] + s1[r];
   }
-  rs = xor_sum16_32(rs);
-  l = l * alpha + rs;
-  m = mnew;
+  l += xor_sum16_32(rs);
   const bf16x8 pf = pack8(s0, s1);
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = mfma16(f.v[dt], pf, o[dt] * alpha);
+  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = mfma16(f.v[dt], pf, o[dt]);
 }
 
 template <int DQ, int DV, bool FWD, typename TO>
@@ -558,27 +599,26 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
     pending &= pending - 1;
     return __shfl(kbv, pos, 64);
   };
-  // three-deep software pipeline: while chunk i is computed, chunks i+1 and
-  // i+2 are in flight.  Unrolled by three so every buffer is a fixed set of
-  // registers and every step has exact wait counts.
-  KFrag<DQ> k0, k1, k2;
-  VFrag<DV> v0, v1, v2;
+  // two-stage software pipeline: the next chunk's reads are in flight while
+  // this one is computed (unrolled by two: fixed registers, exact waits)
+  const float stale = kStaleLog2 / c;
+  KFrag<DQ> k0, k1;
+  VFrag<DV> v0, v1;
   auto load = [&](KFrag<DQ>& kf, VFrag<DV>& vf, int64_t kb) {
     load_k<DQ>(kf, kr, kofs, kb, lr);
     load_v<DV>(vf, vr, vofs, kb);
   };
   auto step = [&](const KFrag<DQ>& kf, const VFrag<DV>& vf, int64_t kb) {
     f32x4 s0, s1;
-    qk_chunk<DQ>(kf, qf, s0, s1, kb, p, lg);
-    pv_chunk<DV>(vf, s0, s1, o, m, l, c);
+    qk_chunk<DQ>(kf, qf, s0, s1);
+    pv_chunk<DV>(vf, s0, s1, o, m, l, c, stale, kb, p, lg);
   };
   if (nch > 0) {
-    int64_t c0 = next_kb(), c1 = next_kb(), c2;
+    int64_t c0 = next_kb(), c1;
     load(k0, v0, c0);
-    load(k1, v1, c1);
-    for (int ci = 0; ci < nch; ci += 3) {
-      c2 = next_kb();
-      load(k2, v2, c2);
+    for (int ci = 0; ci < nch; ci += 2) {
+      c1 = next_kb();
+      load(k1, v1, c1);
       __builtin_amdgcn_sched_barrier(0);
       step(k0, v0, c0);
       __builtin_amdgcn_sched_barrier(0);
@@ -587,12 +627,6 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
       load(k0, v0, c0);
       __builtin_amdgcn_sched_barrier(0);
       step(k1, v1, c1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ci + 2 >= nch) break;
-      c1 = next_kb();
-      load(k1, v1, c1);
-      __builtin_amdgcn_sched_barrier(0);
-      step(k2, v2, c2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -51,14 +51,66 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return r;
 }
 
-__device__ __forceinline__ float xor_max16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+// ---- cross-lane reductions without LDS traffic -------------------------
+// gfx950 v_permlane16_swap / v_permlane32_swap called with the same value
+// twice return, in every lane, its own and its partner's value (partner =
+// lane ^ 16, resp. lane ^ 32), in some order.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xor_sum16_32(float x) {
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor_max16_32(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float xor_sum16_32(float x) { return xor32_sum(xor16_sum(x)); }
+
+// DPP lane moves inside a row of 16 lanes.
+template <int CTRL> __device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
+
+// Maximum over all 64 lanes, returned in every lane.
+__device__ __forceinline__ float wave_allmax(float x) {
+  x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
+  return xor_max16_32(x);
+}
+// Minimum of non-negative ints over all 64 lanes, returned in every lane.
+__device__ __forceinline__ int wave_allmin_u(int x) {
+  x = min(x, dpp_i<kDppXor1>(x));
+  x = min(x, dpp_i<kDppXor2>(x));
+  x = min(x, dpp_i<kDppHalfMirror>(x));
+  x = min(x, dpp_i<kDppMirror>(x));
+  auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = min((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return min((int)r[0], (int)r[1]);
+}
+
+// 2^x with the bare hardware instruction (no denormal range fix-up: results
+// below 2^-126 flush to zero, which softmax weights can afford).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online softmax keeps a stale running maximum: it is only raised when a new
+// score exceeds it by more than 2^8 in probability, so the rescale of the
+// accumulators is rare; probabilities then stay below 2^8 (no overflow).
+constexpr float kStaleLog2 = 8.0f;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
