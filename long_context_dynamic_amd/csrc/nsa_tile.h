@@ -1,0 +1,165 @@
+// nsa_tile.h -- LDS tile machinery shared by the FA-style kernels (internal):
+// a register-prefetching stager for 64-key K / V^T tiles, the 64-key online
+// softmax step with a stale maximum, masks, and the two matrix-op products of
+// one tile.  In an S^T tile, s[mt][r] is key 16*mt + 4*lg + r and lane column
+// lr is one query row (a head of a token, or a token of a head).
+#pragma once
+
+#include "nsa_mfma.h"
+
+namespace nsa {
+
+// ---------------------------------------------------------------------------
+// Register-prefetching tile stager: load() issues the global reads of one
+// 64-key tile (K rows [row0, row0 + 64) of a [B, Nrows, G, DQ] tensor, rows
+// clamped to Nrows - 1, and optionally V^T columns [col0, col0 + 64) of a
+// [B, G, DV, Np] tensor) into registers; store() writes them to LDS.  The
+// next tile's reads are in flight while the current tile is computed on.
+template <int DQ, int DV, int NT>
+struct Stager {
+  static constexpr int KS = DQ + 8, VS = 64 + 8;
+  static constexpr int KC = 64 * DQ / 8, VC = DV * 8;
+  static constexpr int KPT = (KC + NT - 1) / NT, VPT = (VC + NT - 1) / NT;
+  u32x4 kr[KPT], vr[VPT];
+
+  // rows: [B, Nrows, G, DQ], or with group_major one paired-row image of
+  // Nrows (a multiple of 64) rows per (b, g);
+  // colsT: tiled [B, G, Np / 32, DV, 32] (a 64-key tile = two 32-key halves)
+  __device__ __forceinline__ void load(const uint16_t* rows, int64_t Nrows, int64_t row0, bool group_major,
+                                       const uint16_t* colsT, int64_t Np, int64_t col0, int64_t b, int64_t g,
+                                       int64_t G, bool with_v) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (KC % NT == 0 || c < KC) {
+        if (group_major) {  // the tile is one contiguous run of the image
+          kr[i] = *(const u32x4*)(rows + ((b * G + g) * Nrows + row0) * DQ + 8 * c);
+        } else {
+          const int r = c / (DQ / 8), c8 = c % (DQ / 8);
+          int64_t row = row0 + r;
+          if (row > Nrows - 1) row = Nrows - 1;
+          kr[i] = *(const u32x4*)(rows + ((b * Nrows + row) * G + g) * DQ + 8 * c8);
+        }
+      }
+    }
+    if (with_v) {
+      const uint16_t* tile = colsT + ((b * G + g) * (Np / 64) + col0 / 64) * DV * 64;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (VC % NT == 0 || c < VC) vr[i] = *(const u32x4*)(tile + 8 * c);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, bool with_v, bool group_major) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (KC % NT == 0 || c < KC) {
+        int r, d;
+        if (group_major) {  // chunk c of the paired-row image: back to (row, dim)
+          const int e = 8 * c, rg = e / (16 * DQ), rem = e % (16 * DQ);
+          const int ks = rem / 512, w8 = (rem % 512) / 64, h = (rem % 64) / 32;
+          r = 16 * rg + 8 * h + w8;
+          d = 32 * ks + (rem % 32);
+        } else {
+          r = c / (DQ / 8);
+          d = 8 * (c % (DQ / 8));
+        }
+        *(u32x4*)(kt + r * KS + d) = kr[i];
+      }
+    }
+    if (with_v) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * NT;  // 16-byte chunk c: half c / (4 DV), row d, keys 8 * (c % 4)
+        const int h = c / (4 * DV), d = (c / 4) % DV, j8 = c % 4;
+        if (VC % NT == 0 || c < VC) *(u32x4*)(vt + d * VS + 32 * h + 8 * j8) = vr[i];
+      }
+    }
+  }
+};
+
+// One 64-key online-softmax step for one token (16 heads) of one wave.
+// s[mt] holds S^T for keys 16*mt + 4*lg + r (raw dot products, masked ones
+// already -inf); updates the stale maximum m (raw units, raised only by more
+// than 2^kStaleLog2 in probability), the sum l of head lr, and rescales o
+// when m moves.
+template <int DV>
+__device__ __forceinline__ void softmax_step(f32x4 (&s)[4], float& m, float& l, f32x4 (&o)[DV / 16], float c,
+                                             float stale, bool with_o) {
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) tmax = fmaxf(tmax, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+  tmax = xor_max16_32(tmax);
+  const bool raise = tmax > m + stale;
+  if (__ballot(raise)) {
+    const float mnew = raise ? tmax : m;
+    const float alpha = fast_exp2((m - mnew) * c);
+    l *= alpha;
+    if (with_o) {
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
+    }
+    m = mnew;
+  }
+  const float mc = m * c;
+  float rs = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pv = fast_exp2(fmaf(s[mt][r], c, -mc));
+      s[mt][r] = pv;
+      rs += pv;
+    }
+  l += xor_sum16_32(rs);
+}
+
+// Keys (rows of an S^T tile) at or beyond `limit` relative to the tile
+// start are masked: s[mt][r] is key 16*mt + 4*lg + r.
+__device__ __forceinline__ void mask_from(f32x4 (&s)[4], int limit, int lg) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (16 * mt + 4 * lg + r >= limit) s[mt][r] = -INFINITY;
+}
+// ... and keys below `first`.
+__device__ __forceinline__ void mask_below(f32x4 (&s)[4], int first, int lg) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (16 * mt + 4 * lg + r < first) s[mt][r] = -INFINITY;
+}
+
+// O^T[d, h] += V^T[d, keys] P^T[keys, h] over one 64-key LDS tile.
+template <int DV>
+__device__ __forceinline__ void pv_tile(const uint16_t* vt, const f32x4 (&pm)[4], f32x4 (&o)[DV / 16], int lr,
+                                        int lg) {
+  constexpr int VS = 64 + 8;
+  const bf16x8 p0 = pack8(pm[0], pm[1]);
+  const bf16x8 p1 = pack8(pm[2], pm[3]);
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) {
+    const uint16_t* row = vt + (16 * dt + lr) * VS;
+    o[dt] = mfma16(ld4x2(row + 4 * lg, row + 16 + 4 * lg), p0, o[dt]);
+    o[dt] = mfma16(ld4x2(row + 32 + 4 * lg, row + 48 + 4 * lg), p1, o[dt]);
+  }
+}
+
+// S^T[key, h] for 64 keys of an LDS tile: s[mt] = K rows 16*mt.. x Q^T.
+template <int DQ>
+__device__ __forceinline__ void qk_tile_T(const uint16_t* kt, const bf16x8 (&qf)[DQ / 32], f32x4 (&s)[4], int lr,
+                                          int lg) {
+  constexpr int KS = DQ + 8;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DQ / 32; ++ks) s[mt] = mfma16(ld8(kt + (16 * mt + lr) * KS + 8 * lg + 32 * ks), qf[ks], s[mt]);
+  }
+}
+
+}  // namespace nsa
