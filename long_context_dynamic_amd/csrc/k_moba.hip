@@ -1,0 +1,474 @@
+// k_moba.hip -- MoBA on the matrix cores ([P1] s7, [P5] s13): every head has
+// its own K/V, scores its past blocks by the mean key, keeps its own top-k
+// (the current block always), and attends with one softmax to the chosen
+// blocks, causally inside the current one.
+//
+// With one head per KV group the matrix M dimension cannot come from heads,
+// so the work is reorganised around the blocks ([P1] s7: the queries that
+// chose a block are gathered and run against it as one dense product):
+//
+//   k_moba_select  one workgroup per (head, 64-token tile): block scores
+//                  Q . kmean^T on the matrix cores, per-token softmax and top-k
+//                  with row reductions (DPP), sorted idx (+ scores).
+//   k_moba_count / k_moba_scan / k_moba_fill
+//                  list, for every (head, block), the (token, slot) entries
+//                  that chose it (the current block excluded).
+//   k_moba_attn    one workgroup per 64 listed entries of one (head, block):
+//                  the block's K and V^T tiles are staged through LDS once and
+//                  shared by the 64 gathered queries; writes a (max, sum,
+//                  output) partial per entry.
+//   k_moba_diag    one workgroup per (head, 64-token tile): causal attention
+//                  over the query's own block, then the log-sum-exp merge with
+//                  the entries' partials, output.
+#include <math.h>
+
+#include "nsa_mfma.h"
+#include "nsa_moba.h"
+#include "nsa_tile.h"
+
+namespace nsa {
+namespace {
+
+constexpr int kRows = 64;  // gathered query rows per workgroup (4 waves x 16)
+
+// Partial record of one entry: D outputs, max (log2 units), sum, 2 spare
+// (16-byte aligned records).
+template <int D> constexpr int rec_floats() { return D + 4; }
+
+// Row reductions over the 16 lanes of a DPP row (lanes 16*lg .. 16*lg + 15).
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
+  return fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(dpp_i<kDppXor1>(__float_as_int(x)));
+  x += __int_as_float(dpp_i<kDppXor2>(__float_as_int(x)));
+  x += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x)));
+  return x + __int_as_float(dpp_i<kDppMirror>(__float_as_int(x)));
+}
+__device__ __forceinline__ int row_min16(int x) {
+  x = min(x, dpp_i<kDppXor1>(x));
+  x = min(x, dpp_i<kDppXor2>(x));
+  x = min(x, dpp_i<kDppHalfMirror>(x));
+  return min(x, dpp_i<kDppMirror>(x));
+}
+
+// ---------------------------------------------------------------------------
+// NT = number of 16-block column tiles (nbp / 16).
+template <int D, int NT>
+__global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int64_t ntile = (a.T + kRows - 1) / kRows;
+  const int64_t h = blockIdx.x % a.H;
+  const int64_t tile = (blockIdx.x / a.H) % ntile;
+  const int64_t b = blockIdx.x / (a.H * ntile);
+  const int64_t t0 = tile * kRows + 16 * wave;  // this wave's 16 tokens
+  // S = Q . Kc^T: A = token rows (lane: token t0 + lr), B = block rows
+  bf16x8 qf[D / 32];
+  {
+    int64_t tq = t0 + lr;
+    if (tq > a.T - 1) tq = a.T - 1;
+    const uint16_t* qr = a.q + ((b * a.T + tq) * a.H + h) * D + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+  }
+  float z[NT][4];  // z[nt][r]: token t0 + 4*lg + r, block 16*nt + lr
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int64_t blk = 16 * nt + lr;
+    if (blk > a.nb - 1) blk = a.nb - 1;
+    const uint16_t* kr = a.kc + ((b * a.nb + blk) * a.H + h) * D + 8 * lg;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) s = mfma16(qf[ks], ld8(kr + 32 * ks), s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[nt][r] = s[r] * a.scale;
+  }
+  const bool first = a.flags & NSA_F_FORCE_FIRST, current = a.flags & NSA_F_FORCE_CURRENT;
+  int chosen[4][8];  // per token: the chosen blocks, forced ones first
+  float cscore[4][8];
+  int cnt[4];
+  bool done[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = t0 + 4 * lg + r;
+    const int64_t p = a.L - a.T + (t < a.T ? t : a.T - 1);
+    int64_t nvis = (p + 1) / a.bs;
+    if (nvis > a.nb) nvis = a.nb;
+    const int64_t cur = p / a.bs;
+    // per-token softmax over the visible blocks: the probabilities are the
+    // block scores
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (16 * nt + lr >= nvis) z[nt][r] = -INFINITY;
+      mx = fmaxf(mx, z[nt][r]);
+    }
+    mx = row_max16(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float e = z[nt][r] == -INFINITY ? 0.f : expf(z[nt][r] - mx);
+      z[nt][r] = e;
+      sm += e;
+    }
+    const float inv = nvis > 0 ? 1.f / row_sum16(sm) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { chosen[r][i] = 0x7fffffff; cscore[r][i] = -INFINITY; }
+    int nf = 0;
+    if (first) { chosen[r][0] = 0; cscore[r][0] = INFINITY; nf = 1; }
+    if (current && !(first && cur == 0)) {
+      if (nf == 0) { chosen[r][0] = (int)cur; cscore[r][0] = INFINITY; }
+      else { chosen[r][1] = (int)cur; cscore[r][1] = INFINITY; }
+      ++nf;
+    }
+    // candidates: visible and not forced (others get -1, below any probability)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t j = 16 * nt + lr;
+      const bool forced = (first && j == 0) || (current && j == cur);
+      z[nt][r] = (j < nvis && !forced) ? z[nt][r] * inv : -1.f;
+    }
+    cnt[r] = nf;
+    done[r] = nf >= a.n;
+  }
+  // the best remaining candidate, one per round: the row maximum, and the
+  // lowest block among equal maxima (ties go to the earlier block)
+  for (int round = 0; round < 8 && round < a.n; ++round) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (done[r]) continue;  // uniform within a DPP row (the token's 16 lanes)
+      float bv = -1.f;
+      int bj = 0x7fffffff;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (z[nt][r] > bv) { bv = z[nt][r]; bj = 16 * nt + lr; }
+      const float M = row_max16(bv);
+      if (M < 0.f) { done[r] = true; continue; }  // no candidate left
+      const int J = row_min16(bv == M ? bj : 0x7fffffff);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i == cnt[r]) { chosen[r][i] = J; cscore[r][i] = M; }
+      ++cnt[r];
+      done[r] = cnt[r] >= a.n;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (16 * nt + lr == J) z[nt][r] = -1.f;
+    }
+  }
+  if (lr != 0) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = t0 + 4 * lg + r;
+    if (t >= a.T) continue;
+    // ascending block order (unused slots hold INT_MAX and sort last)
+#pragma unroll
+    for (int i = 0; i < 7; ++i)
+#pragma unroll
+      for (int k2 = 0; k2 < 7 - i; ++k2)
+        if (chosen[r][k2] > chosen[r][k2 + 1]) {
+          const int tj = chosen[r][k2];
+          chosen[r][k2] = chosen[r][k2 + 1];
+          chosen[r][k2 + 1] = tj;
+          const float ts = cscore[r][k2];
+          cscore[r][k2] = cscore[r][k2 + 1];
+          cscore[r][k2 + 1] = ts;
+        }
+    int32_t* orow = a.idx + ((b * a.T + t) * a.H + h) * a.n;
+    float* srow = a.score ? a.score + ((b * a.T + t) * a.H + h) * a.n : nullptr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i >= a.n) break;
+      orow[i] = i < cnt[r] ? chosen[r][i] : -1;
+      if (srow) srow[i] = i < cnt[r] ? cscore[r][i] : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+__global__ void k_moba_zero(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// One thread per entry (b, t, h, slot): a chosen block before the token's
+// own goes to its (b, h, block) list; pos = place in the list (-1: not
+// listed: an empty slot, the token's own block, or a block after it, which a
+// valid selection never holds).
+__global__ void k_moba_count(MobaArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= a.B * a.T * a.H * a.n) return;
+  const int64_t h = (e / a.n) % a.H;
+  const int64_t bt = e / (a.n * a.H);
+  const int64_t b = bt / a.T, t = bt % a.T;
+  const int64_t p = a.L - a.T + t;
+  const int j = a.idx[e];
+  int pos = -1;
+  if (j >= 0 && (int64_t)j < p / a.bs) pos = atomicAdd(&a.counts[(b * a.H + h) * a.nb + j], 1);
+  a.pos[e] = pos;
+}
+
+// Single workgroup: exclusive prefix sums of the list lengths and of their
+// 64-entry chunk counts.
+__global__ void __launch_bounds__(1024) k_moba_scan(MobaArgs a) {
+  __shared__ int32_t part_e[1024], part_c[1024];
+  const int64_t n = a.B * a.H * a.nb;
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = tid * per, hi = lo + per < n ? lo + per : n;
+  int32_t se = 0, sc = 0;
+  for (int64_t i = lo; i < hi; ++i) { se += a.counts[i]; sc += (a.counts[i] + kRows - 1) / kRows; }
+  part_e[tid] = se;
+  part_c[tid] = sc;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t ae = 0, ac = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int32_t xe = part_e[i], xc = part_c[i];
+      part_e[i] = ae;
+      part_c[i] = ac;
+      ae += xe;
+      ac += xc;
+    }
+    a.offsets[n] = ae;
+    a.chunk_off[n] = ac;
+  }
+  __syncthreads();
+  int32_t ae = part_e[tid], ac = part_c[tid];
+  for (int64_t i = lo; i < hi; ++i) {
+    a.offsets[i] = ae;
+    a.chunk_off[i] = ac;
+    ae += a.counts[i];
+    ac += (a.counts[i] + kRows - 1) / kRows;
+  }
+}
+
+__global__ void k_moba_fill(MobaArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= a.B * a.T * a.H * a.n) return;
+  const int pos = a.pos[e];
+  if (pos < 0) return;
+  const int64_t h = (e / a.n) % a.H;
+  const int64_t b = e / (a.n * a.H * a.T);
+  const int j = a.idx[e];
+  a.lists[a.offsets[(b * a.H + h) * a.nb + j] + pos] = (int32_t)e;
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) k_moba_attn(MobaArgs a) {
+  __shared__ __align__(16) uint16_t kt[64 * (D + 8)];
+  __shared__ __align__(16) uint16_t vt[D * (64 + 8)];
+  const int64_t nl = a.B * a.H * a.nb;
+  const int32_t w = (int32_t)blockIdx.x;
+  if (w >= a.chunk_off[nl]) return;
+  // the (b, h, block) list this chunk belongs to
+  int64_t lo = 0, hi = nl;  // chunk_off[lo] <= w < chunk_off[hi]
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (a.chunk_off[mid] <= w) lo = mid;
+    else hi = mid;
+  }
+  const int64_t bhj = lo;
+  const int64_t j = bhj % a.nb, h = (bhj / a.nb) % a.H, b = bhj / (a.nb * a.H);
+  const int64_t first = a.offsets[bhj] + (int64_t)(w - a.chunk_off[bhj]) * kRows;
+  const int64_t count = a.offsets[bhj + 1] - first;  // entries left in this list
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int row = 16 * wave + lr;
+  const bool valid = row < count;
+  const int64_t e = a.lists[first + (valid ? row : 0)];
+  const int64_t t = (e / (a.n * a.H)) % a.T;
+  bf16x8 qf[D / 32];
+  {
+    const uint16_t* qr = a.q + ((b * a.T + t) * a.H + h) * D + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+  }
+  const float c = a.scale * kLog2e, stale = kStaleLog2 / c;
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Stager<D, D, 256> st;
+  const int64_t kb0 = j * a.bs, ntl = a.bs / 64;
+  st.load(a.k, a.L, kb0, false, a.vT, a.Lp, kb0, b, h, a.H, true);
+  for (int64_t i = 0; i < ntl; ++i) {
+    __syncthreads();
+    st.store(kt, vt, true, false);
+    __syncthreads();
+    if (i + 1 < ntl) st.load(a.k, a.L, kb0 + 64 * (i + 1), false, a.vT, a.Lp, kb0 + 64 * (i + 1), b, h, a.H, true);
+    f32x4 s[4];
+    qk_tile_T<D>(kt, qf, s, lr, lg);
+    softmax_step<D>(s, m, l, o, c, stale, true);
+    pv_tile<D>(vt, s, o, lr, lg);
+  }
+  if (!valid) return;
+  float* rec = a.part + e * rec_floats<D>();
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(rec + 16 * dt + 4 * lg) = o[dt];
+  if (lg == 0) {
+    rec[D] = m * c;
+    rec[D + 1] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename TO> __device__ __forceinline__ void mstore4(TO* p, f32x4 v);
+template <> __device__ __forceinline__ void mstore4<float>(float* p, f32x4 v) { *(f32x4*)p = v; }
+template <> __device__ __forceinline__ void mstore4<uint16_t>(uint16_t* p, f32x4 v) {
+  u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+             (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+  *(u32x2*)p = w;
+}
+
+// Query tiles follow the absolute 64-position grid, so a tile never spans two
+// blocks (blocks are multiples of 64 long) and its keys start on a tile.
+template <int D, typename TO>
+__global__ void __launch_bounds__(256) k_moba_diag(MobaArgs a) {
+  __shared__ __align__(16) uint16_t kt[64 * (D + 8)];
+  __shared__ __align__(16) uint16_t vt[D * (64 + 8)];
+  const int64_t P0 = a.L - a.T;  // position of token 0
+  const int64_t pt0 = P0 / 64, ntile = (a.L - 1) / 64 - pt0 + 1;
+  const int64_t h = blockIdx.x % a.H;
+  const int64_t pt = pt0 + ntile - 1 - (blockIdx.x / a.H) % ntile;  // longest rows first
+  const int64_t b = blockIdx.x / (a.H * ntile);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int64_t p_first = 64 * pt > P0 ? 64 * pt : P0;
+  const int64_t p_last = 64 * pt + 63 < a.L - 1 ? 64 * pt + 63 : a.L - 1;
+  const int64_t pl = 64 * pt + 16 * wave + lr;
+  const bool valid = pl >= P0 && pl < a.L;
+  const int64_t p = valid ? pl : p_last;  // out-of-range lanes shadow the last row
+  const int64_t t = p - P0;
+  const int64_t cur = 64 * pt / a.bs;
+  // does this token's selection hold its own block?
+  const int32_t* irow = a.idx + ((b * a.T + t) * a.H + h) * a.n;
+  bool has_cur = false;
+  for (int i = 0; i < a.n; ++i) has_cur |= (irow[i] == cur);
+  bf16x8 qf[D / 32];
+  {
+    const uint16_t* qr = a.q + ((b * a.T + t) * a.H + h) * D + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+  }
+  const float c = a.scale * kLog2e, stale = kStaleLog2 / c;
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Stager<D, D, 256> st;
+  const int64_t kt0 = cur * a.bs / 64, kt1 = p_last / 64;
+  st.load(a.k, a.L, kt0 * 64, false, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
+  for (int64_t kb = kt0; kb <= kt1; ++kb) {
+    __syncthreads();
+    st.store(kt, vt, true, false);
+    __syncthreads();
+    if (kb + 1 <= kt1) st.load(a.k, a.L, (kb + 1) * 64, false, a.vT, a.Lp, (kb + 1) * 64, b, h, a.H, true);
+    f32x4 s[4];
+    qk_tile_T<D>(kt, qf, s, lr, lg);
+    // keys after the query (only in the tiles that reach the first row), and
+    // every key of a row whose selection lacks its own block
+    if (kb * 64 + 63 > p_first || !has_cur) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!has_cur || kb * 64 + 16 * mt + 4 * lg + r > p) s[mt][r] = -INFINITY;
+    }
+    softmax_step<D>(s, m, l, o, c, stale, true);
+    pv_tile<D>(vt, s, o, lr, lg);
+  }
+  if (!valid) return;
+  // merge with the partials of the earlier chosen blocks (log2 units)
+  const bool own = has_cur && l > 0.f;  // a row without its own block ran on -inf only
+  const float* prow = a.part + ((b * a.T + t) * a.H + h) * a.n * rec_floats<D>();
+  float M = own ? m * c : -INFINITY;
+  for (int i = 0; i < a.n; ++i) {
+    const int j = irow[i];
+    if (j >= 0 && j < cur) M = fmaxf(M, prow[i * rec_floats<D>() + D]);
+  }
+  const float wd = own ? exp2f(m * c - M) : 0.f;
+  float den = own ? wd * l : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = own ? o[dt] * wd : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < a.n; ++i) {
+    const int j = irow[i];
+    if (j < 0 || j >= cur) continue;
+    const float* rec = prow + i * rec_floats<D>();
+    const float ws = exp2f(rec[D] - M);
+    den = fmaf(ws, rec[D + 1], den);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] += *(const f32x4*)(rec + 16 * dt + 4 * lg) * ws;
+  }
+  float g = den > 0.f ? 1.f / den : 0.f;
+  if (a.gates) {
+    float x = bf16_to_f32(a.gates[((b * a.T + t) * a.H + h) * 3 + 1]);
+    if (a.flags & NSA_F_GATE_LOGITS) x = sigmoid(x);
+    g *= x;
+  }
+  TO* orow = (TO*)a.out + ((b * a.T + t) * a.H + h) * D + 4 * lg;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) mstore4<TO>(orow + 16 * dt, o[dt] * g);
+  if (a.lse && lg == 0) a.lse[(b * a.T + t) * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int D>
+hipError_t run_select_t(const MobaArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.B * a.H * ((a.T + kRows - 1) / kRows));
+  switch (a.nbp / 64) {
+    case 1: k_moba_select<D, 4><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_moba_select<D, 8><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_moba_select<D, 12><<<grid, 256, 0, s>>>(a); break;
+    default: k_moba_select<D, 16><<<grid, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_attend_t(const MobaArgs& a, bool out_f32, hipStream_t s, Phases* ph) {
+  const int64_t ne = a.B * a.T * a.H * a.n, nl = a.B * a.H * a.nb;
+  k_moba_zero<<<(unsigned)((nl + 255) / 256), 256, 0, s>>>(a.counts, nl);
+  k_moba_count<<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(a);
+  k_moba_scan<<<1, 1024, 0, s>>>(a);
+  k_moba_fill<<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(a);
+  if (ph) ph->mark();
+  // an upper bound of the chunk count; surplus workgroups exit at once
+  const unsigned gattn = (unsigned)((ne + kRows - 1) / kRows + nl);
+  k_moba_attn<D><<<gattn, 256, 0, s>>>(a);
+  if (ph) ph->mark();
+  const int64_t pt0 = (a.L - a.T) / 64;
+  const unsigned gdiag = (unsigned)(a.B * a.H * ((a.L - 1) / 64 - pt0 + 1));
+  if (out_f32) k_moba_diag<D, float><<<gdiag, 256, 0, s>>>(a);
+  else k_moba_diag<D, uint16_t><<<gdiag, 256, 0, s>>>(a);
+  if (ph) ph->mark();
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool moba_select_ok(const Prob& P) {
+  const int64_t nbp = (P.nb + 63) / 64 * 64;
+  return P.bf16() && P.hpg == 1 && (P.dq == 64 || P.dq == 128) && P.nb >= 1 && nbp <= 256 && P.n >= 1 &&
+         P.n <= 8;
+}
+
+bool moba_attend_ok(const Prob& P) {
+  return P.bf16() && P.hpg == 1 && P.dq == P.dv && (P.dq == 64 || P.dq == 128) && P.bs % 64 == 0 && P.n >= 1 &&
+         P.n <= 8 && P.B * P.T * P.H * P.n < ((int64_t)1 << 31) && P.B * P.H * P.nb < ((int64_t)1 << 30);
+}
+
+bool moba_ok(const Prob& P) {
+  return moba_select_ok(P) && moba_attend_ok(P) && P.has(NSA_F_SLC) && !P.has(NSA_F_CMP) && !P.has(NSA_F_WIN);
+}
+
+hipError_t launch_moba_select(const Prob& P, const MobaArgs& a, hipStream_t s) {
+  if (P.dq == 128) return run_select_t<128>(a, s);
+  return run_select_t<64>(a, s);
+}
+
+hipError_t launch_moba_attend(const Prob& P, const MobaArgs& a, bool out_f32, hipStream_t s, Phases* ph) {
+  if (P.dq == 128) return run_attend_t<128>(a, out_f32, s, ph);
+  return run_attend_t<64>(a, out_f32, s, ph);
+}
+
+}  // namespace nsa

@@ -18,7 +18,12 @@ struct Workspace {
   size_t vcT = 0;         // value summaries, tiled [B, G, round_up(nb, 64) / 32, d_v, 32]
   size_t acc = 0;         // fp32 [B, T, H, d_v] gated compressed + window sum
   size_t zbuf = 0;        // decoding: fp32 [B*T, G, 16, round_up(nb, 64)] logits
-  size_t part = 0;        // decoding: partial attention records
+  size_t part = 0;        // decoding, MoBA: partial attention records
+  size_t counts = 0;      // MoBA: int32 [B, H, nb] entries per (b, h, block)
+  size_t pos = 0;         // MoBA: int32 [B, T, H, top_k] place of an entry in its list
+  size_t offsets = 0;     // MoBA: int32 [B*H*nb + 1] list starts
+  size_t chunk_off = 0;   // MoBA: int32 [B*H*nb + 1] first 64-entry chunk per list
+  size_t lists = 0;       // MoBA: int32 [B*T*H*top_k] entries grouped by list
 };
 
 // Records an event before the first and after every launch (timing hook).

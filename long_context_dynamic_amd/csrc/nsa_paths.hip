@@ -2,7 +2,10 @@
 // for the shapes they take (bf16, 16 heads per group, 64-token blocks), the
 // any-shape kernels otherwise.
 #include "nsa_paths.h"
+
+#include <functional>
 #include "nsa_decode.h"
+#include "nsa_moba.h"
 #include "nsa_prefill.h"
 
 namespace nsa {
@@ -29,12 +32,42 @@ PfArgs pf_args(const Prob& P) {
   return a;
 }
 
+MobaArgs moba_args(const Prob& P) {
+  MobaArgs a = {};
+  a.B = P.B; a.T = P.T; a.L = P.L; a.H = P.H; a.nb = P.nb;
+  a.nbp = pad64(P.nb); a.Lp = pad64(P.L); a.bs = P.bs; a.n = P.n;
+  a.flags = P.flags; a.scale = P.scale;
+  return a;
+}
+
+// The MoBA attention stage: entry lists and partial records.
+void take_moba(const Prob& P, Workspace& w, const std::function<size_t(size_t)>& take) {
+  const size_t ne = (size_t)(P.B * P.T * P.H * P.n), nl = (size_t)(P.B * P.H * P.nb);
+  w.vT = take((size_t)(P.B * P.H * P.dv * pad64(P.L)) * 2);
+  w.counts = take(nl * sizeof(int32_t));
+  w.pos = take(ne * sizeof(int32_t));
+  w.offsets = take((nl + 1) * sizeof(int32_t));
+  w.chunk_off = take((nl + 1) * sizeof(int32_t));
+  w.lists = take(ne * sizeof(int32_t));
+  w.part = take(ne * (size_t)(P.dv + 4) * sizeof(float));
+}
+
+void set_moba_ws(MobaArgs& a, const Workspace& ws, void* base) {
+  a.vT = at<uint16_t>(base, ws.vT);
+  a.counts = at<int32_t>(base, ws.counts);
+  a.pos = at<int32_t>(base, ws.pos);
+  a.offsets = at<int32_t>(base, ws.offsets);
+  a.chunk_off = at<int32_t>(base, ws.chunk_off);
+  a.lists = at<int32_t>(base, ws.lists);
+  a.part = at<float>(base, ws.part);
+}
+
 }  // namespace
 
 Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
   Workspace w;
   size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
+  std::function<size_t(size_t)> take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   const bool fast = prefill_fast_ok(P);
   const bool dec = decode_ok(P);
   const size_t zbytes = (size_t)(P.B * P.T * P.G * 16 * pad64(P.nb)) * sizeof(float);
@@ -47,7 +80,9 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     return w;
   }
   if (call == Call::SparseAttn) {
-    if (dec) {
+    if (!dec && !fast && moba_attend_ok(P)) {
+      take_moba(P, w, take);
+    } else if (dec) {
       w.part = take(decode_part_bytes(P));
     } else if (fast) {
       w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
@@ -61,7 +96,9 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     w.vc = take((size_t)(P.B * P.nb * P.G * P.dv) * elem_bytes(P));
   }
   w.idx = take((size_t)(P.B * P.T * P.G * P.n) * sizeof(int32_t));
-  if (dec) {
+  if (!dec && !fast && moba_ok(P)) {
+    take_moba(P, w, take);
+  } else if (dec) {
     w.zbuf = take(zbytes);
     w.part = take(decode_part_bytes(P));
   } else if (fast) {
@@ -94,6 +131,12 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
     list[n++] = "dec_select";
     list[n++] = "dec_attn";
     list[n++] = "dec_merge";
+  } else if (moba_ok(P)) {
+    list[n++] = "transpose_v";
+    list[n++] = "moba_select";
+    list[n++] = "moba_lists";
+    list[n++] = "moba_attn";
+    list[n++] = "moba_own_block";
   } else if (prefill_fast_ok(P)) {
     list[n++] = "transpose_vc";
     list[n++] = "transpose_v";
@@ -128,6 +171,14 @@ hipError_t run_select(const Prob& P, const void* q, const void* kc, int32_t* idx
     a.score = score;
     return launch_cmpwin(P, a, false, s);
   }
+  if (moba_select_ok(P)) {
+    MobaArgs a = moba_args(P);
+    a.q = (const uint16_t*)q;
+    a.kc = (const uint16_t*)kc;
+    a.idx = idx;
+    a.score = score;
+    return launch_moba_select(P, a, s);
+  }
   return launch_select_generic(P, q, kc, nullptr, idx, score, nullptr, s);
 }
 
@@ -161,6 +212,18 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
     a.out = out;
     a.lse = lse;
     return launch_sel(P, a, false, P.has(NSA_F_OUT_F32), s);
+  }
+  if (moba_attend_ok(P)) {
+    MobaArgs a = moba_args(S);
+    set_moba_ws(a, ws, base);
+    hipError_t e = launch_transpose(v, (void*)a.vT, P.B, P.L, a.Lp, P.H, (int)P.dv, s);
+    if (e != hipSuccess) return e;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.idx = (int32_t*)idx;
+    a.out = out;
+    a.lse = lse;
+    return launch_moba_attend(P, a, P.has(NSA_F_OUT_F32), s, nullptr);
   }
   return launch_attend_generic(S, q, k, v, nullptr, idx, nullptr, out, lse, P.has(NSA_F_OUT_F32), s);
 }
@@ -220,6 +283,22 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     ph.mark();
     if ((e = launch_sel(P, a, true, P.has(NSA_F_OUT_F32), s)) != hipSuccess) return e;
     ph.mark();
+    return ph.err;
+  }
+  if (moba_ok(P)) {
+    MobaArgs a = moba_args(P);
+    set_moba_ws(a, ws, base);
+    if ((e = launch_transpose(v, (void*)a.vT, P.B, P.L, a.Lp, P.H, (int)P.dv, s)) != hipSuccess) return e;
+    ph.mark();
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.kc = (const uint16_t*)kc;
+    a.gates = (const uint16_t*)gates;
+    a.idx = idx;
+    a.out = out;
+    if ((e = launch_moba_select(P, a, s)) != hipSuccess) return e;
+    ph.mark();
+    if ((e = launch_moba_attend(P, a, P.has(NSA_F_OUT_F32), s, &ph)) != hipSuccess) return e;
     return ph.err;
   }
   float* ocmp = P.has(NSA_F_CMP) ? at<float>(base, ws.ocmp) : nullptr;

@@ -26,6 +26,8 @@ CASES = [
     ("nsa_prefill_8k", {}, 48),
     ("nsa_prefill_64k", {}, 20),
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
+    ("moba_32k", dict(q_len=700, kv_len=3000), None),
+    ("moba_32k", dict(batch=2, q_len=1000, kv_len=12000, block=64, top_k=8, d_qk=64, d_v=64, force_first=1), None),
     ("moba_32k", {}, 24),
     ("nsa_decode_64x64k", dict(batch=6, kv_len=4096 + 17), None),
 ]
@@ -213,3 +215,21 @@ def test_decode_full_size_sampled_sequences():
         err = np.abs(got - want)
         print(f"seq {b}: max err {err.max():.3e}, tie-band groups {band}")
         assert np.all(err <= U.out_tolerance(prob, want, False))
+
+
+def test_moba_forward_applies_the_gate():
+    # one branch with gates given: the output is the gate times that branch
+    prob = workloads.get("moba_32k", q_len=640, kv_len=1600, gate_logits=1)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    out = nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"], out_f32=True)
+    gidx, _ = nsa.select_topk(prob, t["q"], nsa.compress(prob, t["k"], t["v"])[0], want_score=False)
+    torch.cuda.synchronize()
+    rows = np.arange(prob["q_len"])
+    kc, vc = oracle.pool(prob, x["k"], x["v"])
+    idx, imp, _ = oracle.select(prob, x["q"], kc, vc, rows=rows)
+    gsel = U.gather_rows(gidx.cpu().numpy(), prob, rows)
+    U.check_selection(prob, rows, gsel, idx, imp)
+    want, _, _ = oracle.attend(prob, x["q"], x["k"], x["v"], x["gates"], gsel, None, rows=rows)
+    got = U.gather_rows(U.widen_out(out, prob), prob, rows)
+    assert np.abs(got - want).max() <= U.TOL[prob["dtype"]]
