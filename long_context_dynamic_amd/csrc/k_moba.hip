@@ -29,7 +29,10 @@
 namespace nsa {
 namespace {
 
-constexpr int kRows = 64;  // gathered query rows per workgroup (4 waves x 16)
+constexpr int kRows = 64;    // tokens per selection workgroup (4 waves x 16)
+constexpr int kChunk = 128;  // listed entries per attention workgroup (4 waves x 2 x 16)
+constexpr int kCountTok = 256;  // tokens per list-counting workgroup
+constexpr int kXcds = 8;     // the chip's compute dies, each with its own L2
 
 // Partial record of one entry: D outputs, max (log2 units), sum, 2 spare
 // (16-byte aligned records).
@@ -192,25 +195,43 @@ __global__ void k_moba_zero(int32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// One thread per entry (b, t, h, slot): a chosen block before the token's
-// own goes to its (b, h, block) list; pos = place in the list (-1: not
-// listed: an empty slot, the token's own block, or a block after it, which a
-// valid selection never holds).
-__global__ void k_moba_count(MobaArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.B * a.T * a.H * a.n) return;
-  const int64_t h = (e / a.n) % a.H;
-  const int64_t bt = e / (a.n * a.H);
-  const int64_t b = bt / a.T, t = bt % a.T;
-  const int64_t p = a.L - a.T + t;
-  const int j = a.idx[e];
-  int pos = -1;
-  if (j >= 0 && (int64_t)j < p / a.bs) pos = atomicAdd(&a.counts[(b * a.H + h) * a.nb + j], 1);
-  a.pos[e] = pos;
+// One workgroup per (b, h, 256 tokens), one thread per token: a chosen block
+// before the token's own goes to its (b, h, block) list (an empty slot, the
+// token's own block and a block after it, which a valid selection never
+// holds, stay unlisted: pos = -1).  Places are counted in an LDS histogram
+// first, then reserved in the global count with one atomic per touched block.
+__global__ void __launch_bounds__(256) k_moba_count(MobaArgs a) {
+  extern __shared__ int32_t hist[];  // [nb]
+  const int64_t nr = (a.T + kCountTok - 1) / kCountTok;
+  const int64_t h = blockIdx.x % a.H;
+  const int64_t b = blockIdx.x / (a.H * nr);
+  const int64_t t = (blockIdx.x / a.H) % nr * kCountTok + threadIdx.x;
+  for (int64_t j = threadIdx.x; j < a.nb; j += blockDim.x) hist[j] = 0;
+  __syncthreads();
+  const bool tv = t < a.T;
+  const int64_t cur = (a.L - a.T + t) / a.bs;
+  const int64_t e0 = ((b * a.T + t) * a.H + h) * a.n;
+  int js[8], loc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    js[i] = (tv && i < a.n) ? a.idx[e0 + i] : -1;
+    const bool listed = js[i] >= 0 && (int64_t)js[i] < cur;
+    loc[i] = listed ? atomicAdd(&hist[js[i]], 1) : -1;
+  }
+  __syncthreads();
+  int32_t* cnt = a.counts + (b * a.H + h) * a.nb;
+  for (int64_t j = threadIdx.x; j < a.nb; j += blockDim.x) {
+    const int32_t c = hist[j];
+    if (c) hist[j] = atomicAdd(&cnt[j], c);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (tv && i < a.n) a.pos[e0 + i] = loc[i] >= 0 ? hist[js[i]] + loc[i] : -1;
 }
 
 // Single workgroup: exclusive prefix sums of the list lengths and of their
-// 64-entry chunk counts.
+// 128-entry chunk counts.
 __global__ void __launch_bounds__(1024) k_moba_scan(MobaArgs a) {
   __shared__ int32_t part_e[1024], part_c[1024];
   const int64_t n = a.B * a.H * a.nb;
@@ -218,7 +239,7 @@ __global__ void __launch_bounds__(1024) k_moba_scan(MobaArgs a) {
   const int64_t per = (n + 1023) / 1024;
   const int64_t lo = tid * per, hi = lo + per < n ? lo + per : n;
   int32_t se = 0, sc = 0;
-  for (int64_t i = lo; i < hi; ++i) { se += a.counts[i]; sc += (a.counts[i] + kRows - 1) / kRows; }
+  for (int64_t i = lo; i < hi; ++i) { se += a.counts[i]; sc += (a.counts[i] + kChunk - 1) / kChunk; }
   part_e[tid] = se;
   part_c[tid] = sc;
   __syncthreads();
@@ -240,7 +261,7 @@ __global__ void __launch_bounds__(1024) k_moba_scan(MobaArgs a) {
     a.offsets[i] = ae;
     a.chunk_off[i] = ac;
     ae += a.counts[i];
-    ac += (a.counts[i] + kRows - 1) / kRows;
+    ac += (a.counts[i] + kChunk - 1) / kChunk;
   }
 }
 
@@ -256,13 +277,58 @@ __global__ void k_moba_fill(MobaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// S^T for two 16-query sets at once: each K fragment read from LDS feeds
+// both (half the LDS reads per matrix op of one set per wave).
 template <int D>
-__global__ void __launch_bounds__(256) k_moba_attn(MobaArgs a) {
-  __shared__ __align__(16) uint16_t kt[64 * (D + 8)];
-  __shared__ __align__(16) uint16_t vt[D * (64 + 8)];
+__device__ __forceinline__ void qk_tile_T2(const uint16_t* kt, const bf16x8 (&qf)[2][D / 32], f32x4 (&s)[2][4],
+                                           int lr, int lg) {
+  constexpr int KS = k_lds_stride<D>();
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    s[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[1][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16x8 kf = ld8(kt + (16 * mt + lr) * KS + 8 * lg + 32 * ks);
+      s[0][mt] = mfma16(kf, qf[0][ks], s[0][mt]);
+      s[1][mt] = mfma16(kf, qf[1][ks], s[1][mt]);
+    }
+  }
+}
+
+// O^T += V^T P^T for two query sets sharing each V^T fragment.
+template <int D>
+__device__ __forceinline__ void pv_tile2(const uint16_t* vt, const f32x4 (&pm)[2][4], f32x4 (&o)[2][D / 16], int lr,
+                                         int lg) {
+  constexpr int VS = kVtStride;
+  const bf16x8 p00 = pack8(pm[0][0], pm[0][1]), p01 = pack8(pm[0][2], pm[0][3]);
+  const bf16x8 p10 = pack8(pm[1][0], pm[1][1]), p11 = pack8(pm[1][2], pm[1][3]);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const uint16_t* row = vt + (16 * dt + lr) * VS;
+    const bf16x8 v0 = ld4x2(row + 4 * lg, row + 16 + 4 * lg);
+    const bf16x8 v1 = ld4x2(row + 32 + 4 * lg, row + 48 + 4 * lg);
+    o[0][dt] = mfma16(v0, p00, o[0][dt]);
+    o[1][dt] = mfma16(v0, p10, o[1][dt]);
+    o[0][dt] = mfma16(v1, p01, o[0][dt]);
+    o[1][dt] = mfma16(v1, p11, o[1][dt]);
+  }
+}
+
+// One workgroup per 128 listed entries of one (b, h, block) list; the
+// block's K and V^T tiles pass through LDS once for all of them.  Chunks are
+// dealt to the compute dies in contiguous runs (workgroup i runs on die
+// i % 8), so the chunks of one list share that die's L2.
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_moba_attn(MobaArgs a) {
+  __shared__ __align__(16) uint16_t kt[64 * k_lds_stride<D>()];
+  __shared__ __align__(16) uint16_t vt[D * kVtStride];
   const int64_t nl = a.B * a.H * a.nb;
-  const int32_t w = (int32_t)blockIdx.x;
-  if (w >= a.chunk_off[nl]) return;
+  const int32_t total = a.chunk_off[nl];
+  const int32_t per = (total + kXcds - 1) / kXcds;
+  const int32_t run = (int32_t)(blockIdx.x / kXcds);
+  const int32_t w = (int32_t)(blockIdx.x % kXcds) * per + run;
+  if (run >= per || w >= total) return;
   // the (b, h, block) list this chunk belongs to
   int64_t lo = 0, hi = nl;  // chunk_off[lo] <= w < chunk_off[hi]
   while (hi - lo > 1) {
@@ -272,24 +338,28 @@ __global__ void __launch_bounds__(256) k_moba_attn(MobaArgs a) {
   }
   const int64_t bhj = lo;
   const int64_t j = bhj % a.nb, h = (bhj / a.nb) % a.H, b = bhj / (a.nb * a.H);
-  const int64_t first = a.offsets[bhj] + (int64_t)(w - a.chunk_off[bhj]) * kRows;
+  const int64_t first = a.offsets[bhj] + (int64_t)(w - a.chunk_off[bhj]) * kChunk;
   const int64_t count = a.offsets[bhj + 1] - first;  // entries left in this list
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int row = 16 * wave + lr;
-  const bool valid = row < count;
-  const int64_t e = a.lists[first + (valid ? row : 0)];
-  const int64_t t = (e / (a.n * a.H)) % a.T;
-  bf16x8 qf[D / 32];
-  {
+  const bool busy = 32 * wave < count;  // wave-uniform: this wave has rows
+  int64_t e[2];
+  bf16x8 qf[2][D / 32];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 32 * wave + 16 * q + lr;
+    e[q] = a.lists[first + (row < count ? row : 0)];
+    const int64_t t = (e[q] / (a.n * a.H)) % a.T;
     const uint16_t* qr = a.q + ((b * a.T + t) * a.H + h) * D + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+    for (int ks = 0; ks < D / 32; ++ks) qf[q][ks] = ld8(qr + 32 * ks);
   }
   const float c = a.scale * kLog2e, stale = kStaleLog2 / c;
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[D / 16];
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  f32x4 o[2][D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[q][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   Stager<D, D, 256> st;
   const int64_t kb0 = j * a.bs, ntl = a.bs / 64;
   st.load(a.k, a.L, kb0, false, a.vT, a.Lp, kb0, b, h, a.H, true);
@@ -298,18 +368,24 @@ __global__ void __launch_bounds__(256) k_moba_attn(MobaArgs a) {
     st.store(kt, vt, true, false);
     __syncthreads();
     if (i + 1 < ntl) st.load(a.k, a.L, kb0 + 64 * (i + 1), false, a.vT, a.Lp, kb0 + 64 * (i + 1), b, h, a.H, true);
-    f32x4 s[4];
-    qk_tile_T<D>(kt, qf, s, lr, lg);
-    softmax_step<D>(s, m, l, o, c, stale, true);
-    pv_tile<D>(vt, s, o, lr, lg);
+    if (busy) {
+      f32x4 s[2][4];
+      qk_tile_T2<D>(kt, qf, s, lr, lg);
+      softmax_step<D>(s[0], m[0], l[0], o[0], c, stale, true);
+      softmax_step<D>(s[1], m[1], l[1], o[1], c, stale, true);
+      pv_tile2<D>(vt, s, o, lr, lg);
+    }
   }
-  if (!valid) return;
-  float* rec = a.part + e * rec_floats<D>();
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(rec + 16 * dt + 4 * lg) = o[dt];
-  if (lg == 0) {
-    rec[D] = m * c;
-    rec[D + 1] = l;
+  for (int q = 0; q < 2; ++q) {
+    if (32 * wave + 16 * q + lr >= count) continue;
+    float* rec = a.part + e[q] * rec_floats<D>();
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(rec + 16 * dt + 4 * lg) = o[q][dt];
+    if (lg == 0) {
+      rec[D] = m[q] * c;
+      rec[D + 1] = l[q];
+    }
   }
 }
 
@@ -322,40 +398,54 @@ template <> __device__ __forceinline__ void mstore4<uint16_t>(uint16_t* p, f32x4
   *(u32x2*)p = w;
 }
 
-// Query tiles follow the absolute 64-position grid, so a tile never spans two
-// blocks (blocks are multiples of 64 long) and its keys start on a tile.
-template <int D, typename TO>
-__global__ void __launch_bounds__(256) k_moba_diag(MobaArgs a) {
-  __shared__ __align__(16) uint16_t kt[64 * (D + 8)];
-  __shared__ __align__(16) uint16_t vt[D * (64 + 8)];
+// One workgroup per (b, h, 64*NQ query positions): causal attention over
+// the query's own block, then the log-sum-exp merge with the partials of the
+// earlier chosen blocks.  Query tiles follow the absolute position grid, so
+// a tile never spans two blocks (block % (64*NQ) == 0) and its keys start on
+// a 64-key tile; each wave holds NQ sets of 16 queries.
+template <int D, int NQ, typename TO>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_moba_diag(MobaArgs a) {
+  __shared__ __align__(16) uint16_t kt[64 * k_lds_stride<D>()];
+  __shared__ __align__(16) uint16_t vt[D * kVtStride];
+  constexpr int TP = 64 * NQ;
   const int64_t P0 = a.L - a.T;  // position of token 0
-  const int64_t pt0 = P0 / 64, ntile = (a.L - 1) / 64 - pt0 + 1;
+  const int64_t pt0 = P0 / TP, ntile = (a.L - 1) / TP - pt0 + 1;
   const int64_t h = blockIdx.x % a.H;
   const int64_t pt = pt0 + ntile - 1 - (blockIdx.x / a.H) % ntile;  // longest rows first
   const int64_t b = blockIdx.x / (a.H * ntile);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int64_t p_first = 64 * pt > P0 ? 64 * pt : P0;
-  const int64_t p_last = 64 * pt + 63 < a.L - 1 ? 64 * pt + 63 : a.L - 1;
-  const int64_t pl = 64 * pt + 16 * wave + lr;
-  const bool valid = pl >= P0 && pl < a.L;
-  const int64_t p = valid ? pl : p_last;  // out-of-range lanes shadow the last row
-  const int64_t t = p - P0;
-  const int64_t cur = 64 * pt / a.bs;
-  // does this token's selection hold its own block?
-  const int32_t* irow = a.idx + ((b * a.T + t) * a.H + h) * a.n;
-  bool has_cur = false;
-  for (int i = 0; i < a.n; ++i) has_cur |= (irow[i] == cur);
-  bf16x8 qf[D / 32];
-  {
-    const uint16_t* qr = a.q + ((b * a.T + t) * a.H + h) * D + 8 * lg;
+  const int64_t p_first = TP * pt > P0 ? TP * pt : P0;
+  const int64_t p_last = TP * pt + TP - 1 < a.L - 1 ? TP * pt + TP - 1 : a.L - 1;
+  const int64_t cur = TP * pt / a.bs;
+  int64_t p[NQ], t[NQ];
+  bool valid[NQ], has_cur[NQ];
+  bf16x8 qf[NQ][D / 32];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t pl = TP * pt + 16 * (NQ * wave + q) + lr;
+    valid[q] = pl >= P0 && pl < a.L;
+    p[q] = valid[q] ? pl : p_last;  // out-of-range lanes shadow the last row
+    t[q] = p[q] - P0;
+    // does this token's selection hold its own block?
+    const int32_t* irow = a.idx + ((b * a.T + t[q]) * a.H + h) * a.n;
+    has_cur[q] = false;
+    for (int i = 0; i < a.n; ++i) has_cur[q] |= (irow[i] == cur);
+    const uint16_t* qr = a.q + ((b * a.T + t[q]) * a.H + h) * D + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[q][ks] = ld8(qr + 32 * ks);
   }
   const float c = a.scale * kLog2e, stale = kStaleLog2 / c;
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[D / 16];
+  float m[NQ], l[NQ];
+  f32x4 o[NQ][D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NQ; ++q) {
+    m[q] = -INFINITY;
+    l[q] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[q][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the wave's first row: tiles that start after it have nothing for it
+  const int64_t p_wave = TP * pt + 16 * NQ * wave;
   Stager<D, D, 256> st;
   const int64_t kt0 = cur * a.bs / 64, kt1 = p_last / 64;
   st.load(a.k, a.L, kt0 * 64, false, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
@@ -364,52 +454,70 @@ __global__ void __launch_bounds__(256) k_moba_diag(MobaArgs a) {
     st.store(kt, vt, true, false);
     __syncthreads();
     if (kb + 1 <= kt1) st.load(a.k, a.L, (kb + 1) * 64, false, a.vT, a.Lp, (kb + 1) * 64, b, h, a.H, true);
-    f32x4 s[4];
-    qk_tile_T<D>(kt, qf, s, lr, lg);
+    if (kb * 64 > p_wave + 16 * NQ - 1) continue;  // wave-uniform: every key after every row
+    f32x4 s[NQ][4];
+    if constexpr (NQ == 2) {
+      qk_tile_T2<D>(kt, qf, s, lr, lg);
+    } else {
+      qk_tile_T<D>(kt, qf[0], s[0], lr, lg);
+    }
     // keys after the query (only in the tiles that reach the first row), and
     // every key of a row whose selection lacks its own block
-    if (kb * 64 + 63 > p_first || !has_cur) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int q = 0; q < NQ; ++q) {
+      if (kb * 64 + 63 > p_first || !has_cur[q]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!has_cur || kb * 64 + 16 * mt + 4 * lg + r > p) s[mt][r] = -INFINITY;
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!has_cur[q] || kb * 64 + 16 * mt + 4 * lg + r > p[q]) s[q][mt][r] = -INFINITY;
+      }
+      softmax_step<D>(s[q], m[q], l[q], o[q], c, stale, true);
     }
-    softmax_step<D>(s, m, l, o, c, stale, true);
-    pv_tile<D>(vt, s, o, lr, lg);
+    if constexpr (NQ == 2) {
+      pv_tile2<D>(vt, s, o, lr, lg);
+    } else {
+      pv_tile<D>(vt, s[0], o[0], lr, lg);
+    }
   }
-  if (!valid) return;
-  // merge with the partials of the earlier chosen blocks (log2 units)
-  const bool own = has_cur && l > 0.f;  // a row without its own block ran on -inf only
-  const float* prow = a.part + ((b * a.T + t) * a.H + h) * a.n * rec_floats<D>();
-  float M = own ? m * c : -INFINITY;
-  for (int i = 0; i < a.n; ++i) {
-    const int j = irow[i];
-    if (j >= 0 && j < cur) M = fmaxf(M, prow[i * rec_floats<D>() + D]);
-  }
-  const float wd = own ? exp2f(m * c - M) : 0.f;
-  float den = own ? wd * l : 0.f;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = own ? o[dt] * wd : f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < a.n; ++i) {
-    const int j = irow[i];
-    if (j < 0 || j >= cur) continue;
-    const float* rec = prow + i * rec_floats<D>();
-    const float ws = exp2f(rec[D] - M);
-    den = fmaf(ws, rec[D + 1], den);
+  for (int q = 0; q < NQ; ++q) {
+    if (!valid[q]) continue;
+    const int32_t* irow = a.idx + ((b * a.T + t[q]) * a.H + h) * a.n;
+    // merge with the partials of the earlier chosen blocks (log2 units)
+    const bool own = has_cur[q] && l[q] > 0.f;  // a row without its own block ran on -inf only
+    const float* prow = a.part + ((b * a.T + t[q]) * a.H + h) * a.n * rec_floats<D>();
+    float M = own ? m[q] * c : -INFINITY;
+    for (int i = 0; i < a.n; ++i) {
+      const int j = irow[i];
+      if (j >= 0 && j < cur) M = fmaxf(M, prow[i * rec_floats<D>() + D]);
+    }
+    const float wd = own ? exp2f(m[q] * c - M) : 0.f;
+    float den = own ? wd * l[q] : 0.f;
+    f32x4 acc[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] += *(const f32x4*)(rec + 16 * dt + 4 * lg) * ws;
-  }
-  float g = den > 0.f ? 1.f / den : 0.f;
-  if (a.gates) {
-    float x = bf16_to_f32(a.gates[((b * a.T + t) * a.H + h) * 3 + 1]);
-    if (a.flags & NSA_F_GATE_LOGITS) x = sigmoid(x);
-    g *= x;
-  }
-  TO* orow = (TO*)a.out + ((b * a.T + t) * a.H + h) * D + 4 * lg;
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = own ? o[q][dt] * wd : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < a.n; ++i) {
+      const int j = irow[i];
+      if (j < 0 || j >= cur) continue;
+      const float* rec = prow + i * rec_floats<D>();
+      const float ws = exp2f(rec[D] - M);
+      den = fmaf(ws, rec[D + 1], den);
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) mstore4<TO>(orow + 16 * dt, o[dt] * g);
-  if (a.lse && lg == 0) a.lse[(b * a.T + t) * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] += *(const f32x4*)(rec + 16 * dt + 4 * lg) * ws;
+    }
+    float g = den > 0.f ? 1.f / den : 0.f;
+    if (a.gates) {
+      float x = bf16_to_f32(a.gates[((b * a.T + t[q]) * a.H + h) * 3 + 1]);
+      if (a.flags & NSA_F_GATE_LOGITS) x = sigmoid(x);
+      g *= x;
+    }
+    TO* orow = (TO*)a.out + ((b * a.T + t[q]) * a.H + h) * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) mstore4<TO>(orow + 16 * dt, acc[dt] * g);
+    if (a.lse && lg == 0)
+      a.lse[(b * a.T + t[q]) * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+  }
 }
 
 template <int D>
@@ -428,18 +536,26 @@ template <int D>
 hipError_t run_attend_t(const MobaArgs& a, bool out_f32, hipStream_t s, Phases* ph) {
   const int64_t ne = a.B * a.T * a.H * a.n, nl = a.B * a.H * a.nb;
   k_moba_zero<<<(unsigned)((nl + 255) / 256), 256, 0, s>>>(a.counts, nl);
-  k_moba_count<<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(a);
+  const unsigned gcount = (unsigned)(a.B * a.H * ((a.T + kCountTok - 1) / kCountTok));
+  k_moba_count<<<gcount, kCountTok, (size_t)a.nb * sizeof(int32_t), s>>>(a);
   k_moba_scan<<<1, 1024, 0, s>>>(a);
   k_moba_fill<<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(a);
   if (ph) ph->mark();
-  // an upper bound of the chunk count; surplus workgroups exit at once
-  const unsigned gattn = (unsigned)((ne + kRows - 1) / kRows + nl);
+  // an upper bound of the chunk count, in whole runs of 8; surplus
+  // workgroups exit at once
+  const int64_t chunks_max = (ne + kChunk - 1) / kChunk + nl;
+  const unsigned gattn = (unsigned)((chunks_max + kXcds - 1) / kXcds * kXcds);
   k_moba_attn<D><<<gattn, 256, 0, s>>>(a);
   if (ph) ph->mark();
-  const int64_t pt0 = (a.L - a.T) / 64;
-  const unsigned gdiag = (unsigned)(a.B * a.H * ((a.L - 1) / 64 - pt0 + 1));
-  if (out_f32) k_moba_diag<D, float><<<gdiag, 256, 0, s>>>(a);
-  else k_moba_diag<D, uint16_t><<<gdiag, 256, 0, s>>>(a);
+  if (a.bs % 128 == 0) {
+    const unsigned gdiag = (unsigned)(a.B * a.H * ((a.L - 1) / 128 - (a.L - a.T) / 128 + 1));
+    if (out_f32) k_moba_diag<D, 2, float><<<gdiag, 256, 0, s>>>(a);
+    else k_moba_diag<D, 2, uint16_t><<<gdiag, 256, 0, s>>>(a);
+  } else {
+    const unsigned gdiag = (unsigned)(a.B * a.H * ((a.L - 1) / 64 - (a.L - a.T) / 64 + 1));
+    if (out_f32) k_moba_diag<D, 1, float><<<gdiag, 256, 0, s>>>(a);
+    else k_moba_diag<D, 1, uint16_t><<<gdiag, 256, 0, s>>>(a);
+  }
   if (ph) ph->mark();
   return hipGetLastError();
 }

@@ -12,7 +12,8 @@
 namespace nsa {
 namespace {
 
-// One workgroup per (b, j, g) summary row: d_qk key dims then d_v value dims,
+// One workgroup per (b, j, g) summary row: d_qk key dims then d_v value dims
+// (keys only when vc is NULL),
 // one output element per thread and pass; consecutive threads read
 // consecutive dims of a token, so every load instruction is contiguous.
 template <typename T>
@@ -24,7 +25,8 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k, const T* 
   const int64_t g = row % G;
   const int64_t j = (row / G) % nb;
   const int64_t b = row / (G * nb);
-  for (int64_t e = threadIdx.x; e < dq + dv; e += blockDim.x) {
+  const int64_t ne = vc ? dq + dv : dq;  // no value summaries asked for: keys only
+  for (int64_t e = threadIdx.x; e < ne; e += blockDim.x) {
     const bool is_k = e < dq;
     const int64_t d = is_k ? e : e - dq;
     const int64_t width = is_k ? dq : dv;

@@ -162,7 +162,7 @@ __device__ __forceinline__ void topk_row(const float* imp, int64_t nvis, int64_t
 // ---------------------------------------------------------------------------
 template <int DQ, int DV, bool FWD>
 __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
-  constexpr int KS = DQ + 8, VS = 64 + 8;
+  constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* kt = (uint16_t*)smem_raw;                // [64][KS]
   uint16_t* vt = kt + 64 * KS;                       // [DV][VS]
@@ -275,12 +275,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     int64_t lo = p_first - a.w + 1;
     if (lo < 0) lo = 0;
     const int64_t kb0 = lo / 64, kb1 = p_last / 64;
-    st.load(a.kG, a.Lp, kb0 * 64, true, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
+    st.load(a.k, a.L, kb0 * 64, false, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
     for (int64_t kb = kb0; kb <= kb1; ++kb) {
       __syncthreads();
-      st.store(kt, vt, true, true);
+      st.store(kt, vt, true, false);
       __syncthreads();
-      if (kb + 1 <= kb1) st.load(a.kG, a.Lp, (kb + 1) * 64, true, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
+      if (kb + 1 <= kb1) st.load(a.k, a.L, (kb + 1) * 64, false, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
       if (active && kb * 64 <= p && kb * 64 + 63 > p - a.w) {
         f32x4 s[4];
         qk_tile_T<DQ>(kt, qf, s, lr, lg);
@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
 
 template <int DQ, int DV>
 hipError_t launch_cmpwin_t(const PfArgs& a, bool fwd, hipStream_t s) {
-  constexpr int KS = DQ + 8, VS = 64 + 8;
+  constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
   const size_t lds = sizeof(uint16_t) * (64 * KS + (fwd ? DV * VS : 0)) + sizeof(float) * TQ * a.nbp;
   const unsigned grid = (unsigned)(a.B * a.G * ((a.T + TQ - 1) / TQ));
   if (fwd) {

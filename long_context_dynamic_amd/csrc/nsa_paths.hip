@@ -91,12 +91,13 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     w.total = off;
     return w;
   }
+  const bool moba = !dec && !fast && moba_ok(P);
   if (!have_cmp) {
     w.kc = take((size_t)(P.B * P.nb * P.G * P.dq) * elem_bytes(P));
-    w.vc = take((size_t)(P.B * P.nb * P.G * P.dv) * elem_bytes(P));
+    if (!moba) w.vc = take((size_t)(P.B * P.nb * P.G * P.dv) * elem_bytes(P));  // MoBA scores by keys only
   }
   w.idx = take((size_t)(P.B * P.T * P.G * P.n) * sizeof(int32_t));
-  if (!dec && !fast && moba_ok(P)) {
+  if (moba) {
     take_moba(P, w, take);
   } else if (dec) {
     w.zbuf = take(zbytes);
@@ -236,9 +237,10 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
   hipError_t e;
   ph.s = s;
   ph.mark();
+  const bool moba = !decode_ok(P) && !prefill_fast_ok(P) && moba_ok(P);
   if (!kc) {
     kc = at<char>(base, ws.kc);
-    vc = at<char>(base, ws.vc);
+    vc = moba ? nullptr : at<char>(base, ws.vc);
     if ((e = launch_pool(P, k, v, (void*)kc, (void*)vc, s)) != hipSuccess) return e;
     ph.mark();
   }
@@ -285,7 +287,7 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     ph.mark();
     return ph.err;
   }
-  if (moba_ok(P)) {
+  if (moba) {
     MobaArgs a = moba_args(P);
     set_moba_ws(a, ws, base);
     if ((e = launch_transpose(v, (void*)a.vT, P.B, P.L, a.Lp, P.H, (int)P.dv, s)) != hipSuccess) return e;

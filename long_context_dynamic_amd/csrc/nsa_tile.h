@@ -9,6 +9,20 @@
 
 namespace nsa {
 
+// LDS row strides (bf16 elements).  K tile rows are read 16 bytes per lane
+// with lane l on row l % 16: conflict-free when the row stride is 32 bytes
+// past a multiple of 64 (d + 16 elements for d = 64, 128, 192).  V^T rows
+// are read 8 bytes per lane, lane l on row l % 16, and written 16 bytes per
+// lane the same way: conflict-free at 144 bytes (64 keys + 8).
+template <int D> constexpr int k_lds_stride() { return D + 16; }
+constexpr int kVtStride = 64 + 8;
+
+// Within each run of 64 V^T chunks (16 bytes = 8 keys of one dim row; four
+// per 32-key half row) lane l takes chunk 4 * (l % 16) + l / 16, so a wave
+// still reads one contiguous kilobyte and its LDS writes put lane l on row
+// l % 16.
+__device__ __forceinline__ int vt_chunk(int c) { return (c & ~63) | ((c & 15) << 2) | ((c >> 4) & 3); }
+
 // ---------------------------------------------------------------------------
 // Register-prefetching tile stager: load() issues the global reads of one
 // 64-key tile (K rows [row0, row0 + 64) of a [B, Nrows, G, DQ] tensor, rows
@@ -17,7 +31,7 @@ namespace nsa {
 // next tile's reads are in flight while the current tile is computed on.
 template <int DQ, int DV, int NT>
 struct Stager {
-  static constexpr int KS = DQ + 8, VS = 64 + 8;
+  static constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
   static constexpr int KC = 64 * DQ / 8, VC = DV * 8;
   static constexpr int KPT = (KC + NT - 1) / NT, VPT = (VC + NT - 1) / NT;
   u32x4 kr[KPT], vr[VPT];
@@ -47,7 +61,7 @@ struct Stager {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * NT;
-        if (VC % NT == 0 || c < VC) vr[i] = *(const u32x4*)(tile + 8 * c);
+        if (VC % NT == 0 || c < VC) vr[i] = *(const u32x4*)(tile + 8 * vt_chunk(c));
       }
     }
   }
@@ -72,8 +86,9 @@ struct Stager {
     if (with_v) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        const int c = threadIdx.x + i * NT;  // 16-byte chunk c: half c / (4 DV), row d, keys 8 * (c % 4)
-        const int h = c / (4 * DV), d = (c / 4) % DV, j8 = c % 4;
+        const int c = threadIdx.x + i * NT;
+        const int cc = vt_chunk(c);  // 16-byte chunk cc: half cc / (4 DV), row d, keys 8 * (cc % 4)
+        const int h = cc / (4 * DV), d = (cc / 4) % DV, j8 = cc % 4;
         if (VC % NT == 0 || c < VC) *(u32x4*)(vt + d * VS + 32 * h + 8 * j8) = vr[i];
       }
     }
@@ -138,7 +153,7 @@ __device__ __forceinline__ void mask_below(f32x4 (&s)[4], int first, int lg) {
 template <int DV>
 __device__ __forceinline__ void pv_tile(const uint16_t* vt, const f32x4 (&pm)[4], f32x4 (&o)[DV / 16], int lr,
                                         int lg) {
-  constexpr int VS = 64 + 8;
+  constexpr int VS = kVtStride;
   const bf16x8 p0 = pack8(pm[0], pm[1]);
   const bf16x8 p1 = pack8(pm[2], pm[3]);
 #pragma unroll
@@ -153,7 +168,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vt, const f32x4 (&pm)[4]
 template <int DQ>
 __device__ __forceinline__ void qk_tile_T(const uint16_t* kt, const bf16x8 (&qf)[DQ / 32], f32x4 (&s)[4], int lr,
                                           int lg) {
-  constexpr int KS = DQ + 8;
+  constexpr int KS = k_lds_stride<DQ>();
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
