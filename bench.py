@@ -1,14 +1,15 @@
 """Benchmark of the NSA forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-moba] [--no-cpu]
 
 One step is one nsa_forward (pooling, selection, all three branches, gates)
 over the 64k-token prefill workload (B=1, T=65536, 4 KV groups x 16 heads,
 d_qk 192, d_v 128, block 64, top-16, window 512) with inputs resident in
 HBM.  Prints ONE JSON line: tokens/s, per-kernel times from HIP events
 recorded on the library's stream, the roofline of the dominant kernel, the
-batched-decode measurement (64 x 65536-token caches, % of HBM peak) and the
-CPU oracle timed on a bounded sample of the same workload.
+MoBA forward (32k tokens, 32 heads, 512-token blocks, top-3) with its own
+roofline, the batched-decode measurement (64 x 65536-token caches, % of HBM
+peak) and the CPU oracle timed on a bounded sample of the 64k workload.
 """
 from __future__ import annotations
 
@@ -67,9 +68,10 @@ def algorithmic_flops(prob):
 
 # ---------------------------------------------------------------- prefill --
 
-def run_prefill(args, torch, nsa, workloads, inputs):
-    prob = workloads.get(args.workload)
-    log(f"workload {args.workload}: generating inputs")
+def run_prefill(args, torch, nsa, workloads, inputs, workload=None):
+    workload = workload or args.workload
+    prob = workloads.get(workload)
+    log(f"workload {workload}: generating inputs")
     t0 = time.time()
     x = inputs.generate(prob)
     log(f"inputs ready in {time.time() - t0:.1f}s; uploading")
@@ -93,16 +95,66 @@ def run_prefill(args, torch, nsa, workloads, inputs):
     return prob, x, wall / K * 1e3, per_phase
 
 
-def prefill_roofline(prob, per_phase):
-    fl = algorithmic_flops(prob)
-    kernel_flops = {"selected": fl["slc"], "cmp_select_window": fl["cmp"] + fl["win"]}
+def moba_kernel_flops(prob):
+    """Algorithmic FLOPs of the two MoBA attention kernels: the chosen blocks
+    before the query's own (whole blocks) and the own block (causal part)."""
+    p = positions(prob)
+    bs, n = prob["block"], prob["top_k"]
+    H, dq, dv = prob["n_groups"] * prob["heads_per_group"], prob["d_qk"], prob["d_v"]
+    per_key = 2.0 * (dq + dv) * H * prob["batch"]
+    nvis = np.minimum((p + 1) // bs, prob["kv_len"] // bs)
+    cur = p // bs
+    first, current = bool(prob["force_first"]), bool(prob["force_current"])
+    forced_earlier = np.where(first & (cur > 0), 1, 0)             # block 0 before the own block
+    own = np.full(p.shape, current) | ((cur == 0) & first)
+    cand = nvis - forced_earlier - np.where(current & (cur < nvis), 1, 0)
+    earlier = forced_earlier + np.minimum(n - forced_earlier - own.astype(np.int64), cand)
+    return {"moba_attn": per_key * bs * float(earlier.sum()),
+            "moba_own_block": per_key * float(np.where(own, p % bs + 1, 0).sum())}
+
+
+def load_traffic(kernel, workload):
+    """Bytes per launch from the committed counter summary of this kernel and
+    workload, or None when there is none or the kernel's sources changed."""
+    from long_context_dynamic_amd import pmc
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != pmc.source_hash(kernel):
+        log(f"{path}: kernel sources changed since the counters were taken; traffic not reported")
+        return None
+    return int(round(rec["traffic_bytes_per_launch"]))
+
+
+def roofline(kernel_flops, per_phase, workload):
     dominant = max((k for k in per_phase if k in kernel_flops), key=lambda k: per_phase[k])
     ms = per_phase[dominant]
     achieved = kernel_flops[dominant] / (ms * 1e-3) / 1e12
-    roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "algorithmic_flop_per_launch": kernel_flops[dominant]}
-    return roof, fl
+    return {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(dominant, workload), "traffic_unit": "HBM bytes per launch",
+            "algorithmic_flop_per_launch": kernel_flops[dominant], "kernel_ms": round(ms, 4)}
+
+
+def prefill_roofline(prob, per_phase, workload):
+    fl = algorithmic_flops(prob)
+    kernel_flops = {"selected": fl["slc"], "cmp_select_window": fl["cmp"] + fl["win"]}
+    return roofline(kernel_flops, per_phase, workload), fl
+
+
+def run_moba(args, torch, nsa, workloads, inputs):
+    prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs, workload="moba_32k")
+    kf = moba_kernel_flops(prob)
+    tokens = prob["batch"] * prob["q_len"]
+    return {"workload": "moba_32k", "batch": prob["batch"], "seq_len": prob["q_len"],
+            "heads": prob["n_groups"], "d": prob["d_qk"], "block": prob["block"], "top_k": prob["top_k"],
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "phases_ms": {k: round(v, 4) for k, v in per_phase.items()},
+            "algorithmic_tflop": {k: round(v / 1e12, 4) for k, v in kf.items()},
+            "forward_mfma_frac": round(sum(kf.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline(kf, per_phase, "moba_32k")}
 
 
 # ----------------------------------------------------------------- decode --
@@ -220,6 +272,7 @@ def main():
     ap.add_argument("--workload", default="nsa_prefill_64k")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
@@ -237,7 +290,7 @@ def main():
         return
 
     prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs)
-    roof, fl = prefill_roofline(prob, per_phase)
+    roof, fl = prefill_roofline(prob, per_phase, args.workload)
     f_tot = fl["cmp"] + fl["slc"] + fl["win"]
     tokens = prob["batch"] * prob["q_len"]
     rec = {
@@ -255,6 +308,10 @@ def main():
         "roofline": roof,
     }
     log(f"prefill: {ms:.3f} ms/step, phases {rec['phases_ms']}")
+    if not args.no_moba:
+        rec["moba"] = run_moba(args, torch, nsa, workloads, inputs)
+        log(f"moba: {rec['moba']['ms_per_step']} ms/step, phases {rec['moba']['phases_ms']}")
+        torch.cuda.empty_cache()
     if not args.no_decode:
         del x
         torch.cuda.empty_cache()
