@@ -24,6 +24,7 @@
 
 #include "nsa_decode.h"
 #include "nsa_mfma.h"
+#include "nsa_topk.h"
 
 namespace nsa {
 namespace {
@@ -43,6 +44,27 @@ __device__ __forceinline__ bool dbetter(float v, int j, float bv, int bj) {
 }
 
 // ---------------------------------------------------------------------------
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane
+// group, lane i points at 4 consecutive 16-bit elements R_i; lane 4a + c
+// receives element c of R_a, R_(a+4), R_(a+8), R_(a+12).  With lane i on row
+// row0 + i / 4, columns col0 + 4 * (i % 4) .. + 3 of a row-major tile, lane
+// j of the group receives column col0 + j of rows row0 .. row0 + 3.
+__device__ __forceinline__ u32x2 ld_tr4(const uint16_t* tile, int row0, int col0, int stride, int i) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const uint16_t* p = tile + (row0 + (i >> 2)) * stride + col0 + 4 * (i & 3);
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+// A matrix-op operand of V^T: rows rowa .. rowa + 3 then rowb .. rowb + 3 of
+// column col0 + lr.
+__device__ __forceinline__ bf16x8 ld_vt_pair(const uint16_t* tile, int rowa, int rowb, int col0, int stride,
+                                             int lr) {
+  const u32x2 a = ld_tr4(tile, rowa, col0, stride, lr);
+  const u32x2 b = ld_tr4(tile, rowb, col0, stride, lr);
+  const u32x4 r = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Partial record of one wave: [16 heads][DV] unnormalised outputs, then
 // [16] maxima (log2 units) and [16] sums.
 template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
@@ -52,6 +74,10 @@ template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
 // logits to zrow[h * zstride + row] when zrow is given.  Ends by writing the
 // wave's partial record.  WITH_V = false: softmax statistics only, V is never
 // read (its output part of the record is left as zeros).
+// K fragments go from global memory straight into matrix-op registers; the V
+// tile is read as whole rows into registers, passes through the wave's LDS
+// region and is read back transposed.  The next tile's reads are in flight
+// while the current one is computed on.
 template <int DQ, int DV, bool WITH_V, typename Ok>
 __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* V, int64_t N, int64_t b, int64_t g,
                                              int64_t G, const int* tiles, int nt, Ok ok, const bf16x8 (&qf)[DQ / 32],
@@ -86,6 +112,10 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
       vreg[q] = *(const u32x4*)(V + ((b * N + row) * G + g) * DV + 8 * c8);
     }
   };
+  auto lds_order = [] {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  };
   if (nt > 0) {
     load_k(0);
     if (WITH_V) load_v(0);
@@ -105,6 +135,7 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
     __builtin_amdgcn_sched_barrier(0);
     if (PF) load_k(i + 1);
     if (WITH_V) {
+      lds_order();  // the previous tile's V reads are done
 #pragma unroll
       for (int q = 0; q < DV / 8; ++q) {
         const int cidx = lane + 64 * q;
@@ -118,14 +149,16 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
     // s[mt][r]: row kb + 16*mt + 4*lg + r, head lr
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = kb + 16 * mt + 4 * lg + r;
         if (!ok(row)) s[mt][r] = -INFINITY;
-        else if (zrow) zrow[lr * zstride + row] = s[mt][r] * c;
         tmax = fmaxf(tmax, s[mt][r]);
       }
+      // scaled logits, 4 consecutive rows per lane (masked rows hold -inf)
+      if (zrow) *(f32x4*)(zrow + lr * zstride + kb + 16 * mt + 4 * lg) = s[mt] * c;
+    }
     tmax = xor_max16_32(tmax);
     const float mnew = fmaxf(m, tmax);
     const float alpha = mnew == -INFINITY ? 1.f : exp2f((m - mnew) * c);
@@ -142,26 +175,18 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
     l = l * alpha + rs;
     m = mnew;
     if (!WITH_V) return;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    lds_order();
     const bf16x8 p0 = pack8(s[0], s[1]);
     const bf16x8 p1 = pack8(s[2], s[3]);
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
-      const int d = 16 * dt + lr;
-      bf16x8 va, vb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        va[e] = __builtin_bit_cast(__bf16, myv[(4 * lg + e) * VS + d]);
-        va[4 + e] = __builtin_bit_cast(__bf16, myv[(16 + 4 * lg + e) * VS + d]);
-        vb[e] = __builtin_bit_cast(__bf16, myv[(32 + 4 * lg + e) * VS + d]);
-        vb[4 + e] = __builtin_bit_cast(__bf16, myv[(48 + 4 * lg + e) * VS + d]);
-      }
+      // slot e (< 4) of lane (lr, lg) holds V[row 4*lg + e][d = 16*dt + lr],
+      // slots 4.. the rows 16 further on (the key order of p0 / p1)
+      const bf16x8 va = ld_vt_pair(myv, 4 * lg, 16 + 4 * lg, 16 * dt, VS, lr);
+      const bf16x8 vb = ld_vt_pair(myv, 32 + 4 * lg, 48 + 4 * lg, 16 * dt, VS, lr);
       o[dt] = mfma16(va, p0, o[dt] * alpha);
       o[dt] = mfma16(vb, p1, o[dt]);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
   for (int i = 0; i + 1 < nt; ++i) tile(i, std::true_type{});
   if (nt > 0) tile(nt - 1, std::false_type{});
@@ -187,10 +212,12 @@ template <int DQ, int DV, bool WITH_V>
 __global__ void __launch_bounds__(256) k_dec_cmp(DecArgs a) {
   __shared__ __align__(16) uint16_t vt[4][64 * (DV + 8)];
   const int wave = threadIdx.x >> 6;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row, g, cmp wave)
+  // (row, cmp wave, g): the groups of one tile run side by side, so their
+  // interleaved summary rows are read together
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   if (item >= a.R * a.G * a.n_cmp_waves) return;
-  const int64_t cw = item % a.n_cmp_waves;
-  const int64_t g = (item / a.n_cmp_waves) % a.G;
+  const int64_t g = item % a.G;
+  const int64_t cw = (item / a.G) % a.n_cmp_waves;
   const int64_t row = item / (a.n_cmp_waves * a.G);
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
@@ -216,10 +243,10 @@ __global__ void __launch_bounds__(256) k_dec_attn(DecArgs a) {
   __shared__ __align__(16) uint16_t vt[4][64 * (DV + 8)];
   const int wave = threadIdx.x >> 6;
   const int64_t nsw = a.n_sel_waves + a.n_win_waves;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row, g, wave slot)
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row, wave slot, g), groups side by side
   if (item >= a.R * a.G * nsw) return;
-  const int64_t ws = item % nsw;
-  const int64_t g = (item / nsw) % a.G;
+  const int64_t g = item % a.G;
+  const int64_t ws = (item / a.G) % nsw;
   const int64_t row = item / (nsw * a.G);
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
@@ -257,25 +284,24 @@ __global__ void __launch_bounds__(256) k_dec_attn(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// One workgroup per (row, group): per-head softmax statistics from the
+// compressed-branch partial records, the group importance of every visible
+// block from the stored logits (all four waves), top-k (one wave).
 template <int DV>
 __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
   __shared__ float imp[64 * MAX_NB_LANE];
   __shared__ float sM[16], sL[16];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int64_t g = blockIdx.x % a.G;
   const int64_t row = blockIdx.x / a.G;
-  const int64_t t = row % a.T;
-  const int64_t p = a.L - a.T + t;
+  const int64_t p = a.L - a.T + row % a.T;
   int64_t nvis = (p + 1) / 64;
   if (nvis > a.nb) nvis = a.nb;
-  const float* z = a.zbuf + (row * a.G + g) * 16 * a.nbp;
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
   const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
-  // per-head softmax statistics from the compressed-branch partials
   if (tid < 16) {
-    float M = -INFINITY;
+    float M = -INFINITY, L = 0.f;
     for (int64_t w = 0; w < a.n_cmp_waves; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + tid]);
-    float L = 0.f;
     for (int64_t w = 0; w < a.n_cmp_waves; ++w) {
       const float mw = base[w * part_floats<DV>() + 16 * DV + tid];
       if (mw != -INFINITY) L = fmaf(exp2f(mw - M), base[w * part_floats<DV>() + 16 * DV + 16 + tid], L);
@@ -284,68 +310,31 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
     sL[tid] = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
+  const float* z = a.zbuf + (row * a.G + g) * 16 * a.nbp;
   for (int64_t j = tid; j < nvis; j += 256) {
-    float s = 0.f;
+    float sum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) s += exp2f(z[h * a.nbp + j] - sM[h]) * sL[h];
-    imp[j] = s;
+    for (int h = 0; h < 16; ++h) sum += exp2f(z[h * a.nbp + j] - sM[h]) * sL[h];
+    imp[j] = sum;
   }
   __syncthreads();
-  if (wave != 0) return;
-  const int64_t cur = p / 64;
-  int forced[2];
-  int nf = 0;
-  if (a.flags & NSA_F_FORCE_FIRST) forced[nf++] = 0;
-  if ((a.flags & NSA_F_FORCE_CURRENT) && !((a.flags & NSA_F_FORCE_FIRST) && cur == 0)) forced[nf++] = (int)cur;
-  float vals[MAX_NB_LANE];
-#pragma unroll
-  for (int i = 0; i < MAX_NB_LANE; ++i) {
-    const int64_t j = lane + 64 * i;
-    vals[i] = j < nvis ? imp[j] : -1.f;
-  }
-  int ncand = (int)nvis;
-  for (int f = 0; f < nf; ++f) {
-    if (forced[f] < nvis) {
-      --ncand;
-#pragma unroll
-      for (int i = 0; i < MAX_NB_LANE; ++i)
-        if (lane + 64 * i == forced[f]) vals[i] = -1.f;
-    }
-  }
-  const int r_take = ((int)a.n - nf) < ncand ? ((int)a.n - nf) : ncand;
-  int cj = -1;
-  float cs = -INFINITY;
-  for (int f = 0; f < nf; ++f)
-    if (lane == f) { cj = forced[f]; cs = INFINITY; }
-  for (int round = 0; round < r_take; ++round) {
-    float bv = -1.f;
-    int bj = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < MAX_NB_LANE; ++i)
-      if (vals[i] > bv) { bv = vals[i]; bj = lane + 64 * i; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oj = __shfl_xor(bj, off, 64);
-      if (dbetter(ov, oj, bv, bj)) { bv = ov; bj = oj; }
-    }
-#pragma unroll
-    for (int i = 0; i < MAX_NB_LANE; ++i)
-      if (lane + 64 * i == bj) vals[i] = -1.f;
-    if (lane == nf + round) { cj = bj; cs = bv; }
-  }
-  const int cnt = nf + r_take;
-  int rank = 0;
-  for (int k2 = 0; k2 < cnt; ++k2) rank += (__shfl(cj, k2, 64) < cj) ? 1 : 0;
+  if (tid >= 64) return;
   int32_t* orow = a.idx + (row * a.G + g) * a.n;
   float* srow = a.score ? a.score + (row * a.G + g) * a.n : nullptr;
-  if (lane < cnt) {
-    orow[rank] = cj;
-    if (srow) srow[rank] = cs;
-  } else if (lane < a.n) {
-    orow[lane] = -1;
-    if (srow) srow[lane] = -INFINITY;
+  int cj, cnt;
+  float cs;
+  if (a.nbp <= 1024) {
+    float vals[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vals[i] = tid + 64 * i < nvis ? imp[tid + 64 * i] : -1.f;
+    cnt = topk_wave<16>(vals, nvis, p / 64, a.flags, (int)a.n, cj, cs);
+  } else {
+    float vals[MAX_NB_LANE];
+#pragma unroll
+    for (int i = 0; i < MAX_NB_LANE; ++i) vals[i] = tid + 64 * i < nvis ? imp[tid + 64 * i] : -1.f;
+    cnt = topk_wave<MAX_NB_LANE>(vals, nvis, p / 64, a.flags, (int)a.n, cj, cs);
   }
+  topk_write(cnt, cj, cs, (int)a.n, orow, srow);
 }
 
 // ---------------------------------------------------------------------------

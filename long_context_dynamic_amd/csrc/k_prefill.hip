@@ -26,6 +26,7 @@
 #include "nsa_mfma.h"
 #include "nsa_prefill.h"
 #include "nsa_tile.h"
+#include "nsa_topk.h"
 
 namespace nsa {
 namespace {
@@ -92,71 +93,22 @@ __global__ void __launch_bounds__(256) k_group_major(const uint16_t* __restrict_
   }
 }
 
-// Top-k of one token's block importances imp[0 .. nvis) (one wave): forced
-// blocks first, then r rounds; in each the wave finds the largest remaining
-// value (lowest block id on ties) with two cross-lane reductions, and only
-// the winning lane rescans its own candidates.  Writes the sorted list.
+// Top-k of one token's block importances imp[0 .. nvis) (one wave), written
+// sorted to orow / srow.
 template <int NBL>
 __device__ __forceinline__ void topk_row(const float* imp, int64_t nvis, int64_t cur, uint32_t flags, int n,
                                          int32_t* orow, float* srow) {
   const int lane = threadIdx.x & 63;
-  int forced[2];
-  int nf = 0;
-  if (flags & NSA_F_FORCE_FIRST) forced[nf++] = 0;
-  if ((flags & NSA_F_FORCE_CURRENT) && !((flags & NSA_F_FORCE_FIRST) && cur == 0)) forced[nf++] = (int)cur;
   float vals[NBL];
 #pragma unroll
   for (int i = 0; i < NBL; ++i) {
     const int64_t j = lane + 64 * i;
     vals[i] = j < nvis ? imp[j] : -1.f;
   }
-  int ncand = (int)nvis;
-  for (int f = 0; f < nf; ++f) {
-    if (forced[f] < nvis) {
-      --ncand;
-      if (lane == (forced[f] & 63)) {
-#pragma unroll
-        for (int i = 0; i < NBL; ++i)
-          if (i == (forced[f] >> 6)) vals[i] = -1.f;
-      }
-    }
-  }
-  const int r_take = (n - nf) < ncand ? (n - nf) : ncand;
-  int cj = -1;
-  float cs = -INFINITY;
-  for (int f = 0; f < nf; ++f)
-    if (lane == f) { cj = forced[f]; cs = INFINITY; }
-  // this lane's best remaining candidate (first index wins ties)
-  float bv = -1.f;
-  int bi = 0;
-#pragma unroll
-  for (int i = 0; i < NBL; ++i)
-    if (vals[i] > bv) { bv = vals[i]; bi = i; }
-  for (int round = 0; round < r_take; ++round) {
-    const float M = wave_allmax(bv);
-    const int J = wave_allmin_u(bv == M ? lane + 64 * bi : 0x7fffffff);
-    if (lane == nf + round) { cj = J; cs = M; }
-    if (lane == (J & 63)) {
-#pragma unroll
-      for (int i = 0; i < NBL; ++i)
-        if (i == (J >> 6)) vals[i] = -1.f;
-      bv = -1.f;
-      bi = 0;
-#pragma unroll
-      for (int i = 0; i < NBL; ++i)
-        if (vals[i] > bv) { bv = vals[i]; bi = i; }
-    }
-  }
-  const int cnt = nf + r_take;
-  int rank = 0;
-  for (int k2 = 0; k2 < cnt; ++k2) rank += (__shfl(cj, k2, 64) < cj) ? 1 : 0;
-  if (lane < cnt) {
-    orow[rank] = cj;
-    if (srow) srow[rank] = cs;
-  } else if (lane < n) {
-    orow[lane] = -1;
-    if (srow) srow[lane] = -INFINITY;
-  }
+  int cj;
+  float cs;
+  const int cnt = topk_wave<NBL>(vals, nvis, cur, flags, n, cj, cs);
+  topk_write(cnt, cj, cs, n, orow, srow);
 }
 
 // ---------------------------------------------------------------------------
