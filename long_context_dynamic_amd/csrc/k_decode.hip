@@ -287,9 +287,10 @@ __global__ void __launch_bounds__(256) k_dec_attn(DecArgs a) {
 // One workgroup per (row, group): per-head softmax statistics from the
 // compressed-branch partial records, the group importance of every visible
 // block from the stored logits (all four waves), top-k (one wave).
-template <int DV>
+// NBL: blocks per lane in the top-k (nbp <= 64 * NBL).
+template <int DV, int NBL>
 __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
-  __shared__ float imp[64 * MAX_NB_LANE];
+  __shared__ float imp[64 * NBL];
   __shared__ float sM[16], sL[16];
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x % a.G;
@@ -299,6 +300,15 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
   if (nvis > a.nb) nvis = a.nb;
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
   const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
+  // this thread's logits, loaded while the statistics are worked out
+  const float* z = a.zbuf + (row * a.G + g) * 16 * a.nbp;
+  float zv[NBL / 4][16];
+#pragma unroll
+  for (int i = 0; i < NBL / 4; ++i) {
+    const int64_t j = tid + 256 * i;
+#pragma unroll
+    for (int h = 0; h < 16; ++h) zv[i][h] = j < nvis ? z[h * a.nbp + j] : 0.f;
+  }
   if (tid < 16) {
     float M = -INFINITY, L = 0.f;
     for (int64_t w = 0; w < a.n_cmp_waves; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + tid]);
@@ -310,30 +320,26 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
     sL[tid] = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
-  const float* z = a.zbuf + (row * a.G + g) * 16 * a.nbp;
-  for (int64_t j = tid; j < nvis; j += 256) {
-    float sum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) sum += exp2f(z[h * a.nbp + j] - sM[h]) * sL[h];
-    imp[j] = sum;
+  for (int i = 0; i < NBL / 4; ++i) {
+    const int64_t j = tid + 256 * i;
+    if (j < nvis) {
+      float sum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 16; ++h) sum += exp2f(zv[i][h] - sM[h]) * sL[h];
+      imp[j] = sum;
+    }
   }
   __syncthreads();
   if (tid >= 64) return;
   int32_t* orow = a.idx + (row * a.G + g) * a.n;
   float* srow = a.score ? a.score + (row * a.G + g) * a.n : nullptr;
-  int cj, cnt;
+  int cj;
   float cs;
-  if (a.nbp <= 1024) {
-    float vals[16];
+  float vals[NBL];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vals[i] = tid + 64 * i < nvis ? imp[tid + 64 * i] : -1.f;
-    cnt = topk_wave<16>(vals, nvis, p / 64, a.flags, (int)a.n, cj, cs);
-  } else {
-    float vals[MAX_NB_LANE];
-#pragma unroll
-    for (int i = 0; i < MAX_NB_LANE; ++i) vals[i] = tid + 64 * i < nvis ? imp[tid + 64 * i] : -1.f;
-    cnt = topk_wave<MAX_NB_LANE>(vals, nvis, p / 64, a.flags, (int)a.n, cj, cs);
-  }
+  for (int i = 0; i < NBL; ++i) vals[i] = tid + 64 * i < nvis ? imp[tid + 64 * i] : -1.f;
+  const int cnt = topk_wave<NBL>(vals, nvis, p / 64, a.flags, (int)a.n, cj, cs);
   topk_write(cnt, cj, cs, (int)a.n, orow, srow);
 }
 
@@ -341,8 +347,11 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
 // Log-sum-exp merge of each branch's partial records, gates, output.  With
 // gates == NULL every enabled branch has weight 1; lse (selected branch only,
 // natural log) is written when given.
+// One thread per 4 outputs (16 heads x DV/4): each first issues the loads of
+// its slice of every partial record and of its gates, so they are in flight
+// while 48 threads work out the merge weights.
 template <int DV, typename TO>
-__global__ void __launch_bounds__(256) k_dec_merge(DecArgs a) {
+__global__ void __launch_bounds__(4 * DV) k_dec_merge(DecArgs a) {
   constexpr int MAXW = 32;
   __shared__ float coef[16][MAXW];  // weight of each partial in its branch's merge
   __shared__ float slse[16];
@@ -351,44 +360,46 @@ __global__ void __launch_bounds__(256) k_dec_merge(DecArgs a) {
   const int64_t row = blockIdx.x / a.G;
   const int nc = (int)a.n_cmp_waves, ns = (int)a.n_sel_waves, nwaves = nc + ns + (int)a.n_win_waves;
   const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
+  const int h = tid / (DV / 4), d = 4 * (tid % (DV / 4));
+  f32x4 v[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w)
+    if (w < nwaves) v[w] = *(const f32x4*)(base + w * part_floats<DV>() + h * DV + d);
+  const int64_t hrow = row * a.H + g * 16 + h;
+  const float g0 = dgate(a, hrow, 0), g1 = dgate(a, hrow, 1), g2 = dgate(a, hrow, 2);
   if (tid < 48) {
-    const int h = tid & 15, br = tid >> 4;  // 0 cmp, 1 sel, 2 win
+    const int hh = tid & 15, br = tid >> 4;  // 0 cmp, 1 sel, 2 win
     const int w0 = br == 0 ? 0 : (br == 1 ? nc : nc + ns), w1 = br == 0 ? nc : (br == 1 ? nc + ns : nwaves);
     float M = -INFINITY;
-    for (int w = w0; w < w1; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + h]);
+    for (int w = w0; w < w1; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + hh]);
     float den = 0.f;
     for (int w = w0; w < w1; ++w) {
-      const float mw = base[w * part_floats<DV>() + 16 * DV + h];
+      const float mw = base[w * part_floats<DV>() + 16 * DV + hh];
       const float sc = (M == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      coef[h][w] = sc;
-      den = fmaf(sc, base[w * part_floats<DV>() + 16 * DV + 16 + h], den);
+      coef[hh][w] = sc;
+      den = fmaf(sc, base[w * part_floats<DV>() + 16 * DV + 16 + hh], den);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int w = w0; w < w1; ++w) coef[h][w] *= inv;
-    if (br == 1) slse[h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+    for (int w = w0; w < w1; ++w) coef[hh][w] *= inv;
+    if (br == 1) slse[hh] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
   __syncthreads();
   const bool use_cmp = a.flags & NSA_F_CMP, use_slc = a.flags & NSA_F_SLC;
   const bool use_win = (a.flags & NSA_F_WIN) && a.w > 0;
-  for (int item = tid; item < 16 * DV / 4; item += 256) {
-    const int h = item / (DV / 4), d = 4 * (item % (DV / 4));
-    f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int w = 0; w < nwaves; ++w) {
-      const f32x4 v = *(const f32x4*)(base + w * part_floats<DV>() + h * DV + d);
-      br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v * coef[h][w];
-    }
-    const int64_t hrow = row * a.H + g * 16 + h;
-    f32x4 out = {0.f, 0.f, 0.f, 0.f};
-    if (use_cmp) out += br[0] * dgate(a, hrow, 0);
-    if (use_slc) out += br[1] * dgate(a, hrow, 1);
-    if (use_win) out += br[2] * dgate(a, hrow, 2);
-    if (sizeof(TO) == 2) {
-      u32x2 wv = {(uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16),
-                  (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16)};
-      *(u32x2*)((uint16_t*)a.out + hrow * DV + d) = wv;
-    } else {
-      *(f32x4*)((float*)a.out + hrow * DV + d) = out;
-    }
+  f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w)
+    if (w < nwaves) br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v[w] * coef[h][w];
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  if (use_cmp) out += br[0] * g0;
+  if (use_slc) out += br[1] * g1;
+  if (use_win) out += br[2] * g2;
+  if (sizeof(TO) == 2) {
+    u32x2 wv = {(uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16),
+                (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16)};
+    *(u32x2*)((uint16_t*)a.out + hrow * DV + d) = wv;
+  } else {
+    *(f32x4*)((float*)a.out + hrow * DV + d) = out;
   }
   if (a.lse && tid < 16) a.lse[row * a.H + g * 16 + tid] = slse[tid];
 }
@@ -403,14 +414,15 @@ hipError_t run_t(const DecArgs& a, int mode, bool out_f32, hipStream_t s, Phases
     if (mode == 0) k_dec_cmp<DQ, DV, false><<<gc, 256, 0, s>>>(a);
     else k_dec_cmp<DQ, DV, true><<<gc, 256, 0, s>>>(a);
     if (ph) ph->mark();
-    k_dec_select<DV><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+    if (a.nbp <= 1024) k_dec_select<DV, 16><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+    else k_dec_select<DV, MAX_NB_LANE><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
     if (ph) ph->mark();
     if (mode == 0) return hipGetLastError();
   }
   k_dec_attn<DQ, DV><<<(unsigned)((a.R * a.G * nsw + 3) / 4), 256, 0, s>>>(a);
   if (ph) ph->mark();
-  if (out_f32) k_dec_merge<DV, float><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
-  else k_dec_merge<DV, uint16_t><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+  if (out_f32) k_dec_merge<DV, float><<<(unsigned)(a.R * a.G), 4 * DV, 0, s>>>(a);
+  else k_dec_merge<DV, uint16_t><<<(unsigned)(a.R * a.G), 4 * DV, 0, s>>>(a);
   if (ph) ph->mark();
   return hipGetLastError();
 }

@@ -29,11 +29,9 @@ __device__ __forceinline__ int topk_wave(float (&vals)[NBL], int64_t nvis, int64
     const int fb = f == 0 ? f0 : f1;
     if (fb >= 0 && fb < nvis) {
       --ncand;
-      if (lane == (fb & 63)) {
+      // selects, not indexed stores: vals stays in registers
 #pragma unroll
-        for (int i = 0; i < NBL; ++i)
-          if (i == (fb >> 6)) vals[i] = -1.f;
-      }
+      for (int i = 0; i < NBL; ++i) vals[i] = (lane == (fb & 63) && i == (fb >> 6)) ? -1.f : vals[i];
     }
   }
   const int r_take = (n - nf) < ncand ? (n - nf) : ncand;
@@ -53,8 +51,7 @@ __device__ __forceinline__ int topk_wave(float (&vals)[NBL], int64_t nvis, int64
     if (lane == nf + round) { cj = J; cs = M; }
     if (lane == (J & 63)) {
 #pragma unroll
-      for (int i = 0; i < NBL; ++i)
-        if (i == (J >> 6)) vals[i] = -1.f;
+      for (int i = 0; i < NBL; ++i) vals[i] = i == (J >> 6) ? -1.f : vals[i];
       bv = -1.f;
       bi = 0;
 #pragma unroll
