@@ -244,12 +244,61 @@ def run_cpu_baseline(prob, x, target_s=15.0):
             "seconds": round(t_rows + t_pool, 2)}
 
 
+# ---------------------------------------------------------------- ceilings --
+
+def run_ceilings(torch):
+    """Reference rates measured on this chip: a 1 GiB device copy, and random
+    whole 40 KiB block gathers (the selected branch's access pattern: K and V
+    of 64 keys at d 192 / 128) from tables of 160 MiB (fits the 256 MB last-
+    level cache) and 1.25 GiB (does not)."""
+    import ctypes
+    from long_context_dynamic_amd import build as nsa_build
+    if not os.path.exists(nsa_build.PROBE_LIB):
+        raise RuntimeError(f"{nsa_build.PROBE_LIB} is not built (python -m long_context_dynamic_amd.build)")
+    probe = ctypes.CDLL(nsa_build.PROBE_LIB)
+    probe.nsa_probe_gather.restype = ctypes.c_int
+    probe.nsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    res = {}
+    a = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    res["copy_1GiB_GBps"] = round(2 * 2 ** 30 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    stream = torch.cuda.current_stream().cuda_stream
+    waves, per_wave = 262144, 4
+    out = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+    gen = torch.Generator().manual_seed(0)
+    for nblk, label in ((4096, "160MiB"), (32768, "1280MiB")):
+        table = torch.ones(nblk * 40960 // 4, dtype=torch.int32, device="cuda")
+        pick = torch.randint(0, nblk, (2 ** 20,), generator=gen, dtype=torch.int32).cuda()
+        args = (table.data_ptr(), pick.data_ptr(), pick.numel(), out.data_ptr(), waves, per_wave, stream)
+        if probe.nsa_probe_gather(*args) != 0:
+            raise RuntimeError("gather probe launch failed")
+        e0.record()
+        if probe.nsa_probe_gather(*args) != 0:
+            raise RuntimeError("gather probe launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"gather_40KiB_blocks_{label}_TBps"] = round(waves * per_wave * 40960 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 2)
+        del table, pick
+    return res
+
+
 # ------------------------------------------------------- profiling legs --
 
 def run_only(args, torch, nsa, workloads, inputs):
     """One leg for a profiler: prefill or decode steps, or a plain 1 GiB
     device copy whose byte counters calibrate the others'."""
-    if args.only == "copy":
+    if args.only == "ceilings":
+        log(f"ceilings {run_ceilings(torch)}")
+    elif args.only == "copy":
         a = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
         for _ in range(args.steps):
@@ -276,7 +325,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings"], default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -321,6 +370,8 @@ def main():
         rec["decode"] = run_decode(args, torch, nsa, workloads, inputs)
         log(f"decode: {rec['decode']['ms_per_step']} ms/step")
         x = inputs.generate(prob)
+    rec["measured_ceilings"] = run_ceilings(torch)
+    log(f"ceilings: {rec['measured_ceilings']}")
     if not args.no_cpu:
         log("cpu baseline: timing the oracle on a sample")
         rec["cpu_baseline"] = run_cpu_baseline(prob, x)

@@ -45,6 +45,28 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "ceilings.hip")
+PROBE_LIB = os.path.join(PKG, "libnsa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's measurement kernels (not the attention library)."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, "ceilings.hip.o")
+    r = subprocess.run([HIPCC, *CFLAGS, "-c", PROBE_SRC, "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}", file=sys.stderr)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -64,3 +86,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
