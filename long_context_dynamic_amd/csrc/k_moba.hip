@@ -59,8 +59,16 @@ __device__ __forceinline__ int row_min16(int x) {
 }
 
 // ---------------------------------------------------------------------------
-// NT = number of 16-block column tiles (nbp / 16).
-template <int D, int NT>
+// One workgroup per (head, 64 tokens), 16 tokens per wave.  Block scores
+// S = Q . Kc^T come 16 blocks at a time from the matrix cores (lane: block
+// 16*nt + lr, tokens 4*lg + r).  With one head per group the importance of a
+// block is its softmax probability, which ranks exactly like its logit, so
+// the top-k is taken on logits while streaming: each lane keeps, per token, a
+// descending list of its LS best candidate logits (visible, not forced; ties
+// keep the earlier block), and at the end the 16 lanes of a token merge their
+// lists.  SCORES: per-lane online softmax statistics as well, merged the same
+// way, for the probabilities of the chosen blocks.
+template <int D, int LS, bool SCORES>
 __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t ntile = (a.T + kRows - 1) / kRows;
@@ -68,7 +76,7 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
   const int64_t tile = (blockIdx.x / a.H) % ntile;
   const int64_t b = blockIdx.x / (a.H * ntile);
   const int64_t t0 = tile * kRows + 16 * wave;  // this wave's 16 tokens
-  // S = Q . Kc^T: A = token rows (lane: token t0 + lr), B = block rows
+  // A = token rows (lane: token t0 + lr), B = block rows
   bf16x8 qf[D / 32];
   {
     int64_t tq = t0 + lr;
@@ -77,88 +85,99 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
   }
-  float z[NT][4];  // z[nt][r]: token t0 + 4*lg + r, block 16*nt + lr
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int64_t blk = 16 * nt + lr;
-    if (blk > a.nb - 1) blk = a.nb - 1;
-    const uint16_t* kr = a.kc + ((b * a.nb + blk) * a.H + h) * D + 8 * lg;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) s = mfma16(qf[ks], ld8(kr + 32 * ks), s);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[nt][r] = s[r] * a.scale;
-  }
   const bool first = a.flags & NSA_F_FORCE_FIRST, current = a.flags & NSA_F_FORCE_CURRENT;
+  int nvis[4], cur[4];
+  float lv[4][LS], lm[4], ls[4];
+  int lj[4][LS];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int64_t t = t0 + 4 * lg + r;
+    if (t > a.T - 1) t = a.T - 1;
+    const int64_t p = a.L - a.T + t;
+    const int64_t nv = (p + 1) / a.bs;
+    nvis[r] = (int)(nv < a.nb ? nv : a.nb);
+    cur[r] = (int)(p / a.bs);
+    lm[r] = -INFINITY;
+    ls[r] = 0.f;
+#pragma unroll
+    for (int k = 0; k < LS; ++k) { lv[r][k] = -INFINITY; lj[r][k] = 0x7fffffff; }
+  }
+  // blocks visible to any of this wave's tokens (the last one sees the most)
+  int64_t t_last = t0 + 15 < a.T - 1 ? t0 + 15 : a.T - 1;
+  int64_t nv_last = (a.L - a.T + t_last + 1) / a.bs;
+  if (nv_last > a.nb) nv_last = a.nb;
+  const int64_t ntl = (nv_last + 15) / 16;
+  for (int64_t nt = 0; nt < ntl; ++nt) {
+    const int blk = (int)(16 * nt + lr);
+    const int64_t kb = blk < a.nb ? blk : a.nb - 1;
+    const uint16_t* kr = a.kc + ((b * a.nb + kb) * a.H + h) * D + 8 * lg;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) sc = mfma16(qf[ks], ld8(kr + 32 * ks), sc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float z = sc[r] * a.scale;
+      const bool vis = blk < nvis[r];
+      if (SCORES && vis) {
+        const float nm = fmaxf(lm[r], z);
+        ls[r] = ls[r] * __expf(lm[r] - nm) + __expf(z - nm);
+        lm[r] = nm;
+      }
+      const bool cand = vis && !(first && blk == 0) && !(current && blk == cur[r]);
+      if (cand && z > lv[r][LS - 1]) {
+        // insert after equal values (an earlier block wins a tie)
+#pragma unroll
+        for (int k = LS - 1; k > 0; --k) {
+          const bool shift = z > lv[r][k - 1];
+          const bool here = !shift && z > lv[r][k];
+          lv[r][k] = shift ? lv[r][k - 1] : (here ? z : lv[r][k]);
+          lj[r][k] = shift ? lj[r][k - 1] : (here ? blk : lj[r][k]);
+        }
+        if (z > lv[r][0]) { lv[r][0] = z; lj[r][0] = blk; }
+      }
+    }
+  }
   int chosen[4][8];  // per token: the chosen blocks, forced ones first
   float cscore[4][8];
   int cnt[4];
-  bool done[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t t = t0 + 4 * lg + r;
-    const int64_t p = a.L - a.T + (t < a.T ? t : a.T - 1);
-    int64_t nvis = (p + 1) / a.bs;
-    if (nvis > a.nb) nvis = a.nb;
-    const int64_t cur = p / a.bs;
-    // per-token softmax over the visible blocks: the probabilities are the
-    // block scores
-    float mx = -INFINITY;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (16 * nt + lr >= nvis) z[nt][r] = -INFINITY;
-      mx = fmaxf(mx, z[nt][r]);
+    float gm = 0.f, inv = 0.f;
+    if (SCORES) {
+      gm = row_max16(lm[r]);
+      const float part = lm[r] == -INFINITY ? 0.f : ls[r] * __expf(lm[r] - gm);
+      const float gs = row_sum16(part);
+      inv = gs > 0.f ? 1.f / gs : 0.f;
     }
-    mx = row_max16(mx);
-    float sm = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float e = z[nt][r] == -INFINITY ? 0.f : expf(z[nt][r] - mx);
-      z[nt][r] = e;
-      sm += e;
-    }
-    const float inv = nvis > 0 ? 1.f / row_sum16(sm) : 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { chosen[r][i] = 0x7fffffff; cscore[r][i] = -INFINITY; }
     int nf = 0;
     if (first) { chosen[r][0] = 0; cscore[r][0] = INFINITY; nf = 1; }
-    if (current && !(first && cur == 0)) {
-      if (nf == 0) { chosen[r][0] = (int)cur; cscore[r][0] = INFINITY; }
-      else { chosen[r][1] = (int)cur; cscore[r][1] = INFINITY; }
+    if (current && !(first && cur[r] == 0)) {
+      if (nf == 0) { chosen[r][0] = cur[r]; cscore[r][0] = INFINITY; }
+      else { chosen[r][1] = cur[r]; cscore[r][1] = INFINITY; }
       ++nf;
     }
-    // candidates: visible and not forced (others get -1, below any probability)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int64_t j = 16 * nt + lr;
-      const bool forced = (first && j == 0) || (current && j == cur);
-      z[nt][r] = (j < nvis && !forced) ? z[nt][r] * inv : -1.f;
-    }
     cnt[r] = nf;
-    done[r] = nf >= a.n;
-  }
-  // the best remaining candidate, one per round: the row maximum, and the
-  // lowest block among equal maxima (ties go to the earlier block)
-  for (int round = 0; round < 8 && round < a.n; ++round) {
+    // merge the 16 lanes' lists: the best head, the lowest block among equal
+    // heads; the winning lane pops it (uniform within the token's DPP row)
+    for (int round = 0; round < 8; ++round) {
+      if (cnt[r] >= a.n) break;
+      const float hv = lv[r][0];
+      const float M = row_max16(hv);
+      if (M == -INFINITY) break;
+      const int J = row_min16(hv == M ? lj[r][0] : 0x7fffffff);
+      if (hv == M && lj[r][0] == J) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (done[r]) continue;  // uniform within a DPP row (the token's 16 lanes)
-      float bv = -1.f;
-      int bj = 0x7fffffff;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (z[nt][r] > bv) { bv = z[nt][r]; bj = 16 * nt + lr; }
-      const float M = row_max16(bv);
-      if (M < 0.f) { done[r] = true; continue; }  // no candidate left
-      const int J = row_min16(bv == M ? bj : 0x7fffffff);
+        for (int k = 0; k < LS - 1; ++k) { lv[r][k] = lv[r][k + 1]; lj[r][k] = lj[r][k + 1]; }
+        lv[r][LS - 1] = -INFINITY;
+        lj[r][LS - 1] = 0x7fffffff;
+      }
+      const float score = SCORES ? __expf(M - gm) * inv : 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (i == cnt[r]) { chosen[r][i] = J; cscore[r][i] = M; }
+        if (i == cnt[r]) { chosen[r][i] = J; cscore[r][i] = score; }
       ++cnt[r];
-      done[r] = cnt[r] >= a.n;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (16 * nt + lr == J) z[nt][r] = -1.f;
     }
   }
   if (lr != 0) return;
@@ -520,15 +539,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   }
 }
 
-template <int D>
+template <int D, bool SCORES>
 hipError_t run_select_t(const MobaArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * a.H * ((a.T + kRows - 1) / kRows));
-  switch (a.nbp / 64) {
-    case 1: k_moba_select<D, 4><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_moba_select<D, 8><<<grid, 256, 0, s>>>(a); break;
-    case 3: k_moba_select<D, 12><<<grid, 256, 0, s>>>(a); break;
-    default: k_moba_select<D, 16><<<grid, 256, 0, s>>>(a); break;
-  }
+  // list length per lane: the most candidates one token takes
+  const int64_t nf_min = (a.flags & (NSA_F_FORCE_FIRST | NSA_F_FORCE_CURRENT)) ? 1 : 0;
+  const int64_t need = a.n - nf_min;
+  if (need <= 2) k_moba_select<D, 2, SCORES><<<grid, 256, 0, s>>>(a);
+  else if (need <= 4) k_moba_select<D, 4, SCORES><<<grid, 256, 0, s>>>(a);
+  else k_moba_select<D, 8, SCORES><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -563,9 +582,7 @@ hipError_t run_attend_t(const MobaArgs& a, bool out_f32, hipStream_t s, Phases* 
 }  // namespace
 
 bool moba_select_ok(const Prob& P) {
-  const int64_t nbp = (P.nb + 63) / 64 * 64;
-  return P.bf16() && P.hpg == 1 && (P.dq == 64 || P.dq == 128) && P.nb >= 1 && nbp <= 256 && P.n >= 1 &&
-         P.n <= 8;
+  return P.bf16() && P.hpg == 1 && (P.dq == 64 || P.dq == 128) && P.nb >= 1 && P.n >= 1 && P.n <= 8;
 }
 
 bool moba_attend_ok(const Prob& P) {
@@ -578,8 +595,8 @@ bool moba_ok(const Prob& P) {
 }
 
 hipError_t launch_moba_select(const Prob& P, const MobaArgs& a, hipStream_t s) {
-  if (P.dq == 128) return run_select_t<128>(a, s);
-  return run_select_t<64>(a, s);
+  if (P.dq == 128) return a.score ? run_select_t<128, true>(a, s) : run_select_t<128, false>(a, s);
+  return a.score ? run_select_t<64, true>(a, s) : run_select_t<64, false>(a, s);
 }
 
 hipError_t launch_moba_attend(const Prob& P, const MobaArgs& a, bool out_f32, hipStream_t s, Phases* ph) {

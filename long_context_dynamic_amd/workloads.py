@@ -1,11 +1,12 @@
 """Named problem descriptions (shapes and switches only, no arithmetic).
 
 A problem is a plain dict that both the GPU binding and the test oracle
-understand.  The five named workloads are the shapes the pages discuss:
-NSA with 4 KV groups x 16 query heads, d_qk 192, 64-token blocks and top-16
-([P1] s5 "Hardware Makes Sparsity Work"; [P2] numbers table), MoBA with
-512-token blocks and top-3 ([P1] s7 "Kimi Simplifies The Sparse Route"),
-and batched decoding over a 64k context ([P1] s6).
+understand.  The named workloads are the shapes the pages discuss: NSA with
+4 KV groups x 16 query heads, d_qk 192, 64-token blocks and top-16 ([P1] s5
+"Hardware Makes Sparsity Work"; [P2] numbers table), MoBA with 512-token
+blocks and top-3 ([P1] s7 "Kimi Simplifies The Sparse Route") at 32k, 128k
+and 1M tokens (MoBA's evaluation reaches the million-token range: [P1] s7,
+[P2] numbers table), and batched decoding over a 64k context ([P1] s6).
 """
 from __future__ import annotations
 
@@ -33,6 +34,13 @@ WORKLOADS = {
     "moba_32k": dict(_BASE, q_len=32768, kv_len=32768, n_groups=32, heads_per_group=1,
                      d_qk=128, d_v=128, block=512, top_k=3, window=0, force_first=0,
                      force_current=1, use_cmp=0, use_slc=1, use_win=0, dtype="bf16"),
+    # MoBA at longer contexts: the same head layout and rule
+    "moba_128k": dict(_BASE, q_len=131072, kv_len=131072, n_groups=32, heads_per_group=1,
+                      d_qk=128, d_v=128, block=512, top_k=3, window=0, force_first=0,
+                      force_current=1, use_cmp=0, use_slc=1, use_win=0, dtype="bf16"),
+    "moba_1m": dict(_BASE, q_len=1048576, kv_len=1048576, n_groups=32, heads_per_group=1,
+                    d_qk=128, d_v=128, block=512, top_k=3, window=0, force_first=0,
+                    force_current=1, use_cmp=0, use_slc=1, use_win=0, dtype="bf16"),
     # NSA decode: 64 sequences, 65536-token cache each, one new query token
     "nsa_decode_64x64k": dict(_BASE, batch=64, q_len=1, kv_len=65536, n_groups=4,
                               heads_per_group=16, d_qk=192, d_v=128, block=64, top_k=16,

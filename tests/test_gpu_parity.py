@@ -28,7 +28,11 @@ CASES = [
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
     ("moba_32k", dict(q_len=700, kv_len=3000), None),
     ("moba_32k", dict(batch=2, q_len=1000, kv_len=12000, block=64, top_k=8, d_qk=64, d_v=64, force_first=1), None),
+    ("moba_32k", dict(q_len=1200, kv_len=40000, block=64, top_k=8, d_qk=64, d_v=64), None),
+    ("moba_32k", dict(q_len=900, kv_len=5000, block=128, top_k=2, force_first=1, force_current=0), None),
     ("moba_32k", {}, 24),
+    ("moba_128k", {}, 16),
+    ("moba_1m", {}, 8),
     ("nsa_decode_64x64k", dict(batch=6, kv_len=4096 + 17), None),
 ]
 
