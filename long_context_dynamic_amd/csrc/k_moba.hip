@@ -67,9 +67,13 @@ __device__ __forceinline__ int row_min16(int x) {
 // descending list of its LS best candidate logits (visible, not forced; ties
 // keep the earlier block), and at the end the 16 lanes of a token merge their
 // lists.  SCORES: per-lane online softmax statistics as well, merged the same
-// way, for the probabilities of the chosen blocks.
+// way, for the probabilities of the chosen blocks.  The block summaries pass
+// through LDS 64 at a time, shared by the four waves, the next 64 in flight
+// while these are scored.
 template <int D, int LS, bool SCORES>
 __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
+  constexpr int KS = k_lds_stride<D>();
+  __shared__ __align__(16) uint16_t kcs[64 * KS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t ntile = (a.T + kRows - 1) / kRows;
   const int64_t h = blockIdx.x % a.H;
@@ -102,18 +106,30 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
 #pragma unroll
     for (int k = 0; k < LS; ++k) { lv[r][k] = -INFINITY; lj[r][k] = 0x7fffffff; }
   }
-  // blocks visible to any of this wave's tokens (the last one sees the most)
-  int64_t t_last = t0 + 15 < a.T - 1 ? t0 + 15 : a.T - 1;
-  int64_t nv_last = (a.L - a.T + t_last + 1) / a.bs;
-  if (nv_last > a.nb) nv_last = a.nb;
-  const int64_t ntl = (nv_last + 15) / 16;
-  for (int64_t nt = 0; nt < ntl; ++nt) {
+  // blocks visible to any of this wave's tokens (the last one sees the most),
+  // and to any of the workgroup's
+  auto visible_to = [&](int64_t t) {
+    const int64_t tl = t < a.T - 1 ? t : a.T - 1;
+    const int64_t nv = (a.L - a.T + tl + 1) / a.bs;
+    return nv < a.nb ? nv : a.nb;
+  };
+  const int64_t ntl = (visible_to(t0 + 15) + 15) / 16;
+  const int64_t nchunk = (visible_to(tile * kRows + kRows - 1) + 63) / 64;
+  Stager<D, D, 256> st;
+  if (nchunk > 0) st.load(a.kc, a.nb, 0, false, nullptr, 0, 0, b, h, a.H, false);
+  for (int64_t c = 0; c < nchunk; ++c) {
+    __syncthreads();
+    st.store(kcs, nullptr, false, false);
+    __syncthreads();
+    if (c + 1 < nchunk) st.load(a.kc, a.nb, 64 * (c + 1), false, nullptr, 0, 0, b, h, a.H, false);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+    const int64_t nt = 4 * c + tt;
+    if (nt >= ntl) break;  // wave-uniform
     const int blk = (int)(16 * nt + lr);
-    const int64_t kb = blk < a.nb ? blk : a.nb - 1;
-    const uint16_t* kr = a.kc + ((b * a.nb + kb) * a.H + h) * D + 8 * lg;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) sc = mfma16(qf[ks], ld8(kr + 32 * ks), sc);
+    for (int ks = 0; ks < D / 32; ++ks) sc = mfma16(qf[ks], ld8(kcs + (16 * tt + lr) * KS + 8 * lg + 32 * ks), sc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float z = sc[r] * a.scale;
@@ -135,6 +151,7 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
         }
         if (z > lv[r][0]) { lv[r][0] = z; lj[r][0] = blk; }
       }
+    }
     }
   }
   int chosen[4][8];  // per token: the chosen blocks, forced ones first
