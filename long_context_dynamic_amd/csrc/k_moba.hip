@@ -58,15 +58,32 @@ __device__ __forceinline__ int row_min16(int x) {
   return min(x, dpp_i<kDppMirror>(x));
 }
 
+// Descending list insertion without branches: x goes after equal values (the
+// earlier block keeps a tie); -inf changes nothing.
+template <int LS>
+__device__ __forceinline__ void list_insert(float (&v)[LS], int (&j)[LS], float x, int blk) {
+  bool c[LS];
+#pragma unroll
+  for (int k = 0; k < LS; ++k) c[k] = x > v[k];
+#pragma unroll
+  for (int k = LS - 1; k > 0; --k) {
+    v[k] = c[k - 1] ? v[k - 1] : (c[k] ? x : v[k]);
+    j[k] = c[k - 1] ? j[k - 1] : (c[k] ? blk : j[k]);
+  }
+  v[0] = c[0] ? x : v[0];
+  j[0] = c[0] ? blk : j[0];
+}
+
 // ---------------------------------------------------------------------------
 // One workgroup per (head, 64 tokens), 16 tokens per wave.  Block scores
 // S = Q . Kc^T come 16 blocks at a time from the matrix cores (lane: block
 // 16*nt + lr, tokens 4*lg + r).  With one head per group the importance of a
 // block is its softmax probability, which ranks exactly like its logit, so
-// the top-k is taken on logits while streaming: each lane keeps, per token, a
-// descending list of its LS best candidate logits (visible, not forced; ties
-// keep the earlier block), and at the end the 16 lanes of a token merge their
-// lists.  SCORES: per-lane online softmax statistics as well, merged the same
+// the top-k is taken on unscaled dot products while streaming: each lane
+// keeps, per token, a descending list of its LS best candidates (visible, not
+// forced; ties keep the earlier block), and at the end the 16 lanes of a token
+// merge their lists.  Tiles wholly visible to the wave and free of forced
+// blocks skip the masks.  SCORES: per-lane online softmax statistics as well, merged the same
 // way, for the probabilities of the chosen blocks.  The block summaries pass
 // through LDS 64 at a time, shared by the four waves, the next 64 in flight
 // while these are scored.
@@ -114,6 +131,9 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
     return nv < a.nb ? nv : a.nb;
   };
   const int64_t ntl = (visible_to(t0 + 15) + 15) / 16;
+  const int64_t nvis_min = visible_to(t0);  // the wave's first token sees the fewest
+  const int64_t cur_min = (a.L - a.T + (t0 < a.T - 1 ? t0 : a.T - 1)) / a.bs;
+  const int64_t cur_max = (a.L - a.T + (t0 + 15 < a.T - 1 ? t0 + 15 : a.T - 1)) / a.bs;
   const int64_t nchunk = (visible_to(tile * kRows + kRows - 1) + 63) / 64;
   Stager<D, D, 256> st;
   if (nchunk > 0) st.load(a.kc, a.nb, 0, false, nullptr, 0, 0, b, h, a.H, false);
@@ -130,27 +150,22 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) sc = mfma16(qf[ks], ld8(kcs + (16 * tt + lr) * KS + 8 * lg + 32 * ks), sc);
+    const bool plain = 16 * nt + 16 <= nvis_min && !(first && nt == 0) &&
+                       !(current && 16 * nt <= cur_max && 16 * nt + 15 >= cur_min);  // wave-uniform
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float z = sc[r] * a.scale;
-      const bool vis = blk < nvis[r];
-      if (SCORES && vis) {
+      float x = sc[r];
+      if (SCORES && blk < nvis[r]) {
+        const float z = x * a.scale;
         const float nm = fmaxf(lm[r], z);
         ls[r] = ls[r] * __expf(lm[r] - nm) + __expf(z - nm);
         lm[r] = nm;
       }
-      const bool cand = vis && !(first && blk == 0) && !(current && blk == cur[r]);
-      if (cand && z > lv[r][LS - 1]) {
-        // insert after equal values (an earlier block wins a tie)
-#pragma unroll
-        for (int k = LS - 1; k > 0; --k) {
-          const bool shift = z > lv[r][k - 1];
-          const bool here = !shift && z > lv[r][k];
-          lv[r][k] = shift ? lv[r][k - 1] : (here ? z : lv[r][k]);
-          lj[r][k] = shift ? lj[r][k - 1] : (here ? blk : lj[r][k]);
-        }
-        if (z > lv[r][0]) { lv[r][0] = z; lj[r][0] = blk; }
+      if (!plain) {
+        const bool cand = blk < nvis[r] && !(first && blk == 0) && !(current && blk == cur[r]);
+        x = cand ? x : -INFINITY;
       }
+      list_insert<LS>(lv[r], lj[r], x, blk);
     }
     }
   }
@@ -190,7 +205,7 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
         lv[r][LS - 1] = -INFINITY;
         lj[r][LS - 1] = 0x7fffffff;
       }
-      const float score = SCORES ? __expf(M - gm) * inv : 0.f;
+      const float score = SCORES ? __expf(M * a.scale - gm) * inv : 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (i == cnt[r]) { chosen[r][i] = J; cscore[r][i] = score; }
