@@ -34,9 +34,13 @@ constexpr int kChunk = 128;  // listed entries per attention workgroup (4 waves 
 constexpr int kCountTok = 256;  // tokens per list-counting workgroup
 constexpr int kXcds = 8;     // the chip's compute dies, each with its own L2
 
-// Partial record of one entry: D outputs, max (log2 units), sum, 2 spare
-// (16-byte aligned records).
-template <int D> constexpr int rec_floats() { return D + 4; }
+// Partial record of one entry (16-byte aligned): the normalised output o / l
+// as D fp16 values scaled by 2^-ex so that all lie in (-1, 1) (a relative
+// error of 2^-11 of the record's largest value), then the fp32 max (log2
+// units), the fp32 sum l, ex, and a spare word.
+template <int D> constexpr int rec_bytes() { return 2 * D + 16; }
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Row reductions over the 16 lanes of a DPP row (lanes 16*lg .. 16*lg + 15).
 __device__ __forceinline__ float row_max16(float x) {
@@ -429,13 +433,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    if (32 * wave + 16 * q + lr >= count) continue;
-    float* rec = a.part + e[q] * rec_floats<D>();
+    // the record's scale: the largest |o / l| over the query's lanes (all
+    // lanes take part in the reduction)
+    const float inv = l[q] > 0.f ? 1.f / l[q] : 0.f;
+    float amax = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *(f32x4*)(rec + 16 * dt + 4 * lg) = o[q][dt];
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(o[q][dt][r]));
+    amax = xor_max16_32(amax * inv);
+    int ex = 0;
+    (void)frexpf(amax, &ex);
+    const float sc = inv * ldexpf(1.f, -ex);
+    if (32 * wave + 16 * q + lr >= count) continue;
+    char* rec = (char*)a.part + e[q] * rec_bytes<D>();
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const f32x4 v = o[q][dt] * sc;
+      const f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      *(u32x2*)(rec + 2 * (16 * dt + 4 * lg)) = __builtin_bit_cast(u32x2, hv);
+    }
     if (lg == 0) {
-      rec[D] = m[q] * c;
-      rec[D + 1] = l[q];
+      float* tail = (float*)(rec + 2 * D);
+      tail[0] = m[q] * c;
+      tail[1] = l[q];
+      tail[2] = (float)ex;
     }
   }
 }
@@ -537,11 +559,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     const int32_t* irow = a.idx + ((b * a.T + t[q]) * a.H + h) * a.n;
     // merge with the partials of the earlier chosen blocks (log2 units)
     const bool own = has_cur[q] && l[q] > 0.f;  // a row without its own block ran on -inf only
-    const float* prow = a.part + ((b * a.T + t[q]) * a.H + h) * a.n * rec_floats<D>();
+    const char* prow = (const char*)a.part + ((b * a.T + t[q]) * a.H + h) * a.n * rec_bytes<D>();
     float M = own ? m[q] * c : -INFINITY;
     for (int i = 0; i < a.n; ++i) {
       const int j = irow[i];
-      if (j >= 0 && j < cur) M = fmaxf(M, prow[i * rec_floats<D>() + D]);
+      if (j >= 0 && j < cur) M = fmaxf(M, *(const float*)(prow + i * rec_bytes<D>() + 2 * D));
     }
     const float wd = own ? exp2f(m[q] * c - M) : 0.f;
     float den = own ? wd * l[q] : 0.f;
@@ -551,11 +573,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     for (int i = 0; i < a.n; ++i) {
       const int j = irow[i];
       if (j < 0 || j >= cur) continue;
-      const float* rec = prow + i * rec_floats<D>();
-      const float ws = exp2f(rec[D] - M);
-      den = fmaf(ws, rec[D + 1], den);
+      const char* rec = prow + i * rec_bytes<D>();
+      const float* tail = (const float*)(rec + 2 * D);
+      const float ws = exp2f(tail[0] - M) * tail[1];  // the record's weight: its share of the softmax mass
+      den += ws;
+      const float f = ws * ldexpf(1.f, (int)tail[2]);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt] += *(const f32x4*)(rec + 16 * dt + 4 * lg) * ws;
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const f16x4 hv = __builtin_bit_cast(f16x4, *(const u32x2*)(rec + 2 * (16 * dt + 4 * lg)));
+        acc[dt] += f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]} * f;
+      }
     }
     float g = den > 0.f ? 1.f / den : 0.f;
     if (a.gates) {

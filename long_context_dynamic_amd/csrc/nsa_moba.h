@@ -20,7 +20,7 @@ struct MobaArgs {
   int32_t* offsets;       // [B*H*nb + 1] list starts
   int32_t* chunk_off;     // [B*H*nb + 1] first 64-entry chunk of each list
   int32_t* lists;         // [B*T*H*n] entry ids, grouped by list
-  float* part;            // [B, T, H, n, D + 4] partial output, max (log2 units), sum, 2 spare
+  float* part;            // [B, T, H, n] records of 2 D + 16 bytes: fp16 scaled o / l, max, sum, exponent
   void* out;              // [B, T, H, D]
   float* lse;             // [B, T, H] or NULL
   int64_t B, T, L, H, nb, nbp, Lp, bs, n;

@@ -49,7 +49,7 @@ void take_moba(const Prob& P, Workspace& w, const std::function<size_t(size_t)>&
   w.offsets = take((nl + 1) * sizeof(int32_t));
   w.chunk_off = take((nl + 1) * sizeof(int32_t));
   w.lists = take(ne * sizeof(int32_t));
-  w.part = take(ne * (size_t)(P.dv + 4) * sizeof(float));
+  w.part = take(ne * (size_t)(2 * P.dv + 16));  // compact partial records
 }
 
 void set_moba_ws(MobaArgs& a, const Workspace& ws, void* base) {
