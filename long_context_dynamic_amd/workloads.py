@@ -17,6 +17,7 @@ _BASE = dict(
     d_qk=64, d_v=64, block=64, top_k=4, window=128,
     force_first=1, force_current=1, use_cmp=1, use_slc=1, use_win=1,
     gate_logits=0, dtype="f32", scale=0.0,
+    sel_block=0,  # selection block size; 0: the compression block size
     key_offset_std=0.5, seed=0,
 )
 

@@ -12,6 +12,9 @@ A problem is described by a plain dict with the keys
     block, top_k, window, force_first, force_current,
     use_cmp, use_slc, use_win, gate_logits, dtype ('bf16' | 'f32'), scale
 
+and optionally sel_block (selection block, a multiple of block; 0 or absent:
+the same as block).
+
 Tensors are numpy arrays: ``uint16`` bit patterns for bf16, ``float32``
 otherwise, in the layouts listed in ``nsa_oracle.h``.  Every result the
 oracle computes is returned in float64, except the pooled block summaries,
@@ -39,7 +42,7 @@ class _Cfg(ctypes.Structure):
         ("force_first", ctypes.c_int32), ("force_current", ctypes.c_int32),
         ("use_cmp", ctypes.c_int32), ("use_slc", ctypes.c_int32), ("use_win", ctypes.c_int32),
         ("gate_logits", ctypes.c_int32), ("is_bf16", ctypes.c_int32),
-        ("scale", ctypes.c_double),
+        ("sel_block", ctypes.c_int32), ("scale", ctypes.c_double),
     ]
 
 
@@ -85,6 +88,8 @@ def _cfg(prob: dict) -> _Cfg:
             c.is_bf16 = 1 if prob["dtype"] == "bf16" else 0
         elif name == "scale":
             c.scale = float(prob.get("scale", 0.0) or 0.0)
+        elif name == "sel_block":
+            c.sel_block = int(prob.get("sel_block", 0) or 0)
         else:
             setattr(c, name, int(prob[name]))
     return c
@@ -127,17 +132,17 @@ def pool(prob: dict, k: np.ndarray, v: np.ndarray):
 def select(prob: dict, q, kc, vc=None, rows=None, want_imp=True, want_cmp=True):
     """Selection for the given flat rows (b*T + t).
 
-    Returns (idx [R,G,top_k] int32, imp [R,G,nb] float64 or None,
-    o_cmp [R,H,d_v] float64 or None)."""
+    Returns (idx [R,G,top_k] int32, imp [R,G,nbs] float64 or None (one
+    importance per selection block), o_cmp [R,H,d_v] float64 or None)."""
     q, kc = _stored(q, prob), _stored(kc, prob)
     if want_cmp:
         vc = _stored(vc, prob)
     rows = _rows(prob, rows)
     R, G = len(rows), prob["n_groups"]
     H = G * prob["heads_per_group"]
-    nb = prob["kv_len"] // prob["block"]
+    nbs = prob["kv_len"] // (prob.get("sel_block", 0) or prob["block"])
     idx = np.zeros((R, G, prob["top_k"]), dtype=np.int32)
-    imp = np.zeros((R, G, nb), dtype=np.float64) if want_imp else None
+    imp = np.zeros((R, G, nbs), dtype=np.float64) if want_imp else None
     ocmp = np.zeros((R, H, prob["d_v"]), dtype=np.float64) if want_cmp else None
     c = _cfg(prob)
     _check(_load().oracle_select(ctypes.byref(c), _ptr(q), _ptr(kc), _ptr(vc) if want_cmp else None,

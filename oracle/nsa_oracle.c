@@ -23,7 +23,11 @@
  *   - the window holds the last `window` positions up to and including p
  *     ([P5] s12: a sliding window looks at the previous 512 tokens);
  *   - the softmax scale is 1/sqrt(d_qk) in every branch unless given;
- *   - an empty key set gives a zero output.
+ *   - an empty key set gives a zero output;
+ *   - selection blocks may be longer than compression blocks ([P1] s4 notes
+ *     the two sizes can differ and leaves the mechanism open): a selection
+ *     block is a run of whole compression blocks, and its importance is the
+ *     sum of theirs; it is a candidate once complete, like a summary.
  */
 #include "nsa_oracle.h"
 
@@ -74,7 +78,13 @@ static int cfg_ok(const oracle_cfg* c) {
   if (c->batch < 1 || c->q_len < 1 || c->kv_len < c->q_len) return 0;
   if (c->n_groups < 1 || c->heads_per_group < 1) return 0;
   if (c->d_qk < 1 || c->d_v < 1 || c->block < 1 || c->top_k < 0 || c->window < 0) return 0;
+  if (c->sel_block < 0 || (c->sel_block > 0 && c->sel_block % c->block != 0)) return 0;
   return 1;
+}
+
+/* Tokens per selection block. */
+static int64_t sel_block(const oracle_cfg* c) {
+  return c->sel_block > 0 ? c->sel_block : c->block;
 }
 
 static double softmax_scale(const oracle_cfg* c) {
@@ -140,6 +150,8 @@ int oracle_select(const oracle_cfg* c, const void* q, const void* kc, const void
   const int64_t T = c->q_len, L = c->kv_len, G = c->n_groups, hpg = c->heads_per_group;
   const int64_t H = G * hpg, dq = c->d_qk, dv = c->d_v, bs = c->block, n = c->top_k;
   const int64_t nb = L / bs;
+  const int64_t bsel = sel_block(c), per = bsel / bs;  /* compression blocks per selection block */
+  const int64_t nbs = L / bsel;
   const double scale = softmax_scale(c);
   const int64_t n_forced_max = (c->force_first ? 1 : 0) + (c->force_current ? 1 : 0);
   if (n < n_forced_max) return ORACLE_BAD_CONFIG;
@@ -149,12 +161,16 @@ int oracle_select(const oracle_cfg* c, const void* q, const void* kc, const void
   for (int64_t r = 0; r < nrows; ++r) {
     const int64_t b = rows[r] / T, t = rows[r] % T;
     const int64_t p = L - T + t;               /* absolute query position */
-    const int64_t nvis = (p + 1) / bs;         /* blocks j with (j+1)*bs <= p+1 */
-    const int64_t cur = p / bs;                /* the query's own block */
+    const int64_t nvis = (p + 1) / bs;         /* summaries j with (j+1)*bs <= p+1 */
+    const int64_t nvis_s = (p + 1) / bsel;     /* complete selection blocks */
+    const int64_t cur = p / bsel;              /* the query's own selection block */
     double* z = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
     double* importance = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
-    cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(nb > 0 ? nb : 1));
-    if (!z || !importance || !cand) { bad = 1; free(z); free(importance); free(cand); continue; }
+    double* imp_sel = (double*)malloc(sizeof(double) * (size_t)(nbs > 0 ? nbs : 1));
+    cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(nbs > 0 ? nbs : 1));
+    if (!z || !importance || !imp_sel || !cand) {
+      bad = 1; free(z); free(importance); free(imp_sel); free(cand); continue;
+    }
 
     for (int64_t g = 0; g < G; ++g) {
       for (int64_t j = 0; j < nb; ++j) importance[j] = 0.0;
@@ -188,27 +204,34 @@ int oracle_select(const oracle_cfg* c, const void* q, const void* kc, const void
         for (int64_t j = 0; j < nvis; ++j) importance[j] += z[j];
       }
 
+      /* a selection block's importance: the sum over its summaries (all
+         visible once the selection block is complete) */
+      for (int64_t J = 0; J < nvis_s; ++J) {
+        double s = 0.0;
+        for (int64_t i = J * per; i < (J + 1) * per; ++i) s += importance[i];
+        imp_sel[J] = s;
+      }
       if (imp)
-        for (int64_t j = 0; j < nb; ++j)
-          imp[(r * G + g) * nb + j] = j < nvis ? importance[j] : NAN;
+        for (int64_t J = 0; J < nbs; ++J)
+          imp[(r * G + g) * nbs + J] = J < nvis_s ? imp_sel[J] : NAN;
 
-      /* forced blocks, then the best of the remaining visible blocks */
+      /* forced blocks, then the best of the remaining complete blocks */
       int32_t* sel = idx + (r * G + g) * n;
       int64_t cnt = 0;
       if (c->force_first) sel[cnt++] = 0;
       if (c->force_current && !(c->force_first && cur == 0)) sel[cnt++] = (int32_t)cur;
       int64_t ncand = 0;
-      for (int64_t j = 0; j < nvis; ++j) {
+      for (int64_t J = 0; J < nvis_s; ++J) {
         int forced = 0;
-        for (int64_t f = 0; f < cnt; ++f) forced |= (sel[f] == j);
-        if (!forced) { cand[ncand].score = importance[j]; cand[ncand].block = (int32_t)j; ++ncand; }
+        for (int64_t f = 0; f < cnt; ++f) forced |= (sel[f] == J);
+        if (!forced) { cand[ncand].score = imp_sel[J]; cand[ncand].block = (int32_t)J; ++ncand; }
       }
       qsort(cand, (size_t)ncand, sizeof(cand_t), cand_order);
       for (int64_t i = 0; i < ncand && cnt < n; ++i) sel[cnt++] = cand[i].block;
       qsort(sel, (size_t)cnt, sizeof(int32_t), int_order);
       for (int64_t i = cnt; i < n; ++i) sel[i] = -1;
     }
-    free(z); free(importance); free(cand);
+    free(z); free(importance); free(imp_sel); free(cand);
   }
   return bad ? ORACLE_BAD_CONFIG : ORACLE_OK;
 }
@@ -259,7 +282,7 @@ int oracle_attend(const oracle_cfg* c, const void* q, const void* k, const void*
                   double* out, double* o_slc, double* o_win) {
   if (!cfg_ok(c)) return ORACLE_BAD_CONFIG;
   const int64_t T = c->q_len, L = c->kv_len, G = c->n_groups, hpg = c->heads_per_group;
-  const int64_t H = G * hpg, dv = c->d_v, bs = c->block, n = c->top_k;
+  const int64_t H = G * hpg, dv = c->d_v, bs = sel_block(c), n = c->top_k;
   const int n_branches = (c->use_cmp != 0) + (c->use_slc != 0) + (c->use_win != 0);
   if (!gates && n_branches > 1) return ORACLE_BAD_CONFIG;
   if (c->use_cmp && !o_cmp) return ORACLE_BAD_CONFIG;

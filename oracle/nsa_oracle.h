@@ -17,6 +17,8 @@
  *   q     [B, T, H, d_qk]      k  [B, L, G, d_qk]     v  [B, L, G, d_v]
  *   gates [B, T, H, 3]         (compressed, selected, window)
  *   kc    [B, nb, G, d_qk]     vc [B, nb, G, d_v]     nb = floor(L / block)
+ * Selection works on blocks of sel_block tokens (nbs = floor(L / sel_block));
+ * with sel_block = block the two block grids coincide.
  * Storage is fp32, or bf16 given as raw 16-bit patterns (is_bf16 = 1).
  * Query row t sits at absolute position p = L - T + t.
  * Head h belongs to KV group h / heads_per_group.
@@ -39,6 +41,8 @@ typedef struct {
   int32_t use_cmp, use_slc, use_win;  /* branches that enter the output */
   int32_t gate_logits;    /* gates hold logits; apply sigmoid first  */
   int32_t is_bf16;        /* 1: bf16 bit patterns, 0: fp32           */
+  int32_t sel_block;      /* selection block; 0 means block; else a  */
+                          /* multiple of block                       */
   double scale;           /* softmax scale; 0 means 1/sqrt(d_qk)     */
 } oracle_cfg;
 
@@ -52,8 +56,9 @@ int oracle_pool(const oracle_cfg* c, const void* k, const void* v, void* kc, voi
 
 /* Compressed branch + group importance + top-k for the listed query rows
  * (flat row r = b * T + t).
- *   idx   [nrows, G, top_k]  ascending block ids, padded with -1
- *   imp   [nrows, G, nb]     importance of each block (NaN if not visible), may be NULL
+ *   idx   [nrows, G, top_k]  ascending selection-block ids, padded with -1
+ *   imp   [nrows, G, nbs]    importance of each selection block (NaN if not
+ *                            visible), may be NULL
  *   o_cmp [nrows, H, d_v]    compressed-branch output, may be NULL        */
 int oracle_select(const oracle_cfg* c, const void* q, const void* kc, const void* vc,
                   const int64_t* rows, int64_t nrows,

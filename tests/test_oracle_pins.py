@@ -241,6 +241,62 @@ def test_moba_ranking_is_logit_ranking():
             assert list(idx[t, g]) == sorted({cur} | set(order)) + [-1] * (3 - len({cur} | set(order)))
 
 
+# ------------------------------------ decoupled selection block size ----
+
+@pytest.mark.parametrize("block,per,top_k,first", [(4, 2, 3, 1), (8, 2, 4, 0), (4, 4, 3, 1)])
+def test_decoupled_selection_sums_summary_importances(block, per, top_k, first):
+    # selection blocks of `per` summaries: the importance of each is the sum of
+    # its summaries' (independent numpy softmax), and the choice is the best
+    # admissible subset (brute force) on the selection-block grid
+    sb = block * per
+    prob = H.problem(q_len=96, kv_len=96, block=block, sel_block=sb, top_k=top_k, n_groups=2,
+                     heads_per_group=3, d_qk=8, d_v=4, window=8, force_first=first, seed=4)
+    x = H.make(prob)
+    kc, vc = oracle.pool(prob, x["k"], x["v"])
+    idx, imp, _ = oracle.select(prob, x["q"], kc, vc)
+    imp_c, _ = _importance_by_torch(prob, x, kc)
+    nbs = prob["kv_len"] // sb
+    want = imp_c[:, :, :nbs * per].reshape(prob["q_len"], 2, nbs, per).sum(axis=3)
+    pos = H.positions(prob)
+    vis = (np.arange(nbs)[None, :] + 1) * sb <= pos[:, None] + 1
+    np.testing.assert_allclose(np.where(vis[:, None, :], imp, 0.0), np.where(vis[:, None, :], want, 0.0),
+                               atol=1e-12, rtol=0)
+    assert np.all(np.isnan(imp[~np.broadcast_to(vis[:, None, :], imp.shape)]))
+    coarse = dict(prob, block=sb)
+    for t in range(0, prob["q_len"], 3):
+        for g in range(2):
+            assert list(idx[t, g]) == _brute_force_selection(coarse, want[t, g], vis[t], pos[t]), (t, g)
+
+
+@pytest.mark.parametrize("hpg", [1, 4])
+def test_decoupled_selection_equals_coupled_when_keys_repeat_within_a_selection_block(hpg):
+    # keys constant inside each selection block: its summaries are all equal,
+    # so each head's summed probability is the coarse (block = sel_block)
+    # probability times that head's share of softmax mass on complete
+    # selection blocks.  Where every visible summary lies in a complete
+    # selection block the share is 1: importances and choices are the coarse
+    # ones.  With one head per group the factor cannot reorder blocks: the
+    # choices agree on every row.
+    block, per = 8, 4
+    sb = block * per
+    prob = H.problem(q_len=256, kv_len=256, block=block, sel_block=sb, top_k=4, n_groups=2,
+                     heads_per_group=hpg, d_qk=8, d_v=4, window=16, seed=7)
+    x = H.make(prob)
+    k = x["k"].reshape(1, 256 // sb, sb, 2, 8)
+    k[:] = k[:, :, :1]  # the first key of each selection block, repeated
+    fine_kc, fine_vc = oracle.pool(prob, x["k"], x["v"])
+    coarse = dict(prob, block=sb, sel_block=0)
+    coarse_kc, coarse_vc = oracle.pool(coarse, x["k"], x["v"])
+    idx_f, imp_f, _ = oracle.select(prob, x["q"], fine_kc, fine_vc)
+    idx_c, imp_c, _ = oracle.select(coarse, x["q"], coarse_kc, coarse_vc)
+    pos = H.positions(prob)
+    whole = (pos + 1) % sb == 0
+    np.testing.assert_allclose(imp_f[whole], imp_c[whole], atol=1e-12, rtol=0, equal_nan=True)
+    np.testing.assert_array_equal(idx_f[whole], idx_c[whole])
+    if hpg == 1:
+        np.testing.assert_array_equal(idx_f, idx_c)
+
+
 def test_architecture_figure_toy_selection():
     """Figure 2 walk-through: four blocks, top-2, the 2nd and 4th are chosen."""
     with open(os.path.join(GOLDEN, "figure2_toy_selection.json")) as f:
@@ -275,13 +331,16 @@ def test_selecting_every_block_is_dense_causal_attention():
         np.testing.assert_allclose(r["out"][:, h], want, atol=1e-12, rtol=0)
 
 
-def test_selected_branch_is_masked_attention_on_the_chosen_blocks():
-    prob = H.problem(q_len=128, kv_len=128, block=8, top_k=4, n_groups=1, heads_per_group=2,
-                     d_qk=8, d_v=8, window=16, seed=7)
+@pytest.mark.parametrize("sel_block", [0, 16])
+def test_selected_branch_is_masked_attention_on_the_chosen_blocks(sel_block):
+    # masked SDPA over the chosen blocks' tokens (selection blocks of 16
+    # tokens over 8-token summaries in the second case)
+    prob = H.problem(q_len=128, kv_len=128, block=8, sel_block=sel_block, top_k=4, n_groups=1,
+                     heads_per_group=2, d_qk=8, d_v=8, window=16, seed=7)
     x = H.make(prob)
     r = oracle.forward(prob, x["q"], x["k"], x["v"], x["gates"])
     q, k, v = (H.widen(x[n], prob)[0] for n in ("q", "k", "v"))
-    blk = np.arange(128) // 8
+    blk = np.arange(128) // (sel_block or 8)
     for h in range(2):
         mask = np.zeros((128, 128), bool)
         for t in range(128):
