@@ -43,9 +43,12 @@ def algorithmic_flops(prob):
     """Per-branch algorithmic FLOPs of one forward: 2 per multiply-add, over
     exactly the keys each branch attends to (masked work not counted)."""
     p = positions(prob)
-    bs, n, w = prob["block"], prob["top_k"], prob["window"]
+    bc = prob["block"]                      # summaries
+    bs = prob.get("sel_block", 0) or bc     # selection blocks
+    n, w = prob["top_k"], prob["window"]
     H, dq, dv = prob["n_groups"] * prob["heads_per_group"], prob["d_qk"], prob["d_v"]
     per_key = 2.0 * (dq + dv) * H * prob["batch"]
+    nvis_c = np.minimum((p + 1) // bc, prob["kv_len"] // bc)
     nvis = np.minimum((p + 1) // bs, prob["kv_len"] // bs)
     cur = p // bs
     first, current = bool(prob["force_first"]), bool(prob["force_current"])
@@ -60,7 +63,7 @@ def algorithmic_flops(prob):
     sel_keys = bs * chosen - np.where(cur_in, bs - (p % bs + 1), 0)
     win_keys = np.minimum(w, p + 1) if (prob["use_win"] and w > 0) else np.zeros_like(p)
     return {
-        "cmp": per_key * float(nvis.sum()) if prob["use_cmp"] else 0.0,
+        "cmp": per_key * float(nvis_c.sum()) if prob["use_cmp"] else 0.0,
         "slc": per_key * float(sel_keys.sum()),
         "win": per_key * float(win_keys.sum()),
     }

@@ -105,6 +105,13 @@ typedef struct {
    * (as far as events are given); nsa_forward_phases names the kernels. */
   void* const* phase_events;
   int32_t n_phase_events;
+  /* Selection block size in tokens (0 means `block`): a multiple of
+   * `block`.  Selection works on blocks of sel_block tokens, each the run
+   * of sel_block / block whole compression blocks it covers; its importance
+   * is the sum of theirs ([P1] s4 notes the two sizes may differ and leaves
+   * the mechanism open; this is the reading taken).  idx values count
+   * selection blocks. */
+  int32_t sel_block;
 } nsa_params;
 
 /*

@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(256) k_dec_cmp(DecArgs a) {
   const int64_t row = item / (a.n_cmp_waves * a.G);
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
-  int64_t nvis = (p + 1) / 64;
+  int64_t nvis = (p + 1) / a.bs;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
   int tiles[TILES_PER_CMP_WAVE];
   int nt = 0;
@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
   const int64_t g = blockIdx.x % a.G;
   const int64_t row = blockIdx.x / a.G;
   const int64_t p = a.L - a.T + row % a.T;
-  int64_t nvis = (p + 1) / 64;
+  int64_t nvis = (p + 1) / a.bs;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
   const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
@@ -336,10 +336,22 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
   float* srow = a.score ? a.score + (row * a.G + g) * a.n : nullptr;
   int cj;
   float cs;
+  // 64-token selection blocks of `per` summaries each, complete ones are
+  // candidates; importance summed over the summaries
+  int64_t nsel = (p + 1) / 64;
+  if (nsel > a.nbs) nsel = a.nbs;
   float vals[NBL];
 #pragma unroll
-  for (int i = 0; i < NBL; ++i) vals[i] = tid + 64 * i < nvis ? imp[tid + 64 * i] : -1.f;
-  const int cnt = topk_wave<NBL>(vals, nvis, p / 64, a.flags, (int)a.n, cj, cs);
+  for (int i = 0; i < NBL; ++i) {
+    const int64_t J = tid + 64 * i;
+    float v = -1.f;
+    if (J < nsel) {
+      v = imp[a.per * J];
+      for (int64_t k = 1; k < a.per; ++k) v += imp[a.per * J + k];
+    }
+    vals[i] = v;
+  }
+  const int cnt = topk_wave<NBL>(vals, nsel, p / 64, a.flags, (int)a.n, cj, cs);
   topk_write(cnt, cj, cs, (int)a.n, orow, srow);
 }
 
@@ -441,7 +453,8 @@ void decode_layout(const Prob& P, int64_t* n_cmp_waves, int64_t* n_sel_waves, in
 
 bool decode_ok(const Prob& P) {
   const int64_t nbp = (P.nb + 63) / 64 * 64;
-  if (!(P.bf16() && P.hpg == 16 && P.bs == 64 && P.T <= 8 && (P.dq == 64 || P.dq == 128 || P.dq == 192) &&
+  if (!(P.bf16() && P.hpg == 16 && P.sb == 64 && (P.bs == 64 || P.bs == 32 || P.bs == 16) && P.T <= 8 &&
+        (P.dq == 64 || P.dq == 128 || P.dq == 192) &&
         (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE && P.n <= 32 && P.n >= 1))
     return false;
   int64_t nc, ns, nw;

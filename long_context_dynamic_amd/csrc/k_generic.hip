@@ -17,6 +17,7 @@ constexpr int kMaxTopK = 64;
 
 struct GArgs {
   int64_t B, T, L, G, hpg, H, dq, dv, bs, n, w, nb;
+  int64_t sb, nbs;  // selection block, selection-block count
   float scale;
   uint32_t flags;
 };
@@ -51,6 +52,8 @@ __device__ __forceinline__ bool better(float v, int j, float bv, int bj) {
 // ---------------------------------------------------------------------------
 // Compressed branch + importance + top-k for one (b, t, g).
 // LDS: q row [dq] | P [nb] | I [nb] | chosen ids, scores [kMaxTopK] | red.
+// The choice is over selection blocks (sb tokens, sb / bs summaries each,
+// importance summed over them; P holds those sums when sb > bs).
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_select_generic(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -71,7 +74,6 @@ __global__ void __launch_bounds__(kThreads) k_select_generic(
   const int64_t p = a.L - a.T + t;
   int64_t nvis = (p + 1) / a.bs;
   if (nvis > a.nb) nvis = a.nb;
-  const int64_t cur = p / a.bs;
 
   for (int64_t j = tid; j < nvis; j += kThreads) I[j] = 0.f;
 
@@ -112,6 +114,23 @@ __global__ void __launch_bounds__(kThreads) k_select_generic(
   }
   __syncthreads();
 
+  // selection blocks: importance summed over their summaries
+  const int64_t per = a.sb / a.bs;
+  int64_t nsel = (p + 1) / a.sb;
+  if (nsel > a.nbs) nsel = a.nbs;
+  const int64_t cur = p / a.sb;
+  float* Isel = I;
+  if (per > 1) {
+    for (int64_t J = tid; J < nsel; J += kThreads) {
+      float s = 0.f;
+      for (int64_t i = 0; i < per; ++i) s += I[J * per + i];
+      P[J] = s;
+    }
+    Isel = P;
+    __syncthreads();
+  }
+  nvis = nsel;
+
   // forced blocks, removed from the candidates
   if (tid == 0) {
     int cnt = 0;
@@ -119,7 +138,7 @@ __global__ void __launch_bounds__(kThreads) k_select_generic(
     if ((a.flags & NSA_F_FORCE_CURRENT) && !((a.flags & NSA_F_FORCE_FIRST) && cur == 0)) chosen[cnt++] = (int)cur;
     for (int f = 0; f < cnt; ++f) {
       chosen_score[f] = INFINITY;
-      if (chosen[f] < nvis) I[chosen[f]] = -1.f;
+      if (chosen[f] < nvis) Isel[chosen[f]] = -1.f;
     }
     s_cnt = cnt;
   }
@@ -133,7 +152,7 @@ __global__ void __launch_bounds__(kThreads) k_select_generic(
     float bv = -1.f;
     int bj = 0x7fffffff;
     for (int64_t j = tid; j < nvis; j += kThreads) {
-      const float vj = I[j];
+      const float vj = Isel[j];
       if (vj >= 0.f && better(vj, (int)j, bv, bj)) { bv = vj; bj = (int)j; }
     }
 #pragma unroll
@@ -152,7 +171,7 @@ __global__ void __launch_bounds__(kThreads) k_select_generic(
         if (better(red[w], ((int*)red)[kWaves + w], v0, j0)) { v0 = red[w]; j0 = ((int*)red)[kWaves + w]; }
       chosen[nf + round] = j0;
       chosen_score[nf + round] = v0;
-      I[j0] = -1.f;
+      Isel[j0] = -1.f;
     }
     __syncthreads();
   }
@@ -243,7 +262,7 @@ __global__ void __launch_bounds__(kThreads) k_attend_generic(
   for (int i = tid; i < a.n; i += kThreads) sidx[i] = idx[((b * a.T + t) * a.G + g) * a.n + i];
   int64_t wlo = p - a.w + 1;
   if (wlo < 0) wlo = 0;
-  const int64_t bs = a.bs;
+  const int64_t bs = a.sb;  // the chosen blocks are selection blocks
 
   for (int64_t hh = 0; hh < a.hpg; ++hh) {
     const int64_t h = g * a.hpg + hh;
@@ -286,6 +305,7 @@ GArgs make_args(const Prob& P) {
   GArgs a;
   a.B = P.B; a.T = P.T; a.L = P.L; a.G = P.G; a.hpg = P.hpg; a.H = P.H;
   a.dq = P.dq; a.dv = P.dv; a.bs = P.bs; a.n = P.n; a.w = P.w; a.nb = P.nb;
+  a.sb = P.sb; a.nbs = P.nbs;
   a.scale = P.scale; a.flags = P.flags;
   return a;
 }
@@ -313,7 +333,7 @@ hipError_t launch_attend_generic(const Prob& P, const void* q, const void* k, co
                                  const void* gates, const int32_t* idx, const float* ocmp,
                                  void* out, float* lse, bool out_f32, hipStream_t s) {
   const GArgs a = make_args(P);
-  int64_t cap = P.n * P.bs;
+  int64_t cap = P.n * P.sb;
   if (P.w > cap) cap = P.w;
   if (cap < 1) cap = 1;
   const size_t lds = sizeof(float) * (size_t)(P.dq + cap + kMaxTopK + 2 * kWaves);

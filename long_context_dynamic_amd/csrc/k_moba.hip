@@ -641,11 +641,13 @@ hipError_t run_attend_t(const MobaArgs& a, bool out_f32, hipStream_t s, Phases* 
 }  // namespace
 
 bool moba_select_ok(const Prob& P) {
-  return P.bf16() && P.hpg == 1 && (P.dq == 64 || P.dq == 128) && P.nb >= 1 && P.n >= 1 && P.n <= 8;
+  return P.bf16() && P.hpg == 1 && P.sb == P.bs && (P.dq == 64 || P.dq == 128) && P.nb >= 1 && P.n >= 1 &&
+         P.n <= 8;
 }
 
 bool moba_attend_ok(const Prob& P) {
-  return P.bf16() && P.hpg == 1 && P.dq == P.dv && (P.dq == 64 || P.dq == 128) && P.bs % 64 == 0 && P.n >= 1 &&
+  return P.bf16() && P.hpg == 1 && P.sb == P.bs && P.dq == P.dv && (P.dq == 64 || P.dq == 128) &&
+         P.bs % 64 == 0 && P.n >= 1 &&
          P.n <= 8 && P.B * P.T * P.H * P.n < ((int64_t)1 << 31) && P.B * P.H * P.nb < ((int64_t)1 << 30);
 }
 

@@ -93,21 +93,27 @@ __global__ void __launch_bounds__(256) k_group_major(const uint16_t* __restrict_
   }
 }
 
-// Top-k of one token's block importances imp[0 .. nvis) (one wave), written
-// sorted to orow / srow.
+// Top-k of one token's selection blocks (one wave): block J < nsel has the
+// importance imp[per * J] + .. + imp[per * J + per - 1] (its summaries);
+// written sorted to orow / srow.
 template <int NBL>
-__device__ __forceinline__ void topk_row(const float* imp, int64_t nvis, int64_t cur, uint32_t flags, int n,
-                                         int32_t* orow, float* srow) {
+__device__ __forceinline__ void topk_row(const float* imp, int64_t per, int64_t nsel, int64_t cur, uint32_t flags,
+                                         int n, int32_t* orow, float* srow) {
   const int lane = threadIdx.x & 63;
   float vals[NBL];
 #pragma unroll
   for (int i = 0; i < NBL; ++i) {
     const int64_t j = lane + 64 * i;
-    vals[i] = j < nvis ? imp[j] : -1.f;
+    float v = -1.f;
+    if (j < nsel) {
+      v = imp[per * j];
+      for (int64_t k = 1; k < per; ++k) v += imp[per * j + k];
+    }
+    vals[i] = v;
   }
   int cj;
   float cs;
-  const int cnt = topk_wave<NBL>(vals, nvis, cur, flags, n, cj, cs);
+  const int cnt = topk_wave<NBL>(vals, nsel, cur, flags, n, cj, cs);
   topk_write(cnt, cj, cs, n, orow, srow);
 }
 
@@ -130,9 +136,9 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   const int64_t t_last = (tile * TQ + TQ - 1 < a.T - 1) ? tile * TQ + TQ - 1 : a.T - 1;
   const int64_t p = a.L - a.T + (active ? t : t_last);
   const int64_t p_first = a.L - a.T + tile * TQ, p_last = a.L - a.T + t_last;
-  int64_t nvis = active ? (p + 1) / 64 : 0;
+  int64_t nvis = active ? (p + 1) / a.bs : 0;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
-  int64_t nvis_max = (p_last + 1) / 64;
+  int64_t nvis_max = (p_last + 1) / a.bs;
   if (nvis_max > a.nb) nvis_max = a.nb;
   const float c = a.scale * kLog2e;
   const float stale = kStaleLog2 / c;
@@ -213,8 +219,11 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   if (active) {
     int32_t* orow = a.idx + ((b * a.T + t) * a.G + g) * a.n;
     float* srow = a.score ? a.score + ((b * a.T + t) * a.G + g) * a.n : nullptr;
-    if (a.nbp <= 1024) topk_row<16>(my_imp, nvis, p / 64, a.flags, (int)a.n, orow, srow);
-    else topk_row<MAX_NB_LANE>(my_imp, nvis, p / 64, a.flags, (int)a.n, orow, srow);
+    // 64-token selection blocks, complete ones are candidates
+    int64_t nsel = (p + 1) / 64;
+    if (nsel > a.nbs) nsel = a.nbs;
+    if (a.nbs <= 1024) topk_row<16>(my_imp, a.per, nsel, p / 64, a.flags, (int)a.n, orow, srow);
+    else topk_row<MAX_NB_LANE>(my_imp, a.per, nsel, p / 64, a.flags, (int)a.n, orow, srow);
   }
 
   if (!FWD) return;
@@ -481,8 +490,9 @@ hipError_t launch_sel_t(const PfArgs& a, bool fwd, bool out_f32, hipStream_t s) 
 
 bool prefill_fast_ok(const Prob& P) {
   const int64_t nbp = (P.nb + 63) / 64 * 64;
-  return P.bf16() && P.hpg == 16 && P.bs == 64 && (P.dq == 64 || P.dq == 128 || P.dq == 192) &&
-         (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE && P.n <= 32;
+  return P.bf16() && P.hpg == 16 && P.sb == 64 && (P.bs == 64 || P.bs == 32 || P.bs == 16) &&
+         (P.dq == 64 || P.dq == 128 || P.dq == 192) && (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE &&
+         P.n <= 32;
 }
 
 hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, int64_t G, int D, hipStream_t s) {

@@ -27,12 +27,15 @@ nsa_status describe(const nsa_params* p, Prob* P) {
   const int n_forced = ((p->flags & NSA_F_FORCE_FIRST) ? 1 : 0) + ((p->flags & NSA_F_FORCE_CURRENT) ? 1 : 0);
   if (p->top_k < n_forced) return NSA_ERR_INVALID_ARG;
   const int64_t nb = (int64_t)p->kv_len / p->block;
-  if (p->heads_per_group > 16 || p->d_qk > 256 || p->d_v > 256 || p->block > 4096 || p->top_k > 64 ||
-      (int64_t)p->top_k * p->block > 16384 || p->window > 16384 || nb > 16384)
+  const int64_t sb = p->sel_block > 0 ? p->sel_block : p->block;
+  if (p->sel_block < 0 || sb % p->block != 0) return NSA_ERR_INVALID_ARG;
+  if (p->heads_per_group > 16 || p->d_qk > 256 || p->d_v > 256 || p->block > 4096 || sb > 4096 ||
+      p->top_k > 64 || (int64_t)p->top_k * sb > 16384 || p->window > 16384 || nb > 16384)
     return NSA_ERR_UNSUPPORTED;
   P->B = p->batch; P->T = p->q_len; P->L = p->kv_len;
   P->G = p->n_kv_groups; P->hpg = p->heads_per_group; P->H = P->G * P->hpg;
   P->dq = p->d_qk; P->dv = p->d_v; P->bs = p->block; P->n = p->top_k; P->w = p->window; P->nb = nb;
+  P->sb = sb; P->nbs = (int64_t)p->kv_len / sb;
   P->flags = p->flags; P->dtype = p->dtype;
   P->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d_qk));
   // element counts must fit the grid: one workgroup per (b, t, g) and per (b, j, g)

@@ -20,6 +20,7 @@ struct DecArgs {
   void* out;              // [R, H, DV]
   float* lse;             // [R, H] selected-branch log-sum-exp, or NULL
   int64_t B, T, R, L, G, H, nb, nbp, n, w, n_cmp_waves, n_sel_waves, n_win_waves;
+  int64_t bs, per, nbs;  // summary block, summaries per 64-token selection block, selection blocks
   uint32_t flags;
   float scale;
 };

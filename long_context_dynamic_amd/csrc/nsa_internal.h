@@ -13,6 +13,7 @@ namespace nsa {
 // Problem sizes widened to 64 bits, plus derived quantities.
 struct Prob {
   int64_t B, T, L, G, hpg, H, dq, dv, bs, n, w, nb;
+  int64_t sb, nbs;  // selection block and selection-block count (sb = bs unless decoupled)
   uint32_t flags;
   int dtype;
   float scale;

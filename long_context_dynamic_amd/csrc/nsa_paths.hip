@@ -21,6 +21,7 @@ DecArgs dec_args(const Prob& P) {
   DecArgs a = {};
   a.B = P.B; a.T = P.T; a.R = P.B * P.T; a.L = P.L; a.G = P.G; a.H = P.H; a.nb = P.nb;
   a.nbp = pad64(P.nb); a.n = P.n; a.w = P.w; a.flags = P.flags; a.scale = P.scale;
+  a.bs = P.bs; a.per = P.sb / P.bs; a.nbs = P.nbs;
   return a;
 }
 
@@ -28,6 +29,7 @@ PfArgs pf_args(const Prob& P) {
   PfArgs a = {};
   a.B = P.B; a.T = P.T; a.L = P.L; a.G = P.G; a.H = P.H; a.nb = P.nb;
   a.nbp = pad64(P.nb); a.Lp = pad64(P.L); a.n = P.n; a.w = P.w;
+  a.bs = P.bs; a.per = P.sb / P.bs; a.nbs = P.nbs;
   a.flags = P.flags; a.scale = P.scale;
   return a;
 }

@@ -20,12 +20,14 @@ struct PfArgs {
   void* out;              // [B, T, H, DV]
   float* lse;             // [B, T, H] or NULL
   int64_t B, T, L, G, H, nb, nbp, Lp, n, w;
+  int64_t bs, per, nbs;  // summary block, summaries per 64-token selection block, selection blocks
   uint32_t flags;
   float scale;
 };
 
 // True when the matrix-core kernels take this shape: bf16, 16 heads per
-// group, 64-token blocks, d_qk in {64,128,192}, d_v in {64,128}, nb <= 2048, top_k <= 32.
+// group, 64-token selection blocks over 16-, 32- or 64-token summaries,
+// d_qk in {64,128,192}, d_v in {64,128}, nb <= 2048 summaries, top_k <= 32.
 bool prefill_fast_ok(const Prob& P);
 
 hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, int64_t G, int D, hipStream_t s);

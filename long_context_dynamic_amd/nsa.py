@@ -40,6 +40,7 @@ class Params(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_phase_events", ctypes.c_int32),
+        ("sel_block", ctypes.c_int32),
     ]
 
 
@@ -97,6 +98,7 @@ def params(prob: dict, *, out_f32: bool = False, k_cmp=None, v_cmp=None, workspa
     p.n_kv_groups, p.heads_per_group = prob["n_groups"], prob["heads_per_group"]
     p.d_qk, p.d_v = prob["d_qk"], prob["d_v"]
     p.block, p.top_k, p.window = prob["block"], prob["top_k"], prob["window"]
+    p.sel_block = int(prob.get("sel_block", 0) or 0)
     p.flags = flags_of(prob, out_f32) if flags is None else flags
     p.dtype = NSA_BF16 if prob["dtype"] == "bf16" else NSA_F32
     p.scale = float(prob.get("scale") or 0.0)

@@ -49,12 +49,17 @@ def sample_rows(prob: dict, count: int, seed: int = 0) -> np.ndarray:
     return np.sort(bs_ * T + ts)
 
 
+def sel_block(prob) -> int:
+    """Tokens per selection block (the compression block unless decoupled)."""
+    return prob.get("sel_block", 0) or prob["block"]
+
+
 def forced_set(prob, p):
     F = set()
     if prob["force_first"]:
         F.add(0)
     if prob["force_current"]:
-        F.add(p // prob["block"])
+        F.add(p // sel_block(prob))
     return F
 
 
@@ -62,7 +67,7 @@ def check_selection(prob: dict, rows, got_idx: np.ndarray, ora_idx: np.ndarray, 
     """Compare a GPU selection [R,G,n] with the oracle's.  Outside the near-tie
     band the choice must be identical; inside it any choice with the right
     count passes.  Returns how many (row, group) pairs needed the band."""
-    T, L, bs, n = prob["q_len"], prob["kv_len"], prob["block"], prob["top_k"]
+    T, L, bs, n = prob["q_len"], prob["kv_len"], sel_block(prob), prob["top_k"]
     nb = L // bs
     band = 0
     for ri, r in enumerate(rows):

@@ -65,6 +65,7 @@ BASE = workloads.get("nsa_prefill_8k", q_len=256, kv_len=256)
     ("d_v", 257, 2), ("block", 0, 1), ("block", 8192, 2), ("top_k", -1, 1), ("top_k", 1, 1),
     ("top_k", 65, 2), ("window", -1, 1), ("window", 20000, 2), ("dtype", 7, 1), ("flags", 1 << 9, 1),
     ("scale", -1.0, 1), ("scale", float("inf"), 1), ("scale", float("nan"), 1),
+    ("sel_block", -64, 1), ("sel_block", 96, 1), ("sel_block", 8192, 2),
 ])
 def test_bad_params_are_rejected_before_launch(field, value, code):
     p = _p(BASE)

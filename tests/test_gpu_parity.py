@@ -24,6 +24,9 @@ CASES = [
     ("nsa_prefill_8k", dict(q_len=1000, kv_len=1000), None),
     ("nsa_prefill_8k", dict(q_len=333, kv_len=1100, gate_logits=1), None),
     ("nsa_prefill_8k", {}, 48),
+    ("nsa_prefill_8k", dict(q_len=1000, kv_len=1300, block=32, sel_block=64), None),
+    ("nsa_prefill_8k", dict(q_len=600, kv_len=600, block=16, sel_block=64, top_k=8, force_first=0), None),
+    ("nsa_tiny_fp32", dict(q_len=500, kv_len=700, block=16, sel_block=48, top_k=5), None),
     ("nsa_prefill_64k", {}, 20),
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
     ("moba_32k", dict(q_len=700, kv_len=3000), None),
@@ -34,6 +37,7 @@ CASES = [
     ("moba_128k", {}, 16),
     ("moba_1m", {}, 8),
     ("nsa_decode_64x64k", dict(batch=6, kv_len=4096 + 17), None),
+    ("nsa_decode_64x64k", dict(batch=4, kv_len=4096 + 40, block=32, sel_block=64), None),
 ]
 
 
