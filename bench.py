@@ -147,17 +147,40 @@ def prefill_roofline(prob, per_phase, workload):
     return roofline(kernel_flops, per_phase, workload), fl
 
 
-def run_moba(args, torch, nsa, workloads, inputs):
-    prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs, workload="moba_32k")
+def run_moba(args, torch, nsa, workloads, inputs, workload="moba_32k"):
+    prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs, workload=workload)
     kf = moba_kernel_flops(prob)
     tokens = prob["batch"] * prob["q_len"]
-    return {"workload": "moba_32k", "batch": prob["batch"], "seq_len": prob["q_len"],
+    return {"workload": workload, "batch": prob["batch"], "seq_len": prob["q_len"],
             "heads": prob["n_groups"], "d": prob["d_qk"], "block": prob["block"], "top_k": prob["top_k"],
             "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
             "phases_ms": {k: round(v, 4) for k, v in per_phase.items()},
             "algorithmic_tflop": {k: round(v / 1e12, 4) for k, v in kf.items()},
             "forward_mfma_frac": round(sum(kf.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "roofline": roofline(kf, per_phase, "moba_32k")}
+            "roofline": roofline(kf, per_phase, workload)}
+
+
+def run_side_leg(args, torch, nsa, workloads, inputs, workload, fn):
+    """A further configuration measured the same way with fewer steps."""
+    import copy
+    a = copy.copy(args)
+    a.steps, a.warmup = min(args.steps, 3), 1
+    rec = fn(a, torch, nsa, workloads, inputs, workload)
+    rec["steps"], rec["warmup"] = a.steps, a.warmup
+    torch.cuda.empty_cache()
+    return rec
+
+
+def run_nsa_leg(args, torch, nsa, workloads, inputs, workload):
+    prob, x, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs, workload=workload)
+    roof, fl = prefill_roofline(prob, per_phase, workload)
+    tokens = prob["batch"] * prob["q_len"]
+    return {"workload": workload, "block": prob["block"], "sel_block": prob.get("sel_block", 0) or prob["block"],
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "phases_ms": {k: round(v, 4) for k, v in per_phase.items()},
+            "algorithmic_tflop": {k: round(v / 1e12, 4) for k, v in fl.items()},
+            "forward_mfma_frac": round(sum(fl.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roof}
 
 
 # ----------------------------------------------------------------- decode --
@@ -328,6 +351,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip MoBA 128k/1M and the decoupled-block 64k legs")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings"], default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
@@ -363,21 +387,26 @@ def main():
         "roofline": roof,
     }
     log(f"prefill: {ms:.3f} ms/step, phases {rec['phases_ms']}")
+    del x  # host inputs of the 64k workload; made again for the CPU baseline
+    torch.cuda.empty_cache()
     if not args.no_moba:
         rec["moba"] = run_moba(args, torch, nsa, workloads, inputs)
         log(f"moba: {rec['moba']['ms_per_step']} ms/step, phases {rec['moba']['phases_ms']}")
         torch.cuda.empty_cache()
+    if not args.no_extra:
+        # MoBA at longer contexts, and the 64k prefill with decoupled block sizes
+        for wl, fn in (("moba_128k", run_moba), ("moba_1m", run_moba), ("nsa_prefill_64k_c32", run_nsa_leg)):
+            rec.setdefault("more_configs", {})[wl] = run_side_leg(args, torch, nsa, workloads, inputs, wl, fn)
+            log(f"{wl}: {rec['more_configs'][wl]['ms_per_step']} ms/step")
     if not args.no_decode:
-        del x
-        torch.cuda.empty_cache()
         rec["decode"] = run_decode(args, torch, nsa, workloads, inputs)
         log(f"decode: {rec['decode']['ms_per_step']} ms/step")
-        x = inputs.generate(prob)
+        torch.cuda.empty_cache()
     rec["measured_ceilings"] = run_ceilings(torch)
     log(f"ceilings: {rec['measured_ceilings']}")
     if not args.no_cpu:
         log("cpu baseline: timing the oracle on a sample")
-        rec["cpu_baseline"] = run_cpu_baseline(prob, x)
+        rec["cpu_baseline"] = run_cpu_baseline(prob, inputs.generate(prob))
     print(json.dumps(rec), flush=True)
 
 

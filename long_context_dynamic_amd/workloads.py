@@ -30,6 +30,11 @@ WORKLOADS = {
     # the same at 64k tokens
     "nsa_prefill_64k": dict(_BASE, q_len=65536, kv_len=65536, n_groups=4, heads_per_group=16,
                             d_qk=192, d_v=128, block=64, top_k=16, window=512, dtype="bf16"),
+    # the 64k prefill with 32-token summaries under 64-token selection blocks
+    # (compression and selection block sizes decoupled)
+    "nsa_prefill_64k_c32": dict(_BASE, q_len=65536, kv_len=65536, n_groups=4, heads_per_group=16,
+                                d_qk=192, d_v=128, block=32, sel_block=64, top_k=16, window=512,
+                                dtype="bf16"),
     # MoBA: 32 heads each with its own K/V, d 128, block 512, top-3 with the current
     # block always in, selected branch only, no gates
     "moba_32k": dict(_BASE, q_len=32768, kv_len=32768, n_groups=32, heads_per_group=1,
