@@ -129,11 +129,14 @@ nsa_status nsa_compress(const void* k, const void* v, void* k_cmp, void* v_cmp,
  * [P1] s7 and [P5] s13 for MoBA).  For query token t at position p and
  * group g: each head's softmax over the summaries of the complete blocks
  * j with (j + 1) * block <= p + 1, added up over the group's heads, is the
- * importance of block j.  Forced blocks (flags) come first; the remaining
- * top_k slots take the visible blocks with the highest importance (ties to
- * the lower block id).  idx[b, t, g, :] lists the chosen blocks ascending,
- * padded with -1.  score_or_null (fp32, same shape) receives each listed
- * block's importance, +inf for forced blocks and -inf for padding.
+ * importance of summary j; a selection block (sel_block tokens, = block by
+ * default) has the summed importance of the summaries it covers and is a
+ * candidate once complete.  Forced blocks (flags: selection block 0, the
+ * query's own selection block) come first; the remaining top_k slots take
+ * the candidates with the highest importance (ties to the lower block id).
+ * idx[b, t, g, :] lists the chosen selection blocks ascending, padded with
+ * -1.  score_or_null (fp32, same shape) receives each listed block's
+ * importance, +inf for forced blocks and -inf for padding.
  * Reads q and k_cmp (params->k_cmp is ignored here); may use the workspace.
  */
 nsa_status nsa_select_topk(const void* q, const void* k_cmp, int32_t* idx,
@@ -141,8 +144,9 @@ nsa_status nsa_select_topk(const void* q, const void* k_cmp, int32_t* idx,
 
 /*
  * Selected branch alone ([P1] s4, s5): for each token and head, one softmax
- * over every position s <= p of the blocks listed in idx (entries < 0 are
- * skipped; entries must be distinct and begin at or before p), written to
+ * over every position s <= p of the selection blocks listed in idx
+ * (sel_block tokens each; entries < 0 are skipped; entries must be distinct
+ * and begin at or before p), written to
  * out (no gate).  lse_or_null (fp32 [B, q_len, H]) receives the natural-log
  * sum of the exponentiated scaled logits (-inf for an empty set, whose
  * output is 0).  May use the workspace.
