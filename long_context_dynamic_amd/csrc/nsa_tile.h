@@ -177,4 +177,42 @@ __device__ __forceinline__ void qk_tile_T(const uint16_t* kt, const bf16x8 (&qf)
   }
 }
 
+// S^T for two 16-query sets at once: each K fragment read from LDS feeds
+// both (half the LDS reads per matrix op of one set per wave).
+template <int DQ>
+__device__ __forceinline__ void qk_tile_T2(const uint16_t* kt, const bf16x8 (&qf)[2][DQ / 32], f32x4 (&s)[2][4],
+                                           int lr, int lg) {
+  constexpr int KS = k_lds_stride<DQ>();
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    s[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[1][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DQ / 32; ++ks) {
+      const bf16x8 kf = ld8(kt + (16 * mt + lr) * KS + 8 * lg + 32 * ks);
+      s[0][mt] = mfma16(kf, qf[0][ks], s[0][mt]);
+      s[1][mt] = mfma16(kf, qf[1][ks], s[1][mt]);
+    }
+  }
+}
+
+// O^T += V^T P^T for two query sets sharing each V^T fragment.
+template <int DV>
+__device__ __forceinline__ void pv_tile2(const uint16_t* vt, const f32x4 (&pm)[2][4], f32x4 (&o)[2][DV / 16], int lr,
+                                         int lg) {
+  constexpr int VS = kVtStride;
+  const bf16x8 p00 = pack8(pm[0][0], pm[0][1]), p01 = pack8(pm[0][2], pm[0][3]);
+  const bf16x8 p10 = pack8(pm[1][0], pm[1][1]), p11 = pack8(pm[1][2], pm[1][3]);
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) {
+    const uint16_t* row = vt + (16 * dt + lr) * VS;
+    const bf16x8 v0 = ld4x2(row + 4 * lg, row + 16 + 4 * lg);
+    const bf16x8 v1 = ld4x2(row + 32 + 4 * lg, row + 48 + 4 * lg);
+    o[0][dt] = mfma16(v0, p00, o[0][dt]);
+    o[1][dt] = mfma16(v0, p10, o[1][dt]);
+    o[0][dt] = mfma16(v1, p01, o[0][dt]);
+    o[1][dt] = mfma16(v1, p11, o[1][dt]);
+  }
+}
+
 }  // namespace nsa
