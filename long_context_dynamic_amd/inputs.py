@@ -13,6 +13,9 @@ parallel and a shorter problem is a prefix of a longer one.  Values:
                             added to every key of its block
     v       ~ N(0, 1)       [L, G, d_v]
     gates   ~ U(0, 1)       [T, H, 3]
+    dout    ~ N(0, 1)       [T, H, d_v]  (the upstream gradient of a backward
+                            pass; its stream is the fifth child, so the first
+                            four tensors do not depend on whether it is drawn)
 
 all float32, then stored as float32 or rounded to bf16 (nearest, ties to
 even).  The per-block key offset gives blocks distinct summaries, so the
@@ -78,7 +81,7 @@ def generate_sequence(prob: dict, b: int, want=("q", "k", "v", "gates"), pool=No
     dt = prob["dtype"]
     st = np.uint16 if dt == "bf16" else np.float32
     seq = np.random.SeedSequence(int(prob.get("seed", 0))).spawn(int(prob["batch"]))[b]
-    s_q, s_k, s_v, s_g = seq.spawn(4)
+    s_q, s_k, s_v, s_g, s_d = seq.spawn(5)
     own = pool is None
     pool = pool or cf.ThreadPoolExecutor(_workers())
     try:
@@ -98,6 +101,9 @@ def generate_sequence(prob: dict, b: int, want=("q", "k", "v", "gates"), pool=No
         if "gates" in want:
             out["gates"] = np.empty((1, T, H, 3), st)
             _fill(out["gates"][0], s_g, T, (H, 3), dt, "uniform", pool)
+        if "dout" in want:
+            out["dout"] = np.empty((1, T, H, dv), st)
+            _fill(out["dout"][0], s_d, T, (H, dv), dt, "normal", pool)
         return out
     finally:
         if own:
