@@ -164,6 +164,39 @@ nsa_status nsa_sparse_attn(const void* q, const void* k, const void* v, const in
 nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates,
                        const nsa_params* params, void* out);
 
+/*
+ * Backward of nsa_forward ([P1] s4 the gated three-branch sum; [P1] s6: NSA
+ * trains end to end, the top-k choice passes no gradient, and the compressed
+ * branch's output carries a training signal to every block).  Given the
+ * upstream gradient dout [B, q_len, H, d_v] (dtype) and the selection idx
+ * the forward used (nsa_select_topk's output for the same inputs; any
+ * selection of distinct blocks that begin at or before each query is
+ * accepted), writes the fp32 gradients
+ *   dq      [B, q_len, H, d_qk]
+ *   dk      [B, kv_len, G, d_qk]   dv [B, kv_len, G, d_v]
+ *           (the compressed branch's summary gradient reaches every token of
+ *           its block divided by `block`: the mean's derivative; the rounding
+ *           of the stored summaries is passed through unchanged)
+ *   dgates  [B, q_len, H, 3] or NULL: the gradient with respect to the
+ *           gates as given (logits when NSA_F_GATE_LOGITS is set); 0 for a
+ *           branch that is off.  Must be NULL when gates is NULL.
+ * Per branch b with key set S, P = softmax(scale q.k), O_b = sum P v and
+ * gate g_b: dg_b = <dout, O_b>, dS = g_b P (<dout, v> - dg_b),
+ * dq += scale sum dS k, dk += scale dS q, dv += g_b P dout.
+ * The summaries are recomputed (params->k_cmp / v_cmp are ignored).
+ * Results are deterministic (no floating-point atomics).
+ * Limits (NSA_ERR_UNSUPPORTED otherwise): dtype NSA_BF16, heads_per_group
+ * 16, block 64 with sel_block 0 or 64, d_qk in {64, 128, 192}, d_v in
+ * {64, 128}, top_k <= 32.  Needs nsa_backward_workspace_bytes of workspace.
+ */
+nsa_status nsa_backward(const void* q, const void* k, const void* v, const void* gates,
+                        const int32_t* idx, const void* dout, float* dq, float* dk, float* dv,
+                        float* dgates, const nsa_params* params);
+
+/* Workspace bytes nsa_backward needs for these params (0 if they are invalid
+ * or outside its limits). */
+size_t nsa_backward_workspace_bytes(const nsa_params* params);
+
 /* Number of kernels nsa_forward launches for these params (0 if they are
  * invalid); names[i] (i < max_names) receives a static name of kernel i. */
 int32_t nsa_forward_phases(const nsa_params* params, const char** names, int32_t max_names);

@@ -1,0 +1,821 @@
+// k_backward.hip -- matrix-core backward pass of the NSA forward for GQA
+// groups of 16 query heads and 64-token blocks ([P1] s4: the gated sum of
+// the compressed, selected and window branches; [P1] s6: NSA trains end to
+// end, the top-k choice passes no gradient, and the compressed branch's
+// output is what carries a training signal to every block).
+//
+// For a branch with key set S, P = softmax(scale * q.k_s), O = sum_s P v_s,
+// gate gamma and upstream gradient dout, the gradients are
+//   dgamma = <dout, O>,  dS_s = gamma P_s (<dout, v_s> - dgamma),
+//   dq += scale sum_s dS_s k_s,  dk_s += scale dS_s q,  dv_s += gamma P_s dout,
+// and the compressed branch's key/value gradients reach each token of block
+// j as dk_cmp_j / 64.  The work splits by which side owns the sums:
+//
+//   images     paired-row and tiled-transposed copies of k, v and of the
+//              summaries, so that every matrix-op operand below is one
+//              contiguous 16-byte read.
+//   k_bwd_q    one wave per (token, group), 16 heads as the matrix N:
+//              per branch, a statistics pass (log-sum-exp, output, dgamma)
+//              and a gradient pass that recomputes P and accumulates dq.
+//   lists      for every (group, block), the tokens that chose it, in token
+//              order (deterministic: per 256-token chunk histograms, column
+//              prefix sums, one ordered fill per chunk).
+//   k_bwd_kv   one workgroup per 64 keys and a run of queries, 4 waves of 16
+//              keys each: queries are taken two tokens (32 head rows) at a
+//              time through LDS, and dk^T, dv^T accumulate in registers with
+//              the head rows as the contraction.  Window: the keys' own
+//              window of queries, written to dk, dv.  Selected: a chunk of
+//              a block's token list.  Compressed: a run of tokens against 64
+//              summaries.  The last two write partial sums.
+//   k_bwd_reduce  one workgroup per 64-token block: window part + the
+//              selected partials of the block + the block's summary gradient
+//              / 64, in a fixed order.
+#include <math.h>
+
+#include "nsa_backward.h"
+#include "nsa_frag.h"
+#include "nsa_mfma.h"
+#include "nsa_prefill.h"
+
+namespace nsa {
+namespace {
+
+constexpr int kBlk = 64;         // block and selection-block size of this path
+constexpr int kCountTok = 256;   // tokens per list-count chunk
+constexpr int kListChunk = 256;  // listed tokens per selected-branch workgroup
+constexpr int kCmpChunk = 512;   // tokens per compressed-branch workgroup
+
+enum { BR_CMP = 0, BR_SLC = 1, BR_WIN = 2 };
+
+// Compressed branch: token chunk c of summary tile J covers tokens
+// [max(c * kCmpChunk, t0), min((c + 1) * kCmpChunk, T)), t0 the first token
+// that sees summary 64 * J; an empty range writes no partial.
+__host__ __device__ __forceinline__ void cmp_chunk_range(const BwArgs& a, int64_t J, int64_t c, int64_t& lo,
+                                                         int64_t& hi) {
+  int64_t t0 = (J * 64 + 1) * kBlk - 1 - (a.L - a.T);
+  if (t0 < 0) t0 = 0;
+  lo = c * kCmpChunk;
+  hi = lo + kCmpChunk;
+  if (lo < t0) lo = t0;
+  if (hi > a.T) hi = a.T;
+}
+
+__device__ __forceinline__ uint32_t branch_flag(int br) {
+  return br == BR_CMP ? NSA_F_CMP : (br == BR_SLC ? NSA_F_SLC : NSA_F_WIN);
+}
+
+__device__ __forceinline__ float gate_val(const BwArgs& a, int64_t row, int br, float* dsig) {
+  if (!a.gates) {
+    *dsig = 0.f;
+    return 1.f;
+  }
+  const float x = bf16_to_f32(a.gates[row * 3 + br]);
+  if (a.flags & NSA_F_GATE_LOGITS) {
+    const float s = sigmoid(x);
+    *dsig = s * (1.f - s);
+    return s;
+  }
+  *dsig = 1.f;
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Query side.  Chunk c of a branch covers keys kb .. kb + 31 (kb a multiple
+// of 32); keys outside [klo, khi] are masked.  S^T tiles s0, s1 hold keys
+// kb + 8*lg + r and kb + 8*lg + 4 + r (the interleaved order of load_k).
+__device__ __forceinline__ void mask_chunk(f32x4& s0, f32x4& s1, int64_t kb, int64_t klo, int64_t khi, int lg) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t k0 = kb + 8 * lg + r, k1 = k0 + 4;
+    if (k0 < klo || k0 > khi) s0[r] = -INFINITY;
+    if (k1 < klo || k1 > khi) s1[r] = -INFINITY;
+  }
+}
+
+template <int DQ>
+__device__ __forceinline__ void qk_chunk_b(const KFrag<DQ>& f, const bf16x8 (&qf)[DQ / 32], f32x4& s0, f32x4& s1) {
+  s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) {
+    s0 = mfma16(f.k0[ks], qf[ks], s0);
+    s1 = mfma16(f.k1[ks], qf[ks], s1);
+  }
+}
+
+// The chunks of branch br for token position p (wave-uniform loop driver).
+// Selected chunks come from the lanes' list (lane c: slot c / 2, half c % 2).
+struct ChunkIter {
+  int br;
+  int64_t next, end;      // compressed / window: next chunk start, exclusive end
+  uint64_t pending;       // selected: lanes still holding a chunk
+  int64_t kbv;            // selected: this lane's chunk start or -1
+  int64_t klo, khi;
+
+  __device__ __forceinline__ int64_t pop() {
+    if (br == BR_SLC) {
+      if (!pending) return -1;
+      const int pos = __ffsll((unsigned long long)pending) - 1;
+      pending &= pending - 1;
+      return __shfl(kbv, pos, 64);
+    }
+    if (next >= end) return -1;
+    const int64_t kb = next;
+    next += 32;
+    return kb;
+  }
+};
+
+__device__ __forceinline__ ChunkIter chunks_of(const BwArgs& a, int br, int64_t b, int64_t t, int64_t g, int64_t p,
+                                               int lane) {
+  ChunkIter it;
+  it.br = br;
+  it.pending = 0;
+  it.kbv = -1;
+  it.next = 0;
+  it.end = 0;
+  if (br == BR_CMP) {
+    int64_t nvis = (p + 1) / kBlk;
+    if (nvis > a.nb) nvis = a.nb;
+    it.end = nvis;
+    it.klo = 0;
+    it.khi = nvis - 1;
+  } else if (br == BR_WIN) {
+    int64_t lo = p - a.w + 1;
+    if (lo < 0) lo = 0;
+    it.next = a.w > 0 ? lo / 32 * 32 : 0;
+    it.end = a.w > 0 ? p + 1 : 0;
+    it.klo = lo;
+    it.khi = p;
+  } else {
+    const int slot = lane >> 1;
+    const int j = slot < a.n ? a.idx[((b * a.T + t) * a.G + g) * a.n + slot] : -1;
+    const int64_t kb = (int64_t)j * kBlk + 32 * (lane & 1);
+    if (j >= 0 && (int64_t)j * kBlk < a.L && kb <= p) it.kbv = kb;
+    it.pending = __ballot(it.kbv >= 0);
+    it.klo = 0;
+    it.khi = p;
+  }
+  return it;
+}
+
+template <int DQ, int DV>
+__global__ void __launch_bounds__(256) k_bwd_q(BwArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int64_t g = blockIdx.x % a.G;
+  const int64_t tg = (blockIdx.x / a.G) * 4 + wave;  // flat (b, t)
+  if (tg >= a.B * a.T) return;
+  const int64_t b = tg / a.T, t = tg % a.T;
+  const int64_t p = a.L - a.T + t;
+  const float c2 = a.scale * kLog2e;
+  const int64_t row = tg * a.H + g * 16 + lr;  // (b, t, head lr)
+  const int64_t nrow = a.B * a.T * a.H;
+
+  bf16x8 qf[DQ / 32];
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = ld8(a.q + row * DQ + 8 * lg + 32 * ks);
+
+  const uint32_t kofs = 16 * lg, tofs = (lr * 32 + 8 * lg) * 2;
+  const int64_t bg = b * a.G + g;
+  auto rs = [&](const uint16_t* base, int64_t rows, int D) {
+    return make_rsrc(base + bg * rows * D, (uint32_t)(rows * D * 2));
+  };
+
+  // ---- statistics of every branch: log-sum-exp, <dout, O_b>, gate ----
+  float lse[3], dd[3], gam[3];
+#pragma unroll
+  for (int br = 0; br < 3; ++br) {
+    lse[br] = INFINITY;
+    dd[br] = 0.f;
+    gam[br] = 0.f;
+    float dsig = 0.f;
+    if (!(a.flags & branch_flag(br))) {
+      if (lg == 0) {
+        a.stat[(br * 3 + 0) * nrow + row] = INFINITY;
+        a.stat[(br * 3 + 1) * nrow + row] = 0.f;
+        a.stat[(br * 3 + 2) * nrow + row] = 0.f;
+        if (a.dgates) a.dgates[row * 3 + br] = 0.f;
+      }
+      continue;
+    }
+    gam[br] = gate_val(a, row, br, &dsig);
+    const bool cmp = br == BR_CMP;
+    const __amdgpu_buffer_rsrc_t kr = cmp ? rs(a.kcG, a.nbp, DQ) : rs(a.kG, a.Lp, DQ);
+    const __amdgpu_buffer_rsrc_t vr = cmp ? rs(a.vcT, a.nbp, DV) : rs(a.vT, a.Lp, DV);
+    ChunkIter it = chunks_of(a, br, b, t, g, p, lane);
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[DV / 16];
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t kb = it.pop(); kb >= 0; kb = it.pop()) {
+      KFrag<DQ> kf;
+      VFrag<DV> vf;
+      load_k<DQ>(kf, kr, kofs, kb, lr);
+      load_v<DV>(vf, vr, tofs, kb);
+      f32x4 s0, s1;
+      qk_chunk_b<DQ>(kf, qf, s0, s1);
+      mask_chunk(s0, s1, kb, it.klo, it.khi, lg);
+      float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      tmax = xor_max16_32(tmax);
+      if (tmax > m) {  // every chunk holds a visible key, so tmax is finite
+        const float alpha = fast_exp2((m - tmax) * c2);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DV / 16; ++dt) o[dt] *= alpha;
+        m = tmax;
+      }
+      const float mc = m * c2;
+      float rsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s0[r] = fast_exp2(fmaf(s0[r], c2, -mc));
+        s1[r] = fast_exp2(fmaf(s1[r], c2, -mc));
+        rsum += s0[r] + s1[r];
+      }
+      l += xor_sum16_32(rsum);
+      const bf16x8 pf = pack8(s0, s1);
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) o[dt] = mfma16(vf.v[dt], pf, o[dt]);
+    }
+    if (l > 0.f) {
+      lse[br] = m * c2 + __log2f(l);
+      // o^T: lane holds dims 16*dt + 4*lg + r of head lr
+      float s = 0.f;
+      const uint16_t* dr = a.dout + row * DV + 4 * lg;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const u32x2 w = *(const u32x2*)(dr + 16 * dt);
+        s += o[dt][0] * bf16_to_f32((uint16_t)(w.x & 0xFFFF)) + o[dt][1] * bf16_to_f32((uint16_t)(w.x >> 16)) +
+             o[dt][2] * bf16_to_f32((uint16_t)(w.y & 0xFFFF)) + o[dt][3] * bf16_to_f32((uint16_t)(w.y >> 16));
+      }
+      dd[br] = xor_sum16_32(s) / l;
+    }
+    if (lg == 0) {
+      a.stat[(br * 3 + 0) * nrow + row] = lse[br];
+      a.stat[(br * 3 + 1) * nrow + row] = dd[br];
+      a.stat[(br * 3 + 2) * nrow + row] = gam[br];
+      if (a.dgates) a.dgates[row * 3 + br] = dd[br] * dsig;
+    }
+  }
+
+  // ---- dq: recompute P, dP = dout . v, dS, dq += K^T dS ----
+  bf16x8 df[DV / 32];
+#pragma unroll
+  for (int ks = 0; ks < DV / 32; ++ks) df[ks] = ld8(a.dout + row * DV + 8 * lg + 32 * ks);
+  f32x4 dqa[DQ / 16];
+#pragma unroll
+  for (int dt = 0; dt < DQ / 16; ++dt) dqa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int br = 0; br < 3; ++br) {
+    if (!(a.flags & branch_flag(br)) || !(lse[br] < INFINITY)) continue;  // lse is wave-uniform per head row
+    const bool cmp = br == BR_CMP;
+    const __amdgpu_buffer_rsrc_t kr = cmp ? rs(a.kcG, a.nbp, DQ) : rs(a.kG, a.Lp, DQ);
+    const __amdgpu_buffer_rsrc_t vgr = cmp ? rs(a.vcG, a.nbp, DV) : rs(a.vG, a.Lp, DV);
+    const __amdgpu_buffer_rsrc_t ktr = cmp ? rs(a.kcT, a.nbp, DQ) : rs(a.kT, a.Lp, DQ);
+    ChunkIter it = chunks_of(a, br, b, t, g, p, lane);
+    const float lb = lse[br], db = dd[br], gb = gam[br];
+    for (int64_t kb = it.pop(); kb >= 0; kb = it.pop()) {
+      KFrag<DQ> kf;
+      KFrag<DV> vf;
+      VFrag<DQ> ktf;
+      load_k<DQ>(kf, kr, kofs, kb, lr);
+      load_k<DV>(vf, vgr, kofs, kb, lr);
+      load_v<DQ>(ktf, ktr, tofs, kb);
+      f32x4 s0, s1;
+      qk_chunk_b<DQ>(kf, qf, s0, s1);
+      mask_chunk(s0, s1, kb, it.klo, it.khi, lg);
+      f32x4 p0, p1;
+      qk_chunk_b<DV>(vf, df, p0, p1);  // dP^T = V dout^T on the same interleaved rows
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e0 = fast_exp2(fmaf(s0[r], c2, -lb)), e1 = fast_exp2(fmaf(s1[r], c2, -lb));
+        s0[r] = gb * e0 * (p0[r] - db);
+        s1[r] = gb * e1 * (p1[r] - db);
+      }
+      const bf16x8 dsf = pack8(s0, s1);
+#pragma unroll
+      for (int dt = 0; dt < DQ / 16; ++dt) dqa[dt] = mfma16(ktf.v[dt], dsf, dqa[dt]);
+    }
+  }
+  // dq^T: lane holds dims 16*dt + 4*lg + r of head lr
+  float* dqr = a.dq + row * DQ + 4 * lg;
+#pragma unroll
+  for (int dt = 0; dt < DQ / 16; ++dt) *(f32x4*)(dqr + 16 * dt) = dqa[dt] * a.scale;
+}
+
+// ---------------------------------------------------------------------------
+// Lists of the tokens that chose each (b, g, block).  A token lists block j
+// when 0 <= j < nbk and the block starts at or before the token (the
+// query's own block, always chosen when forced, may be the partial last one).
+__global__ void __launch_bounds__(kCountTok) k_bwd_count(BwArgs a) {
+  const int64_t nbs = a.nbk;
+  extern __shared__ int32_t hist[];  // [nbs]
+  const int64_t c = blockIdx.x % a.nct;
+  const int64_t bg = blockIdx.x / a.nct;
+  const int64_t g = bg % a.G, b = bg / a.G;
+  for (int64_t j = threadIdx.x; j < nbs; j += blockDim.x) hist[j] = 0;
+  __syncthreads();
+  const int64_t t = c * kCountTok + threadIdx.x;
+  if (t < a.T) {
+    const int64_t p = a.L - a.T + t;
+    const int32_t* ir = a.idx + ((b * a.T + t) * a.G + g) * a.n;
+    for (int i = 0; i < a.n; ++i) {
+      const int j = ir[i];
+      if (j >= 0 && j < nbs && (int64_t)j * kBlk <= p) atomicAdd(&hist[j], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* crow = a.cnt + (bg * a.nct + c) * nbs;
+  for (int64_t j = threadIdx.x; j < nbs; j += blockDim.x) crow[j] = hist[j];
+}
+
+// Per (b, g, block): exclusive prefix of the chunk counts (in place) and the list length.
+__global__ void __launch_bounds__(256) k_bwd_colscan(BwArgs a) {
+  const int64_t nbs = a.nbk;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, g, j)
+  if (i >= a.B * a.G * nbs) return;
+  const int64_t j = i % nbs, bg = i / nbs;
+  int32_t run = 0;
+  for (int64_t c = 0; c < a.nct; ++c) {
+    int32_t* x = a.cnt + (bg * a.nct + c) * nbs + j;
+    const int32_t v = *x;
+    *x = run;
+    run += v;
+  }
+  a.tot[i] = run;
+}
+
+// Single workgroup: list starts and first work chunk of every list.
+__global__ void __launch_bounds__(1024) k_bwd_scan(BwArgs a, int64_t nl) {
+  __shared__ int32_t part_e[1024], part_c[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (nl + 1023) / 1024;
+  const int64_t lo = tid * per, hi = lo + per < nl ? lo + per : nl;
+  int32_t se = 0, sc = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    se += a.tot[i];
+    sc += (a.tot[i] + kListChunk - 1) / kListChunk;
+  }
+  part_e[tid] = se;
+  part_c[tid] = sc;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t ae = 0, ac = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int32_t xe = part_e[i], xc = part_c[i];
+      part_e[i] = ae;
+      part_c[i] = ac;
+      ae += xe;
+      ac += xc;
+    }
+    a.offsets[nl] = ae;
+    a.chunk_off[nl] = ac;
+  }
+  __syncthreads();
+  int32_t ae = part_e[tid], ac = part_c[tid];
+  for (int64_t i = lo; i < hi; ++i) {
+    a.offsets[i] = ae;
+    a.chunk_off[i] = ac;
+    ae += a.tot[i];
+    ac += (a.tot[i] + kListChunk - 1) / kListChunk;
+  }
+}
+
+// One wave per (b, g, 256-token chunk): tokens in order, one lane per slot;
+// the lanes of one token hold distinct blocks, so their cursor updates touch
+// distinct words and every list comes out in token order.
+__global__ void __launch_bounds__(64) k_bwd_fill(BwArgs a) {
+  const int64_t nbs = a.nbk;
+  extern __shared__ int32_t cur[];  // [nbs]
+  const int64_t c = blockIdx.x % a.nct;
+  const int64_t bg = blockIdx.x / a.nct;
+  const int64_t g = bg % a.G, b = bg / a.G;
+  const int32_t* crow = a.cnt + (bg * a.nct + c) * nbs;
+  for (int64_t j = threadIdx.x; j < nbs; j += 64) cur[j] = a.offsets[bg * nbs + j] + crow[j];
+  __syncthreads();
+  const int lane = threadIdx.x;
+  const int64_t t1 = (c + 1) * kCountTok < a.T ? (c + 1) * kCountTok : a.T;
+  for (int64_t t = c * kCountTok; t < t1; ++t) {
+    const int64_t p = a.L - a.T + t;
+    const int j = lane < a.n ? a.idx[((b * a.T + t) * a.G + g) * a.n + lane] : -1;
+    if (j >= 0 && j < nbs && (int64_t)j * kBlk <= p) a.lists[atomicAdd(&cur[j], 1)] = (int32_t)t;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side.  Wave w owns keys 16w .. 16w + 15 of the workgroup's 64; in the
+// products below a lane holds key lr and head rows 4*lg + r of one token:
+//   S  = Q K^T, dP = dout V^T           (A: 16 head rows of one token, from LDS)
+//   dv^T += dout^T (gamma P),  dk^T += Q^T dS   (contraction over the 32 head
+//          rows of two tokens: A from LDS by transposing reads)
+enum { KV_WIN = 0, KV_SLC = 1, KV_CMP = 2 };
+
+template <int DQ, int DV>
+struct KvLds {
+  static constexpr int QS = DQ + 16, DS = DV + 16;  // row strides (bf16): 16-byte row reads conflict-free
+  uint16_t qs[2][16 * QS];
+  uint16_t ds[2][16 * DS];
+};
+
+template <int DQ, int DV, int MODE>
+__global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
+  constexpr int QS = KvLds<DQ, DV>::QS, DS = KvLds<DQ, DV>::DS;
+  constexpr int QC = 16 * DQ / 8, DC = 16 * DV / 8;   // 16-byte chunks of one token's q / dout rows
+  constexpr int NCH = 2 * (QC + DC);
+  constexpr int CPT = (NCH + 255) / 256;
+  __shared__ __align__(16) KvLds<DQ, DV> sm;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int br = MODE == KV_WIN ? BR_WIN : (MODE == KV_SLC ? BR_SLC : BR_CMP);
+
+  // ---- work item: (b, g), the 64 keys, the query tokens ----
+  int64_t b, g, key0;    // key0: first key (token position, or summary id)
+  int64_t tfirst = 0, ntok = 0;  // window / compressed: token range
+  const int32_t* elist = nullptr;  // selected: this chunk's tokens
+  int64_t chunk_id = 0;
+  if (MODE == KV_WIN) {
+    const int64_t ntile = (a.L + 63) / 64;
+    const int64_t K = blockIdx.x % ntile;
+    const int64_t bg = blockIdx.x / ntile;
+    g = bg % a.G;
+    b = bg / a.G;
+    key0 = K * 64;
+    // tokens whose window [p - w + 1, p] meets [key0, key0 + 63]
+    int64_t plo = key0, phi = key0 + 63 + a.w - 1;
+    int64_t tlo = plo - (a.L - a.T), thi = phi - (a.L - a.T);
+    if (tlo < 0) tlo = 0;
+    if (thi > a.T - 1) thi = a.T - 1;
+    tfirst = tlo;
+    ntok = thi >= tlo ? thi - tlo + 1 : 0;
+  } else if (MODE == KV_CMP) {
+    const int64_t c = blockIdx.x % a.nC;
+    const int64_t J = (blockIdx.x / a.nC) % a.nJ;
+    const int64_t bg = blockIdx.x / (a.nC * a.nJ);
+    g = bg % a.G;
+    b = bg / a.G;
+    key0 = J * 64;
+    chunk_id = blockIdx.x;
+    int64_t lo, hi;
+    cmp_chunk_range(a, J, c, lo, hi);
+    if (hi <= lo) return;  // the reduce skips this chunk by the same rule
+    tfirst = lo;
+    ntok = hi - lo;
+  } else {
+    const int64_t nl = a.B * a.G * a.nbk;
+    const int32_t total = a.chunk_off[nl];
+    const int32_t w = (int32_t)blockIdx.x;
+    if (w >= total) return;
+    int64_t lo = 0, hi = nl;  // chunk_off[lo] <= w < chunk_off[hi]
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (a.chunk_off[mid] <= w) lo = mid;
+      else hi = mid;
+    }
+    const int64_t j = lo % a.nbk, bg = lo / a.nbk;
+    g = bg % a.G;
+    b = bg / a.G;
+    key0 = j * kBlk;
+    const int64_t first = a.offsets[lo] + (int64_t)(w - a.chunk_off[lo]) * kListChunk;
+    int64_t cnt = a.offsets[lo + 1] - first;
+    if (cnt > kListChunk) cnt = kListChunk;
+    elist = a.lists + first;
+    ntok = cnt;
+    chunk_id = w;
+  }
+
+  // ---- this wave's 16 keys in registers: B operands K[key lr][dims 8*lg + 32*ks ..] ----
+  const int64_t key = key0 + 16 * wave + lr;
+  const int64_t nkeys = MODE == KV_CMP ? a.nb : a.L;
+  const bool key_ok = key < nkeys;
+  const uint16_t* krow = MODE == KV_CMP ? a.kc + ((b * a.nb + key) * a.G + g) * DQ : a.k + ((b * a.L + key) * a.G + g) * DQ;
+  const uint16_t* vrow = MODE == KV_CMP ? a.vc + ((b * a.nb + key) * a.G + g) * DV : a.v + ((b * a.L + key) * a.G + g) * DV;
+  bf16x8 kf[DQ / 32], vf[DV / 32];
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) kf[ks] = key_ok ? ld8(krow + 8 * lg + 32 * ks) : bf16x8{};
+#pragma unroll
+  for (int ks = 0; ks < DV / 32; ++ks) vf[ks] = key_ok ? ld8(vrow + 8 * lg + 32 * ks) : bf16x8{};
+
+  f32x4 dkt[DQ / 16], dvt[DV / 16];
+#pragma unroll
+  for (int dt = 0; dt < DQ / 16; ++dt) dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nrow = a.B * a.T * a.H;
+  const float c2 = a.scale * kLog2e;
+  const int64_t npair = (ntok + 1) / 2;
+  auto token_of = [&](int64_t i) -> int64_t {  // i-th token of the work item, or -1
+    if (i >= ntok) return -1;
+    return MODE == KV_SLC ? (int64_t)elist[i] : tfirst + i;
+  };
+
+  // register prefetch of one pair: q and dout rows (all threads), stats (per lane)
+  u32x4 pre[CPT];
+  f32x4 pst[2][3];
+  auto fetch = [&](int64_t pi) {
+    const int64_t tt[2] = {token_of(2 * pi), token_of(2 * pi + 1)};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cc = threadIdx.x + 256 * i;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (cc < NCH) {
+        const bool isq = cc < 2 * QC;
+        const int x = isq ? cc : cc - 2 * QC;
+        const int per = isq ? QC : DC;
+        const int tok = x / per, rem = x % per;
+        const int D = isq ? DQ : DV;
+        const int hh = rem / (D / 8), c8 = rem % (D / 8);
+        if (tt[tok] >= 0) {
+          const int64_t r = (b * a.T + tt[tok]) * a.H + g * 16 + hh;
+          val = isq ? *(const u32x4*)(a.q + r * DQ + 8 * c8) : *(const u32x4*)(a.dout + r * DV + 8 * c8);
+        }
+      }
+      pre[i] = val;
+    }
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+#pragma unroll
+      for (int f = 0; f < 3; ++f) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        if (tt[tk] >= 0) s = *(const f32x4*)(a.stat + (br * 3 + f) * nrow + (b * a.T + tt[tk]) * a.H + g * 16 + 4 * lg);
+        pst[tk][f] = s;
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cc = threadIdx.x + 256 * i;
+      if (cc < NCH) {
+        const bool isq = cc < 2 * QC;
+        const int x = isq ? cc : cc - 2 * QC;
+        const int per = isq ? QC : DC;
+        const int tok = x / per, rem = x % per;
+        const int D = isq ? DQ : DV;
+        const int hh = rem / (D / 8), c8 = rem % (D / 8);
+        if (isq) *(u32x4*)(sm.qs[tok] + hh * QS + 8 * c8) = pre[i];
+        else *(u32x4*)(sm.ds[tok] + hh * DS + 8 * c8) = pre[i];
+      }
+    }
+  };
+
+  if (npair > 0) fetch(0);
+  for (int64_t pi = 0; pi < npair; ++pi) {
+    const int64_t tt[2] = {token_of(2 * pi), token_of(2 * pi + 1)};
+    f32x4 st[2][3];
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int f = 0; f < 3; ++f) st[tk][f] = pst[tk][f];
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (pi + 1 < npair) fetch(pi + 1);
+
+    f32x4 pg[2], dsv[2];
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DQ / 32; ++ks) s = mfma16(ld8(sm.qs[tk] + lr * QS + 8 * lg + 32 * ks), kf[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < DV / 32; ++ks) dp = mfma16(ld8(sm.ds[tk] + lr * DS + 8 * lg + 32 * ks), vf[ks], dp);
+      // visibility of key lr for this token
+      bool vis = key_ok && tt[tk] >= 0;
+      if (vis) {
+        const int64_t pp = a.L - a.T + tt[tk];
+        if (MODE == KV_WIN) vis = key <= pp && key > pp - a.w;
+        else if (MODE == KV_SLC) vis = key <= pp;
+        else vis = (key + 1) * kBlk <= pp + 1;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = vis ? fast_exp2(fmaf(s[r], c2, -st[tk][0][r])) : 0.f;
+        pg[tk][r] = st[tk][2][r] * pr;
+        dsv[tk][r] = pg[tk][r] * (dp[r] - st[tk][1][r]);
+      }
+    }
+    const bf16x8 pgf = pack8(pg[0], pg[1]), dsf = pack8(dsv[0], dsv[1]);
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      const u32x2 x0 = ld_tr4(sm.ds[0], 4 * lg, 16 * dt, DS, lr), x1 = ld_tr4(sm.ds[1], 4 * lg, 16 * dt, DS, lr);
+      const u32x4 x = {x0.x, x0.y, x1.x, x1.y};
+      dvt[dt] = mfma16(__builtin_bit_cast(bf16x8, x), pgf, dvt[dt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DQ / 16; ++dt) {
+      const u32x2 x0 = ld_tr4(sm.qs[0], 4 * lg, 16 * dt, QS, lr), x1 = ld_tr4(sm.qs[1], 4 * lg, 16 * dt, QS, lr);
+      const u32x4 x = {x0.x, x0.y, x1.x, x1.y};
+      dkt[dt] = mfma16(__builtin_bit_cast(bf16x8, x), dsf, dkt[dt]);
+    }
+  }
+
+  // ---- write: lane holds dims 16*dt + 4*lg + r of key lr ----
+  if (MODE == KV_WIN) {
+    if (!key_ok) return;
+    float* dkr = a.dk + ((b * a.L + key) * a.G + g) * DQ + 4 * lg;
+    float* dvr = a.dv + ((b * a.L + key) * a.G + g) * DV + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < DQ / 16; ++dt) *(f32x4*)(dkr + 16 * dt) = dkt[dt] * a.scale;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(dvr + 16 * dt) = dvt[dt];
+  } else {
+    float* prow = (MODE == KV_SLC ? a.part_s : a.part_c) + (chunk_id * 64 + 16 * wave + lr) * (DQ + DV) + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < DQ / 16; ++dt) *(f32x4*)(prow + 16 * dt) = dkt[dt] * a.scale;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(prow + DQ + 16 * dt) = dvt[dt];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (b, g, 64-token tile): dk, dv of its tokens = window part
+// (already in dk, dv when that branch is on) + the selected partials of the
+// tile's block + the block's summary gradient / 64 (the mean's gradient).
+template <int DQ, int DV>
+__global__ void __launch_bounds__(256) k_bwd_reduce(BwArgs a) {
+  constexpr int E = DQ + DV;
+  const int64_t ntile = (a.L + 63) / 64;
+  const int64_t K = blockIdx.x % ntile;
+  const int64_t bg = blockIdx.x / ntile;
+  const int64_t g = bg % a.G, b = bg / a.G;
+  const bool win = (a.flags & NSA_F_WIN) && a.w > 0;
+  const bool slc = (a.flags & NSA_F_SLC) != 0;  // K < nbk always
+  const bool cmp = (a.flags & NSA_F_CMP) && K < a.nb;
+  int64_t c_lo = 0, c_hi = 0;
+  if (slc) {
+    c_lo = a.chunk_off[bg * a.nbk + K];
+    c_hi = a.chunk_off[bg * a.nbk + K + 1];
+  }
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float cm = 0.f;
+    if (cmp) {
+      const int64_t J = K / 64, jj = K % 64;
+      for (int64_t c = 0; c < a.nC; ++c) {
+        int64_t lo, hi;
+        cmp_chunk_range(a, J, c, lo, hi);
+        if (hi > lo) cm += a.part_c[(((bg * a.nJ + J) * a.nC + c) * 64 + jj) * E + e];
+      }
+      cm *= 1.f / kBlk;
+    }
+    for (int i = 0; i < 64; ++i) {
+      const int64_t s = K * 64 + i;
+      if (s >= a.L) break;
+      float* dst = e < DQ ? a.dk + ((b * a.L + s) * a.G + g) * DQ + e : a.dv + ((b * a.L + s) * a.G + g) * DV + (e - DQ);
+      float x = win ? *dst : 0.f;
+      x += cm;
+      for (int64_t ch = c_lo; ch < c_hi; ++ch) x += a.part_s[(ch * 64 + i) * E + e];
+      *dst = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+struct BwPlan {
+  size_t total = 0;
+  size_t kc, vc, kG, vG, kT, vT, kcG, vcG, kcT, vcT, stat, cnt, tot, offsets, chunk_off, lists, part_s, part_c;
+};
+
+BwPlan plan(const Prob& P) {
+  BwPlan w;
+  auto take = [&](size_t bytes) {
+    const size_t off = w.total;
+    w.total += (bytes + 255) / 256 * 256;
+    return off;
+  };
+  const int64_t Lp = (P.L + 63) / 64 * 64, nbp = (P.nb + 63) / 64 * 64;
+  const int64_t nbk = (P.L + kBlk - 1) / kBlk, nct = (P.T + kCountTok - 1) / kCountTok;
+  const int64_t nJ = (P.nb + 63) / 64, nC = (P.T + kCmpChunk - 1) / kCmpChunk;
+  const int64_t nl = P.B * P.G * nbk;
+  const int64_t ne = P.B * P.T * P.G * P.n;
+  const int64_t chunks = (ne + kListChunk - 1) / kListChunk + nl;
+  w.kc = take(P.B * P.nb * P.G * P.dq * 2);
+  w.vc = take(P.B * P.nb * P.G * P.dv * 2);
+  w.kG = take(P.B * P.G * Lp * P.dq * 2);
+  w.vG = take(P.B * P.G * Lp * P.dv * 2);
+  w.kT = take(P.B * P.G * Lp * P.dq * 2);
+  w.vT = take(P.B * P.G * Lp * P.dv * 2);
+  w.kcG = take(P.B * P.G * nbp * P.dq * 2);
+  w.vcG = take(P.B * P.G * nbp * P.dv * 2);
+  w.kcT = take(P.B * P.G * nbp * P.dq * 2);
+  w.vcT = take(P.B * P.G * nbp * P.dv * 2);
+  w.stat = take((size_t)9 * P.B * P.T * P.H * 4);
+  w.cnt = take((size_t)P.B * P.G * nct * nbk * 4);
+  w.tot = take((nl + 1) * 4);
+  w.offsets = take((nl + 1) * 4);
+  w.chunk_off = take((nl + 1) * 4);
+  w.lists = take((ne > 0 ? ne : 1) * 4);
+  w.part_s = take((size_t)chunks * 64 * (P.dq + P.dv) * 4);
+  w.part_c = take((size_t)P.B * P.G * nJ * nC * 64 * (P.dq + P.dv) * 4);
+  return w;
+}
+
+template <int DQ, int DV>
+hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s) {
+  const int64_t nl = P.B * P.G * a.nbk;
+  const unsigned gq = (unsigned)(P.G * ((P.B * P.T + 3) / 4));
+  k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
+  const bool slc = P.has(NSA_F_SLC);
+  if (slc) {
+    const size_t lds = (size_t)a.nbk * 4;
+    k_bwd_count<<<(unsigned)(P.B * P.G * a.nct), kCountTok, lds, s>>>(a);
+    k_bwd_colscan<<<(unsigned)((nl + 255) / 256), 256, 0, s>>>(a);
+    k_bwd_scan<<<1, 1024, 0, s>>>(a, nl);
+    k_bwd_fill<<<(unsigned)(P.B * P.G * a.nct), 64, lds, s>>>(a);
+  }
+  const int64_t ntile = (P.L + 63) / 64;
+  if (P.has(NSA_F_WIN) && P.w > 0) k_bwd_kv<DQ, DV, KV_WIN><<<(unsigned)(P.B * P.G * ntile), 256, 0, s>>>(a);
+  if (slc) {
+    const int64_t ne = P.B * P.T * P.G * P.n;
+    const int64_t chunks_max = (ne + kListChunk - 1) / kListChunk + nl;  // surplus workgroups exit at once
+    k_bwd_kv<DQ, DV, KV_SLC><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+  }
+  if (P.has(NSA_F_CMP) && P.nb > 0)
+    k_bwd_kv<DQ, DV, KV_CMP><<<(unsigned)(P.B * P.G * a.nJ * a.nC), 256, 0, s>>>(a);
+  k_bwd_reduce<DQ, DV><<<(unsigned)(P.B * P.G * ntile), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_ok(const Prob& P) {
+  return P.bf16() && P.hpg == 16 && P.bs == kBlk && P.sb == kBlk && (P.dq == 64 || P.dq == 128 || P.dq == 192) &&
+         (P.dv == 64 || P.dv == 128) && P.n <= 32 && P.B * P.T * P.G * P.n < ((int64_t)1 << 31) &&
+         P.B * P.T * P.H * 9 < ((int64_t)1 << 31) * 4;
+}
+
+size_t backward_workspace_bytes(const Prob& P) { return backward_ok(P) ? plan(P).total : 0; }
+
+hipError_t run_backward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
+                        const int32_t* idx, const void* dout, float* dq, float* dk, float* dv, float* dgates,
+                        void* ws, hipStream_t s) {
+  const BwPlan w = plan(P);
+  char* base = (char*)ws;
+  BwArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.gates = (const uint16_t*)gates;
+  a.idx = idx;
+  a.dout = (const uint16_t*)dout;
+  uint16_t* kc = (uint16_t*)(base + w.kc);
+  uint16_t* vc = (uint16_t*)(base + w.vc);
+  a.kc = kc;
+  a.vc = vc;
+  a.kG = (const uint16_t*)(base + w.kG);
+  a.vG = (const uint16_t*)(base + w.vG);
+  a.kT = (const uint16_t*)(base + w.kT);
+  a.vT = (const uint16_t*)(base + w.vT);
+  a.kcG = (const uint16_t*)(base + w.kcG);
+  a.vcG = (const uint16_t*)(base + w.vcG);
+  a.kcT = (const uint16_t*)(base + w.kcT);
+  a.vcT = (const uint16_t*)(base + w.vcT);
+  a.stat = (float*)(base + w.stat);
+  a.cnt = (int32_t*)(base + w.cnt);
+  a.tot = (int32_t*)(base + w.tot);
+  a.offsets = (int32_t*)(base + w.offsets);
+  a.chunk_off = (int32_t*)(base + w.chunk_off);
+  a.lists = (int32_t*)(base + w.lists);
+  a.part_s = (float*)(base + w.part_s);
+  a.part_c = (float*)(base + w.part_c);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dgates = dgates;
+  a.B = P.B; a.T = P.T; a.L = P.L; a.G = P.G; a.H = P.H; a.nb = P.nb;
+  a.nbp = (P.nb + 63) / 64 * 64;
+  a.Lp = (P.L + 63) / 64 * 64;
+  a.n = P.n; a.w = P.w;
+  a.nbk = (P.L + kBlk - 1) / kBlk;
+  a.nct = (P.T + kCountTok - 1) / kCountTok;
+  a.nJ = (P.nb + 63) / 64;
+  a.nC = (P.T + kCmpChunk - 1) / kCmpChunk;
+  a.flags = P.flags;
+  a.scale = P.scale;
+
+  // summaries and the operand images
+  hipError_t e = launch_pool(P, k, v, kc, vc, s);
+  if (e != hipSuccess) return e;
+  const int64_t B = P.B, G = P.G;
+  if ((e = launch_group_major(k, (void*)a.kG, B, P.L, G, (int)P.dq, s)) != hipSuccess) return e;
+  if ((e = launch_group_major(v, (void*)a.vG, B, P.L, G, (int)P.dv, s)) != hipSuccess) return e;
+  if ((e = launch_transpose(k, (void*)a.kT, B, P.L, a.Lp, G, (int)P.dq, s)) != hipSuccess) return e;
+  if ((e = launch_transpose(v, (void*)a.vT, B, P.L, a.Lp, G, (int)P.dv, s)) != hipSuccess) return e;
+  if (P.nb > 0) {
+    if ((e = launch_group_major(kc, (void*)a.kcG, B, P.nb, G, (int)P.dq, s)) != hipSuccess) return e;
+    if ((e = launch_group_major(vc, (void*)a.vcG, B, P.nb, G, (int)P.dv, s)) != hipSuccess) return e;
+    if ((e = launch_transpose(kc, (void*)a.kcT, B, P.nb, a.nbp, G, (int)P.dq, s)) != hipSuccess) return e;
+    if ((e = launch_transpose(vc, (void*)a.vcT, B, P.nb, a.nbp, G, (int)P.dv, s)) != hipSuccess) return e;
+  }
+#define CALL_BW(DQ, DV) return launch_t<DQ, DV>(P, a, s)
+  if (P.dq == 192 && P.dv == 128) CALL_BW(192, 128);
+  if (P.dq == 128 && P.dv == 128) CALL_BW(128, 128);
+  if (P.dq == 64 && P.dv == 64) CALL_BW(64, 64);
+  if (P.dq == 192 && P.dv == 64) CALL_BW(192, 64);
+  if (P.dq == 128 && P.dv == 64) CALL_BW(128, 64);
+  if (P.dq == 64 && P.dv == 128) CALL_BW(64, 128);
+#undef CALL_BW
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nsa

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include "nsa_backward.h"
 #include "nsa_internal.h"
 #include "nsa_paths.h"
 
@@ -121,6 +122,29 @@ nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* 
   return hip_status(nsa::run_forward(P, q, k, v, gates, have_cmp ? p->k_cmp : nullptr,
                                      have_cmp ? p->v_cmp : nullptr, out, ws, p->workspace,
                                      (hipStream_t)p->stream, ph));
+}
+
+size_t nsa_backward_workspace_bytes(const nsa_params* p) {
+  Prob P;
+  if (describe(p, &P) != NSA_OK) return 0;
+  return nsa::backward_workspace_bytes(P);
+}
+
+nsa_status nsa_backward(const void* q, const void* k, const void* v, const void* gates, const int32_t* idx,
+                        const void* dout, float* dq, float* dk, float* dv, float* dgates, const nsa_params* p) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  const int nbr = n_branches(P.flags);
+  if (nbr == 0 || (gates == nullptr && nbr > 1) || (gates == nullptr && dgates != nullptr)) return NSA_ERR_INVALID_ARG;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) ||
+      !ptr_ok(dv) || !opt_ok(gates) || !opt_ok(dgates))
+    return NSA_ERR_INVALID_ARG;
+  if (!nsa::backward_ok(P)) return NSA_ERR_UNSUPPORTED;
+  const size_t need = nsa::backward_workspace_bytes(P);
+  if (!ptr_ok(p->workspace) || p->workspace_bytes < need) return NSA_ERR_WORKSPACE;
+  return hip_status(nsa::run_backward(P, q, k, v, gates, idx, dout, dq, dk, dv, dgates, p->workspace,
+                                      (hipStream_t)p->stream));
 }
 
 int32_t nsa_forward_phases(const nsa_params* p, const char** names, int32_t max_names) {

@@ -1,0 +1,55 @@
+// nsa_backward.h -- arguments, workspace plan and entry of the matrix-core
+// NSA backward pass (internal).
+#pragma once
+
+#include "nsa_internal.h"
+
+namespace nsa {
+
+struct BwArgs {
+  const uint16_t* q;      // [B, T, H, DQ]
+  const uint16_t* k;      // [B, L, G, DQ]
+  const uint16_t* v;      // [B, L, G, DV]
+  const uint16_t* gates;  // [B, T, H, 3] or NULL
+  const int32_t* idx;     // [B, T, G, n] selection blocks of 64 tokens
+  const uint16_t* dout;   // [B, T, H, DV]
+  const uint16_t* kc;     // [B, nb, G, DQ] block summaries
+  const uint16_t* vc;     // [B, nb, G, DV]
+  const uint16_t* kG;     // paired-row images [B, G, Lp, D] of k, v
+  const uint16_t* vG;
+  const uint16_t* kT;     // tiled transposes [B, G, Lp / 32, D, 32] of k, v
+  const uint16_t* vT;
+  const uint16_t* kcG;    // the same four images of the summaries (nbp rows)
+  const uint16_t* vcG;
+  const uint16_t* kcT;
+  const uint16_t* vcT;
+  float* stat;            // [3 branches][3: lse (log2 units), <dout, O_b>, gate][B*T*H]
+  int32_t* cnt;           // [B, G, nct, nbk] entries per (256-token chunk, block)
+  int32_t* tot;           // [B*G*nbk + 1] entries per list
+  int32_t* offsets;       // [B*G*nbk + 1] list starts
+  int32_t* chunk_off;     // [B*G*nbk + 1] first work chunk of each list
+  int32_t* lists;         // tokens, grouped by (b, g, block), in token order
+  float* part_s;          // [chunks][64][DQ + DV] selected-branch key gradients
+  float* part_c;          // [B, G, nJ, nC][64][DQ + DV] compressed-branch summary gradients
+  float* dq;              // [B, T, H, DQ]
+  float* dk;              // [B, L, G, DQ]
+  float* dv;              // [B, L, G, DV]
+  float* dgates;          // [B, T, H, 3] or NULL
+  int64_t B, T, L, G, H, nb, nbp, Lp, n, w;
+  int64_t nbk;            // 64-token blocks, the last one possibly partial
+  int64_t nct;            // 256-token chunks of the list count
+  int64_t nJ, nC;         // 64-summary tiles, token chunks of the compressed branch
+  uint32_t flags;
+  float scale;
+};
+
+// True when the backward kernels take this shape: bf16, 16 heads per group,
+// 64-token blocks (compression = selection), d_qk in {64,128,192},
+// d_v in {64,128}, top_k <= 32.
+bool backward_ok(const Prob& P);
+size_t backward_workspace_bytes(const Prob& P);
+hipError_t run_backward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
+                        const int32_t* idx, const void* dout, float* dq, float* dk, float* dv, float* dgates,
+                        void* ws, hipStream_t s);
+
+}  // namespace nsa

@@ -51,6 +51,27 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return r;
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane
+// group, lane i points at 4 consecutive 16-bit elements R_i; lane 4a + c
+// receives element c of R_a, R_(a+4), R_(a+8), R_(a+12).  With lane i on row
+// row0 + i / 4, columns col0 + 4 * (i % 4) .. + 3 of a row-major tile, lane
+// j of the group receives column col0 + j of rows row0 .. row0 + 3.
+__device__ __forceinline__ u32x2 ld_tr4(const uint16_t* tile, int row0, int col0, int stride, int i) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const uint16_t* p = tile + (row0 + (i >> 2)) * stride + col0 + 4 * (i & 3);
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+// A matrix-op operand of V^T: rows rowa .. rowa + 3 then rowb .. rowb + 3 of
+// column col0 + lr.
+__device__ __forceinline__ bf16x8 ld_vt_pair(const uint16_t* tile, int rowa, int rowb, int col0, int stride,
+                                             int lr) {
+  const u32x2 a = ld_tr4(tile, rowa, col0, stride, lr);
+  const u32x2 b = ld_tr4(tile, rowb, col0, stride, lr);
+  const u32x4 r = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // ---- cross-lane reductions without LDS traffic -------------------------
 // gfx950 v_permlane16_swap / v_permlane32_swap called with the same value
 // twice return, in every lane, its own and its partner's value (partner =

@@ -20,7 +20,8 @@ STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "N
           4: "NSA_ERR_HIP"}
 
 EXPORTS = ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
-           "nsa_forward_phases", "nsa_workspace_bytes", "nsa_status_str")
+           "nsa_forward_phases", "nsa_workspace_bytes", "nsa_backward", "nsa_backward_workspace_bytes",
+           "nsa_status_str")
 
 
 class NsaError(RuntimeError):
@@ -63,9 +64,12 @@ def lib() -> ctypes.CDLL:
         L.nsa_workspace_bytes.restype = ctypes.c_size_t
         L.nsa_forward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
         L.nsa_forward_phases.restype = ctypes.c_int32
+        L.nsa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, P]
+        L.nsa_backward_workspace_bytes.argtypes = [P]
+        L.nsa_backward_workspace_bytes.restype = ctypes.c_size_t
         L.nsa_status_str.argtypes = [ctypes.c_int]
         L.nsa_status_str.restype = ctypes.c_char_p
-        for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward"):
+        for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_backward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -237,6 +241,38 @@ def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f3
     _call("nsa_forward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), ctypes.byref(p),
           out.data_ptr())
     return out
+
+
+def backward_workspace_bytes(prob: dict) -> int:
+    p = params(prob, stream=_NoStream)
+    return int(lib().nsa_backward_workspace_bytes(ctypes.byref(p)))
+
+
+def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, dgates=None,
+             want_dgates=True, workspace=None, stream=None):
+    """Gradients of nsa_forward on the selection idx: (dq, dk, dv, dgates), fp32."""
+    s, dt = _shapes(prob), torch_dtype(prob)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", dout)):
+        _check(t, s[name], dt, "dout" if name == "out" else name)
+    if gates is not None:
+        _check(gates, s["gates"], dt, "gates")
+    _check(idx, s["idx"], torch.int32, "idx")
+    f32, dev = torch.float32, q.device
+    dq = torch.empty(s["q"], dtype=f32, device=dev) if dq is None else dq
+    dk = torch.empty(s["k"], dtype=f32, device=dev) if dk is None else dk
+    dv = torch.empty(s["v"], dtype=f32, device=dev) if dv is None else dv
+    if gates is not None and want_dgates and dgates is None:
+        dgates = torch.empty(s["gates"], dtype=f32, device=dev)
+    for name, t, shp in (("dq", dq, s["q"]), ("dk", dk, s["k"]), ("dv", dv, s["v"])):
+        _check(t, shp, f32, name)
+    if dgates is not None:
+        _check(dgates, s["gates"], f32, "dgates")
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_bytes(prob), 256), dtype=torch.uint8, device=dev)
+    p = params(prob, workspace=workspace, stream=stream)
+    _call("nsa_backward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), idx.data_ptr(),
+          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dgates), ctypes.byref(p))
+    return dq, dk, dv, dgates
 
 
 def to_device(a, prob: dict, device="cuda") -> torch.Tensor:

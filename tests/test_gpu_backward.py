@@ -1,0 +1,99 @@
+"""GPU parity of nsa_backward against the fp64 backward oracle
+(oracle/backward.py), on the oracle's own selection.
+
+Tolerance (bf16 operands, fp32 accumulation): every operand of the matrix
+products is rounded to bf16 once (q, k, v, dout as stored; P, gamma*P and
+dS rounded when packed), a relative error of at most 2^-9 per factor, and
+the sums run in fp32.  The error of a gradient entry is then a sum of
+independently rounded terms; it stays below 1% of the largest entry of the
+same tensor, which is the bound checked here (GRAD_REL), together with an
+RMS bound (GRAD_RMS) that a systematic error of any one term would break.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as BW
+from long_context_dynamic_amd import inputs, nsa, workloads
+from tests import gpu_util as U
+
+GRAD_REL = 1e-2   # max |gpu - ref| <= GRAD_REL * max |ref|  (per tensor)
+GRAD_RMS = 4e-3   # rms(gpu - ref) <= GRAD_RMS * rms(ref)
+
+BASE = dict(workloads.get("nsa_prefill_8k"), q_len=700, kv_len=700, n_groups=2, top_k=8, window=100)
+
+CASES = [
+    ("ragged T=L=700 G2 top8 w100", dict(BASE)),
+    ("logits, queries at the end T=300 L=1000", dict(BASE, q_len=300, kv_len=1000, top_k=6, window=200,
+                                                      gate_logits=1)),
+    ("d64 slc only T=L=520", dict(BASE, q_len=520, kv_len=520, n_groups=1, d_qk=64, d_v=64, use_cmp=0,
+                                   use_win=0, top_k=4)),
+    ("cmp only T=L=600", dict(BASE, q_len=600, kv_len=600, n_groups=1, use_slc=0, use_win=0)),
+    ("win only T=L=333 w64", dict(BASE, q_len=333, kv_len=333, n_groups=1, use_cmp=0, use_slc=0, window=64)),
+    ("dq128 dv64 no forced blocks", dict(BASE, q_len=640, kv_len=640, d_qk=128, d_v=64, force_first=0,
+                                          force_current=0, top_k=5)),
+    ("long T=L=4200 G1 top16 w512", dict(BASE, q_len=4200, kv_len=4200, n_groups=1, top_k=16, window=512)),
+]
+
+
+def _ids():
+    return [c[0] for c in CASES]
+
+
+def _inputs(prob):
+    x = inputs.generate(prob, want=("q", "k", "v", "gates", "dout"))
+    if not (prob["use_cmp"] + prob["use_slc"] + prob["use_win"] > 1):
+        x["gates"] = None
+    return x
+
+
+def _oracle_idx(prob, x):
+    kc, vc = oracle.pool(prob, x["k"], x["v"])
+    idx, _, _ = oracle.select(prob, x["q"], kc, vc, want_imp=False, want_cmp=False)
+    return idx.reshape(prob["batch"], prob["q_len"], prob["n_groups"], prob["top_k"])
+
+
+def _run_gpu(prob, x, idx):
+    d = {k: nsa.to_device(a, prob) for k, a in x.items() if a is not None}
+    import torch
+    idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    dq, dk, dv, dg = nsa.backward(prob, d["q"], d["k"], d["v"], d.get("gates"), idx_t, d["dout"])
+    torch.cuda.synchronize()
+    return [None if t is None else t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv, dg)]
+
+
+def _compare(name, got, ref):
+    err = np.abs(got - ref)
+    scale = max(np.abs(ref).max(), 1e-30)
+    rms_ref = max(np.sqrt(np.mean(ref ** 2)), 1e-30)
+    rel, rms = err.max() / scale, np.sqrt(np.mean(err ** 2)) / rms_ref
+    print(f"[bwd] {name}: max|ref| {scale:.3g} max err {err.max():.3g} (rel {rel:.2e}) rms rel {rms:.2e}", flush=True)
+    assert rel <= GRAD_REL, (name, rel)
+    assert rms <= GRAD_RMS, (name, rms)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(len(CASES)), ids=_ids())
+def test_backward_matches_oracle(i):
+    name, prob = CASES[i]
+    print(f"[case] backward {name}", flush=True)
+    x = _inputs(prob)
+    idx = _oracle_idx(prob, x)
+    got = _run_gpu(prob, x, idx)
+    ref = BW.backward(prob, x["q"], x["k"], x["v"], x["gates"], idx, x["dout"])
+    for nm, g, r in zip(("dq", "dk", "dv", "dgates"), got, ref):
+        if r is None:
+            assert g is None
+            continue
+        _compare(f"{name} {nm}", g, r)
+
+
+@pytest.mark.gpu
+def test_backward_is_deterministic():
+    name, prob = CASES[0]
+    x = _inputs(prob)
+    idx = _oracle_idx(prob, x)
+    a = _run_gpu(prob, x, idx)
+    b = _run_gpu(prob, x, idx)
+    for ga, gb in zip(a, b):
+        assert np.array_equal(ga, gb)
