@@ -1,6 +1,6 @@
 """Benchmark of the NSA forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-moba] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-moba] [--no-backward] [--no-cpu]
 
 One step is one nsa_forward (pooling, selection, all three branches, gates)
 over the 64k-token prefill workload (B=1, T=65536, 4 KV groups x 16 heads,
@@ -8,7 +8,8 @@ d_qk 192, d_v 128, block 64, top-16, window 512) with inputs resident in
 HBM.  Prints ONE JSON line: tokens/s, per-kernel times from HIP events
 recorded on the library's stream, the roofline of the dominant kernel, the
 MoBA forward (32k tokens, 32 heads, 512-token blocks, top-3) with its own
-roofline, the batched-decode measurement (64 x 65536-token caches, % of HBM
+roofline, the backward pass of the 64k workload (dq, dk, dv, dgates on its
+selection) with its roofline, the batched-decode measurement (64 x 65536-token caches, % of HBM
 peak) and the CPU oracle timed on a bounded sample of the 64k workload.
 """
 from __future__ import annotations
@@ -183,6 +184,70 @@ def run_nsa_leg(args, torch, nsa, workloads, inputs, workload):
             "roofline": roof}
 
 
+# --------------------------------------------------------------- backward --
+
+def backward_kernel_flops(prob):
+    """Algorithmic FLOPs of the backward per kernel group: five products per
+    attended (key, head) -- S = q.k, dP = dout.v, dq, dk, dv -- over exactly
+    the keys of each branch.  The query side (dq) is charged S, dP and dq;
+    each branch's key side its dk and dv."""
+    fl = algorithmic_flops(prob)  # 2 (dq + dv) per key and head
+    dq, dv = prob["d_qk"], prob["d_v"]
+    keys = {b: f / (2.0 * (dq + dv)) for b, f in fl.items()}  # key-head pairs per branch
+    out = {"bwd_q": sum(keys.values()) * 2.0 * (2 * dq + dv)}
+    for b, name in (("cmp", "bwd_kv_compressed"), ("slc", "bwd_kv_selected"), ("win", "bwd_kv_window")):
+        if keys[b] > 0:
+            out[name] = keys[b] * 2.0 * (dq + dv)
+    return out
+
+
+def run_backward(args, torch, nsa, workloads, inputs, workload="nsa_prefill_64k"):
+    """nsa_backward on the workload's own selection (from nsa_select_topk)."""
+    prob = workloads.get(workload)
+    log(f"backward {workload}: generating inputs")
+    x = inputs.generate(prob, want=("q", "k", "v", "gates", "dout"))
+    t = {k: nsa.to_device(a, prob) for k, a in x.items()}
+    del x
+    kc, _ = nsa.compress(prob, t["k"], t["v"])
+    idx, _ = nsa.select_topk(prob, t["q"], kc, want_score=False)
+    del kc
+    ws = torch.empty(nsa.backward_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    f32 = torch.float32
+    B, T, L, G, H = prob["batch"], prob["q_len"], prob["kv_len"], prob["n_groups"], workloads.n_heads(prob)
+    dq = torch.empty((B, T, H, prob["d_qk"]), dtype=f32, device="cuda")
+    dk = torch.empty((B, L, G, prob["d_qk"]), dtype=f32, device="cuda")
+    dv = torch.empty((B, L, G, prob["d_v"]), dtype=f32, device="cuda")
+    dg = torch.empty((B, T, H, 3), dtype=f32, device="cuda")
+    phases = nsa.backward_phases(prob)
+    K, W = args.steps, args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
+
+    def step(events=None):
+        nsa.backward(prob, t["q"], t["k"], t["v"], t["gates"], idx, t["dout"], dq=dq, dk=dk, dv=dv, dgates=dg,
+                     workspace=ws, events=events)
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / K * 1e3
+    per_phase = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                 for j, name in enumerate(phases)}
+    kf = backward_kernel_flops(prob)
+    tokens = B * T
+    rec = {"workload": workload, "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+           "steps": K, "warmup": W, "phases_ms": {k: round(v, 4) for k, v in per_phase.items()},
+           "algorithmic_tflop": {k: round(v / 1e12, 4) for k, v in kf.items()},
+           "backward_mfma_frac": round(sum(kf.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "roofline": roofline(kf, per_phase, workload),
+           "note": "gradients of the whole forward on its selection: dq, dk, dv (fp32), dgates"}
+    del t, ws, dq, dk, dv, dg
+    torch.cuda.empty_cache()
+    return rec
+
+
 # ----------------------------------------------------------------- decode --
 
 def run_decode(args, torch, nsa, workloads, inputs):
@@ -331,6 +396,9 @@ def run_only(args, torch, nsa, workloads, inputs):
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copied 1 GiB x {args.steps}")
+    elif args.only == "backward":
+        rec = run_backward(args, torch, nsa, workloads, inputs, args.workload)
+        log(f"backward {rec['ms_per_step']} ms/step {rec['phases_ms']}")
     elif args.only == "prefill":
         args.steps, args.warmup = max(1, args.steps), args.warmup
         _, _, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs)
@@ -352,7 +420,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip MoBA 128k/1M and the decoupled-block 64k legs")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings"], default=None,
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings", "backward"], default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -398,6 +467,11 @@ def main():
         for wl, fn in (("moba_128k", run_moba), ("moba_1m", run_moba), ("nsa_prefill_64k_c32", run_nsa_leg)):
             rec.setdefault("more_configs", {})[wl] = run_side_leg(args, torch, nsa, workloads, inputs, wl, fn)
             log(f"{wl}: {rec['more_configs'][wl]['ms_per_step']} ms/step")
+    if not args.no_backward:
+        a = __import__("copy").copy(args)
+        a.steps, a.warmup = min(args.steps, 3), 1
+        rec["backward"] = run_backward(a, torch, nsa, workloads, inputs, args.workload)
+        log(f"backward: {rec['backward']['ms_per_step']} ms/step, phases {rec['backward']['phases_ms']}")
     if not args.no_decode:
         rec["decode"] = run_decode(args, torch, nsa, workloads, inputs)
         log(f"decode: {rec['decode']['ms_per_step']} ms/step")

@@ -102,7 +102,8 @@ typedef struct {
   /* Optional timing hook (NULL = none): n_phase_events hipEvent_t handles
    * owned by the caller.  nsa_forward records phase_events[0] on `stream`
    * before its first kernel and phase_events[i + 1] after its i-th kernel
-   * (as far as events are given); nsa_forward_phases names the kernels. */
+   * (as far as events are given); nsa_forward_phases names the kernels.
+   * nsa_backward does the same per kernel group (nsa_backward_phases). */
   void* const* phase_events;
   int32_t n_phase_events;
   /* Selection block size in tokens (0 means `block`): a multiple of
@@ -196,6 +197,13 @@ nsa_status nsa_backward(const void* q, const void* k, const void* v, const void*
 /* Workspace bytes nsa_backward needs for these params (0 if they are invalid
  * or outside its limits). */
 size_t nsa_backward_workspace_bytes(const nsa_params* params);
+
+/* Number of kernel groups nsa_backward times through params->phase_events
+ * (0 if the params are invalid or outside its limits); names[i]
+ * (i < max_names) receives a static name of group i.  nsa_backward records
+ * phase_events[0] before its first kernel and phase_events[i + 1] after
+ * group i, as far as events are given. */
+int32_t nsa_backward_phases(const nsa_params* params, const char** names, int32_t max_names);
 
 /* Number of kernels nsa_forward launches for these params (0 if they are
  * invalid); names[i] (i < max_names) receives a static name of kernel i. */

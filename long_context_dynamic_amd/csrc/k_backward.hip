@@ -11,15 +11,21 @@
 // and the compressed branch's key/value gradients reach each token of block
 // j as dk_cmp_j / 64.  The work splits by which side owns the sums:
 //
-//   images     paired-row and tiled-transposed copies of k, v and of the
-//              summaries, so that every matrix-op operand below is one
-//              contiguous 16-byte read.
+//   images     paired-row copies of k, v and of the summaries and tiled V^T
+//              copies, so that the global matrix-op operands below are
+//              contiguous 16-byte reads.
 //   k_bwd_q    one wave per (token, group), 16 heads as the matrix N:
 //              per branch, a statistics pass (log-sum-exp, output, dgamma)
-//              and a gradient pass that recomputes P and accumulates dq.
-//   lists      for every (group, block), the tokens that chose it, in token
-//              order (deterministic: per 256-token chunk histograms, column
-//              prefix sums, one ordered fill per chunk).
+//              and a gradient pass that recomputes P and accumulates dq
+//              (K^T operands by transposing reads of the wave's LDS copy of
+//              the chunk's K rows).
+//   lists      for every (group, block), the (token, slot) entries that
+//              chose it, in token order (deterministic: per 256-token chunk
+//              histograms, column prefix sums, one ordered fill per chunk).
+//   k_bwd_kv<KV_STAT>  the selected branch's softmax statistics from the
+//              key side: per entry and head the block's max, sum and
+//              sum of p * <dout, v> (a 16-byte record), so that the query
+//              side never streams the selected blocks twice.
 //   k_bwd_kv   one workgroup per 64 keys and a run of queries, 4 waves of 16
 //              keys each: queries are taken two tokens (32 head rows) at a
 //              time through LDS, and dk^T, dv^T accumulate in registers with
@@ -35,6 +41,7 @@
 #include "nsa_backward.h"
 #include "nsa_frag.h"
 #include "nsa_mfma.h"
+#include "nsa_paths.h"
 #include "nsa_prefill.h"
 
 namespace nsa {
@@ -160,7 +167,7 @@ __device__ __forceinline__ ChunkIter chunks_of(const BwArgs& a, int br, int64_t 
 }
 
 template <int DQ, int DV>
-__global__ void __launch_bounds__(256) k_bwd_q(BwArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_bwd_q(BwArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t g = blockIdx.x % a.G;
   const int64_t tg = (blockIdx.x / a.G) * 4 + wave;  // flat (b, t)
@@ -170,6 +177,9 @@ __global__ void __launch_bounds__(256) k_bwd_q(BwArgs a) {
   const float c2 = a.scale * kLog2e;
   const int64_t row = tg * a.H + g * 16 + lr;  // (b, t, head lr)
   const int64_t nrow = a.B * a.T * a.H;
+  constexpr int KS = DQ + 16;
+  __shared__ __align__(16) uint16_t ktile[4][32 * KS];  // per wave: the chunk's 32 K rows
+  uint16_t* kt = ktile[wave];
 
   bf16x8 qf[DQ / 32];
 #pragma unroll
@@ -199,6 +209,35 @@ __global__ void __launch_bounds__(256) k_bwd_q(BwArgs a) {
       continue;
     }
     gam[br] = gate_val(a, row, br, &dsig);
+    if (br == BR_SLC) {  // merge the key side's per-block records of this token's entries
+      float M = -INFINITY, L = 0.f, U = 0.f;
+      for (int i = 0; i < a.n; ++i) {
+        const int64_t e = (tg * a.G + g) * a.n + i;
+        const int j = a.idx[e];
+        if (!(j >= 0 && j < a.nbk && (int64_t)j * kBlk <= p)) continue;  // unlisted: no record
+        const f32x4 r = *(const f32x4*)(a.srec + (e * 16 + lr) * 4);
+        if (r[0] > M) {
+          const float f = fast_exp2(M - r[0]);  // 0 while M is -inf
+          L *= f;
+          U *= f;
+          M = r[0];
+        }
+        const float f = fast_exp2(r[0] - M);
+        L += r[1] * f;
+        U += r[2] * f;
+      }
+      if (L > 0.f) {
+        lse[br] = M + __log2f(L);
+        dd[br] = U / L;
+      }
+      if (lg == 0) {
+        a.stat[(br * 3 + 0) * nrow + row] = lse[br];
+        a.stat[(br * 3 + 1) * nrow + row] = dd[br];
+        a.stat[(br * 3 + 2) * nrow + row] = gam[br];
+        if (a.dgates) a.dgates[row * 3 + br] = dd[br] * dsig;
+      }
+      continue;
+    }
     const bool cmp = br == BR_CMP;
     const __amdgpu_buffer_rsrc_t kr = cmp ? rs(a.kcG, a.nbp, DQ) : rs(a.kG, a.Lp, DQ);
     const __amdgpu_buffer_rsrc_t vr = cmp ? rs(a.vcT, a.nbp, DV) : rs(a.vT, a.Lp, DV);
@@ -271,16 +310,23 @@ __global__ void __launch_bounds__(256) k_bwd_q(BwArgs a) {
     const bool cmp = br == BR_CMP;
     const __amdgpu_buffer_rsrc_t kr = cmp ? rs(a.kcG, a.nbp, DQ) : rs(a.kG, a.Lp, DQ);
     const __amdgpu_buffer_rsrc_t vgr = cmp ? rs(a.vcG, a.nbp, DV) : rs(a.vG, a.Lp, DV);
-    const __amdgpu_buffer_rsrc_t ktr = cmp ? rs(a.kcT, a.nbp, DQ) : rs(a.kT, a.Lp, DQ);
     ChunkIter it = chunks_of(a, br, b, t, g, p, lane);
     const float lb = lse[br], db = dd[br], gb = gam[br];
     for (int64_t kb = it.pop(); kb >= 0; kb = it.pop()) {
       KFrag<DQ> kf;
       KFrag<DV> vf;
-      VFrag<DQ> ktf;
       load_k<DQ>(kf, kr, kofs, kb, lr);
       load_k<DV>(vf, vgr, kofs, kb, lr);
-      load_v<DQ>(ktf, ktr, tofs, kb);
+      // the K fragments, back to rows (key - kb) of the wave's LDS tile, so
+      // that K^T operands come out of transposing reads
+      {
+        const int r0 = 8 * (lr >> 2) + (lr & 3);
+#pragma unroll
+        for (int ks = 0; ks < DQ / 32; ++ks) {
+          *(bf16x8*)(kt + r0 * KS + 32 * ks + 8 * lg) = kf.k0[ks];
+          *(bf16x8*)(kt + (r0 + 4) * KS + 32 * ks + 8 * lg) = kf.k1[ks];
+        }
+      }
       f32x4 s0, s1;
       qk_chunk_b<DQ>(kf, qf, s0, s1);
       mask_chunk(s0, s1, kb, it.klo, it.khi, lg);
@@ -294,7 +340,8 @@ __global__ void __launch_bounds__(256) k_bwd_q(BwArgs a) {
       }
       const bf16x8 dsf = pack8(s0, s1);
 #pragma unroll
-      for (int dt = 0; dt < DQ / 16; ++dt) dqa[dt] = mfma16(ktf.v[dt], dsf, dqa[dt]);
+      for (int dt = 0; dt < DQ / 16; ++dt)
+        dqa[dt] = mfma16(ld_vt_pair(kt, 8 * lg, 8 * lg + 4, 16 * dt, KS, lr), dsf, dqa[dt]);
     }
   }
   // dq^T: lane holds dims 16*dt + 4*lg + r of head lr
@@ -398,7 +445,8 @@ __global__ void __launch_bounds__(64) k_bwd_fill(BwArgs a) {
   for (int64_t t = c * kCountTok; t < t1; ++t) {
     const int64_t p = a.L - a.T + t;
     const int j = lane < a.n ? a.idx[((b * a.T + t) * a.G + g) * a.n + lane] : -1;
-    if (j >= 0 && j < nbs && (int64_t)j * kBlk <= p) a.lists[atomicAdd(&cur[j], 1)] = (int32_t)t;
+    if (j >= 0 && j < nbs && (int64_t)j * kBlk <= p)
+      a.lists[atomicAdd(&cur[j], 1)] = (int32_t)(((b * a.T + t) * a.G + g) * a.n + lane);
     __syncthreads();
   }
 }
@@ -409,7 +457,7 @@ __global__ void __launch_bounds__(64) k_bwd_fill(BwArgs a) {
 //   S  = Q K^T, dP = dout V^T           (A: 16 head rows of one token, from LDS)
 //   dv^T += dout^T (gamma P),  dk^T += Q^T dS   (contraction over the 32 head
 //          rows of two tokens: A from LDS by transposing reads)
-enum { KV_WIN = 0, KV_SLC = 1, KV_CMP = 2 };
+enum { KV_WIN = 0, KV_SLC = 1, KV_CMP = 2, KV_STAT = 3 };
 
 template <int DQ, int DV>
 struct KvLds {
@@ -419,19 +467,21 @@ struct KvLds {
 };
 
 template <int DQ, int DV, int MODE>
-__global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_bwd_kv(BwArgs a) {
   constexpr int QS = KvLds<DQ, DV>::QS, DS = KvLds<DQ, DV>::DS;
   constexpr int QC = 16 * DQ / 8, DC = 16 * DV / 8;   // 16-byte chunks of one token's q / dout rows
   constexpr int NCH = 2 * (QC + DC);
   constexpr int CPT = (NCH + 255) / 256;
   __shared__ __align__(16) KvLds<DQ, DV> sm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int br = MODE == KV_WIN ? BR_WIN : (MODE == KV_SLC ? BR_SLC : BR_CMP);
+  const int br = MODE == KV_WIN ? BR_WIN : (MODE == KV_CMP ? BR_CMP : BR_SLC);
+  constexpr bool LISTED = MODE == KV_SLC || MODE == KV_STAT;
+  __shared__ f32x4 red[4][2][16];  // KV_STAT: per wave, token and head: max, sum, sum p.dP
 
   // ---- work item: (b, g), the 64 keys, the query tokens ----
   int64_t b, g, key0;    // key0: first key (token position, or summary id)
   int64_t tfirst = 0, ntok = 0;  // window / compressed: token range
-  const int32_t* elist = nullptr;  // selected: this chunk's tokens
+  const int32_t* elist = nullptr;  // selected: this chunk's entries
   int64_t chunk_id = 0;
   if (MODE == KV_WIN) {
     const int64_t ntile = (a.L + 63) / 64;
@@ -460,7 +510,7 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
     if (hi <= lo) return;  // the reduce skips this chunk by the same rule
     tfirst = lo;
     ntok = hi - lo;
-  } else {
+  } else {  // KV_SLC, KV_STAT
     const int64_t nl = a.B * a.G * a.nbk;
     const int32_t total = a.chunk_off[nl];
     const int32_t w = (int32_t)blockIdx.x;
@@ -506,7 +556,7 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
   const int64_t npair = (ntok + 1) / 2;
   auto token_of = [&](int64_t i) -> int64_t {  // i-th token of the work item, or -1
     if (i >= ntok) return -1;
-    return MODE == KV_SLC ? (int64_t)elist[i] : tfirst + i;
+    return LISTED ? ((int64_t)elist[i] / (a.n * a.G)) % a.T : tfirst + i;
   };
 
   // register prefetch of one pair: q and dout rows (all threads), stats (per lane)
@@ -532,13 +582,15 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
       }
       pre[i] = val;
     }
+    if (MODE != KV_STAT) {
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk) {
+      for (int tk = 0; tk < 2; ++tk) {
 #pragma unroll
-      for (int f = 0; f < 3; ++f) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        if (tt[tk] >= 0) s = *(const f32x4*)(a.stat + (br * 3 + f) * nrow + (b * a.T + tt[tk]) * a.H + g * 16 + 4 * lg);
-        pst[tk][f] = s;
+        for (int f = 0; f < 3; ++f) {
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+          if (tt[tk] >= 0) s = *(const f32x4*)(a.stat + (br * 3 + f) * nrow + (b * a.T + tt[tk]) * a.H + g * 16 + 4 * lg);
+          pst[tk][f] = s;
+        }
       }
     }
   };
@@ -572,6 +624,46 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
     __syncthreads();
     if (pi + 1 < npair) fetch(pi + 1);
 
+    if (MODE == KV_STAT) {
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DQ / 32; ++ks) s = mfma16(ld8(sm.qs[tk] + lr * QS + 8 * lg + 32 * ks), kf[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks) dp = mfma16(ld8(sm.ds[tk] + lr * DS + 8 * lg + 32 * ks), vf[ks], dp);
+        const bool vis = key_ok && tt[tk] >= 0 && key <= a.L - a.T + tt[tk];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // head 4*lg + r: reduce over the wave's 16 keys (the lanes of a row)
+          const float z = vis ? s[r] * c2 : -INFINITY;
+          const float mx = row_max16(z);
+          const float e = vis ? fast_exp2(z - mx) : 0.f;
+          const float l = row_sum16(e), u = row_sum16(e * dp[r]);
+          if (lr == 0) red[wave][tk][4 * lg + r] = f32x4{mx, l, u, 0.f};
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < 32) {  // combine the four waves: one (token, head) per thread
+        const int tk = threadIdx.x >> 4, hh = threadIdx.x & 15;
+        const int64_t i = 2 * pi + tk;
+        if (i < ntok) {
+          float M = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][tk][hh][0]);
+          float L = 0.f, U = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x4 r = red[w][tk][hh];
+            const float f = r[0] == -INFINITY ? 0.f : fast_exp2(r[0] - M);
+            L += r[1] * f;
+            U += r[2] * f;
+          }
+          *(f32x4*)(a.srec + ((int64_t)elist[i] * 16 + hh) * 4) = f32x4{M, L, U, 0.f};
+        }
+      }
+      continue;
+    }
+
     f32x4 pg[2], dsv[2];
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk) {
@@ -585,7 +677,7 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
       if (vis) {
         const int64_t pp = a.L - a.T + tt[tk];
         if (MODE == KV_WIN) vis = key <= pp && key > pp - a.w;
-        else if (MODE == KV_SLC) vis = key <= pp;
+        else if (LISTED) vis = key <= pp;
         else vis = (key + 1) * kBlk <= pp + 1;
       }
 #pragma unroll
@@ -611,6 +703,7 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
   }
 
   // ---- write: lane holds dims 16*dt + 4*lg + r of key lr ----
+  if (MODE == KV_STAT) return;
   if (MODE == KV_WIN) {
     if (!key_ok) return;
     float* dkr = a.dk + ((b * a.L + key) * a.G + g) * DQ + 4 * lg;
@@ -629,51 +722,84 @@ __global__ void __launch_bounds__(256) k_bwd_kv(BwArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per (b, g, 64-token tile): dk, dv of its tokens = window part
-// (already in dk, dv when that branch is on) + the selected partials of the
-// tile's block + the block's summary gradient / 64 (the mean's gradient).
+// Summary gradients: dkc[b, g, j, :] = (sum over the token chunks of j's
+// tile, in chunk order) / 64, one thread per (summary, column).
+template <int DQ, int DV>
+__global__ void __launch_bounds__(256) k_bwd_cmpsum(BwArgs a) {
+  constexpr int E = DQ + DV;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // ((b * G + g) * nb + j) * E + e
+  if (i >= a.B * a.G * a.nb * E) return;
+  const int64_t e = i % E, j = (i / E) % a.nb, bg = i / (E * a.nb);
+  const int64_t J = j / 64, jj = j % 64;
+  float cm = 0.f;
+  for (int64_t c = 0; c < a.nC; ++c) {
+    int64_t lo, hi;
+    cmp_chunk_range(a, J, c, lo, hi);
+    if (hi > lo) cm += a.part_c[(((bg * a.nJ + J) * a.nC + c) * 64 + jj) * E + e];
+  }
+  a.dkc[i] = cm * (1.f / kBlk);
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv of each 64-token tile = window part (already in dk, dv when that
+// branch is on) + the selected partials of the tile's block, summed in chunk
+// order + the block's summary gradient / 64.  Eight workgroups per tile, each
+// on one eighth of the 64 x (DQ + DV) elements, so that the long lists (the
+// forced first block is chosen by every token) are read by many waves.
+constexpr int kReduceSlices = 8;
+
 template <int DQ, int DV>
 __global__ void __launch_bounds__(256) k_bwd_reduce(BwArgs a) {
   constexpr int E = DQ + DV;
+  constexpr int NE = 64 * E / (256 * kReduceSlices);  // elements per thread (E is a multiple of 64)
   const int64_t ntile = (a.L + 63) / 64;
-  const int64_t K = blockIdx.x % ntile;
-  const int64_t bg = blockIdx.x / ntile;
+  const int slice = blockIdx.x % kReduceSlices;
+  const int64_t K = (blockIdx.x / kReduceSlices) % ntile;
+  const int64_t bg = blockIdx.x / (kReduceSlices * ntile);
   const int64_t g = bg % a.G, b = bg / a.G;
   const bool win = (a.flags & NSA_F_WIN) && a.w > 0;
   const bool slc = (a.flags & NSA_F_SLC) != 0;  // K < nbk always
   const bool cmp = (a.flags & NSA_F_CMP) && K < a.nb;
-  int64_t c_lo = 0, c_hi = 0;
+  const int x0 = slice * (64 * E / kReduceSlices) + threadIdx.x;  // element x0 + 256 m of the tile
+  float acc[NE];
+#pragma unroll
+  for (int m = 0; m < NE; ++m) acc[m] = 0.f;
   if (slc) {
-    c_lo = a.chunk_off[bg * a.nbk + K];
-    c_hi = a.chunk_off[bg * a.nbk + K + 1];
-  }
-  for (int e = threadIdx.x; e < E; e += 256) {
-    float cm = 0.f;
-    if (cmp) {
-      const int64_t J = K / 64, jj = K % 64;
-      for (int64_t c = 0; c < a.nC; ++c) {
-        int64_t lo, hi;
-        cmp_chunk_range(a, J, c, lo, hi);
-        if (hi > lo) cm += a.part_c[(((bg * a.nJ + J) * a.nC + c) * 64 + jj) * E + e];
+    const int64_t c_lo = a.chunk_off[bg * a.nbk + K], c_hi = a.chunk_off[bg * a.nbk + K + 1];
+    int64_t ch = c_lo;
+    for (; ch + 1 < c_hi; ch += 2) {  // two chunks' loads in flight
+      const float* p0 = a.part_s + ch * 64 * E + x0;
+      const float* p1 = p0 + 64 * E;
+      float v0[NE], v1[NE];
+#pragma unroll
+      for (int m = 0; m < NE; ++m) {
+        v0[m] = p0[256 * m];
+        v1[m] = p1[256 * m];
       }
-      cm *= 1.f / kBlk;
+#pragma unroll
+      for (int m = 0; m < NE; ++m) acc[m] += v0[m] + v1[m];
     }
-    for (int i = 0; i < 64; ++i) {
-      const int64_t s = K * 64 + i;
-      if (s >= a.L) break;
-      float* dst = e < DQ ? a.dk + ((b * a.L + s) * a.G + g) * DQ + e : a.dv + ((b * a.L + s) * a.G + g) * DV + (e - DQ);
-      float x = win ? *dst : 0.f;
-      x += cm;
-      for (int64_t ch = c_lo; ch < c_hi; ++ch) x += a.part_s[(ch * 64 + i) * E + e];
-      *dst = x;
+    if (ch < c_hi) {
+      const float* p0 = a.part_s + ch * 64 * E + x0;
+#pragma unroll
+      for (int m = 0; m < NE; ++m) acc[m] += p0[256 * m];
     }
+  }
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int x = x0 + 256 * m, i = x / E, e = x % E;
+    const int64_t s = K * 64 + i;
+    if (s >= a.L) continue;
+    float* dst = e < DQ ? a.dk + ((b * a.L + s) * a.G + g) * DQ + e : a.dv + ((b * a.L + s) * a.G + g) * DV + (e - DQ);
+    const float cm = cmp ? a.dkc[(bg * a.nb + K) * E + e] : 0.f;
+    *dst = (win ? *dst : 0.f) + cm + acc[m];
   }
 }
 
 // ---------------------------------------------------------------------------
 struct BwPlan {
   size_t total = 0;
-  size_t kc, vc, kG, vG, kT, vT, kcG, vcG, kcT, vcT, stat, cnt, tot, offsets, chunk_off, lists, part_s, part_c;
+  size_t kc, vc, kG, vG, vT, kcG, vcG, vcT, dkc, srec, stat, cnt, tot, offsets, chunk_off, lists, part_s, part_c;
 };
 
 BwPlan plan(const Prob& P) {
@@ -693,13 +819,12 @@ BwPlan plan(const Prob& P) {
   w.vc = take(P.B * P.nb * P.G * P.dv * 2);
   w.kG = take(P.B * P.G * Lp * P.dq * 2);
   w.vG = take(P.B * P.G * Lp * P.dv * 2);
-  w.kT = take(P.B * P.G * Lp * P.dq * 2);
   w.vT = take(P.B * P.G * Lp * P.dv * 2);
   w.kcG = take(P.B * P.G * nbp * P.dq * 2);
   w.vcG = take(P.B * P.G * nbp * P.dv * 2);
-  w.kcT = take(P.B * P.G * nbp * P.dq * 2);
   w.vcT = take(P.B * P.G * nbp * P.dv * 2);
   w.stat = take((size_t)9 * P.B * P.T * P.H * 4);
+  w.srec = take((size_t)(ne > 0 ? ne : 1) * 16 * 16);
   w.cnt = take((size_t)P.B * P.G * nct * nbk * 4);
   w.tot = take((nl + 1) * 4);
   w.offsets = take((nl + 1) * 4);
@@ -707,33 +832,46 @@ BwPlan plan(const Prob& P) {
   w.lists = take((ne > 0 ? ne : 1) * 4);
   w.part_s = take((size_t)chunks * 64 * (P.dq + P.dv) * 4);
   w.part_c = take((size_t)P.B * P.G * nJ * nC * 64 * (P.dq + P.dv) * 4);
+  w.dkc = take((size_t)P.B * P.G * P.nb * (P.dq + P.dv) * 4);
   return w;
 }
 
 template <int DQ, int DV>
-hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s) {
+hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
   const int64_t nl = P.B * P.G * a.nbk;
   const unsigned gq = (unsigned)(P.G * ((P.B * P.T + 3) / 4));
-  k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
   const bool slc = P.has(NSA_F_SLC);
+  const int64_t ne = P.B * P.T * P.G * P.n;
+  const int64_t chunks_max = (ne + kListChunk - 1) / kListChunk + nl;  // surplus workgroups exit at once
   if (slc) {
     const size_t lds = (size_t)a.nbk * 4;
     k_bwd_count<<<(unsigned)(P.B * P.G * a.nct), kCountTok, lds, s>>>(a);
     k_bwd_colscan<<<(unsigned)((nl + 255) / 256), 256, 0, s>>>(a);
     k_bwd_scan<<<1, 1024, 0, s>>>(a, nl);
     k_bwd_fill<<<(unsigned)(P.B * P.G * a.nct), 64, lds, s>>>(a);
+    ph.mark();
+    k_bwd_kv<DQ, DV, KV_STAT><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    ph.mark();
   }
+  k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
+  ph.mark();
   const int64_t ntile = (P.L + 63) / 64;
-  if (P.has(NSA_F_WIN) && P.w > 0) k_bwd_kv<DQ, DV, KV_WIN><<<(unsigned)(P.B * P.G * ntile), 256, 0, s>>>(a);
-  if (slc) {
-    const int64_t ne = P.B * P.T * P.G * P.n;
-    const int64_t chunks_max = (ne + kListChunk - 1) / kListChunk + nl;  // surplus workgroups exit at once
-    k_bwd_kv<DQ, DV, KV_SLC><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+  if (P.has(NSA_F_WIN) && P.w > 0) {
+    k_bwd_kv<DQ, DV, KV_WIN><<<(unsigned)(P.B * P.G * ntile), 256, 0, s>>>(a);
+    ph.mark();
   }
-  if (P.has(NSA_F_CMP) && P.nb > 0)
+  if (slc) {
+    k_bwd_kv<DQ, DV, KV_SLC><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    ph.mark();
+  }
+  if (P.has(NSA_F_CMP) && P.nb > 0) {
     k_bwd_kv<DQ, DV, KV_CMP><<<(unsigned)(P.B * P.G * a.nJ * a.nC), 256, 0, s>>>(a);
-  k_bwd_reduce<DQ, DV><<<(unsigned)(P.B * P.G * ntile), 256, 0, s>>>(a);
-  return hipGetLastError();
+    k_bwd_cmpsum<DQ, DV><<<(unsigned)((P.B * P.G * P.nb * (DQ + DV) + 255) / 256), 256, 0, s>>>(a);
+    ph.mark();
+  }
+  k_bwd_reduce<DQ, DV><<<(unsigned)(P.B * P.G * ntile * kReduceSlices), 256, 0, s>>>(a);
+  ph.mark();
+  return ph.err != hipSuccess ? ph.err : hipGetLastError();
 }
 
 }  // namespace
@@ -746,9 +884,26 @@ bool backward_ok(const Prob& P) {
 
 size_t backward_workspace_bytes(const Prob& P) { return backward_ok(P) ? plan(P).total : 0; }
 
+int backward_phase_names(const Prob& P, const char** names, int max_names) {
+  const char* list[10];
+  int n = 0;
+  list[n++] = "bwd_images";
+  if (P.has(NSA_F_SLC)) {
+    list[n++] = "bwd_lists";
+    list[n++] = "bwd_kv_selected_stats";
+  }
+  list[n++] = "bwd_q";
+  if (P.has(NSA_F_WIN) && P.w > 0) list[n++] = "bwd_kv_window";
+  if (P.has(NSA_F_SLC)) list[n++] = "bwd_kv_selected";
+  if (P.has(NSA_F_CMP) && P.nb > 0) list[n++] = "bwd_kv_compressed";
+  list[n++] = "bwd_reduce";
+  for (int i = 0; i < n && i < max_names; ++i) names[i] = list[i];
+  return n;
+}
+
 hipError_t run_backward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
                         const int32_t* idx, const void* dout, float* dq, float* dk, float* dv, float* dgates,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, Phases& ph) {
   const BwPlan w = plan(P);
   char* base = (char*)ws;
   BwArgs a;
@@ -764,13 +919,12 @@ hipError_t run_backward(const Prob& P, const void* q, const void* k, const void*
   a.vc = vc;
   a.kG = (const uint16_t*)(base + w.kG);
   a.vG = (const uint16_t*)(base + w.vG);
-  a.kT = (const uint16_t*)(base + w.kT);
   a.vT = (const uint16_t*)(base + w.vT);
   a.kcG = (const uint16_t*)(base + w.kcG);
   a.vcG = (const uint16_t*)(base + w.vcG);
-  a.kcT = (const uint16_t*)(base + w.kcT);
   a.vcT = (const uint16_t*)(base + w.vcT);
   a.stat = (float*)(base + w.stat);
+  a.srec = (float*)(base + w.srec);
   a.cnt = (int32_t*)(base + w.cnt);
   a.tot = (int32_t*)(base + w.tot);
   a.offsets = (int32_t*)(base + w.offsets);
@@ -778,6 +932,7 @@ hipError_t run_backward(const Prob& P, const void* q, const void* k, const void*
   a.lists = (int32_t*)(base + w.lists);
   a.part_s = (float*)(base + w.part_s);
   a.part_c = (float*)(base + w.part_c);
+  a.dkc = (float*)(base + w.dkc);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -794,20 +949,20 @@ hipError_t run_backward(const Prob& P, const void* q, const void* k, const void*
   a.scale = P.scale;
 
   // summaries and the operand images
+  ph.mark();
   hipError_t e = launch_pool(P, k, v, kc, vc, s);
   if (e != hipSuccess) return e;
   const int64_t B = P.B, G = P.G;
   if ((e = launch_group_major(k, (void*)a.kG, B, P.L, G, (int)P.dq, s)) != hipSuccess) return e;
   if ((e = launch_group_major(v, (void*)a.vG, B, P.L, G, (int)P.dv, s)) != hipSuccess) return e;
-  if ((e = launch_transpose(k, (void*)a.kT, B, P.L, a.Lp, G, (int)P.dq, s)) != hipSuccess) return e;
   if ((e = launch_transpose(v, (void*)a.vT, B, P.L, a.Lp, G, (int)P.dv, s)) != hipSuccess) return e;
   if (P.nb > 0) {
     if ((e = launch_group_major(kc, (void*)a.kcG, B, P.nb, G, (int)P.dq, s)) != hipSuccess) return e;
     if ((e = launch_group_major(vc, (void*)a.vcG, B, P.nb, G, (int)P.dv, s)) != hipSuccess) return e;
-    if ((e = launch_transpose(kc, (void*)a.kcT, B, P.nb, a.nbp, G, (int)P.dq, s)) != hipSuccess) return e;
     if ((e = launch_transpose(vc, (void*)a.vcT, B, P.nb, a.nbp, G, (int)P.dv, s)) != hipSuccess) return e;
   }
-#define CALL_BW(DQ, DV) return launch_t<DQ, DV>(P, a, s)
+  ph.mark();
+#define CALL_BW(DQ, DV) return launch_t<DQ, DV>(P, a, s, ph)
   if (P.dq == 192 && P.dv == 128) CALL_BW(192, 128);
   if (P.dq == 128 && P.dv == 128) CALL_BW(128, 128);
   if (P.dq == 64 && P.dv == 64) CALL_BW(64, 64);

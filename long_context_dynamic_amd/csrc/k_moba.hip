@@ -42,26 +42,6 @@ template <int D> constexpr int rec_bytes() { return 2 * D + 16; }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// Row reductions over the 16 lanes of a DPP row (lanes 16*lg .. 16*lg + 15).
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
-  x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
-  x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
-  return fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(dpp_i<kDppXor1>(__float_as_int(x)));
-  x += __int_as_float(dpp_i<kDppXor2>(__float_as_int(x)));
-  x += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x)));
-  return x + __int_as_float(dpp_i<kDppMirror>(__float_as_int(x)));
-}
-__device__ __forceinline__ int row_min16(int x) {
-  x = min(x, dpp_i<kDppXor1>(x));
-  x = min(x, dpp_i<kDppXor2>(x));
-  x = min(x, dpp_i<kDppHalfMirror>(x));
-  return min(x, dpp_i<kDppMirror>(x));
-}
-
 // Descending list insertion without branches: x goes after equal values (the
 // earlier block keeps a tie); -inf changes nothing.
 template <int LS>

@@ -143,8 +143,19 @@ nsa_status nsa_backward(const void* q, const void* k, const void* v, const void*
   if (!nsa::backward_ok(P)) return NSA_ERR_UNSUPPORTED;
   const size_t need = nsa::backward_workspace_bytes(P);
   if (!ptr_ok(p->workspace) || p->workspace_bytes < need) return NSA_ERR_WORKSPACE;
+  if (p->n_phase_events < 0 || (p->n_phase_events > 0 && !p->phase_events)) return NSA_ERR_INVALID_ARG;
+  nsa::Phases ph;
+  ph.ev = p->phase_events;
+  ph.n = p->phase_events ? p->n_phase_events : 0;
+  ph.s = (hipStream_t)p->stream;
   return hip_status(nsa::run_backward(P, q, k, v, gates, idx, dout, dq, dk, dv, dgates, p->workspace,
-                                      (hipStream_t)p->stream));
+                                      (hipStream_t)p->stream, ph));
+}
+
+int32_t nsa_backward_phases(const nsa_params* p, const char** names, int32_t max_names) {
+  Prob P;
+  if (describe(p, &P) != NSA_OK || !nsa::backward_ok(P)) return 0;
+  return nsa::backward_phase_names(P, names, names ? max_names : 0);
 }
 
 int32_t nsa_forward_phases(const nsa_params* p, const char** names, int32_t max_names) {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "nsa_internal.h"
+#include "nsa_paths.h"
 
 namespace nsa {
 
@@ -17,20 +18,20 @@ struct BwArgs {
   const uint16_t* vc;     // [B, nb, G, DV]
   const uint16_t* kG;     // paired-row images [B, G, Lp, D] of k, v
   const uint16_t* vG;
-  const uint16_t* kT;     // tiled transposes [B, G, Lp / 32, D, 32] of k, v
-  const uint16_t* vT;
-  const uint16_t* kcG;    // the same four images of the summaries (nbp rows)
+  const uint16_t* vT;     // tiled transpose [B, G, Lp / 32, DV, 32] of v
+  const uint16_t* kcG;    // the same three images of the summaries (nbp rows)
   const uint16_t* vcG;
-  const uint16_t* kcT;
   const uint16_t* vcT;
   float* stat;            // [3 branches][3: lse (log2 units), <dout, O_b>, gate][B*T*H]
   int32_t* cnt;           // [B, G, nct, nbk] entries per (256-token chunk, block)
   int32_t* tot;           // [B*G*nbk + 1] entries per list
   int32_t* offsets;       // [B*G*nbk + 1] list starts
   int32_t* chunk_off;     // [B*G*nbk + 1] first work chunk of each list
-  int32_t* lists;         // tokens, grouped by (b, g, block), in token order
+  int32_t* lists;         // entries ((b * T + t) * G + g) * n + slot, grouped by (b, g, block), in token order
+  float* srec;            // [entries][16 heads][4]: selected block's max (log2 units), sum, sum p.dP, 0
   float* part_s;          // [chunks][64][DQ + DV] selected-branch key gradients
   float* part_c;          // [B, G, nJ, nC][64][DQ + DV] compressed-branch summary gradients
+  float* dkc;             // [B, G, nb][DQ + DV] summary gradients / 64
   float* dq;              // [B, T, H, DQ]
   float* dk;              // [B, L, G, DQ]
   float* dv;              // [B, L, G, DV]
@@ -48,8 +49,10 @@ struct BwArgs {
 // d_v in {64,128}, top_k <= 32.
 bool backward_ok(const Prob& P);
 size_t backward_workspace_bytes(const Prob& P);
+// Names of the kernel groups run_backward times (one event after each), in order.
+int backward_phase_names(const Prob& P, const char** names, int max_names);
 hipError_t run_backward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
                         const int32_t* idx, const void* dout, float* dq, float* dk, float* dv, float* dgates,
-                        void* ws, hipStream_t s);
+                        void* ws, hipStream_t s, Phases& ph);
 
 }  // namespace nsa

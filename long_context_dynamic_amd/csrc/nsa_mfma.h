@@ -104,6 +104,26 @@ constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
 constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
 
+// Row reductions over the 16 lanes of a DPP row (lanes 16*lg .. 16*lg + 15).
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
+  return fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(dpp_i<kDppXor1>(__float_as_int(x)));
+  x += __int_as_float(dpp_i<kDppXor2>(__float_as_int(x)));
+  x += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x)));
+  return x + __int_as_float(dpp_i<kDppMirror>(__float_as_int(x)));
+}
+__device__ __forceinline__ int row_min16(int x) {
+  x = min(x, dpp_i<kDppXor1>(x));
+  x = min(x, dpp_i<kDppXor2>(x));
+  x = min(x, dpp_i<kDppHalfMirror>(x));
+  return min(x, dpp_i<kDppMirror>(x));
+}
+
 // Maximum over all 64 lanes, returned in every lane.
 __device__ __forceinline__ float wave_allmax(float x) {
   x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));

@@ -21,6 +21,7 @@ STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "N
 
 EXPORTS = ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
            "nsa_forward_phases", "nsa_workspace_bytes", "nsa_backward", "nsa_backward_workspace_bytes",
+           "nsa_backward_phases",
            "nsa_status_str")
 
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, P]
         L.nsa_backward_workspace_bytes.argtypes = [P]
         L.nsa_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.nsa_backward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
+        L.nsa_backward_phases.restype = ctypes.c_int32
         L.nsa_status_str.argtypes = [ctypes.c_int]
         L.nsa_status_str.restype = ctypes.c_char_p
         for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_backward"):
@@ -248,8 +251,16 @@ def backward_workspace_bytes(prob: dict) -> int:
     return int(lib().nsa_backward_workspace_bytes(ctypes.byref(p)))
 
 
+def backward_phases(prob: dict) -> list:
+    """Names of the kernel groups nsa_backward times, in order."""
+    p = params(prob, stream=_NoStream)
+    names = (ctypes.c_char_p * 16)()
+    n = lib().nsa_backward_phases(ctypes.byref(p), names, 16)
+    return [names[i].decode() for i in range(min(n, 16))]
+
+
 def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, dgates=None,
-             want_dgates=True, workspace=None, stream=None):
+             want_dgates=True, workspace=None, stream=None, events=None):
     """Gradients of nsa_forward on the selection idx: (dq, dk, dv, dgates), fp32."""
     s, dt = _shapes(prob), torch_dtype(prob)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", dout)):
@@ -270,6 +281,12 @@ def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, d
     if workspace is None:
         workspace = torch.empty(max(backward_workspace_bytes(prob), 256), dtype=torch.uint8, device=dev)
     p = params(prob, workspace=workspace, stream=stream)
+    if events is not None:  # torch.cuda.Event list: recorded around each kernel group
+        for e in events:
+            if not e.cuda_event:
+                e.record()
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        p.phase_events, p.n_phase_events = handles, len(events)
     _call("nsa_backward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), idx.data_ptr(),
           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dgates), ctypes.byref(p))
     return dq, dk, dv, dgates
