@@ -162,6 +162,18 @@ def forward(prob, q, k, v, gates, idx, rounded=True):
     return out, O
 
 
+def _branch_grads(qh, doh, K, V, gb, c):
+    """One (row, group, branch): the softmax over the key set and the
+    gradient terms.  Returns (dq part [hpg, dqk], dK [n, dqk], dV [n, dv],
+    dgamma [hpg])."""
+    P = _softmax_rows(c * qh @ K.T)                # [hpg, n]
+    O = P @ V                                      # [hpg, dv]
+    dgb = np.sum(doh * O, axis=1)                  # [hpg]
+    dP = gb * (doh @ V.T)                          # [hpg, n]
+    dS = P * (dP - gb * dgb[:, None])
+    return c * dS @ K, c * dS.T @ qh, P.T @ (gb * doh), dgb
+
+
 def backward(prob, q, k, v, gates, idx, dout, rounded=True):
     """Gradients (dq [B,T,H,d_qk], dk [B,L,G,d_qk], dv [B,L,G,d_v],
     dgates [B,T,H,3] or None), float64, on the GIVEN selection idx."""
@@ -185,7 +197,6 @@ def backward(prob, q, k, v, gates, idx, dout, rounded=True):
         for t in range(T):
             for g in range(G):
                 hs = slice(g * hpg, (g + 1) * hpg)
-                qh, doh = qq[b, t, hs], do[b, t, hs]
                 sets = key_sets(prob, idx, b, t, g)
                 for br in on:
                     s_ids = sets[br]
@@ -193,16 +204,10 @@ def backward(prob, q, k, v, gates, idx, dout, rounded=True):
                         continue
                     K = kc[b, s_ids, g] if br == 0 else kk[b, s_ids, g]
                     V = vc[b, s_ids, g] if br == 0 else vv[b, s_ids, g]
-                    P = _softmax_rows(c * qh @ K.T)                # [hpg, n]
-                    O = P @ V                                      # [hpg, dv]
-                    gb = gam[b, t, hs, br][:, None]                # [hpg, 1]
-                    dgb = np.sum(doh * O, axis=1)                  # [hpg]
+                    dqp, dK, dV, dgb = _branch_grads(qq[b, t, hs], do[b, t, hs], K, V,
+                                                     gam[b, t, hs, br][:, None], c)
                     dgam[b, t, hs, br] = dgb
-                    dP = gb * (doh @ V.T)                          # [hpg, n]
-                    dS = P * (dP - gb * dgb[:, None])
-                    dq[b, t, hs] += c * dS @ K
-                    dK = c * dS.T @ qh                             # [n, dqk]
-                    dV = P.T @ (gb * doh)                          # [n, dv]
+                    dq[b, t, hs] += dqp
                     if br == 0:
                         dkc[b, s_ids, g] += dK
                         dvc[b, s_ids, g] += dV
@@ -219,3 +224,54 @@ def backward(prob, q, k, v, gates, idx, dout, rounded=True):
             if br not in on:
                 dgates[..., br] = 0.0
     return dq, dk, dvv, dgates
+
+
+def query_grads(prob, q, k, v, gates, idx, dout, rows, kc=None, vc=None):
+    """dq [R, H, d_qk] and dgates [R, H, 3] (or None) of the listed flat rows
+    b * T + t alone -- the query-side terms of backward(), which depend on
+    nothing but the row's own key sets.  kc, vc: float64 summaries as pooled()
+    returns them (computed when omitted)."""
+    B, T, L, G, hpg, bs, sb = _shapes(prob)
+    H, dqk, dv = G * hpg, prob["d_qk"], prob["d_v"]
+    c = _scale(prob)
+    if kc is None or vc is None:
+        kc, vc = pooled(prob, k, v, True)
+    on = _branches(prob)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((len(rows), H, dqk))
+    dgam = np.zeros((len(rows), H, 3))
+    dsig_rows = np.zeros((len(rows), H, 3))
+    for ri, r in enumerate(rows):
+        b, t = int(r) // T, int(r) % T
+        qr = _widen(q[b, t], prob)
+        dor = _widen(dout[b, t], prob).reshape(H, dv)
+        if gates is None:
+            gam = np.zeros((H, 3))
+            gam[:, on[0]] = 1.0
+        else:
+            x = _widen(gates[b, t], prob).reshape(H, 3)
+            if prob["gate_logits"]:
+                gam = 1.0 / (1.0 + np.exp(-x))
+                dsig_rows[ri] = gam * (1.0 - gam)
+            else:
+                gam = x
+                dsig_rows[ri] = 1.0
+        for g in range(G):
+            hs = slice(g * hpg, (g + 1) * hpg)
+            sets = key_sets(prob, idx, b, t, g)
+            for br in on:
+                s_ids = sets[br]
+                if len(s_ids) == 0:
+                    continue
+                K = kc[b, s_ids, g] if br == 0 else _widen(k[b, s_ids, g], prob)
+                V = vc[b, s_ids, g] if br == 0 else _widen(v[b, s_ids, g], prob)
+                dqp, _, _, dgb = _branch_grads(qr[hs], dor[hs], K, V, gam[hs, br][:, None], c)
+                dq[ri, hs] += dqp
+                dgam[ri, hs, br] = dgb
+    dgates = None
+    if gates is not None:
+        dgates = dgam * dsig_rows
+        for br in range(3):
+            if br not in on:
+                dgates[..., br] = 0.0
+    return dq, dgates

@@ -174,3 +174,15 @@ def test_compressed_branch_is_attention_over_block_means():
     np.testing.assert_allclose(dq[0], qt.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dk[0, :, 0], kt.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dv[0, :, 0], vt.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("gate_logits", [0, 1])
+def test_query_grads_of_chosen_rows_equal_the_full_backward(gate_logits):
+    prob = _tiny(gate_logits=gate_logits, q_len=30, kv_len=52)
+    q, k, v, gates, dout = _inputs64(prob, seed=12)
+    idx = _selection(prob, q, k, v)
+    dq, _, _, dg = BW.backward(prob, q, k, v, gates, idx, dout)
+    rows = np.array([0, 7, 29])
+    dq_r, dg_r = BW.query_grads(prob, q, k, v, gates, idx, dout, rows)
+    np.testing.assert_allclose(dq_r, dq.reshape(-1, *dq.shape[2:])[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dg_r, dg.reshape(-1, *dg.shape[2:])[rows], rtol=0, atol=1e-12)
