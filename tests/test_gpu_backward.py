@@ -97,3 +97,64 @@ def test_backward_is_deterministic():
     b = _run_gpu(prob, x, idx)
     for ga, gb in zip(a, b):
         assert np.array_equal(ga, gb)
+
+
+def _random_selection(prob, seed=0):
+    """A valid selection for every row: the forced blocks, then distinct
+    random complete blocks before the query (the structure a top-k choice
+    has; the backward takes any such selection)."""
+    rng = np.random.default_rng(seed)
+    B, T, L, G, n = prob["batch"], prob["q_len"], prob["kv_len"], prob["n_groups"], prob["top_k"]
+    idx = np.full((B, T, G, n), -1, dtype=np.int32)
+    for t in range(T):
+        p = L - T + t
+        nvis = min((p + 1) // 64, L // 64)
+        forced = sorted({0, p // 64})
+        cand = np.setdiff1d(np.arange(nvis), forced)
+        for b in range(B):
+            for g in range(G):
+                pick = rng.choice(cand, size=min(n - len(forced), len(cand)), replace=False) if len(cand) else []
+                row = np.sort(np.concatenate([np.array(forced), np.asarray(pick, dtype=np.int64)]))
+                idx[b, t, g, :len(row)] = row
+    return idx
+
+
+@pytest.mark.gpu
+def test_backward_full_size_64k_sampled_rows_and_sums():
+    """The 64k workload as bench.py times it: dq and dgates of sampled rows
+    against the oracle's query-side terms, and two sums over every key that
+    hold at any size (key gradients sum to zero per group; value gradients
+    sum to the gated upstream gradient of all rows)."""
+    import torch
+    prob = workloads.get("nsa_prefill_64k")
+    print("[case] backward full size nsa_prefill_64k", flush=True)
+    x = inputs.generate(prob, want=("q", "k", "v", "gates", "dout"))
+    idx = _random_selection(prob, seed=1)
+    d = {k: nsa.to_device(a, prob) for k, a in x.items()}
+    idx_t = torch.from_numpy(idx).cuda()
+    dq, dk, dv, dg = nsa.backward(prob, d["q"], d["k"], d["v"], d["gates"], idx_t, d["dout"])
+    torch.cuda.synchronize()
+    rows = U.sample_rows(prob, 24, seed=3)
+    ref_dq, ref_dg = BW.query_grads(prob, x["q"], x["k"], x["v"], x["gates"], idx, x["dout"], rows)
+    got_dq = dq.reshape(-1, *dq.shape[2:])[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    got_dg = dg.reshape(-1, *dg.shape[2:])[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    _compare("64k sampled dq", got_dq, ref_dq)
+    _compare("64k sampled dgates", got_dg, ref_dg)
+    # sums over all keys, per group (fp64 on the device)
+    G, hpg, T, L = prob["n_groups"], prob["heads_per_group"], prob["q_len"], prob["kv_len"]
+    sk = dk.double().sum(dim=1)[0].cpu().numpy()              # [G, dqk]
+    ak = dk.double().abs().sum(dim=1)[0].cpu().numpy()
+    sv = dv.double().sum(dim=1)[0].cpu().numpy()              # [G, dv]
+    gam = inputs.bf16_bits_to_f32(x["gates"][0]).astype(np.float64)  # [T, H, 3]
+    pos = L - T + np.arange(T)
+    w = gam[:, :, 1] + gam[:, :, 2] + gam[:, :, 0] * (pos >= 63)[:, None]  # rows whose sets are not empty
+    want = np.zeros_like(sv)
+    for g in range(G):
+        for c0 in range(0, T, 8192):
+            dob = inputs.bf16_bits_to_f32(x["dout"][0, c0:c0 + 8192, g * hpg:(g + 1) * hpg]).astype(np.float64)
+            want[g] += np.einsum("th,thd->d", w[c0:c0 + 8192, g * hpg:(g + 1) * hpg], dob)
+    rel_k = np.abs(sk).max() / ak.max()
+    rel_v = np.abs(sv - want).max() / np.abs(want).max()
+    print(f"[bwd] 64k sum dk {rel_k:.2e} of sum |dk|; sum dv off by {rel_v:.2e}", flush=True)
+    assert rel_k <= 1e-4
+    assert rel_v <= 1e-3
