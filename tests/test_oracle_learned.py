@@ -1,0 +1,105 @@
+"""Pins for the learned-compression and gate-projection oracle
+(oracle/learned.py): brute-force loops on tiny inputs (the flattening order,
+the head/branch placement of the gates), the choice of weights that turns the
+MLP into the block mean (checked against the C oracle's pooling), and the
+sigmoid against scipy's expit.
+"""
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+from oracle import learned as LR
+from tests import helpers as H
+
+
+def _brute_phi(block_rows, w1, b1, w2, b2):
+    """phi of one block by explicit loops: block_rows [bs][d]."""
+    bs, d = len(block_rows), len(block_rows[0])
+    dh = len(w1)
+    h = []
+    for n in range(dh):
+        acc = 0.0 if b1 is None else float(b1[n])
+        for i in range(bs):
+            for c in range(d):
+                acc += float(w1[n][i * d + c]) * float(block_rows[i][c])
+        h.append(max(acc, 0.0))
+    y = []
+    for c in range(len(w2)):
+        acc = 0.0 if b2 is None else float(b2[c])
+        for n in range(dh):
+            acc += float(w2[c][n]) * h[n]
+        y.append(acc)
+    return y
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_mlp_compression_matches_loops(with_bias):
+    prob = H.problem(batch=2, q_len=13, kv_len=13, n_groups=2, heads_per_group=1, d_qk=3, d_v=2, block=4)
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((2, 13, 2, 3)).astype(np.float32)
+    v = rng.standard_normal((2, 13, 2, 2)).astype(np.float32)
+    dh = 5
+    wk = {"w1": rng.standard_normal((dh, 4 * 3)), "b1": rng.standard_normal(dh) if with_bias else None,
+          "w2": rng.standard_normal((3, dh)), "b2": rng.standard_normal(3) if with_bias else None}
+    wv = {"w1": rng.standard_normal((dh, 4 * 2)), "b1": rng.standard_normal(dh) if with_bias else None,
+          "w2": rng.standard_normal((2, dh)), "b2": rng.standard_normal(2) if with_bias else None}
+    kc, vc = LR.compress(prob, k, v, wk, wv)
+    assert kc.shape == (2, 3, 2, 3) and vc.shape == (2, 3, 2, 2)
+    for b in range(2):
+        for j in range(3):
+            for g in range(2):
+                for x, w, got in ((k, wk, kc), (v, wv, vc)):
+                    rows = [list(x[b, j * 4 + i, g]) for i in range(4)]
+                    want = np.float32(_brute_phi(rows, w["w1"], w["b1"], w["w2"], w["b2"]))
+                    np.testing.assert_allclose(got[b, j, g], want, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mlp_with_averaging_weights_is_the_block_mean(dtype):
+    # W1 averages the block's tokens dim by dim, a bias of +C keeps the ReLU
+    # linear, W2 = I and -C undo it: phi is the mean pooling
+    prob = H.problem(q_len=100, kv_len=100, n_groups=2, d_qk=8, d_v=4, block=16, dtype=dtype)
+    x = H.make(prob)
+    C = 64.0
+    ws = []
+    for d in (8, 4):
+        w1 = np.zeros((d, 16 * d))
+        for i in range(16):
+            w1[np.arange(d), i * d + np.arange(d)] = 1.0 / 16
+        ws.append({"w1": w1, "b1": np.full(d, C), "w2": np.eye(d), "b2": np.full(d, -C)})
+    kc, vc = LR.compress(prob, x["k"], x["v"], ws[0], ws[1])
+    rk, rv = oracle.pool(prob, x["k"], x["v"])
+    for got, ref in ((kc, rk), (vc, rv)):
+        a = H.widen(got, prob)
+        r = H.widen(ref, prob)
+        # equal after rounding, but for an fp64 sum in another order landing
+        # across a rounding boundary: then one step apart
+        step = np.abs(r) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)
+        assert np.all(np.abs(a - r) <= step + 1e-30)
+        assert np.mean(a == r) > 0.999
+
+
+def test_gate_projection_matches_loops_and_expit():
+    rng = np.random.default_rng(1)
+    B, T, DM, Hh = 2, 5, 7, 3
+    x = rng.standard_normal((B, T, DM)).astype(np.float32)
+    w = rng.standard_normal((3 * Hh, DM)).astype(np.float32)
+    b = rng.standard_normal(3 * Hh).astype(np.float32)
+    g = LR.gate_proj(x, w, b, "f32")
+    z = LR.gate_proj(x, w, b, "f32", logits=True)
+    assert g.shape == (B, T, Hh, 3)
+    for bb in range(B):
+        for t in range(T):
+            for h in range(Hh):
+                for br in range(3):
+                    o = 3 * h + br
+                    want = float(b[o]) + sum(float(w[o, c]) * float(x[bb, t, c]) for c in range(DM))
+                    assert abs(z[bb, t, h, br] - want) <= 1e-12 * max(1.0, abs(want))
+                    assert abs(g[bb, t, h, br] - expit(want)) <= 1e-12
+
+
+def test_gate_projection_of_zero_weights_is_one_half():
+    x = np.ones((1, 3, 8), dtype=np.float32)
+    g = LR.gate_proj(x, np.zeros((6, 8), dtype=np.float32), None, "f32")
+    assert np.all(g == 0.5)
