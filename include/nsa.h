@@ -126,6 +126,53 @@ nsa_status nsa_compress(const void* k, const void* v, void* k_cmp, void* v_cmp,
                         const nsa_params* params);
 
 /*
+ * Learned block compression ([P1] s4: each block is compressed into one
+ * learned representation; [P1] s7: NSA forms it with an MLP where MoBA takes
+ * the mean).  For every complete block j and group g, with X the block's
+ * `block` keys flattened in token order (vec(X)[i * d + c] = k[b, j*block + i,
+ * g, c]):  k_cmp[b, j, g, :] = W2 relu(W1 vec(X) + b1) + b2, and v_cmp
+ * likewise with the value weights.  One MLP for keys and one for values,
+ * shared by every block and group; flattening in order gives each position
+ * in the block its own weights.  Weights and biases are dtype, row-major,
+ * output features first:
+ *   w1 [d_hidden, block * d]   b1 [d_hidden] or NULL
+ *   w2 [d, d_hidden]           b2 [d] or NULL      (d = d_qk for keys, d_v for values)
+ * Arithmetic: fp32 accumulation on bf16 matrix cores; the hidden layer is
+ * rounded to bf16 after the ReLU, the summaries once to dtype.  The result
+ * can be handed to nsa_forward through params->k_cmp / v_cmp.
+ * Limits (NSA_ERR_UNSUPPORTED otherwise): dtype NSA_BF16; d_qk, d_v and
+ * d_hidden in {64, 128, 192, 256}; block a multiple of 4.  No workspace.
+ */
+typedef struct {
+  int32_t d_hidden;
+  const void* k_w1;
+  const void* k_b1;
+  const void* k_w2;
+  const void* k_b2;
+  const void* v_w1;
+  const void* v_b1;
+  const void* v_w2;
+  const void* v_b2;
+} nsa_mlp_weights;
+
+nsa_status nsa_compress_mlp(const void* k, const void* v, const nsa_mlp_weights* weights, void* k_cmp,
+                            void* v_cmp, const nsa_params* params);
+
+/*
+ * Gate projection ([P1] s4: each branch's weight is learned from the token's
+ * input representation through a projection):
+ *   gates[b, t, h, branch] = sigmoid(x[b, t, :] . w[3 h + branch, :] + bias[3 h + branch])
+ * x [B, q_len, d_model], w [3 H, d_model], bias [3 H] or NULL, gates
+ * [B, q_len, H, 3], all dtype.  With NSA_F_GATE_LOGITS in params->flags the
+ * sigmoid is left out (the attention then applies it).  fp32 accumulation on
+ * bf16 matrix cores, one rounding to dtype.
+ * Limits (NSA_ERR_UNSUPPORTED otherwise): dtype NSA_BF16, d_model a positive
+ * multiple of 32.  No workspace.
+ */
+nsa_status nsa_gate_proj(const void* x, int32_t d_model, const void* w, const void* bias, void* gates,
+                         const nsa_params* params);
+
+/*
  * Block selection ([P1] s4 compressed branch + group-summed importance;
  * [P1] s7 and [P5] s13 for MoBA).  For query token t at position p and
  * group g: each head's softmax over the summaries of the complete blocks

@@ -5,6 +5,7 @@
 
 #include "nsa_backward.h"
 #include "nsa_internal.h"
+#include "nsa_learned.h"
 #include "nsa_paths.h"
 
 using nsa::Prob;
@@ -78,6 +79,52 @@ nsa_status nsa_compress(const void* k, const void* v, void* k_cmp, void* v_cmp, 
   if (st != NSA_OK) return st;
   if (!ptr_ok(k) || !ptr_ok(v) || !ptr_ok(k_cmp) || !ptr_ok(v_cmp)) return NSA_ERR_INVALID_ARG;
   return hip_status(nsa::launch_pool(P, k, v, k_cmp, v_cmp, (hipStream_t)p->stream));
+}
+
+nsa_status nsa_compress_mlp(const void* k, const void* v, const nsa_mlp_weights* w, void* k_cmp, void* v_cmp,
+                            const nsa_params* p) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  if (!w || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(k_cmp) || !ptr_ok(v_cmp) || !ptr_ok(w->k_w1) || !ptr_ok(w->k_w2) ||
+      !ptr_ok(w->v_w1) || !ptr_ok(w->v_w2) || !opt_ok(w->k_b1) || !opt_ok(w->k_b2) || !opt_ok(w->v_b1) ||
+      !opt_ok(w->v_b2) || w->d_hidden < 1)
+    return NSA_ERR_INVALID_ARG;
+  if (!nsa::mlp_ok(P, w->d_hidden)) return NSA_ERR_UNSUPPORTED;
+  nsa::MlpArgs a;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.k_w1 = (const uint16_t*)w->k_w1;
+  a.k_b1 = (const uint16_t*)w->k_b1;
+  a.k_w2 = (const uint16_t*)w->k_w2;
+  a.k_b2 = (const uint16_t*)w->k_b2;
+  a.v_w1 = (const uint16_t*)w->v_w1;
+  a.v_b1 = (const uint16_t*)w->v_b1;
+  a.v_w2 = (const uint16_t*)w->v_w2;
+  a.v_b2 = (const uint16_t*)w->v_b2;
+  a.kc = (uint16_t*)k_cmp;
+  a.vc = (uint16_t*)v_cmp;
+  a.B = P.B; a.L = P.L; a.G = P.G; a.nb = P.nb; a.bs = P.bs; a.dh = w->d_hidden;
+  return hip_status(nsa::launch_mlp_compress(P, a, (hipStream_t)p->stream));
+}
+
+nsa_status nsa_gate_proj(const void* x, int32_t d_model, const void* w, const void* bias, void* gates,
+                         const nsa_params* p) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  if (!ptr_ok(x) || !ptr_ok(w) || !opt_ok(bias) || !ptr_ok(gates) || d_model < 1) return NSA_ERR_INVALID_ARG;
+  if (!nsa::gate_proj_ok(P, d_model)) return NSA_ERR_UNSUPPORTED;
+  nsa::GateArgs a;
+  a.x = (const uint16_t*)x;
+  a.w = (const uint16_t*)w;
+  a.bias = (const uint16_t*)bias;
+  a.gates = (uint16_t*)gates;
+  a.M = P.B * P.T;
+  a.DM = d_model;
+  a.N = 3 * P.H;
+  a.logits = P.has(NSA_F_GATE_LOGITS) ? 1 : 0;
+  return hip_status(nsa::launch_gate_proj(a, (hipStream_t)p->stream));
 }
 
 nsa_status nsa_select_topk(const void* q, const void* k_cmp, int32_t* idx, float* score, const nsa_params* p) {

@@ -110,6 +110,35 @@ def generate_sequence(prob: dict, b: int, want=("q", "k", "v", "gates"), pool=No
             pool.shutdown()
 
 
+def learned_weights(prob: dict, d_hidden: int, d_model: int = 2560, seed: int = 0, bias: bool = True) -> dict:
+    """Random-initialised weights of the learned block compression and of the
+    gate projection, plus hidden states x [B, T, d_model] ~ N(0, 1), stored
+    like the other inputs.  Scales keep every layer's output near unit size:
+    w1 ~ N(0, 1 / (block * d)), w2 ~ N(0, 1 / d_hidden), gate w ~ N(0, 1 /
+    d_model), biases ~ N(0, 0.1^2).  Returns {"k": {w1, b1, w2, b2}, "v":
+    {...}, "gate_w", "gate_b", "x"} (biases None when bias is False)."""
+    dt = prob["dtype"]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 0x5EED])))
+    H, bs = prob["n_groups"] * prob["heads_per_group"], prob["block"]
+
+    def st(a):
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        return f32_to_bf16_bits(a) if dt == "bf16" else a
+
+    out = {}
+    for name, d in (("k", prob["d_qk"]), ("v", prob["d_v"])):
+        out[name] = {
+            "w1": st(rng.standard_normal((d_hidden, bs * d), dtype=np.float32) / np.sqrt(bs * d)),
+            "b1": st(0.1 * rng.standard_normal(d_hidden, dtype=np.float32)) if bias else None,
+            "w2": st(rng.standard_normal((d, d_hidden), dtype=np.float32) / np.sqrt(d_hidden)),
+            "b2": st(0.1 * rng.standard_normal(d, dtype=np.float32)) if bias else None,
+        }
+    out["gate_w"] = st(rng.standard_normal((3 * H, d_model), dtype=np.float32) / np.sqrt(d_model))
+    out["gate_b"] = st(0.1 * rng.standard_normal(3 * H, dtype=np.float32)) if bias else None
+    out["x"] = st(rng.standard_normal((prob["batch"], prob["q_len"], d_model), dtype=np.float32))
+    return out
+
+
 def generate(prob: dict, want=("q", "k", "v", "gates")) -> dict:
     """Inputs for every batch element, concatenated along the batch axis."""
     with cf.ThreadPoolExecutor(_workers()) as pool:

@@ -21,7 +21,7 @@ STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "N
 
 EXPORTS = ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
            "nsa_forward_phases", "nsa_workspace_bytes", "nsa_backward", "nsa_backward_workspace_bytes",
-           "nsa_backward_phases",
+           "nsa_backward_phases", "nsa_compress_mlp", "nsa_gate_proj",
            "nsa_status_str")
 
 
@@ -29,6 +29,11 @@ class NsaError(RuntimeError):
     def __init__(self, call: str, code: int, text: str):
         super().__init__(f"{call}: {STATUS.get(code, code)} ({text})")
         self.code = code
+
+
+class MlpWeights(ctypes.Structure):
+    _fields_ = [("d_hidden", ctypes.c_int32)] + [
+        (n, ctypes.c_void_p) for n in ("k_w1", "k_b1", "k_w2", "k_b2", "v_w1", "v_b1", "v_w2", "v_b2")]
 
 
 class Params(ctypes.Structure):
@@ -70,9 +75,12 @@ def lib() -> ctypes.CDLL:
         L.nsa_backward_workspace_bytes.restype = ctypes.c_size_t
         L.nsa_backward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
         L.nsa_backward_phases.restype = ctypes.c_int32
+        L.nsa_compress_mlp.argtypes = [vp, vp, ctypes.POINTER(MlpWeights), vp, vp, P]
+        L.nsa_gate_proj.argtypes = [vp, ctypes.c_int32, vp, vp, vp, P]
         L.nsa_status_str.argtypes = [ctypes.c_int]
         L.nsa_status_str.restype = ctypes.c_char_p
-        for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_backward"):
+        for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_backward",
+                     "nsa_compress_mlp", "nsa_gate_proj"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -290,6 +298,52 @@ def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, d
     _call("nsa_backward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), idx.data_ptr(),
           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dgates), ctypes.byref(p))
     return dq, dk, dv, dgates
+
+
+def compress_mlp(prob: dict, k, v, wk: dict, wv: dict, kc=None, vc=None, stream=None):
+    """Learned summaries: wk, wv hold device tensors w1, w2 and optional b1, b2."""
+    s, dt = _shapes(prob), torch_dtype(prob)
+    _check(k, s["k"], dt, "k")
+    _check(v, s["v"], dt, "v")
+    dh = wk["w1"].shape[0]
+    for name, w, d in (("k", wk, prob["d_qk"]), ("v", wv, prob["d_v"])):
+        _check(w["w1"], (dh, prob["block"] * d), dt, f"{name}_w1")
+        _check(w["w2"], (d, dh), dt, f"{name}_w2")
+        if w.get("b1") is not None:
+            _check(w["b1"], (dh,), dt, f"{name}_b1")
+        if w.get("b2") is not None:
+            _check(w["b2"], (d,), dt, f"{name}_b2")
+    kc = torch.empty(s["kc"], dtype=dt, device=k.device) if kc is None else kc
+    vc = torch.empty(s["vc"], dtype=dt, device=k.device) if vc is None else vc
+    _check(kc, s["kc"], dt, "k_cmp")
+    _check(vc, s["vc"], dt, "v_cmp")
+    mw = MlpWeights()
+    mw.d_hidden = dh
+    for pre, w in (("k_", wk), ("v_", wv)):
+        for n in ("w1", "b1", "w2", "b2"):
+            setattr(mw, pre + n, _ptr(w.get(n)))
+    p = params(prob, stream=stream)
+    _call("nsa_compress_mlp", k.data_ptr(), v.data_ptr(), ctypes.byref(mw), kc.data_ptr(), vc.data_ptr(),
+          ctypes.byref(p))
+    return kc, vc
+
+
+def gate_proj(prob: dict, x, w, bias=None, gates=None, logits=False, stream=None):
+    """gates [B, T, H, 3] = sigmoid(x w^T + bias) (or the logits)."""
+    s, dt = _shapes(prob), torch_dtype(prob)
+    B, T, dm = x.shape
+    _check(x, (prob["batch"], prob["q_len"], dm), dt, "x")
+    _check(w, (3 * s["q"][2], dm), dt, "w")
+    if bias is not None:
+        _check(bias, (3 * s["q"][2],), dt, "bias")
+    gates = torch.empty(s["gates"], dtype=dt, device=x.device) if gates is None else gates
+    _check(gates, s["gates"], dt, "gates")
+    flags = flags_of(prob) | (F_GATE_LOGITS if logits else 0)
+    if not logits:
+        flags &= ~F_GATE_LOGITS
+    p = params(prob, stream=stream, flags=flags)
+    _call("nsa_gate_proj", x.data_ptr(), dm, w.data_ptr(), _ptr(bias), gates.data_ptr(), ctypes.byref(p))
+    return gates
 
 
 def to_device(a, prob: dict, device="cuda") -> torch.Tensor:
