@@ -248,6 +248,57 @@ def run_backward(args, torch, nsa, workloads, inputs, workload="nsa_prefill_64k"
     return rec
 
 
+# ---------------------------------------------------------------- learned --
+
+def run_learned(args, torch, nsa, workloads, inputs, workload="nsa_prefill_64k", d_hidden=192, d_model=2560):
+    """The learned block compression (MLP per 64-token block, hidden width
+    d_hidden) and the gate projection (d_model 2560, the pages' hidden size)
+    for the workload, each timed alone with HIP events."""
+    prob = workloads.get(workload)
+    x = inputs.generate(prob, want=("k", "v"))
+    w = inputs.learned_weights(prob, d_hidden, d_model=d_model, seed=0)
+    dev = lambda a: None if a is None else nsa.to_device(a, prob)
+    k, v = dev(x["k"]), dev(x["v"])
+    wk = {n: dev(a) for n, a in w["k"].items()}
+    wv = {n: dev(a) for n, a in w["v"].items()}
+    xs, gw, gb = dev(w["x"]), dev(w["gate_w"]), dev(w["gate_b"])
+    del x, w
+    kc, vc = nsa.compress_mlp(prob, k, v, wk, wv)
+    gates = nsa.gate_proj(prob, xs, gw, gb)
+    K = max(3, min(args.steps, 10))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+    ms_mlp = timed(lambda: nsa.compress_mlp(prob, k, v, wk, wv, kc=kc, vc=vc))
+    ms_gate = timed(lambda: nsa.gate_proj(prob, xs, gw, gb, gates=gates))
+    B, L, G, bs, nb = prob["batch"], prob["kv_len"], prob["n_groups"], prob["block"], prob["kv_len"] // prob["block"]
+    rows = B * nb * G
+    fl_mlp = sum(2.0 * rows * (bs * d * d_hidden + d_hidden * d) for d in (prob["d_qk"], prob["d_v"]))
+    M, N = B * prob["q_len"], 3 * workloads.n_heads(prob)
+    fl_gate = 2.0 * M * d_model * N
+    by_gate = 2.0 * (M * d_model + N * d_model + M * N)
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    del k, v, wk, wv, xs, gw, gb, kc, vc, gates
+    torch.cuda.empty_cache()
+    return {"workload": workload, "d_hidden": d_hidden, "d_model": d_model, "steps": K,
+            "compress_mlp": {"ms": round(ms_mlp, 4), "algorithmic_gflop": round(fl_mlp / 1e9, 2),
+                             "tflops": round(tf(fl_mlp, ms_mlp), 1),
+                             "mfma_frac": round(tf(fl_mlp, ms_mlp) / PEAK_BF16_TFLOPS, 4)},
+            "gate_proj": {"ms": round(ms_gate, 4), "algorithmic_gflop": round(fl_gate / 1e9, 2),
+                          "tflops": round(tf(fl_gate, ms_gate), 1),
+                          "mfma_frac": round(tf(fl_gate, ms_gate) / PEAK_BF16_TFLOPS, 4),
+                          "hbm_gbs": round(by_gate / (ms_gate * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(by_gate / (ms_gate * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+
+
 # ----------------------------------------------------------------- decode --
 
 def run_decode(args, torch, nsa, workloads, inputs):
@@ -396,6 +447,8 @@ def run_only(args, torch, nsa, workloads, inputs):
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copied 1 GiB x {args.steps}")
+    elif args.only == "learned":
+        log(f"learned {run_learned(args, torch, nsa, workloads, inputs, args.workload)}")
     elif args.only == "backward":
         rec = run_backward(args, torch, nsa, workloads, inputs, args.workload)
         log(f"backward {rec['ms_per_step']} ms/step {rec['phases_ms']}")
@@ -421,7 +474,7 @@ def main():
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip MoBA 128k/1M and the decoupled-block 64k legs")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings", "backward", "learned"], default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -472,6 +525,9 @@ def main():
         a.steps, a.warmup = min(args.steps, 3), 1
         rec["backward"] = run_backward(a, torch, nsa, workloads, inputs, args.workload)
         log(f"backward: {rec['backward']['ms_per_step']} ms/step, phases {rec['backward']['phases_ms']}")
+    if not args.no_backward:
+        rec["learned"] = run_learned(args, torch, nsa, workloads, inputs, args.workload)
+        log(f"learned: {rec['learned']}")
     if not args.no_decode:
         rec["decode"] = run_decode(args, torch, nsa, workloads, inputs)
         log(f"decode: {rec['decode']['ms_per_step']} ms/step")

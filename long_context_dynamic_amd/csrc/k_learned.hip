@@ -11,10 +11,11 @@
 //                   the bias and ReLU are applied, the hidden rows (bf16)
 //                   stay in LDS for the second layer, whose output tiles the
 //                   waves share out.
-//   k_gate_proj     gates = sigmoid(x W^T + b): one workgroup per 64 tokens,
-//                   a wave per 16 tokens, all 3H outputs in registers across
-//                   the d_model contraction; the sigmoid (unless gate logits
-//                   are asked for) and the bf16 rounding in the epilogue.
+//   k_gate_proj     gates = sigmoid(x W^T + b): one workgroup per 128 tokens,
+//                   a wave per 16 tokens, 192 outputs at a time in registers
+//                   across the d_model contraction, the weight slices shared
+//                   through LDS; the sigmoid (unless gate logits are asked
+//                   for) and the bf16 rounding in the epilogue.
 // Both are dense contractions on bf16 matrix cores with fp32 accumulation.
 #include <math.h>
 
@@ -100,30 +101,56 @@ __global__ void __launch_bounds__(256) k_mlp_compress(MlpArgs a, int which) {
 }
 
 // ---------------------------------------------------------------------------
-// N = 3H outputs in passes of 16 * NT columns.
+// N = 3H outputs in passes of 16 * kGateNT columns; the weight slice of each
+// 64-wide step of the contraction passes through LDS once for the
+// workgroup's 8 waves (128 tokens), the next slice's reads in flight while
+// the current one is used.
 constexpr int kGateNT = 12;
+constexpr int kGateWS = 64 + 16;  // LDS row stride of a weight slice (16-byte reads conflict-free)
 
-__global__ void __launch_bounds__(256) k_gate_proj(GateArgs a) {
+__global__ void __launch_bounds__(512) k_gate_proj(GateArgs a) {
+  __shared__ __align__(16) uint16_t ws[16 * kGateNT * kGateWS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 64 + 16 * wave;
+  const int64_t m0 = (int64_t)blockIdx.x * 128 + 16 * wave;
   int64_t m = m0 + lr;
   if (m > a.M - 1) m = a.M - 1;
   const uint16_t* xrow = a.x + m * a.DM + 8 * lg;
+  constexpr int CH = 16 * kGateNT * 64 / 8;  // 16-byte chunks of one slice
+  constexpr int CPT = (CH + 511) / 512;
   for (int64_t n0 = 0; n0 < a.N; n0 += 16 * kGateNT) {
     f32x4 acc[kGateNT];
 #pragma unroll
     for (int n = 0; n < kGateNT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* wrow[kGateNT];
+    u32x4 pre[CPT];
+    auto fetch = [&](int64_t k) {
 #pragma unroll
-    for (int n = 0; n < kGateNT; ++n) {
-      int64_t c = n0 + 16 * n + lr;
-      if (c > a.N - 1) c = a.N - 1;  // columns past N are computed on a copy and never stored
-      wrow[n] = a.w + c * a.DM + 8 * lg;
-    }
-    for (int64_t k = 0; k < a.DM; k += 32) {
-      const bf16x8 af = ld8(xrow + k);
+      for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + 512 * i;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (c < CH) {
+          const int64_t col = n0 + c / 8, kk = k + 8 * (c % 8);  // past N or d_model: zeros
+          if (col < a.N && kk < a.DM) val = *(const u32x4*)(a.w + col * a.DM + kk);
+        }
+        pre[i] = val;
+      }
+    };
+    fetch(0);
+    for (int64_t k = 0; k < a.DM; k += 64) {
+      __syncthreads();
 #pragma unroll
-      for (int n = 0; n < kGateNT; ++n) acc[n] = mfma16(af, ld8(wrow[n] + k), acc[n]);
+      for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + 512 * i;
+        if (c < CH) *(u32x4*)(ws + (c / 8) * kGateWS + 8 * (c % 8)) = pre[i];
+      }
+      __syncthreads();
+      if (k + 64 < a.DM) fetch(k + 64);
+      const int kn = a.DM - k >= 64 ? 2 : 1;  // d_model is a multiple of 32
+      for (int ks = 0; ks < kn; ++ks) {
+        const bf16x8 af = ld8(xrow + k + 32 * ks);
+#pragma unroll
+        for (int n = 0; n < kGateNT; ++n)
+          acc[n] = mfma16(af, ld8(ws + (16 * n + lr) * kGateWS + 32 * ks + 8 * lg), acc[n]);
+      }
     }
     // lane holds Z[token 4 lg + q][column 16 n + lr]
 #pragma unroll
@@ -186,9 +213,9 @@ hipError_t launch_mlp_compress(const Prob& P, const MlpArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gate_proj(const GateArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.M + 63) / 64);
+  const unsigned grid = (unsigned)((a.M + 127) / 128);
   if (grid == 0) return hipSuccess;
-  k_gate_proj<<<grid, 256, 0, s>>>(a);
+  k_gate_proj<<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
