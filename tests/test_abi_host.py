@@ -105,3 +105,49 @@ def test_workspace_sizes():
     # a caller-provided summary cache needs less room than computing it
     dec = workloads.get("nsa_decode_64x64k")
     assert nsa.workspace_bytes(dec, have_cmp=True) < nsa.workspace_bytes(dec)
+
+
+def _backward(p, gates=FAKE, dout=FAKE, dgates=FAKE):
+    return nsa.lib().nsa_backward(FAKE, FAKE, FAKE, gates, FAKE, dout, FAKE, FAKE, FAKE, dgates, ctypes.byref(p))
+
+
+def test_backward_validation():
+    lib = nsa.lib()
+    p = _p(BASE)
+    assert _backward(p, dout=0) == 1                          # NULL dout
+    assert _backward(p, gates=0, dgates=0) == 1               # three branches need gates
+    pw = _p(BASE, flags=nsa.F_SLC)
+    assert _backward(pw, gates=0, dgates=FAKE) == 1           # dgates without gates
+    assert _backward(p) == 3                                  # no workspace
+    p.workspace, p.workspace_bytes = FAKE, 16
+    assert _backward(p) == 3                                  # too small
+    tiny = _p(workloads.get("nsa_tiny_fp32"))
+    assert _backward(tiny) == 2                               # fp32: outside the kernels' limits
+    assert lib.nsa_backward_workspace_bytes(ctypes.byref(tiny)) == 0
+    odd = _p(workloads.get("nsa_prefill_8k", q_len=256, kv_len=256, block=32))
+    assert _backward(odd) == 2                                # 32-token blocks
+    need = nsa.backward_workspace_bytes(workloads.get("nsa_prefill_64k"))
+    assert need > 0 and need % 256 == 0
+    assert nsa.backward_phases(BASE) == ["bwd_images", "bwd_lists", "bwd_kv_selected_stats", "bwd_q",
+                                         "bwd_kv_window", "bwd_kv_selected", "bwd_kv_compressed", "bwd_reduce"]
+
+
+def test_learned_parts_validation():
+    lib = nsa.lib()
+    p = _p(BASE)
+    w = nsa.MlpWeights()
+    w.d_hidden = 192
+    for n in ("k_w1", "k_w2", "v_w1", "v_w2"):
+        setattr(w, n, FAKE)
+    assert lib.nsa_compress_mlp(FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(p)) == 1   # no weights
+    w.k_w1 = 0
+    assert lib.nsa_compress_mlp(FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, ctypes.byref(p)) == 1
+    w.k_w1 = FAKE
+    w.d_hidden = 100
+    assert lib.nsa_compress_mlp(FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, ctypes.byref(p)) == 2
+    tiny = _p(workloads.get("nsa_tiny_fp32"))
+    w.d_hidden = 64
+    assert lib.nsa_compress_mlp(FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, ctypes.byref(tiny)) == 2
+    assert lib.nsa_gate_proj(0, 2560, FAKE, 0, FAKE, ctypes.byref(p)) == 1             # NULL x
+    assert lib.nsa_gate_proj(FAKE, 100, FAKE, 0, FAKE, ctypes.byref(p)) == 2           # d_model % 32
+    assert lib.nsa_gate_proj(FAKE, 2560, FAKE, 0, FAKE, ctypes.byref(tiny)) == 2       # fp32
