@@ -3,16 +3,17 @@
 // group-shared selection keeps small).  Same arithmetic as the prefill path,
 // reorganised so that many waves stream the cache at once:
 //
-//   k_dec_cmp     one wave per (row, group, 2 tiles of 64 block summaries):
-//                 compressed-branch logits (kept in zbuf for the importance)
-//                 and a partial softmax-weighted sum of the value summaries.
-//   k_dec_select  one workgroup per (row, group): per-head softmax statistics
-//                 from the partials, group importance, top-k (one wave).
-//   k_dec_attn    one wave per (row, group, slice of the key blocks): the
-//                 selected blocks (4 per wave) and the window blocks, each
-//                 with its own online softmax.
-//   k_dec_merge   one workgroup per (row, group): log-sum-exp merge of each
-//                 branch's partials, gates, output.
+//   k_dec_cmpsel     one workgroup per (row, group): 4 waves share out the
+//                    64-summary tiles (compressed-branch logits kept in zbuf
+//                    for the importance, a partial softmax-weighted sum of
+//                    the value summaries per wave); after a barrier the same
+//                    workgroup works out per-head softmax statistics, the
+//                    group importance and the top-k (one wave).
+//   k_dec_attnmerge  one workgroup per (row, group): 4 waves share out the
+//                    chosen blocks and the window's blocks (an online softmax
+//                    and a record per wave and branch); after a barrier the
+//                    log-sum-exp merge of every branch's records, gates,
+//                    output.
 // Every streaming wave runs the same tile loop: K fragments straight from
 // global memory into matrix-op registers, the V tile through LDS (read back
 // transposed), the next tile's reads issued before the current softmax, and
@@ -30,8 +31,9 @@ namespace nsa {
 namespace {
 
 constexpr int MAX_NB_LANE = 32;  // nb <= 2048
-constexpr int SLOTS_PER_WAVE = 4;      // selected blocks per streaming wave
-constexpr int TILES_PER_CMP_WAVE = 2;  // 64-summary tiles per compressed-branch wave
+constexpr int MAX_CMP_WAVES = 4;     // compressed-branch waves per (row, group)
+constexpr int kAttnWaves = 4;        // selected + window waves per (row, group)
+constexpr int kMaxSlotsPerWave = 8;  // chosen blocks per such wave: top_k <= 32
 
 __device__ __forceinline__ float dgate(const DecArgs& a, int64_t hrow, int branch) {
   if (!a.gates) return 1.f;
@@ -48,7 +50,7 @@ __device__ __forceinline__ bool dbetter(float v, int j, float bv, int bj) {
 // [16] maxima (log2 units) and [16] sums.
 template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
 
-// Stream 64-row tiles `tiles[0..nt)` of K [B, N, G, DQ] / V [B, N, G, DV] for
+// Stream 64-row tiles tile_at(0 .. nt-1) of K [B, N, G, DQ] / V [B, N, G, DV] for
 // one (b, g) and the 16 heads in qf; keep rows where ok(row).  Writes scaled
 // logits to zrow[h * zstride + row] when zrow is given.  Ends by writing the
 // wave's partial record.  WITH_V = false: softmax statistics only, V is never
@@ -57,9 +59,9 @@ template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
 // tile is read as whole rows into registers, passes through the wave's LDS
 // region and is read back transposed.  The next tile's reads are in flight
 // while the current one is computed on.
-template <int DQ, int DV, bool WITH_V, typename Ok>
+template <int DQ, int DV, bool WITH_V, typename TileAt, typename Ok>
 __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* V, int64_t N, int64_t b, int64_t g,
-                                             int64_t G, const int* tiles, int nt, Ok ok, const bf16x8 (&qf)[DQ / 32],
+                                             int64_t G, TileAt tile_at, int nt, Ok ok, const bf16x8 (&qf)[DQ / 32],
                                              float c, uint16_t* myv, float* zrow, int64_t zstride, float* rec) {
   constexpr int VS = DV + 8;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -70,7 +72,7 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
   bf16x8 kf[4][DQ / 32];
   u32x4 vreg[DV / 8];
   auto load_k = [&](int i) {
-    const int64_t kb = (int64_t)tiles[i] * 64;
+    const int64_t kb = (int64_t)tile_at(i) * 64;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       int64_t r = kb + 16 * mt + lr;
@@ -81,7 +83,7 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
     }
   };
   auto load_v = [&](int i) {
-    const int64_t kb = (int64_t)tiles[i] * 64;
+    const int64_t kb = (int64_t)tile_at(i) * 64;
 #pragma unroll
     for (int q = 0; q < DV / 8; ++q) {
       const int cidx = lane + 64 * q;  // 64 rows x DV/8 chunks
@@ -103,7 +105,7 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
   // free; the last tile is peeled so no tile is read twice
   auto tile = [&](int i, auto prefetch) {
     constexpr bool PF = decltype(prefetch)::value;
-    const int64_t kb = (int64_t)tiles[i] * 64;
+    const int64_t kb = (int64_t)tile_at(i) * 64;
     f32x4 s[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -187,93 +189,65 @@ __device__ __forceinline__ void load_q(const DecArgs& a, int64_t row, int64_t g,
 }
 
 // ---------------------------------------------------------------------------
+// The compressed branch of one (row, group) on one wave: every
+// n_cmp_waves-th summary tile from its own, logits to zbuf, a partial record.
 template <int DQ, int DV, bool WITH_V>
-__global__ void __launch_bounds__(256) k_dec_cmp(DecArgs a) {
-  __shared__ __align__(16) uint16_t vt[4][64 * (DV + 8)];
-  const int wave = threadIdx.x >> 6;
-  // (row, cmp wave, g): the groups of one tile run side by side, so their
-  // interleaved summary rows are read together
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  if (item >= a.R * a.G * a.n_cmp_waves) return;
-  const int64_t g = item % a.G;
-  const int64_t cw = (item / a.G) % a.n_cmp_waves;
-  const int64_t row = item / (a.n_cmp_waves * a.G);
+__device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t g, int wave, uint16_t* myv) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
   int64_t nvis = (p + 1) / a.bs;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
-  int tiles[TILES_PER_CMP_WAVE];
-  int nt = 0;
-  for (int i = 0; i < TILES_PER_CMP_WAVE; ++i) {
-    const int64_t jt = cw * TILES_PER_CMP_WAVE + i;
-    if (jt * 64 < nvis) tiles[nt++] = (int)jt;
-  }
+  const int ncw = (int)a.n_cmp_waves;
+  const int64_t ntv = (nvis + 63) / 64;  // tiles with a visible summary
+  const int nt = ntv > wave ? (int)((ntv - wave + ncw - 1) / ncw) : 0;
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
-  float* rec = a.part + ((row * a.G + g) * nwaves + cw) * part_floats<DV>();
+  float* rec = a.part + ((row * a.G + g) * nwaves + wave) * part_floats<DV>();
   float* zrow = a.zbuf + (row * a.G + g) * 16 * a.nbp;
-  stream_tiles<DQ, DV, WITH_V>(a.kc, a.vc, a.nb, b, g, a.G, tiles, nt, [&](int64_t j) { return j < nvis; }, qf,
-                               a.scale * kLog2e, vt[wave], zrow, a.nbp, rec);
+  stream_tiles<DQ, DV, WITH_V>(a.kc, a.vc, a.nb, b, g, a.G, [&](int i) { return wave + i * ncw; }, nt,
+                               [&](int64_t j) { return j < nvis; }, qf, a.scale * kLog2e, myv, zrow, a.nbp, rec);
 }
 
+// The selected and window blocks of one (row, group) on wave w of
+// kAttnWaves: chosen slots w, w + 4, .. (a record in selected slot w), then
+// window tiles w, w + 4, .. (a record in window slot w).
 template <int DQ, int DV>
-__global__ void __launch_bounds__(256) k_dec_attn(DecArgs a) {
-  __shared__ __align__(16) uint16_t vt[4][64 * (DV + 8)];
-  const int wave = threadIdx.x >> 6;
-  const int64_t nsw = a.n_sel_waves + a.n_win_waves;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (row, wave slot, g), groups side by side
-  if (item >= a.R * a.G * nsw) return;
-  const int64_t g = item % a.G;
-  const int64_t ws = (item / a.G) % nsw;
-  const int64_t row = item / (nsw * a.G);
+__device__ __forceinline__ void attn_wave(const DecArgs& a, int64_t row, int64_t g, int w, uint16_t* myv) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
-  const bool is_win = ws >= a.n_sel_waves;
-  int tiles[SLOTS_PER_WAVE + 1];
-  int nt = 0;
-  int64_t lo = 0;
-  if (!is_win) {
-    if (a.flags & NSA_F_SLC) {
-      for (int i = 0; i < SLOTS_PER_WAVE; ++i) {
-        const int64_t slot = ws * SLOTS_PER_WAVE + i;
-        const int j = slot < a.n ? a.idx[(row * a.G + g) * a.n + slot] : -1;
-        if (j >= 0 && (int64_t)j * 64 <= p) tiles[nt++] = j;
-      }
-    }
-  } else if ((a.flags & NSA_F_WIN) && a.w > 0) {
-    lo = p - a.w + 1;
-    if (lo < 0) lo = 0;
-    const int64_t kb0 = lo / 64, kb1 = p / 64;
-    const int64_t per = (kb1 - kb0 + a.n_win_waves) / a.n_win_waves;
-    const int64_t first = kb0 + (ws - a.n_sel_waves) * per;
-    for (int64_t j = first; j <= kb1 && j < first + per && nt < SLOTS_PER_WAVE + 1; ++j) tiles[nt++] = (int)j;
-  }
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
-  const int64_t nwaves = a.n_cmp_waves + nsw;
-  float* rec = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves + ws) * part_floats<DV>();
+  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
+  float* recs = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves) * part_floats<DV>();
   const float c = a.scale * kLog2e;
-  if (!is_win)
-    stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, tiles, nt, [&](int64_t s) { return s <= p; }, qf, c,
-                               vt[wave], nullptr, 0, rec);
-  else
-    stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, tiles, nt, [&](int64_t s) { return s <= p && s >= lo; }, qf,
-                               c, vt[wave], nullptr, 0, rec);
+  int sel[kMaxSlotsPerWave];
+  int ns = 0;
+  if (a.flags & NSA_F_SLC) {
+    for (int i = 0; i < kMaxSlotsPerWave; ++i) {
+      const int64_t slot = w + kAttnWaves * i;
+      const int j = slot < a.n ? a.idx[(row * a.G + g) * a.n + slot] : -1;
+      if (j >= 0 && (int64_t)j * 64 <= p) sel[ns++] = j;
+    }
+  }
+  stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return sel[i]; }, ns,
+                             [&](int64_t s) { return s <= p; }, qf, c, myv, nullptr, 0, recs + w * part_floats<DV>());
+  int64_t lo = p - a.w + 1;
+  if (lo < 0) lo = 0;
+  const int64_t kb0 = lo / 64, nwt = ((a.flags & NSA_F_WIN) && a.w > 0) ? p / 64 - kb0 + 1 : 0;
+  const int nt = nwt > w ? (int)((nwt - w + kAttnWaves - 1) / kAttnWaves) : 0;
+  stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return (int)(kb0 + w + kAttnWaves * i); }, nt,
+                             [&](int64_t s) { return s <= p && s >= lo; }, qf, c, myv, nullptr, 0,
+                             recs + (a.n_sel_waves + w) * part_floats<DV>());
 }
 
-// ---------------------------------------------------------------------------
-// One workgroup per (row, group): per-head softmax statistics from the
-// compressed-branch partial records, the group importance of every visible
-// block from the stored logits (all four waves), top-k (one wave).
-// NBL: blocks per lane in the top-k (nbp <= 64 * NBL).
+// Per-head softmax statistics of one (row, group) from the compressed-branch
+// records, the group importance of every visible block from the logits, and
+// the top-k (wave 0).  Every thread of the workgroup calls it (it holds a
+// barrier); threads 0..255 do the work.  NBL: blocks per lane (nbp <= 64 NBL).
 template <int DV, int NBL>
-__global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
-  __shared__ float imp[64 * NBL];
-  __shared__ float sM[16], sL[16];
-  const int tid = threadIdx.x;
-  const int64_t g = blockIdx.x % a.G;
-  const int64_t row = blockIdx.x / a.G;
+__device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64_t g, int tid, float* imp, float* sM,
+                                            float* sL) {
   const int64_t p = a.L - a.T + row % a.T;
   int64_t nvis = (p + 1) / a.bs;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
@@ -286,7 +260,7 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
   for (int i = 0; i < NBL / 4; ++i) {
     const int64_t j = tid + 256 * i;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) zv[i][h] = j < nvis ? z[h * a.nbp + j] : 0.f;
+    for (int h = 0; h < 16; ++h) zv[i][h] = (tid < 256 && j < nvis) ? z[h * a.nbp + j] : 0.f;
   }
   if (tid < 16) {
     float M = -INFINITY, L = 0.f;
@@ -299,14 +273,16 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
     sL[tid] = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
+  if (tid < 256) {
 #pragma unroll
-  for (int i = 0; i < NBL / 4; ++i) {
-    const int64_t j = tid + 256 * i;
-    if (j < nvis) {
-      float sum = 0.f;
+    for (int i = 0; i < NBL / 4; ++i) {
+      const int64_t j = tid + 256 * i;
+      if (j < nvis) {
+        float sum = 0.f;
 #pragma unroll
-      for (int h = 0; h < 16; ++h) sum += exp2f(zv[i][h] - sM[h]) * sL[h];
-      imp[j] = sum;
+        for (int h = 0; h < 16; ++h) sum += exp2f(zv[i][h] - sM[h]) * sL[h];
+        imp[j] = sum;
+      }
     }
   }
   __syncthreads();
@@ -334,30 +310,17 @@ __global__ void __launch_bounds__(256) k_dec_select(DecArgs a) {
   topk_write(cnt, cj, cs, (int)a.n, orow, srow);
 }
 
-// ---------------------------------------------------------------------------
 // Log-sum-exp merge of each branch's partial records, gates, output.  With
 // gates == NULL every enabled branch has weight 1; lse (selected branch only,
-// natural log) is written when given.
-// One thread per 4 outputs (16 heads x DV/4): each first issues the loads of
-// its slice of every partial record and of its gates, so they are in flight
-// while 48 threads work out the merge weights.
+// natural log) is written when given.  Every thread of the workgroup calls it
+// (it holds a barrier); the 16 x DV/4 output slices are dealt over nthr threads.
+constexpr int kMaxRecords = 32;
+
 template <int DV, typename TO>
-__global__ void __launch_bounds__(4 * DV) k_dec_merge(DecArgs a) {
-  constexpr int MAXW = 32;
-  __shared__ float coef[16][MAXW];  // weight of each partial in its branch's merge
-  __shared__ float slse[16];
-  const int tid = threadIdx.x;
-  const int64_t g = blockIdx.x % a.G;
-  const int64_t row = blockIdx.x / a.G;
+__device__ __forceinline__ void merge_body(const DecArgs& a, int64_t row, int64_t g, int tid, int nthr,
+                                           float (*coef)[kMaxRecords], float* slse) {
   const int nc = (int)a.n_cmp_waves, ns = (int)a.n_sel_waves, nwaves = nc + ns + (int)a.n_win_waves;
   const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
-  const int h = tid / (DV / 4), d = 4 * (tid % (DV / 4));
-  f32x4 v[MAXW];
-#pragma unroll
-  for (int w = 0; w < MAXW; ++w)
-    if (w < nwaves) v[w] = *(const f32x4*)(base + w * part_floats<DV>() + h * DV + d);
-  const int64_t hrow = row * a.H + g * 16 + h;
-  const float g0 = dgate(a, hrow, 0), g1 = dgate(a, hrow, 1), g2 = dgate(a, hrow, 2);
   if (tid < 48) {
     const int hh = tid & 15, br = tid >> 4;  // 0 cmp, 1 sel, 2 win
     const int w0 = br == 0 ? 0 : (br == 1 ? nc : nc + ns), w1 = br == 0 ? nc : (br == 1 ? nc + ns : nwaves);
@@ -377,43 +340,94 @@ __global__ void __launch_bounds__(4 * DV) k_dec_merge(DecArgs a) {
   __syncthreads();
   const bool use_cmp = a.flags & NSA_F_CMP, use_slc = a.flags & NSA_F_SLC;
   const bool use_win = (a.flags & NSA_F_WIN) && a.w > 0;
-  f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int it = tid; it < 16 * (DV / 4); it += nthr) {
+    const int h = it / (DV / 4), d = 4 * (it % (DV / 4));
+    f32x4 v[kMaxRecords];
 #pragma unroll
-  for (int w = 0; w < MAXW; ++w)
-    if (w < nwaves) br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v[w] * coef[h][w];
-  f32x4 out = {0.f, 0.f, 0.f, 0.f};
-  if (use_cmp) out += br[0] * g0;
-  if (use_slc) out += br[1] * g1;
-  if (use_win) out += br[2] * g2;
-  if (sizeof(TO) == 2) {
-    u32x2 wv = {(uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16),
-                (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16)};
-    *(u32x2*)((uint16_t*)a.out + hrow * DV + d) = wv;
-  } else {
-    *(f32x4*)((float*)a.out + hrow * DV + d) = out;
+    for (int w = 0; w < kMaxRecords; ++w)
+      if (w < nwaves) v[w] = *(const f32x4*)(base + w * part_floats<DV>() + h * DV + d);
+    const int64_t hrow = row * a.H + g * 16 + h;
+    f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int w = 0; w < kMaxRecords; ++w)
+      if (w < nwaves) br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v[w] * coef[h][w];
+    f32x4 out = {0.f, 0.f, 0.f, 0.f};
+    if (use_cmp) out += br[0] * dgate(a, hrow, 0);
+    if (use_slc) out += br[1] * dgate(a, hrow, 1);
+    if (use_win) out += br[2] * dgate(a, hrow, 2);
+    if (sizeof(TO) == 2) {
+      u32x2 wv = {(uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16),
+                  (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16)};
+      *(u32x2*)((uint16_t*)a.out + hrow * DV + d) = wv;
+    } else {
+      *(f32x4*)((float*)a.out + hrow * DV + d) = out;
+    }
   }
   if (a.lse && tid < 16) a.lse[row * a.H + g * 16 + tid] = slse[tid];
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup of 4 waves per (row, group): the compressed branch (each wave
+// with its own LDS V tile), then, after a barrier, the selection.  The waves'
+// logits and records go through global memory and are read back by the same
+// workgroup (no launch in between).
+template <int DQ, int DV, bool WITH_V, int NBL>
+__global__ void __launch_bounds__(256) k_dec_cmpsel(DecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* imp = (float*)smem;                    // [64 * NBL]
+  float* sM = imp + 64 * NBL;                   // [16]
+  float* sL = sM + 16;                          // [16]
+  uint16_t* vt = (uint16_t*)(sL + 16);          // [4][64 * (DV + 8)] when WITH_V
+  const int wave = threadIdx.x >> 6;
+  const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
+  if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, WITH_V>(a, row, g, wave, vt + (WITH_V ? wave * 64 * (DV + 8) : 0));
+  __syncthreads();
+  select_body<DV, NBL>(a, row, g, threadIdx.x, imp, sM, sL);
+}
+
+// One workgroup of 4 waves per (row, group): the selected and window blocks,
+// a barrier, the merge of every branch's records, gates, output.
+template <int DQ, int DV, typename TO>
+__global__ void __launch_bounds__(256) k_dec_attnmerge(DecArgs a) {
+  __shared__ __align__(16) uint16_t vt[kAttnWaves][64 * (DV + 8)];
+  __shared__ float coef[16][kMaxRecords];
+  __shared__ float slse[16];
+  const int wave = threadIdx.x >> 6;
+  const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
+  attn_wave<DQ, DV>(a, row, g, wave, vt[wave]);
+  __syncthreads();
+  merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
+}
+
+template <int DQ, int DV, bool WITH_V>
+hipError_t launch_cmpsel(const DecArgs& a, hipStream_t s) {
+  const size_t vbytes = WITH_V ? (size_t)4 * 64 * (DV + 8) * 2 : 0;
+  if (a.nbp <= 1024) {
+    auto k = k_dec_cmpsel<DQ, DV, WITH_V, 16>;
+    const size_t lds = (64 * 16 + 32) * 4 + vbytes;
+    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+  } else {
+    auto k = k_dec_cmpsel<DQ, DV, WITH_V, MAX_NB_LANE>;
+    const size_t lds = (64 * MAX_NB_LANE + 32) * 4 + vbytes;
+    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+  }
+  return hipGetLastError();
 }
 
 // mode: 0 selection only, 1 whole forward, 2 selected branch on a given idx
 template <int DQ, int DV>
 hipError_t run_t(const DecArgs& a, int mode, bool out_f32, hipStream_t s, Phases* ph) {
-  const int64_t nsw = a.n_sel_waves + a.n_win_waves;
   if (mode != 2) {
     // selection only: the value summaries are not an input (and not read)
-    const unsigned gc = (unsigned)((a.R * a.G * a.n_cmp_waves + 3) / 4);
-    if (mode == 0) k_dec_cmp<DQ, DV, false><<<gc, 256, 0, s>>>(a);
-    else k_dec_cmp<DQ, DV, true><<<gc, 256, 0, s>>>(a);
+    hipError_t e = mode == 0 ? launch_cmpsel<DQ, DV, false>(a, s) : launch_cmpsel<DQ, DV, true>(a, s);
+    if (e != hipSuccess) return e;
     if (ph) ph->mark();
-    if (a.nbp <= 1024) k_dec_select<DV, 16><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
-    else k_dec_select<DV, MAX_NB_LANE><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
-    if (ph) ph->mark();
-    if (mode == 0) return hipGetLastError();
+    if (mode == 0) return hipSuccess;
   }
-  k_dec_attn<DQ, DV><<<(unsigned)((a.R * a.G * nsw + 3) / 4), 256, 0, s>>>(a);
-  if (ph) ph->mark();
-  if (out_f32) k_dec_merge<DV, float><<<(unsigned)(a.R * a.G), 4 * DV, 0, s>>>(a);
-  else k_dec_merge<DV, uint16_t><<<(unsigned)(a.R * a.G), 4 * DV, 0, s>>>(a);
+  if (out_f32) k_dec_attnmerge<DQ, DV, float><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+  else k_dec_attnmerge<DQ, DV, uint16_t><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
   if (ph) ph->mark();
   return hipGetLastError();
 }
@@ -422,12 +436,12 @@ hipError_t run_t(const DecArgs& a, int mode, bool out_f32, hipStream_t s, Phases
 
 void decode_layout(const Prob& P, int64_t* n_cmp_waves, int64_t* n_sel_waves, int64_t* n_win_waves) {
   const int64_t nbp = (P.nb + 63) / 64 * 64;
-  *n_cmp_waves = (nbp / 64 + TILES_PER_CMP_WAVE - 1) / TILES_PER_CMP_WAVE;
+  // the summary tiles dealt round-robin over at most 4 waves; the chosen
+  // blocks and the window's blocks round-robin over 4 waves, one record each
+  *n_cmp_waves = nbp / 64 < MAX_CMP_WAVES ? nbp / 64 : MAX_CMP_WAVES;
   if (*n_cmp_waves < 1) *n_cmp_waves = 1;
-  *n_sel_waves = (P.n + SLOTS_PER_WAVE - 1) / SLOTS_PER_WAVE;
-  // window blocks: at most ceil(w / 64) + 1, spread over waves of <= SLOTS_PER_WAVE + 1 blocks
-  const int64_t wblocks = P.w > 0 ? (P.w + 63) / 64 + 1 : 0;
-  *n_win_waves = wblocks > 0 ? (wblocks + SLOTS_PER_WAVE) / (SLOTS_PER_WAVE + 1) : 1;
+  *n_sel_waves = kAttnWaves;
+  *n_win_waves = kAttnWaves;
 }
 
 bool decode_ok(const Prob& P) {

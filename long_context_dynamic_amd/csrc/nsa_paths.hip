@@ -130,10 +130,8 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
   int n = 0;
   if (!have_cmp) list[n++] = "pool";
   if (decode_ok(P)) {
-    list[n++] = "dec_cmp";
-    list[n++] = "dec_select";
-    list[n++] = "dec_attn";
-    list[n++] = "dec_merge";
+    list[n++] = "dec_cmp_select";
+    list[n++] = "dec_attn_merge";
   } else if (moba_ok(P)) {
     list[n++] = "transpose_v";
     list[n++] = "moba_select";
