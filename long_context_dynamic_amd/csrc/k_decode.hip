@@ -3,6 +3,8 @@
 // group-shared selection keeps small).  Same arithmetic as the prefill path,
 // reorganised so that many waves stream the cache at once:
 //
+//   k_dec_fused      one workgroup per (row, group) for the whole step: the
+//                    two phases below back to back, with barriers between.
 //   k_dec_cmpsel     one workgroup per (row, group): 4 waves share out the
 //                    64-summary tiles (compressed-branch logits kept in zbuf
 //                    for the importance, a partial softmax-weighted sum of
@@ -286,7 +288,7 @@ __device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64
     }
   }
   __syncthreads();
-  if (tid >= 64) return;
+  if (tid >= 64) return;  // callers that continue hold a barrier after this
   int32_t* orow = a.idx + (row * a.G + g) * a.n;
   float* srow = a.score ? a.score + (row * a.G + g) * a.n : nullptr;
   int cj;
@@ -399,6 +401,48 @@ __global__ void __launch_bounds__(256) k_dec_attnmerge(DecArgs a) {
   merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
 }
 
+// The whole decoding step of one (row, group) in one workgroup: compressed
+// branch, selection, chosen and window blocks, merge -- three barriers, no
+// launch in between, and the (row, group)s of the batch at different phases
+// across the chip.
+template <int DQ, int DV, int NBL, typename TO>
+__global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* imp = (float*)smem;                          // [64 * NBL]
+  float* sM = imp + 64 * NBL;                         // [16]
+  float* sL = sM + 16;                                // [16]
+  float(*coef)[kMaxRecords] = (float(*)[kMaxRecords])(sL + 16);  // [16][kMaxRecords]
+  float* slse = (float*)(coef + 16);                  // [16]
+  uint16_t* vt = (uint16_t*)(slse + 16);              // [4][64 * (DV + 8)]
+  const int wave = threadIdx.x >> 6;
+  const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
+  uint16_t* myv = vt + wave * 64 * (DV + 8);
+  if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, true>(a, row, g, wave, myv);
+  __syncthreads();
+  select_body<DV, NBL>(a, row, g, threadIdx.x, imp, sM, sL);
+  __syncthreads();  // the chosen blocks are in idx
+  attn_wave<DQ, DV>(a, row, g, wave, myv);
+  __syncthreads();
+  merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
+}
+
+template <int DQ, int DV, typename TO>
+hipError_t launch_fused(const DecArgs& a, hipStream_t s) {
+  const size_t fixed = (16 + 16 + 16 * kMaxRecords + 16) * 4 + (size_t)4 * 64 * (DV + 8) * 2;
+  if (a.nbp <= 1024) {
+    auto k = k_dec_fused<DQ, DV, 16, TO>;
+    const size_t lds = 64 * 16 * 4 + fixed;
+    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+  } else {
+    auto k = k_dec_fused<DQ, DV, MAX_NB_LANE, TO>;
+    const size_t lds = 64 * MAX_NB_LANE * 4 + fixed;
+    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
 template <int DQ, int DV, bool WITH_V>
 hipError_t launch_cmpsel(const DecArgs& a, hipStream_t s) {
   const size_t vbytes = WITH_V ? (size_t)4 * 64 * (DV + 8) * 2 : 0;
@@ -419,17 +463,19 @@ hipError_t launch_cmpsel(const DecArgs& a, hipStream_t s) {
 // mode: 0 selection only, 1 whole forward, 2 selected branch on a given idx
 template <int DQ, int DV>
 hipError_t run_t(const DecArgs& a, int mode, bool out_f32, hipStream_t s, Phases* ph) {
-  if (mode != 2) {
+  hipError_t e;
+  if (mode == 0) {
     // selection only: the value summaries are not an input (and not read)
-    hipError_t e = mode == 0 ? launch_cmpsel<DQ, DV, false>(a, s) : launch_cmpsel<DQ, DV, true>(a, s);
-    if (e != hipSuccess) return e;
-    if (ph) ph->mark();
-    if (mode == 0) return hipSuccess;
+    e = launch_cmpsel<DQ, DV, false>(a, s);
+  } else if (mode == 1) {
+    e = out_f32 ? launch_fused<DQ, DV, float>(a, s) : launch_fused<DQ, DV, uint16_t>(a, s);
+  } else {
+    if (out_f32) k_dec_attnmerge<DQ, DV, float><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+    else k_dec_attnmerge<DQ, DV, uint16_t><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+    e = hipGetLastError();
   }
-  if (out_f32) k_dec_attnmerge<DQ, DV, float><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
-  else k_dec_attnmerge<DQ, DV, uint16_t><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
   if (ph) ph->mark();
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace

@@ -130,8 +130,7 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
   int n = 0;
   if (!have_cmp) list[n++] = "pool";
   if (decode_ok(P)) {
-    list[n++] = "dec_cmp_select";
-    list[n++] = "dec_attn_merge";
+    list[n++] = "dec_step";
   } else if (moba_ok(P)) {
     list[n++] = "transpose_v";
     list[n++] = "moba_select";
