@@ -14,11 +14,18 @@
 //   images     paired-row copies of k, v and of the summaries and tiled V^T
 //              copies, so that the global matrix-op operands below are
 //              contiguous 16-byte reads.
-//   k_bwd_q    one wave per (token, group), 16 heads as the matrix N:
-//              per branch, a statistics pass (log-sum-exp, output, dgamma)
-//              and a gradient pass that recomputes P and accumulates dq
-//              (K^T operands by transposing reads of the wave's LDS copy of
-//              the chunk's K rows).
+//   k_bwd_qcw  compressed and window branches from the query side: one
+//              workgroup per 8 tokens of a group, one wave per token (16
+//              heads as the matrix N), the 64-key tiles of K and V rows
+//              through LDS once for all 8; per branch a statistics pass
+//              (max, sum, sum p * <dout, v>) and a gradient pass that
+//              recomputes P and accumulates dq (K^T operands by transposing
+//              reads of the K tile).
+//   k_bwd_q    the selected branch's dq, one wave per (token, group): its
+//              statistics merged from the key side's records, then P
+//              recomputed over the chosen blocks streamed from global
+//              memory (K^T operands by transposing reads of the wave's LDS
+//              copy of each 32-key chunk).
 //   lists      for every (group, block), the (token, slot) entries that
 //              chose it, in token order (deterministic: per 256-token chunk
 //              histograms, column prefix sums, one ordered fill per chunk).
@@ -43,6 +50,7 @@
 #include "nsa_mfma.h"
 #include "nsa_paths.h"
 #include "nsa_prefill.h"
+#include "nsa_tile.h"
 
 namespace nsa {
 namespace {
@@ -166,6 +174,8 @@ __device__ __forceinline__ ChunkIter chunks_of(const BwArgs& a, int br, int64_t 
   return it;
 }
 
+// The selected branch's dq (its statistics come from the key side's
+// records), added to the dq that k_bwd_qcw wrote for the other two branches.
 template <int DQ, int DV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_bwd_q(BwArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -191,13 +201,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     return make_rsrc(base + bg * rows * D, (uint32_t)(rows * D * 2));
   };
 
-  // ---- statistics of every branch: log-sum-exp, <dout, O_b>, gate ----
+  // ---- statistics of the selected branch: log-sum-exp, <dout, O_b>, gate ----
   float lse[3], dd[3], gam[3];
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
     lse[br] = INFINITY;
     dd[br] = 0.f;
     gam[br] = 0.f;
+    if (br != BR_SLC) continue;  // the other two: k_bwd_qcw
     float dsig = 0.f;
     if (!(a.flags & branch_flag(br))) {
       if (lg == 0) {
@@ -306,7 +317,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   for (int dt = 0; dt < DQ / 16; ++dt) dqa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
-    if (!(a.flags & branch_flag(br)) || !(lse[br] < INFINITY)) continue;  // lse is wave-uniform per head row
+    if (br != BR_SLC || !(a.flags & branch_flag(br)) || !(lse[br] < INFINITY)) continue;  // uniform per token
     const bool cmp = br == BR_CMP;
     const __amdgpu_buffer_rsrc_t kr = cmp ? rs(a.kcG, a.nbp, DQ) : rs(a.kG, a.Lp, DQ);
     const __amdgpu_buffer_rsrc_t vgr = cmp ? rs(a.vcG, a.nbp, DV) : rs(a.vG, a.Lp, DV);
@@ -344,7 +355,189 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
         dqa[dt] = mfma16(ld_vt_pair(kt, 8 * lg, 8 * lg + 4, 16 * dt, KS, lr), dsf, dqa[dt]);
     }
   }
-  // dq^T: lane holds dims 16*dt + 4*lg + r of head lr
+  // dq^T: lane holds dims 16*dt + 4*lg + r of head lr; k_bwd_qcw wrote the rest
+  float* dqr = a.dq + row * DQ + 4 * lg;
+#pragma unroll
+  for (int dt = 0; dt < DQ / 16; ++dt) *(f32x4*)(dqr + 16 * dt) += dqa[dt] * a.scale;
+}
+
+// ---------------------------------------------------------------------------
+// Compressed and window branches from the query side, for 8 consecutive
+// tokens of one group per workgroup (one wave per token): the 64-key tiles of
+// K rows and V rows pass through LDS once for all 8.  Per branch a
+// statistics pass (max, sum and sum p * <dout, v> online) and a gradient
+// pass (dS = gamma P (dP - <dout, O>), dq^T += K^T dS^T with K^T operands by
+// transposing reads of the K tile).  Writes dq (the selected branch's part
+// is added later), the statistics the key side reads, and dgates.
+constexpr int kQTok = 8;
+
+template <int D, int NT>
+struct RowStager {  // 64 rows of a [B, N, G, D] tensor, rows clamped to N - 1
+  static constexpr int C = 64 * D / 8, PT = (C + NT - 1) / NT, S = D + 16;
+  u32x4 r[PT];
+  __device__ __forceinline__ void load(const uint16_t* src, int64_t N, int64_t row0, int64_t b, int64_t g, int64_t G) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + NT * i;
+      if (C % NT == 0 || c < C) {
+        int64_t row = row0 + c / (D / 8);
+        if (row > N - 1) row = N - 1;
+        r[i] = *(const u32x4*)(src + ((b * N + row) * G + g) * D + 8 * (c % (D / 8)));
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst) const {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + NT * i;
+      if (C % NT == 0 || c < C) *(u32x4*)(dst + (c / (D / 8)) * S + 8 * (c % (D / 8))) = r[i];
+    }
+  }
+};
+
+template <int DQ, int DV>
+__global__ void __launch_bounds__(64 * kQTok) k_bwd_qcw(BwArgs a) {
+  constexpr int KS = DQ + 16;
+  __shared__ __align__(16) uint16_t kt[64 * KS];
+  __shared__ __align__(16) uint16_t vr[64 * (DV + 16)];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int64_t ntt = (a.T + kQTok - 1) / kQTok;
+  const int64_t g = blockIdx.x % a.G;
+  const int64_t tile = ntt - 1 - (blockIdx.x / a.G) % ntt;  // longest rows first
+  const int64_t b = blockIdx.x / (a.G * ntt);
+  const int64_t t = tile * kQTok + wave;
+  const bool active = t < a.T;
+  const int64_t t_last = (tile * kQTok + kQTok - 1 < a.T - 1) ? tile * kQTok + kQTok - 1 : a.T - 1;
+  const int64_t p = a.L - a.T + (active ? t : t_last);
+  const int64_t p_first = a.L - a.T + tile * kQTok, p_last = a.L - a.T + t_last;
+  const int64_t row = ((b * a.T + (active ? t : t_last)) * a.G + g) * 16 + lr;  // (b, t, head lr)
+  const int64_t nrow = a.B * a.T * a.H;
+  const float c2 = a.scale * kLog2e;
+
+  bf16x8 qf[DQ / 32], df[DV / 32];
+#pragma unroll
+  for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = ld8(a.q + row * DQ + 8 * lg + 32 * ks);
+#pragma unroll
+  for (int ks = 0; ks < DV / 32; ++ks) df[ks] = ld8(a.dout + row * DV + 8 * lg + 32 * ks);
+  f32x4 dqa[DQ / 16];
+#pragma unroll
+  for (int dt = 0; dt < DQ / 16; ++dt) dqa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  RowStager<DQ, 64 * kQTok> sk;
+  RowStager<DV, 64 * kQTok> sv;
+
+  // the selected branch's statistics are written by k_bwd_q; when that
+  // branch is off, its defaults here
+  if (!(a.flags & NSA_F_SLC) && active && lg == 0) {
+    a.stat[(BR_SLC * 3 + 0) * nrow + row] = INFINITY;
+    a.stat[(BR_SLC * 3 + 1) * nrow + row] = 0.f;
+    a.stat[(BR_SLC * 3 + 2) * nrow + row] = 0.f;
+    if (a.dgates) a.dgates[row * 3 + BR_SLC] = 0.f;
+  }
+  for (int br = 0; br < 3; br += 2) {  // BR_CMP, BR_WIN
+    const bool on = (a.flags & branch_flag(br)) && (br == BR_CMP ? a.nb > 0 : a.w > 0);
+    float dsig = 0.f;
+    const float gb = on ? gate_val(a, row, br, &dsig) : 0.f;
+    // tiles and this token's visible keys [klo, khi]
+    const uint16_t* ksrc = br == BR_CMP ? a.kc : a.k;
+    const uint16_t* vsrc = br == BR_CMP ? a.vc : a.v;
+    const int64_t N = br == BR_CMP ? a.nb : a.L;
+    int64_t j0 = 0, j1 = -1, klo = 0, khi = -1;  // tiles j0 .. j1
+    if (on) {
+      if (br == BR_CMP) {
+        int64_t nvm = (p_last + 1) / kBlk;
+        if (nvm > a.nb) nvm = a.nb;
+        j1 = (nvm + 63) / 64 - 1;
+        int64_t nv = (p + 1) / kBlk;
+        if (nv > a.nb) nv = a.nb;
+        khi = nv - 1;
+      } else {
+        int64_t lo = p_first - a.w + 1;
+        if (lo < 0) lo = 0;
+        j0 = lo / 64;
+        j1 = p_last / 64;
+        klo = p - a.w + 1 < 0 ? 0 : p - a.w + 1;
+        khi = p;
+      }
+    }
+    if (!active) khi = -1;
+    float m = -INFINITY, l = 0.f, u = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+      // every wave stays in the tile loop (it holds barriers); a token with
+      // an empty key set computes nothing in the gradient pass
+      const bool live = pass == 0 || l > 0.f;
+      const float lb = live && pass == 1 ? m * c2 + __log2f(l) : 0.f;
+      const float db = live && pass == 1 ? u / l : 0.f;
+      if (j1 >= j0) {
+        sk.load(ksrc, N, j0 * 64, b, g, a.G);
+        sv.load(vsrc, N, j0 * 64, b, g, a.G);
+      }
+      for (int64_t jt = j0; jt <= j1; ++jt) {
+        __syncthreads();
+        sk.store(kt);
+        sv.store(vr);
+        __syncthreads();
+        if (jt + 1 <= j1) {
+          sk.load(ksrc, N, (jt + 1) * 64, b, g, a.G);
+          sv.load(vsrc, N, (jt + 1) * 64, b, g, a.G);
+        }
+        if (!live || jt * 64 > khi || jt * 64 + 63 < klo) continue;  // nothing visible to this token
+        f32x4 s[4], dp[4];
+        qk_tile_T<DQ>(kt, qf, s, lr, lg);
+        qk_tile_T<DV>(vr, df, dp, lr, lg);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t key = jt * 64 + 16 * mt + 4 * lg + r;
+            if (key < klo || key > khi) s[mt][r] = -INFINITY;
+          }
+        if (pass == 0) {
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) tmax = fmaxf(tmax, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+          tmax = xor_max16_32(tmax);
+          if (tmax > m) {
+            const float alpha = fast_exp2((m - tmax) * c2);
+            l *= alpha;
+            u *= alpha;
+            m = tmax;
+          }
+          const float mc = m * c2;
+          float ls = 0.f, us = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float e = fast_exp2(fmaf(s[mt][r], c2, -mc));
+              ls += e;
+              us = fmaf(e, dp[mt][r], us);
+            }
+          l += xor_sum16_32(ls);
+          u += xor_sum16_32(us);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[mt][r] = gb * fast_exp2(fmaf(s[mt][r], c2, -lb)) * (dp[mt][r] - db);
+          const bf16x8 d01 = pack8(s[0], s[1]), d23 = pack8(s[2], s[3]);
+#pragma unroll
+          for (int dt = 0; dt < DQ / 16; ++dt) {
+            dqa[dt] = mfma16(ld_vt_pair(kt, 4 * lg, 16 + 4 * lg, 16 * dt, KS, lr), d01, dqa[dt]);
+            dqa[dt] = mfma16(ld_vt_pair(kt, 32 + 4 * lg, 48 + 4 * lg, 16 * dt, KS, lr), d23, dqa[dt]);
+          }
+        }
+      }
+    }
+    // statistics for the key side and dgates
+    if (active && lg == 0) {
+      const bool any = on && l > 0.f;
+      a.stat[(br * 3 + 0) * nrow + row] = any ? m * c2 + __log2f(l) : INFINITY;
+      a.stat[(br * 3 + 1) * nrow + row] = any ? u / l : 0.f;
+      a.stat[(br * 3 + 2) * nrow + row] = on ? gb : 0.f;
+      if (a.dgates) a.dgates[row * 3 + br] = any ? (u / l) * dsig : 0.f;
+    }
+  }
+  if (!active) return;
   float* dqr = a.dq + row * DQ + 4 * lg;
 #pragma unroll
   for (int dt = 0; dt < DQ / 16; ++dt) *(f32x4*)(dqr + 16 * dt) = dqa[dt] * a.scale;
@@ -853,7 +1046,8 @@ hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
     k_bwd_kv<DQ, DV, KV_STAT><<<(unsigned)chunks_max, 256, 0, s>>>(a);
     ph.mark();
   }
-  k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
+  k_bwd_qcw<DQ, DV><<<(unsigned)(P.B * P.G * ((P.T + kQTok - 1) / kQTok)), 64 * kQTok, 0, s>>>(a);
+  if (slc) k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
   ph.mark();
   const int64_t ntile = (P.L + 63) / 64;
   if (P.has(NSA_F_WIN) && P.w > 0) {
