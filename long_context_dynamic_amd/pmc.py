@@ -32,8 +32,10 @@ CSRC = os.path.join(PKG, "csrc")
 
 # sources whose text decides each kernel's code
 KERNEL_SOURCES = {
-    "selected": ["k_prefill.hip", "nsa_prefill.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
-    "cmp_select_window": ["k_prefill.hip", "nsa_prefill.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
+    "selected": ["k_prefill.hip", "nsa_prefill.h", "nsa_frag.h", "nsa_tile.h", "nsa_topk.h", "nsa_mfma.h",
+                 "nsa_internal.h"],
+    "cmp_select_window": ["k_prefill.hip", "nsa_prefill.h", "nsa_frag.h", "nsa_tile.h", "nsa_topk.h", "nsa_mfma.h",
+                          "nsa_internal.h"],
     "moba_attn": ["k_moba.hip", "nsa_moba.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
     "moba_own_block": ["k_moba.hip", "nsa_moba.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
 }
