@@ -344,15 +344,21 @@ __device__ __forceinline__ void merge_body(const DecArgs& a, int64_t row, int64_
   const bool use_win = (a.flags & NSA_F_WIN) && a.w > 0;
   for (int it = tid; it < 16 * (DV / 4); it += nthr) {
     const int h = it / (DV / 4), d = 4 * (it % (DV / 4));
-    f32x4 v[kMaxRecords];
-#pragma unroll
-    for (int w = 0; w < kMaxRecords; ++w)
-      if (w < nwaves) v[w] = *(const f32x4*)(base + w * part_floats<DV>() + h * DV + d);
     const int64_t hrow = row * a.H + g * 16 + h;
     f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // records in groups of 4 loads in flight (few registers: the streaming
+    // phase before sets the budget)
+    for (int w0 = 0; w0 < nwaves; w0 += 4) {
+      f32x4 v[4];
 #pragma unroll
-    for (int w = 0; w < kMaxRecords; ++w)
-      if (w < nwaves) br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v[w] * coef[h][w];
+      for (int i = 0; i < 4; ++i)
+        if (w0 + i < nwaves) v[i] = *(const f32x4*)(base + (w0 + i) * part_floats<DV>() + h * DV + d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int w = w0 + i;
+        if (w < nwaves) br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v[i] * coef[h][w];
+      }
+    }
     f32x4 out = {0.f, 0.f, 0.f, 0.f};
     if (use_cmp) out += br[0] * dgate(a, hrow, 0);
     if (use_slc) out += br[1] * dgate(a, hrow, 1);
