@@ -63,9 +63,10 @@ __global__ void __launch_bounds__(256) k_pool_vec(const T* __restrict__ k, const
   double sum[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) sum[e] = 0.0;
-#pragma unroll 8
-  for (int64_t t = 0; t < bs; ++t) {
-    const uint4 w = *(const uint4*)(src + t * stride);
+  // the tokens' loads go out kBatch at a time (long blocks would otherwise
+  // wait on one load after another); the adds stay in token order
+  constexpr int kBatch = 32;
+  auto add = [&](uint4 w) {
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
@@ -74,7 +75,16 @@ __global__ void __launch_bounds__(256) k_pool_vec(const T* __restrict__ k, const
       else x = __uint_as_float(u[e]);
       sum[e] += (double)x;
     }
+  };
+  int64_t t = 0;
+  for (; t + kBatch <= bs; t += kBatch) {
+    uint4 w[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) w[i] = *(const uint4*)(src + (t + i) * stride);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) add(w[i]);
   }
+  for (; t < bs; ++t) add(*(const uint4*)(src + t * stride));
   T* dst = (is_k ? kc : vc) + row * width + c0;
 #pragma unroll
   for (int e = 0; e < VE; ++e) st64(dst, e, sum[e] / (double)bs);
