@@ -4,7 +4,8 @@
 // reorganised so that many waves stream the cache at once:
 //
 //   k_dec_fused      one workgroup per (row, group) for the whole step: the
-//                    two phases below back to back, with barriers between.
+//                    two phases below back to back, with barriers between;
+//                    waves 1..3 stream the window while wave 0 does the top-k.
 //   k_dec_cmpsel     one workgroup per (row, group): 4 waves share out the
 //                    64-summary tiles (compressed-branch logits kept in zbuf
 //                    for the importance, a partial softmax-weighted sum of
@@ -211,18 +212,15 @@ __device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t 
                                [&](int64_t j) { return j < nvis; }, qf, a.scale * kLog2e, myv, zrow, a.nbp, rec);
 }
 
-// The selected and window blocks of one (row, group) on wave w of
-// kAttnWaves: chosen slots w, w + 4, .. (a record in selected slot w), then
-// window tiles w, w + 4, .. (a record in window slot w).
+// The chosen blocks of one (row, group) on wave w of kAttnWaves: slots w,
+// w + 4, .. (a record in selected slot w).
 template <int DQ, int DV>
-__device__ __forceinline__ void attn_wave(const DecArgs& a, int64_t row, int64_t g, int w, uint16_t* myv) {
+__device__ __forceinline__ void sel_wave(const DecArgs& a, int64_t row, int64_t g, int w, const bf16x8 (&qf)[DQ / 32],
+                                         uint16_t* myv) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
-  bf16x8 qf[DQ / 32];
-  load_q<DQ>(a, row, g, qf);
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
   float* recs = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves) * part_floats<DV>();
-  const float c = a.scale * kLog2e;
   int sel[kMaxSlotsPerWave];
   int ns = 0;
   if (a.flags & NSA_F_SLC) {
@@ -233,14 +231,26 @@ __device__ __forceinline__ void attn_wave(const DecArgs& a, int64_t row, int64_t
     }
   }
   stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return sel[i]; }, ns,
-                             [&](int64_t s) { return s <= p; }, qf, c, myv, nullptr, 0, recs + w * part_floats<DV>());
+                             [&](int64_t s) { return s <= p; }, qf, a.scale * kLog2e, myv, nullptr, 0,
+                             recs + w * part_floats<DV>());
+}
+
+// The window's 64-key tiles first, first + stride, .. of one (row, group)
+// (a record in window slot `slot`; none of them gives an empty record).
+template <int DQ, int DV>
+__device__ __forceinline__ void win_wave(const DecArgs& a, int64_t row, int64_t g, int slot, int first, int stride,
+                                         const bf16x8 (&qf)[DQ / 32], uint16_t* myv) {
+  const int64_t b = row / a.T, t = row % a.T;
+  const int64_t p = a.L - a.T + t;
+  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
+  float* recs = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves + a.n_sel_waves) * part_floats<DV>();
   int64_t lo = p - a.w + 1;
   if (lo < 0) lo = 0;
   const int64_t kb0 = lo / 64, nwt = ((a.flags & NSA_F_WIN) && a.w > 0) ? p / 64 - kb0 + 1 : 0;
-  const int nt = nwt > w ? (int)((nwt - w + kAttnWaves - 1) / kAttnWaves) : 0;
-  stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return (int)(kb0 + w + kAttnWaves * i); }, nt,
-                             [&](int64_t s) { return s <= p && s >= lo; }, qf, c, myv, nullptr, 0,
-                             recs + (a.n_sel_waves + w) * part_floats<DV>());
+  const int nt = nwt > first ? (int)((nwt - first + stride - 1) / stride) : 0;
+  stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return (int)(kb0 + first + stride * i); }, nt,
+                             [&](int64_t s) { return s <= p && s >= lo; }, qf, a.scale * kLog2e, myv, nullptr, 0,
+                             recs + slot * part_floats<DV>());
 }
 
 // Per-head softmax statistics of one (row, group) from the compressed-branch
@@ -402,7 +412,10 @@ __global__ void __launch_bounds__(256) k_dec_attnmerge(DecArgs a) {
   __shared__ float slse[16];
   const int wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
-  attn_wave<DQ, DV>(a, row, g, wave, vt[wave]);
+  bf16x8 qf[DQ / 32];
+  load_q<DQ>(a, row, g, qf);
+  sel_wave<DQ, DV>(a, row, g, wave, qf, vt[wave]);
+  win_wave<DQ, DV>(a, row, g, wave, wave, kAttnWaves, qf, vt[wave]);
   __syncthreads();
   merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
 }
@@ -425,9 +438,15 @@ __global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
   uint16_t* myv = vt + wave * 64 * (DV + 8);
   if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, true>(a, row, g, wave, myv);
   __syncthreads();
+  bf16x8 qf[DQ / 32];
+  load_q<DQ>(a, row, g, qf);
+  // wave 0 finishes the selection (top-k) while waves 1..3 stream the
+  // window, which does not depend on it; wave 0's window record is empty
   select_body<DV, NBL>(a, row, g, threadIdx.x, imp, sM, sL);
+  if (wave == 0) win_wave<DQ, DV>(a, row, g, 0, 1 << 30, 1, qf, myv);
+  else win_wave<DQ, DV>(a, row, g, wave, wave - 1, kAttnWaves - 1, qf, myv);
   __syncthreads();  // the chosen blocks are in idx
-  attn_wave<DQ, DV>(a, row, g, wave, myv);
+  sel_wave<DQ, DV>(a, row, g, wave, qf, myv);
   __syncthreads();
   merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
 }
