@@ -243,9 +243,54 @@ def run_backward(args, torch, nsa, workloads, inputs, workload="nsa_prefill_64k"
            "backward_mfma_frac": round(sum(kf.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
            "roofline": roofline(kf, per_phase, workload),
            "note": "gradients of the whole forward on its selection: dq, dk, dv (fp32), dgates"}
+    del idx
+    rec["training_step"] = run_training_step(args, torch, nsa, prob, t, ws, dq, dk, dv, dg, phases)
     del t, ws, dq, dk, dv, dg
     torch.cuda.empty_cache()
     return rec
+
+
+def run_training_step(args, torch, nsa, prob, t, bws, dq, dk, dv, dg, phases):
+    """One training step of the attention: nsa_forward_train (output,
+    selection and the per-branch statistics) then nsa_backward reading those
+    statistics, each timed with HIP events on the current stream."""
+    B, T, H = prob["batch"], prob["q_len"], prob["n_groups"] * prob["heads_per_group"]
+    out = torch.empty((B, T, H, prob["d_v"]), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((B, T, prob["n_groups"], prob["top_k"]), dtype=torch.int32, device="cuda")
+    saved = torch.empty(nsa.train_saved_bytes(prob), dtype=torch.uint8, device="cuda")
+    fws = nsa.alloc_workspace(prob)
+    K, W = args.steps, args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
+    fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+
+    def fwd():
+        nsa.forward_train(prob, t["q"], t["k"], t["v"], t["gates"], out=out, idx=idx, saved=saved, workspace=fws)
+
+    def bwd(events=None):
+        nsa.backward(prob, t["q"], t["k"], t["v"], t["gates"], idx, t["dout"], dq=dq, dk=dk, dv=dv, dgates=dg,
+                     workspace=bws, events=events, saved=saved)
+    for _ in range(W):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        fe[i][0].record()
+        fwd()
+        fe[i][1].record()
+        bwd(ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / K * 1e3
+    f_ms = float(np.mean([fe[i][0].elapsed_time(fe[i][1]) for i in range(K)]))
+    per_phase = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                 for j, name in enumerate(phases)}
+    b_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(K)]))
+    del out, idx, saved, fws
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "forward_train_ms": round(f_ms, 4), "backward_from_saved_ms": round(b_ms, 4),
+            "backward_phases_ms": {k: round(v, 4) for k, v in per_phase.items()},
+            "saved_bytes": nsa.train_saved_bytes(prob),
+            "note": "forward keeping per-branch log-sum-exp and bf16 outputs, backward reading them"}
 
 
 # ---------------------------------------------------------------- learned --
@@ -452,6 +497,7 @@ def run_only(args, torch, nsa, workloads, inputs):
     elif args.only == "backward":
         rec = run_backward(args, torch, nsa, workloads, inputs, args.workload)
         log(f"backward {rec['ms_per_step']} ms/step {rec['phases_ms']}")
+        log(f"training step {rec['training_step']}")
     elif args.only == "prefill":
         args.steps, args.warmup = max(1, args.steps), args.warmup
         _, _, ms, per_phase = run_prefill(args, torch, nsa, workloads, inputs)

@@ -213,6 +213,32 @@ nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* 
                        const nsa_params* params, void* out);
 
 /*
+ * Training forward: nsa_forward (summaries mean-pooled in the workspace)
+ * that also hands back what its backward needs, so nsa_backward need not
+ * recompute it ([P1] s6: NSA trains end to end, so every forward in
+ * training is followed by a backward over the same selection).
+ *   out    as nsa_forward.
+ *   idx    int32 [B, q_len, G, top_k]: the selection (as nsa_select_topk).
+ *   saved  nsa_train_saved_bytes(params) bytes, owned by the caller, to be
+ *          passed to nsa_backward with the same q, k, v, gates and idx:
+ *          fp32 [3][B, q_len, H] per branch (compressed, selected, window)
+ *          the natural log-sum-exp of the scaled logits over the branch's
+ *          key set (-inf when the set is empty or the branch off), then at
+ *          the next 256-byte boundary bf16 [3][B, q_len, H, d_v] the
+ *          branch's normalised output O_b (zeros when empty or off).
+ * params->k_cmp / v_cmp must be NULL.  Limits (NSA_ERR_UNSUPPORTED
+ * otherwise): those of nsa_backward, and q_len > 8 (shorter calls take the
+ * decoding path, which keeps no statistics).  Needs the workspace of
+ * nsa_forward.
+ */
+nsa_status nsa_forward_train(const void* q, const void* k, const void* v, const void* gates,
+                             const nsa_params* params, void* out, int32_t* idx, void* saved);
+
+/* Bytes of nsa_forward_train's saved statistics (0 if the params are invalid
+ * or outside its limits). */
+size_t nsa_train_saved_bytes(const nsa_params* params);
+
+/*
  * Backward of nsa_forward ([P1] s4 the gated three-branch sum; [P1] s6: NSA
  * trains end to end, the top-k choice passes no gradient, and the compressed
  * branch's output carries a training signal to every block).  Given the
@@ -232,14 +258,19 @@ nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* 
  * gate g_b: dg_b = <dout, O_b>, dS = g_b P (<dout, v> - dg_b),
  * dq += scale sum dS k, dk += scale dS q, dv += g_b P dout.
  * The summaries are recomputed (params->k_cmp / v_cmp are ignored).
+ * saved_or_null: nsa_forward_train's statistics for these inputs and idx;
+ * the per-branch log-sum-exp and <dout, O_b> are then read from it (the
+ * latter from the bf16 O_b) instead of being recomputed from q, k and v.
+ * NULL: all of it is recomputed.
  * Results are deterministic (no floating-point atomics).
  * Limits (NSA_ERR_UNSUPPORTED otherwise): dtype NSA_BF16, heads_per_group
  * 16, block 64 with sel_block 0 or 64, d_qk in {64, 128, 192}, d_v in
- * {64, 128}, top_k <= 32.  Needs nsa_backward_workspace_bytes of workspace.
+ * {64, 128}, top_k <= 32; with saved statistics also q_len > 8.  Needs
+ * nsa_backward_workspace_bytes of workspace.
  */
 nsa_status nsa_backward(const void* q, const void* k, const void* v, const void* gates,
-                        const int32_t* idx, const void* dout, float* dq, float* dk, float* dv,
-                        float* dgates, const nsa_params* params);
+                        const int32_t* idx, const void* dout, const void* saved_or_null, float* dq,
+                        float* dk, float* dv, float* dgates, const nsa_params* params);
 
 /* Workspace bytes nsa_backward needs for these params (0 if they are invalid
  * or outside its limits). */
@@ -249,7 +280,8 @@ size_t nsa_backward_workspace_bytes(const nsa_params* params);
  * (0 if the params are invalid or outside its limits); names[i]
  * (i < max_names) receives a static name of group i.  nsa_backward records
  * phase_events[0] before its first kernel and phase_events[i + 1] after
- * group i, as far as events are given. */
+ * group i, as far as events are given.  With saved statistics the group
+ * "bwd_kv_selected_stats" launches nothing. */
 int32_t nsa_backward_phases(const nsa_params* params, const char** names, int32_t max_names);
 
 /* Number of kernels nsa_forward launches for these params (0 if they are

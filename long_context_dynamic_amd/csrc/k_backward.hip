@@ -94,6 +94,26 @@ __device__ __forceinline__ float gate_val(const BwArgs& a, int64_t row, int br, 
   return x;
 }
 
+// <dout, O_b> for head lr from the training forward's saved normalised
+// branch output (bf16); df holds dout dims 32*ks + 8*lg + e of that head.
+template <int DV>
+__device__ __forceinline__ float saved_dot(const BwArgs& a, int br, int64_t row, int64_t nrow,
+                                           const bf16x8 (&df)[DV / 32], int lg) {
+  const uint16_t* orow = a.sv_o + (br * nrow + row) * DV + 8 * lg;
+  float s = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < DV / 32; ++ks) {
+    const u32x4 o = __builtin_bit_cast(u32x4, ld8(orow + 32 * ks));
+    const u32x4 d = __builtin_bit_cast(u32x4, df[ks]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(d[e] << 16), s);
+      s = fmaf(__uint_as_float(o[e] & 0xFFFF0000u), __uint_as_float(d[e] & 0xFFFF0000u), s);
+    }
+  }
+  return xor_sum16_32(s);
+}
+
 // ---------------------------------------------------------------------------
 // Query side.  Chunk c of a branch covers keys kb .. kb + 31 (kb a multiple
 // of 32); keys outside [klo, khi] are masked.  S^T tiles s0, s1 hold keys
@@ -191,9 +211,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   __shared__ __align__(16) uint16_t ktile[4][32 * KS];  // per wave: the chunk's 32 K rows
   uint16_t* kt = ktile[wave];
 
-  bf16x8 qf[DQ / 32];
+  bf16x8 qf[DQ / 32], df[DV / 32];
 #pragma unroll
   for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = ld8(a.q + row * DQ + 8 * lg + 32 * ks);
+#pragma unroll
+  for (int ks = 0; ks < DV / 32; ++ks) df[ks] = ld8(a.dout + row * DV + 8 * lg + 32 * ks);
 
   const uint32_t kofs = 16 * lg, tofs = (lr * 32 + 8 * lg) * 2;
   const int64_t bg = b * a.G + g;
@@ -220,6 +242,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
       continue;
     }
     gam[br] = gate_val(a, row, br, &dsig);
+    if (br == BR_SLC && a.sv_lse) {  // the training forward's statistics
+      const float lse_nat = a.sv_lse[br * nrow + row];
+      if (lse_nat > -INFINITY) {
+        lse[br] = lse_nat * kLog2e;
+        dd[br] = saved_dot<DV>(a, br, row, nrow, df, lg);
+      }
+      if (lg == 0) {
+        a.stat[(br * 3 + 0) * nrow + row] = lse[br];
+        a.stat[(br * 3 + 1) * nrow + row] = dd[br];
+        a.stat[(br * 3 + 2) * nrow + row] = gam[br];
+        if (a.dgates) a.dgates[row * 3 + br] = dd[br] * dsig;
+      }
+      continue;
+    }
     if (br == BR_SLC) {  // merge the key side's per-block records of this token's entries
       float M = -INFINITY, L = 0.f, U = 0.f;
       for (int i = 0; i < a.n; ++i) {
@@ -309,9 +345,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   }
 
   // ---- dq: recompute P, dP = dout . v, dS, dq += K^T dS ----
-  bf16x8 df[DV / 32];
-#pragma unroll
-  for (int ks = 0; ks < DV / 32; ++ks) df[ks] = ld8(a.dout + row * DV + 8 * lg + 32 * ks);
   f32x4 dqa[DQ / 16];
 #pragma unroll
   for (int dt = 0; dt < DQ / 16; ++dt) dqa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -460,13 +493,30 @@ __global__ void __launch_bounds__(64 * kQTok) k_bwd_qcw(BwArgs a) {
       }
     }
     if (!active) khi = -1;
-    float m = -INFINITY, l = 0.f, u = 0.f;
-    for (int pass = 0; pass < 2; ++pass) {
+    // statistics (lb: log-sum-exp in log2 units, db: <dout, O_b>) from the
+    // training forward, or from a first pass over the tiles
+    const bool saved = a.sv_lse != nullptr;
+    float m = -INFINITY, l = 0.f, u = 0.f, lb = 0.f, db = 0.f;
+    bool any = false;
+    if (saved && on && active) {
+      const float lse_nat = a.sv_lse[br * nrow + row];
+      any = lse_nat > -INFINITY;
+      if (any) {
+        lb = lse_nat * kLog2e;
+        db = saved_dot<DV>(a, br, row, nrow, df, lg);
+      }
+    }
+    for (int pass = saved ? 1 : 0; pass < 2; ++pass) {
+      if (pass == 1 && !saved) {
+        any = on && l > 0.f;
+        if (any) {
+          lb = m * c2 + __log2f(l);
+          db = u / l;
+        }
+      }
       // every wave stays in the tile loop (it holds barriers); a token with
       // an empty key set computes nothing in the gradient pass
-      const bool live = pass == 0 || l > 0.f;
-      const float lb = live && pass == 1 ? m * c2 + __log2f(l) : 0.f;
-      const float db = live && pass == 1 ? u / l : 0.f;
+      const bool live = pass == 0 || any;
       if (j1 >= j0) {
         sk.load(ksrc, N, j0 * 64, b, g, a.G);
         sv.load(vsrc, N, j0 * 64, b, g, a.G);
@@ -530,11 +580,10 @@ __global__ void __launch_bounds__(64 * kQTok) k_bwd_qcw(BwArgs a) {
     }
     // statistics for the key side and dgates
     if (active && lg == 0) {
-      const bool any = on && l > 0.f;
-      a.stat[(br * 3 + 0) * nrow + row] = any ? m * c2 + __log2f(l) : INFINITY;
-      a.stat[(br * 3 + 1) * nrow + row] = any ? u / l : 0.f;
+      a.stat[(br * 3 + 0) * nrow + row] = any ? lb : INFINITY;
+      a.stat[(br * 3 + 1) * nrow + row] = any ? db : 0.f;
       a.stat[(br * 3 + 2) * nrow + row] = on ? gb : 0.f;
-      if (a.dgates) a.dgates[row * 3 + br] = any ? (u / l) * dsig : 0.f;
+      if (a.dgates) a.dgates[row * 3 + br] = any ? db * dsig : 0.f;
     }
   }
   if (!active) return;
@@ -1043,7 +1092,8 @@ hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
     k_bwd_scan<<<1, 1024, 0, s>>>(a, nl);
     k_bwd_fill<<<(unsigned)(P.B * P.G * a.nct), 64, lds, s>>>(a);
     ph.mark();
-    k_bwd_kv<DQ, DV, KV_STAT><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    // with the training forward's statistics the group launches nothing
+    if (!a.sv_lse) k_bwd_kv<DQ, DV, KV_STAT><<<(unsigned)chunks_max, 256, 0, s>>>(a);
     ph.mark();
   }
   k_bwd_qcw<DQ, DV><<<(unsigned)(P.B * P.G * ((P.T + kQTok - 1) / kQTok)), 64 * kQTok, 0, s>>>(a);
@@ -1096,8 +1146,8 @@ int backward_phase_names(const Prob& P, const char** names, int max_names) {
 }
 
 hipError_t run_backward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
-                        const int32_t* idx, const void* dout, float* dq, float* dk, float* dv, float* dgates,
-                        void* ws, hipStream_t s, Phases& ph) {
+                        const int32_t* idx, const void* dout, const void* saved, float* dq, float* dk, float* dv,
+                        float* dgates, void* ws, hipStream_t s, Phases& ph) {
   const BwPlan w = plan(P);
   char* base = (char*)ws;
   BwArgs a;
@@ -1117,6 +1167,8 @@ hipError_t run_backward(const Prob& P, const void* q, const void* k, const void*
   a.kcG = (const uint16_t*)(base + w.kcG);
   a.vcG = (const uint16_t*)(base + w.vcG);
   a.vcT = (const uint16_t*)(base + w.vcT);
+  a.sv_lse = (const float*)saved;
+  a.sv_o = saved ? (const uint16_t*)((const char*)saved + saved_lse_bytes(P)) : nullptr;
   a.stat = (float*)(base + w.stat);
   a.srec = (float*)(base + w.srec);
   a.cnt = (int32_t*)(base + w.cnt);

@@ -41,6 +41,24 @@ __device__ __forceinline__ float gate_of(const PfArgs& a, int64_t row, int branc
   return (a.flags & NSA_F_GATE_LOGITS) ? sigmoid(x) : x;
 }
 
+// Training forward: branch br's natural log-sum-exp of the scaled logits
+// (-inf when the branch is off or its key set empty) and its normalised
+// output in bf16, for head lr of the row; o^T holds dims 16*dt + 4*lg + r.
+template <int DV>
+__device__ __forceinline__ void save_branch(const PfArgs& a, int br, int64_t row, bool on, float lse,
+                                            const f32x4 (&o)[DV / 16], float inv_l, int lg) {
+  const int64_t nrow = a.B * a.T * a.H;
+  if (lg == 0) a.sv_lse[br * nrow + row] = on ? lse : -INFINITY;
+  uint16_t* orow = a.sv_o + (br * nrow + row) * DV + 4 * lg;
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) {
+    const f32x4 v = on ? o[dt] * inv_l : f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                     (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+    *(u32x2*)(orow + 16 * dt) = w;
+  }
+}
+
 __device__ __forceinline__ bool better(float v, int j, float bv, int bj) {
   return v > bv || (v == bv && j < bj);
 }
@@ -183,6 +201,7 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     const float g0 = use_cmp ? gate_of(a, row, 0) * inv_l : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) fin[dt] = o[dt] * g0;
+    if (a.sv_lse && active) save_branch<DV>(a, 0, row, use_cmp && l > 0.f, m * a.scale + logf(l), o, inv_l, lg);
   }
 
   // ---- pass 2: importance of each visible block, summed over the heads ----
@@ -255,6 +274,9 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     const float g2 = gate_of(a, row, 2) * (l2 > 0.f ? 1.f / l2 : 0.f);
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) fin[dt] += o[dt] * g2;
+    if (a.sv_lse && active) save_branch<DV>(a, 2, row, l2 > 0.f, m2 * a.scale + logf(l2), o, 1.f / l2, lg);
+  } else if (FWD && a.sv_lse && active) {
+    save_branch<DV>(a, 2, row, false, 0.f, o, 0.f, lg);
   }
 
   if (active) {
@@ -411,6 +433,7 @@ __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
   if (FWD) {
     float g1 = 0.f;
     if (a.flags & NSA_F_SLC) g1 = gate_of(a, row, 1) * inv_l;
+    if (a.sv_lse) save_branch<DV>(a, 1, row, use_slc && l > 0.f, m * a.scale + logf(l), o, inv_l, lg);
     const float* arow = a.acc + row * DV + 4 * lg;
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt)

@@ -4,9 +4,11 @@
 #include <string.h>
 
 #include "nsa_backward.h"
+#include "nsa_decode.h"
 #include "nsa_internal.h"
 #include "nsa_learned.h"
 #include "nsa_paths.h"
+#include "nsa_prefill.h"
 
 using nsa::Prob;
 
@@ -167,7 +169,37 @@ nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* 
   ph.ev = p->phase_events;
   ph.n = p->phase_events ? p->n_phase_events : 0;
   return hip_status(nsa::run_forward(P, q, k, v, gates, have_cmp ? p->k_cmp : nullptr,
-                                     have_cmp ? p->v_cmp : nullptr, out, ws, p->workspace,
+                                     have_cmp ? p->v_cmp : nullptr, out, nullptr, nullptr, ws, p->workspace,
+                                     (hipStream_t)p->stream, ph));
+}
+
+// A training forward runs the matrix-core prefill path (its kernels write the
+// statistics) with mean-pooled summaries (what the backward recomputes).
+static bool train_ok(const Prob& P) { return nsa::backward_ok(P) && nsa::prefill_fast_ok(P) && !nsa::decode_ok(P); }
+
+size_t nsa_train_saved_bytes(const nsa_params* p) {
+  Prob P;
+  if (describe(p, &P) != NSA_OK || !train_ok(P)) return 0;
+  return nsa::saved_bytes(P);
+}
+
+nsa_status nsa_forward_train(const void* q, const void* k, const void* v, const void* gates, const nsa_params* p,
+                             void* out, int32_t* idx, void* saved) {
+  Prob P;
+  nsa_status st = describe(p, &P);
+  if (st != NSA_OK) return st;
+  const int nbr = n_branches(P.flags);
+  if (nbr == 0 || (gates == nullptr && nbr > 1)) return NSA_ERR_INVALID_ARG;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out) || !opt_ok(gates) || !ptr_ok(idx) || !ptr_ok(saved))
+    return NSA_ERR_INVALID_ARG;
+  if (p->k_cmp != nullptr || p->v_cmp != nullptr || !train_ok(P)) return NSA_ERR_UNSUPPORTED;
+  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Forward, false);
+  if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
+  if (p->n_phase_events < 0 || (p->n_phase_events > 0 && !p->phase_events)) return NSA_ERR_INVALID_ARG;
+  nsa::Phases ph;
+  ph.ev = p->phase_events;
+  ph.n = p->phase_events ? p->n_phase_events : 0;
+  return hip_status(nsa::run_forward(P, q, k, v, gates, nullptr, nullptr, out, idx, saved, ws, p->workspace,
                                      (hipStream_t)p->stream, ph));
 }
 
@@ -178,16 +210,17 @@ size_t nsa_backward_workspace_bytes(const nsa_params* p) {
 }
 
 nsa_status nsa_backward(const void* q, const void* k, const void* v, const void* gates, const int32_t* idx,
-                        const void* dout, float* dq, float* dk, float* dv, float* dgates, const nsa_params* p) {
+                        const void* dout, const void* saved, float* dq, float* dk, float* dv, float* dgates,
+                        const nsa_params* p) {
   Prob P;
   nsa_status st = describe(p, &P);
   if (st != NSA_OK) return st;
   const int nbr = n_branches(P.flags);
   if (nbr == 0 || (gates == nullptr && nbr > 1) || (gates == nullptr && dgates != nullptr)) return NSA_ERR_INVALID_ARG;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) ||
-      !ptr_ok(dv) || !opt_ok(gates) || !opt_ok(dgates))
+      !ptr_ok(dv) || !opt_ok(gates) || !opt_ok(dgates) || !opt_ok(saved))
     return NSA_ERR_INVALID_ARG;
-  if (!nsa::backward_ok(P)) return NSA_ERR_UNSUPPORTED;
+  if (!nsa::backward_ok(P) || (saved && !train_ok(P))) return NSA_ERR_UNSUPPORTED;
   const size_t need = nsa::backward_workspace_bytes(P);
   if (!ptr_ok(p->workspace) || p->workspace_bytes < need) return NSA_ERR_WORKSPACE;
   if (p->n_phase_events < 0 || (p->n_phase_events > 0 && !p->phase_events)) return NSA_ERR_INVALID_ARG;
@@ -195,7 +228,7 @@ nsa_status nsa_backward(const void* q, const void* k, const void* v, const void*
   ph.ev = p->phase_events;
   ph.n = p->phase_events ? p->n_phase_events : 0;
   ph.s = (hipStream_t)p->stream;
-  return hip_status(nsa::run_backward(P, q, k, v, gates, idx, dout, dq, dk, dv, dgates, p->workspace,
+  return hip_status(nsa::run_backward(P, q, k, v, gates, idx, dout, saved, dq, dk, dv, dgates, p->workspace,
                                       (hipStream_t)p->stream, ph));
 }
 

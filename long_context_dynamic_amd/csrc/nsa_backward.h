@@ -22,6 +22,8 @@ struct BwArgs {
   const uint16_t* kcG;    // the same three images of the summaries (nbp rows)
   const uint16_t* vcG;
   const uint16_t* vcT;
+  const float* sv_lse;    // training forward's statistics or NULL: [3][B*T*H] natural log-sum-exp,
+  const uint16_t* sv_o;   //   [3][B*T*H][DV] normalised branch outputs (bf16)
   float* stat;            // [3 branches][3: lse (log2 units), <dout, O_b>, gate][B*T*H]
   int32_t* cnt;           // [B, G, nct, nbk] entries per (256-token chunk, block)
   int32_t* tot;           // [B*G*nbk + 1] entries per list
@@ -52,7 +54,7 @@ size_t backward_workspace_bytes(const Prob& P);
 // Names of the kernel groups run_backward times (one event after each), in order.
 int backward_phase_names(const Prob& P, const char** names, int max_names);
 hipError_t run_backward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
-                        const int32_t* idx, const void* dout, float* dq, float* dk, float* dv, float* dgates,
-                        void* ws, hipStream_t s, Phases& ph);
+                        const int32_t* idx, const void* dout, const void* saved, float* dq, float* dk, float* dv,
+                        float* dgates, void* ws, hipStream_t s, Phases& ph);
 
 }  // namespace nsa

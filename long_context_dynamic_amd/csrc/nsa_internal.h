@@ -22,6 +22,13 @@ struct Prob {
   int n_forced() const { return (has(NSA_F_FORCE_FIRST) ? 1 : 0) + (has(NSA_F_FORCE_CURRENT) ? 1 : 0); }
 };
 
+// Statistics a training forward keeps for the backward: per branch and
+// (b, t, h) the natural log-sum-exp of the scaled logits (fp32 [3][B, T, H],
+// -inf for an empty or disabled branch), then, 256-byte aligned, the
+// branch's normalised output (bf16 [3][B, T, H, d_v], zeros when empty).
+inline size_t saved_lse_bytes(const Prob& P) { return ((size_t)3 * P.B * P.T * P.H * 4 + 255) / 256 * 256; }
+inline size_t saved_bytes(const Prob& P) { return saved_lse_bytes(P) + (size_t)3 * P.B * P.T * P.H * P.dv * 2; }
+
 // ---- element conversions (device) ----------------------------------------
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

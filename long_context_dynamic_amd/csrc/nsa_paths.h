@@ -51,8 +51,10 @@ hipError_t run_select(const Prob& P, const void* q, const void* kc, int32_t* idx
                       const Workspace& ws, void* base, hipStream_t s);
 hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const void* v, const int32_t* idx,
                            void* out, float* lse, const Workspace& ws, void* base, hipStream_t s);
+// idx_out (or NULL: the workspace) receives the selection; saved (or NULL)
+// the training statistics, on the matrix-core prefill path only.
 hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
-                       const void* kc_given, const void* vc_given, void* out, const Workspace& ws,
-                       void* base, hipStream_t s, Phases& ph);
+                       const void* kc_given, const void* vc_given, void* out, int32_t* idx_out, void* saved,
+                       const Workspace& ws, void* base, hipStream_t s, Phases& ph);
 
 }  // namespace nsa

@@ -229,8 +229,8 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
 }
 
 hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* v, const void* gates,
-                       const void* kc_given, const void* vc_given, void* out, const Workspace& ws,
-                       void* base, hipStream_t s, Phases& ph) {
+                       const void* kc_given, const void* vc_given, void* out, int32_t* idx_out, void* saved,
+                       const Workspace& ws, void* base, hipStream_t s, Phases& ph) {
   const void* kc = kc_given;
   const void* vc = vc_given;
   hipError_t e;
@@ -243,7 +243,8 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     if ((e = launch_pool(P, k, v, (void*)kc, (void*)vc, s)) != hipSuccess) return e;
     ph.mark();
   }
-  int32_t* idx = at<int32_t>(base, ws.idx);
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(base, ws.idx);
+  if (saved && (decode_ok(P) || !prefill_fast_ok(P))) return hipErrorInvalidValue;
   if (decode_ok(P)) {
     DecArgs a = dec_args(P);
     a.q = (const uint16_t*)q;
@@ -280,6 +281,10 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     a.acc = at<float>(base, ws.acc);
     a.idx = idx;
     a.out = out;
+    if (saved) {
+      a.sv_lse = (float*)saved;
+      a.sv_o = (uint16_t*)((char*)saved + saved_lse_bytes(P));
+    }
     if ((e = launch_cmpwin(P, a, true, s)) != hipSuccess) return e;
     ph.mark();
     if ((e = launch_sel(P, a, true, P.has(NSA_F_OUT_F32), s)) != hipSuccess) return e;

@@ -19,6 +19,8 @@ struct PfArgs {
   float* score;           // [B, T, G, n] or NULL
   void* out;              // [B, T, H, DV]
   float* lse;             // [B, T, H] or NULL
+  float* sv_lse;          // training forward: [3][B, T, H] per-branch natural log-sum-exp, or NULL
+  uint16_t* sv_o;         // training forward: [3][B, T, H, DV] per-branch outputs (bf16), or NULL
   int64_t B, T, L, G, H, nb, nbp, Lp, n, w;
   int64_t bs, per, nbs;  // summary block, summaries per 64-token selection block, selection blocks
   uint32_t flags;

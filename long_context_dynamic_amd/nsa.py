@@ -21,8 +21,8 @@ STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "N
 
 EXPORTS = ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
            "nsa_forward_phases", "nsa_workspace_bytes", "nsa_backward", "nsa_backward_workspace_bytes",
-           "nsa_backward_phases", "nsa_compress_mlp", "nsa_gate_proj",
-           "nsa_status_str")
+           "nsa_backward_phases", "nsa_compress_mlp", "nsa_gate_proj", "nsa_forward_train",
+           "nsa_train_saved_bytes", "nsa_status_str")
 
 
 class NsaError(RuntimeError):
@@ -70,7 +70,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_workspace_bytes.restype = ctypes.c_size_t
         L.nsa_forward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
         L.nsa_forward_phases.restype = ctypes.c_int32
-        L.nsa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, P]
+        L.nsa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, P]
+        L.nsa_forward_train.argtypes = [vp, vp, vp, vp, P, vp, vp, vp]
+        L.nsa_train_saved_bytes.argtypes = [P]
+        L.nsa_train_saved_bytes.restype = ctypes.c_size_t
         L.nsa_backward_workspace_bytes.argtypes = [P]
         L.nsa_backward_workspace_bytes.restype = ctypes.c_size_t
         L.nsa_backward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
@@ -80,7 +83,7 @@ def lib() -> ctypes.CDLL:
         L.nsa_status_str.argtypes = [ctypes.c_int]
         L.nsa_status_str.restype = ctypes.c_char_p
         for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_backward",
-                     "nsa_compress_mlp", "nsa_gate_proj"):
+                     "nsa_compress_mlp", "nsa_gate_proj", "nsa_forward_train"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -254,6 +257,51 @@ def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f3
     return out
 
 
+def train_saved_bytes(prob: dict) -> int:
+    p = params(prob, stream=_NoStream)
+    return int(lib().nsa_train_saved_bytes(ctypes.byref(p)))
+
+
+def saved_views(prob: dict, saved: torch.Tensor):
+    """(lse fp32 [3, B, T, H], O bf16 [3, B, T, H, d_v]) views of a saved buffer."""
+    B, T, H, dv = prob["batch"], prob["q_len"], prob["n_groups"] * prob["heads_per_group"], prob["d_v"]
+    n = 3 * B * T * H
+    lse_bytes = (n * 4 + 255) // 256 * 256
+    lse = saved[:n * 4].view(torch.float32).view(3, B, T, H)
+    o = saved[lse_bytes:lse_bytes + n * dv * 2].view(torch.bfloat16).view(3, B, T, H, dv)
+    return lse, o
+
+
+def forward_train(prob: dict, q, k, v, gates, out=None, idx=None, saved=None, out_f32=False,
+                  workspace=None, stream=None, events=None):
+    """nsa_forward_train: (out, idx, saved) -- saved is the uint8 statistics buffer."""
+    s, dt = _shapes(prob), torch_dtype(prob)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, s[name], dt, name)
+    if gates is not None:
+        _check(gates, s["gates"], dt, "gates")
+    odt = torch.float32 if out_f32 else dt
+    out = torch.empty(s["out"], dtype=odt, device=q.device) if out is None else out
+    _check(out, s["out"], odt, "out")
+    idx = torch.empty(s["idx"], dtype=torch.int32, device=q.device) if idx is None else idx
+    _check(idx, s["idx"], torch.int32, "idx")
+    need = train_saved_bytes(prob)
+    if saved is None:
+        saved = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(prob, False, q.device)
+    p = params(prob, out_f32=out_f32, workspace=workspace, stream=stream)
+    if events is not None:
+        for e in events:
+            if not e.cuda_event:
+                e.record()
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        p.phase_events, p.n_phase_events = handles, len(events)
+    _call("nsa_forward_train", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), ctypes.byref(p),
+          out.data_ptr(), idx.data_ptr(), saved.data_ptr())
+    return out, idx, saved
+
+
 def backward_workspace_bytes(prob: dict) -> int:
     p = params(prob, stream=_NoStream)
     return int(lib().nsa_backward_workspace_bytes(ctypes.byref(p)))
@@ -268,8 +316,9 @@ def backward_phases(prob: dict) -> list:
 
 
 def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, dgates=None,
-             want_dgates=True, workspace=None, stream=None, events=None):
-    """Gradients of nsa_forward on the selection idx: (dq, dk, dv, dgates), fp32."""
+             want_dgates=True, workspace=None, stream=None, events=None, saved=None):
+    """Gradients of nsa_forward on the selection idx: (dq, dk, dv, dgates), fp32.
+    saved: forward_train's statistics for the same inputs and idx, or None."""
     s, dt = _shapes(prob), torch_dtype(prob)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", dout)):
         _check(t, s[name], dt, "dout" if name == "out" else name)
@@ -296,7 +345,8 @@ def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, d
         handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         p.phase_events, p.n_phase_events = handles, len(events)
     _call("nsa_backward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), idx.data_ptr(),
-          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dgates), ctypes.byref(p))
+          dout.data_ptr(), _ptr(saved), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dgates),
+          ctypes.byref(p))
     return dq, dk, dv, dgates
 
 

@@ -162,6 +162,36 @@ def forward(prob, q, k, v, gates, idx, rounded=True):
     return out, O
 
 
+def branch_lse(prob, q, k, v, idx, rounded=True, rows=None):
+    """Per branch the natural log-sum-exp of the scaled logits over the row's
+    key set, lse_b = log sum_s exp(scale * q_h . k_s) (the softmax's
+    normaliser, so that P_b[s] = exp(scale * q_h . k_s - lse_b)): float64
+    [3, B, T, H] (or [3, R, H] for the flat rows b * T + t listed in rows),
+    -inf for an empty key set or a branch that is off.  With forward()'s O
+    this is what a training forward keeps for the backward."""
+    B, T, L, G, hpg, bs, sb = _shapes(prob)
+    H = G * hpg
+    c = _scale(prob)
+    kc, _ = pooled(prob, k, v, rounded)
+    flat = np.arange(B * T) if rows is None else np.asarray(rows, dtype=np.int64)
+    lse = np.full((3, len(flat), H), -np.inf)
+    for ri, r in enumerate(flat):
+        b, t = int(r) // T, int(r) % T
+        qr = _widen(q[b, t], prob)
+        for g in range(G):
+            hs = slice(g * hpg, (g + 1) * hpg)
+            sets = key_sets(prob, idx, b, t, g)
+            for br in _branches(prob):
+                s_ids = sets[br]
+                if len(s_ids) == 0:
+                    continue
+                K = kc[b, s_ids, g] if br == 0 else _widen(k[b, s_ids, g], prob)
+                z = c * qr[hs] @ K.T                           # [hpg, n]
+                m = z.max(axis=1)
+                lse[br, ri, hs] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return lse if rows is not None else lse.reshape(3, B, T, H)
+
+
 def _branch_grads(qh, doh, K, V, gb, c):
     """One (row, group, branch): the softmax over the key set and the
     gradient terms.  Returns (dq part [hpg, dqk], dK [n, dqk], dV [n, dv],

@@ -107,8 +107,13 @@ def test_workspace_sizes():
     assert nsa.workspace_bytes(dec, have_cmp=True) < nsa.workspace_bytes(dec)
 
 
-def _backward(p, gates=FAKE, dout=FAKE, dgates=FAKE):
-    return nsa.lib().nsa_backward(FAKE, FAKE, FAKE, gates, FAKE, dout, FAKE, FAKE, FAKE, dgates, ctypes.byref(p))
+def _backward(p, gates=FAKE, dout=FAKE, dgates=FAKE, saved=0):
+    return nsa.lib().nsa_backward(FAKE, FAKE, FAKE, gates, FAKE, dout, saved, FAKE, FAKE, FAKE, dgates,
+                                  ctypes.byref(p))
+
+
+def _forward_train(p, gates=FAKE, idx=FAKE, saved=FAKE):
+    return nsa.lib().nsa_forward_train(FAKE, FAKE, FAKE, gates, ctypes.byref(p), FAKE, idx, saved)
 
 
 def test_backward_validation():
@@ -151,3 +156,27 @@ def test_learned_parts_validation():
     assert lib.nsa_gate_proj(0, 2560, FAKE, 0, FAKE, ctypes.byref(p)) == 1             # NULL x
     assert lib.nsa_gate_proj(FAKE, 100, FAKE, 0, FAKE, ctypes.byref(p)) == 2           # d_model % 32
     assert lib.nsa_gate_proj(FAKE, 2560, FAKE, 0, FAKE, ctypes.byref(tiny)) == 2       # fp32
+
+
+def test_training_forward_validation():
+    lib = nsa.lib()
+    p = _p(BASE)
+    assert _forward_train(p, idx=0) == 1                      # the selection goes to the caller
+    assert _forward_train(p, saved=0) == 1                    # NULL statistics
+    assert _forward_train(p, saved=FAKE + 8) == 1             # misaligned statistics
+    assert _forward_train(p) == 3                             # no workspace
+    pc = _p(BASE)
+    pc.k_cmp = pc.v_cmp = FAKE                                # learned summaries: not what the backward pools
+    assert _forward_train(pc) == 2
+    tiny = _p(workloads.get("nsa_tiny_fp32"))
+    assert _forward_train(tiny) == 2 and lib.nsa_train_saved_bytes(ctypes.byref(tiny)) == 0
+    dec = workloads.get("nsa_decode_64x64k")
+    pd = _p(dec)
+    assert _forward_train(pd) == 2                            # decoding shapes keep no statistics
+    assert lib.nsa_train_saved_bytes(ctypes.byref(pd)) == 0
+    pd.workspace, pd.workspace_bytes = FAKE, 1 << 40
+    assert _backward(pd, saved=FAKE) == 2                     # nor can the backward take them
+    assert _backward(_p(BASE), saved=FAKE + 8) == 1
+    B, T, H, dv = BASE["batch"], BASE["q_len"], BASE["n_groups"] * BASE["heads_per_group"], BASE["d_v"]
+    lse_bytes = (3 * B * T * H * 4 + 255) // 256 * 256
+    assert nsa.train_saved_bytes(BASE) == lse_bytes + 3 * B * T * H * dv * 2

@@ -186,3 +186,45 @@ def test_query_grads_of_chosen_rows_equal_the_full_backward(gate_logits):
     dq_r, dg_r = BW.query_grads(prob, q, k, v, gates, idx, dout, rows)
     np.testing.assert_allclose(dq_r, dq.reshape(-1, *dq.shape[2:])[rows], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dg_r, dg.reshape(-1, *dg.shape[2:])[rows], rtol=0, atol=1e-12)
+
+
+def test_branch_lse_is_torch_logsumexp_on_the_plain_cases():
+    # selected branch with every block chosen = causal, window = banded,
+    # compressed = block-causal over torch's own block means
+    prob = H.problem(q_len=40, kv_len=64, n_groups=1, heads_per_group=3, d_qk=8, d_v=4, block=8,
+                     top_k=8, window=11, use_cmp=1, use_slc=1, use_win=1)
+    q, k, v, _, _ = _inputs64(prob, seed=21)
+    idx = _selection(prob, q, k, v)
+    lse = BW.branch_lse(prob, q, k, v, idx, rounded=False)
+    sc = H.default_scale(prob)
+    pos = torch.from_numpy(H.positions(prob))
+    s = torch.arange(64)
+    qt, kt = torch.from_numpy(q[0]), torch.from_numpy(k[0, :, 0])
+    z = torch.einsum("thd,sd->ths", qt, kt) * sc
+    causal = s[None, :] <= pos[:, None]
+    band = causal & (s[None, :] > pos[:, None] - 11)
+    for br, mask in ((1, causal), (2, band)):
+        want = torch.logsumexp(z.masked_fill(~mask[:, None, :], float("-inf")), dim=-1).numpy()
+        np.testing.assert_allclose(lse[br, 0], want, rtol=0, atol=1e-12)
+    kc = kt.reshape(8, 8, -1).mean(1)
+    zc = torch.einsum("thd,nd->thn", qt, kc) * sc
+    vis = (torch.arange(8)[None, :] + 1) * 8 <= pos[:, None] + 1
+    want = torch.logsumexp(zc.masked_fill(~vis[:, None, :], float("-inf")), dim=-1).numpy()
+    np.testing.assert_allclose(lse[0, 0], want, rtol=0, atol=1e-12)   # -inf where no block is complete
+    assert np.all(np.isneginf(lse[0, 0][H.positions(prob) < 7]))
+
+
+def test_branch_lse_single_key_and_disabled_branches():
+    # a one-token window holds the query's own key: lse is that one logit
+    prob = _tiny(window=1, use_cmp=0, use_slc=1, use_win=1)
+    q, k, v, _, _ = _inputs64(prob, seed=22)
+    idx = _selection(prob, q, k, v)
+    lse = BW.branch_lse(prob, q, k, v, idx, rounded=False)
+    sc = H.default_scale(prob)
+    pos = H.positions(prob)
+    for t in range(prob["q_len"]):
+        for h in range(4):
+            want = sc * float(q[0, t, h] @ k[0, pos[t], h // 2])
+            assert abs(lse[2, 0, t, h] - want) <= 1e-12 * max(1.0, abs(want))
+    assert np.all(np.isneginf(lse[0]))            # compressed branch off
+    assert np.all(np.isfinite(lse[1]))            # the forced current block is never empty
