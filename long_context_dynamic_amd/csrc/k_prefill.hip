@@ -352,8 +352,13 @@ __device__ __forceinline__ void pv_chunk(const VFrag<DV>& f, f32x4 s0, f32x4 s1,
 template <int DQ, int DV, bool FWD, typename TO>
 __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int64_t g = blockIdx.x % a.G;  // consecutive workgroups alternate groups: each XCD serves fixed groups
-  const int64_t tg = (blockIdx.x / a.G) * 4 + wave;  // flat (b, t)
+  // 4 consecutive tokens of one group per workgroup; each XCD takes a
+  // contiguous run of a group's tokens
+  const int64_t nq = (a.B * a.T + 3) / 4;
+  const int64_t j = xcd_run(a.G * nq);
+  if (j >= a.G * nq) return;
+  const int64_t g = j / nq;
+  const int64_t tg = (j % nq) * 4 + wave;  // flat (b, t)
   if (tg >= a.B * a.T) return;
   const int64_t b = tg / a.T, t = tg % a.T;
   const int64_t p = a.L - a.T + t;
@@ -464,7 +469,7 @@ hipError_t launch_cmpwin_t(const PfArgs& a, bool fwd, hipStream_t s) {
 
 template <int DQ, int DV>
 hipError_t launch_sel_t(const PfArgs& a, bool fwd, bool out_f32, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.G * ((a.B * a.T + 3) / 4));
+  const unsigned grid = xcd_grid(a.G * ((a.B * a.T + 3) / 4));
   if (fwd) {
     if (out_f32) k_sel<DQ, DV, true, float><<<grid, 256, 0, s>>>(a);
     else k_sel<DQ, DV, true, uint16_t><<<grid, 256, 0, s>>>(a);

@@ -29,6 +29,18 @@ struct Prob {
 inline size_t saved_lse_bytes(const Prob& P) { return ((size_t)3 * P.B * P.T * P.H * 4 + 255) / 256 * 256; }
 inline size_t saved_bytes(const Prob& P) { return saved_lse_bytes(P) + (size_t)3 * P.B * P.T * P.H * P.dv * 2; }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i to XCD
+// i % 8), each XCD with its own L2.  xcd_run renumbers them so that XCD x
+// takes the contiguous run [x * per, (x + 1) * per) of n logical ids:
+// neighbouring work items, which read the same keys, then share one L2
+// instead of fetching them into every XCD's.  Launch xcd_grid(n)
+// workgroups; ids >= n have nothing to do.
+__device__ __forceinline__ int64_t xcd_run(int64_t n) {
+  const int64_t per = (n + 7) / 8;
+  return (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+}
+inline unsigned xcd_grid(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
+
 // ---- element conversions (device) ----------------------------------------
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

@@ -225,9 +225,9 @@ def forward_phases(prob: dict, have_cmp: bool = False) -> list:
     """Names of the kernels nsa_forward launches for this problem, in order."""
     p = params(prob, stream=_NoStream)
     p.k_cmp = p.v_cmp = (16 if have_cmp else None)
-    names = (ctypes.c_char_p * 16)()
-    n = lib().nsa_forward_phases(ctypes.byref(p), names, 16)
-    return [names[i].decode() for i in range(min(n, 16))]
+    names = (ctypes.c_char_p * 64)()
+    n = lib().nsa_forward_phases(ctypes.byref(p), names, 64)
+    return [names[i].decode() for i in range(min(n, 64))]
 
 
 def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f32=False,
@@ -310,9 +310,9 @@ def backward_workspace_bytes(prob: dict) -> int:
 def backward_phases(prob: dict) -> list:
     """Names of the kernel groups nsa_backward times, in order."""
     p = params(prob, stream=_NoStream)
-    names = (ctypes.c_char_p * 16)()
-    n = lib().nsa_backward_phases(ctypes.byref(p), names, 16)
-    return [names[i].decode() for i in range(min(n, 16))]
+    names = (ctypes.c_char_p * 64)()
+    n = lib().nsa_backward_phases(ctypes.byref(p), names, 64)
+    return [names[i].decode() for i in range(min(n, 64))]
 
 
 def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, dgates=None,
