@@ -28,7 +28,7 @@ CASES = [
     ("nsa_prefill_8k", dict(q_len=600, kv_len=600, block=16, sel_block=64, top_k=8, force_first=0), None),
     ("nsa_tiny_fp32", dict(q_len=500, kv_len=700, block=16, sel_block=48, top_k=5), None),
     ("nsa_prefill_64k", {}, 20),
-    # token chunks of the overlapped forward: 2048 + 2048 + a ragged 404, and two sequences
+    # a longer ragged prefill checked on every row, and two sequences of one launch
     ("nsa_prefill_8k", dict(q_len=4500, kv_len=4600), None),
     ("nsa_prefill_8k", dict(batch=2, q_len=2100, kv_len=2100, n_groups=2), None),
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
@@ -149,7 +149,7 @@ def test_forward(i, out_f32):
 
 
 def test_forward_is_deterministic():
-    prob = workloads.get("nsa_prefill_8k", q_len=4200, kv_len=4200)  # three token chunks
+    prob = workloads.get("nsa_prefill_8k", q_len=4200, kv_len=4200)
     x = inputs.generate(prob)
     t = U.upload(x, prob)
     a = nsa.forward(prob, t["q"], t["k"], t["v"], t["gates"])
