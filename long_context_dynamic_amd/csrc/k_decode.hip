@@ -62,10 +62,11 @@ template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
 // tile is read as whole rows into registers, passes through the wave's LDS
 // region and is read back transposed.  The next tile's reads are in flight
 // while the current one is computed on.
-template <int DQ, int DV, bool WITH_V, typename TileAt, typename Ok>
+template <int DQ, int DV, bool WITH_V, typename TileAt, typename Ok, typename Pre>
 __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* V, int64_t N, int64_t b, int64_t g,
                                              int64_t G, TileAt tile_at, int nt, Ok ok, const bf16x8 (&qf)[DQ / 32],
-                                             float c, uint16_t* myv, float* zrow, int64_t zstride, float* rec) {
+                                             float c, uint16_t* myv, float* zrow, int64_t zstride, float* rec,
+                                             Pre pre) {
   constexpr int VS = DV + 8;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   float m = -INFINITY, l = 0.f;
@@ -104,6 +105,7 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
     load_k(0);
     if (WITH_V) load_v(0);
   }
+  pre();  // other work of the wave while the first tile's reads are in flight
   // the next tile's reads are issued as soon as this tile's registers are
   // free; the last tile is peeled so no tile is read twice
   auto tile = [&](int i, auto prefetch) {
@@ -195,7 +197,8 @@ __device__ __forceinline__ void load_q(const DecArgs& a, int64_t row, int64_t g,
 // The compressed branch of one (row, group) on one wave: every
 // n_cmp_waves-th summary tile from its own, logits to zbuf, a partial record.
 template <int DQ, int DV, bool WITH_V>
-__device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t g, int wave, uint16_t* myv) {
+__device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t g, int wave, uint16_t* myv,
+                                         float* zrow, int64_t zstride) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
   int64_t nvis = (p + 1) / a.bs;  // visible summaries
@@ -207,9 +210,9 @@ __device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t 
   load_q<DQ>(a, row, g, qf);
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
   float* rec = a.part + ((row * a.G + g) * nwaves + wave) * part_floats<DV>();
-  float* zrow = a.zbuf + (row * a.G + g) * 16 * a.nbp;
   stream_tiles<DQ, DV, WITH_V>(a.kc, a.vc, a.nb, b, g, a.G, [&](int i) { return wave + i * ncw; }, nt,
-                               [&](int64_t j) { return j < nvis; }, qf, a.scale * kLog2e, myv, zrow, a.nbp, rec);
+                               [&](int64_t j) { return j < nvis; }, qf, a.scale * kLog2e, myv, zrow, zstride, rec,
+                               [] {});
 }
 
 // The chosen blocks of one (row, group) on wave w of kAttnWaves: slots w,
@@ -232,14 +235,15 @@ __device__ __forceinline__ void sel_wave(const DecArgs& a, int64_t row, int64_t 
   }
   stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return sel[i]; }, ns,
                              [&](int64_t s) { return s <= p; }, qf, a.scale * kLog2e, myv, nullptr, 0,
-                             recs + w * part_floats<DV>());
+                             recs + w * part_floats<DV>(), [] {});
 }
 
 // The window's 64-key tiles first, first + stride, .. of one (row, group)
 // (a record in window slot `slot`; none of them gives an empty record).
-template <int DQ, int DV>
+// pre(): other work done while the first tile's reads are in flight.
+template <int DQ, int DV, typename Pre>
 __device__ __forceinline__ void win_wave(const DecArgs& a, int64_t row, int64_t g, int slot, int first, int stride,
-                                         const bf16x8 (&qf)[DQ / 32], uint16_t* myv) {
+                                         const bf16x8 (&qf)[DQ / 32], uint16_t* myv, Pre pre) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
@@ -250,55 +254,65 @@ __device__ __forceinline__ void win_wave(const DecArgs& a, int64_t row, int64_t 
   const int nt = nwt > first ? (int)((nwt - first + stride - 1) / stride) : 0;
   stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return (int)(kb0 + first + stride * i); }, nt,
                              [&](int64_t s) { return s <= p && s >= lo; }, qf, a.scale * kLog2e, myv, nullptr, 0,
-                             recs + slot * part_floats<DV>());
+                             recs + slot * part_floats<DV>(), pre);
 }
 
-// Per-head softmax statistics of one (row, group) from the compressed-branch
-// records, the group importance of every visible block from the logits, and
-// the top-k (wave 0).  Every thread of the workgroup calls it (it holds a
-// barrier); threads 0..255 do the work.  NBL: blocks per lane (nbp <= 64 NBL).
+// The group importance of visible summaries j = tid + 256 i of one (row,
+// group): each wave works out the per-head softmax statistics from the
+// compressed-branch records itself (lanes 0..15, then shuffled to all), so
+// no barrier is needed before; imp[j] = sum over heads of exp2(z - M) / L.
+// The caller holds a barrier before imp is read.  NBL: blocks per lane of
+// one wave (nbp <= 64 NBL).
 template <int DV, int NBL>
-__device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64_t g, int tid, float* imp, float* sM,
-                                            float* sL) {
+__device__ __forceinline__ void importance_share(const DecArgs& a, int64_t row, int64_t g, int tid, const float* z,
+                                                 int64_t zstride, float* imp) {
+  const int lane = tid & 63;
   const int64_t p = a.L - a.T + row % a.T;
   int64_t nvis = (p + 1) / a.bs;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
   const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
   const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
-  // this thread's logits, loaded while the statistics are worked out
-  const float* z = a.zbuf + (row * a.G + g) * 16 * a.nbp;
+  // this thread's logits (z[h * zstride + j]), loaded while the statistics
+  // are worked out
   float zv[NBL / 4][16];
 #pragma unroll
   for (int i = 0; i < NBL / 4; ++i) {
     const int64_t j = tid + 256 * i;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) zv[i][h] = (tid < 256 && j < nvis) ? z[h * a.nbp + j] : 0.f;
+    for (int h = 0; h < 16; ++h) zv[i][h] = j < nvis ? z[h * zstride + j] : 0.f;
   }
-  if (tid < 16) {
-    float M = -INFINITY, L = 0.f;
-    for (int64_t w = 0; w < a.n_cmp_waves; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + tid]);
+  float M = -INFINITY, L = 0.f;
+  if (lane < 16) {
+    for (int64_t w = 0; w < a.n_cmp_waves; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + lane]);
     for (int64_t w = 0; w < a.n_cmp_waves; ++w) {
-      const float mw = base[w * part_floats<DV>() + 16 * DV + tid];
-      if (mw != -INFINITY) L = fmaf(exp2f(mw - M), base[w * part_floats<DV>() + 16 * DV + 16 + tid], L);
-    }
-    sM[tid] = M;
-    sL[tid] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  if (tid < 256) {
-#pragma unroll
-    for (int i = 0; i < NBL / 4; ++i) {
-      const int64_t j = tid + 256 * i;
-      if (j < nvis) {
-        float sum = 0.f;
-#pragma unroll
-        for (int h = 0; h < 16; ++h) sum += exp2f(zv[i][h] - sM[h]) * sL[h];
-        imp[j] = sum;
-      }
+      const float mw = base[w * part_floats<DV>() + 16 * DV + lane];
+      if (mw != -INFINITY) L = fmaf(exp2f(mw - M), base[w * part_floats<DV>() + 16 * DV + 16 + lane], L);
     }
   }
-  __syncthreads();
-  if (tid >= 64) return;  // callers that continue hold a barrier after this
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float hm[16], hl[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    hm[h] = __shfl(M, h, 64);
+    hl[h] = __shfl(inv, h, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < NBL / 4; ++i) {
+    const int64_t j = tid + 256 * i;
+    if (j < nvis) {
+      float sum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 16; ++h) sum += exp2f(zv[i][h] - hm[h]) * hl[h];
+      imp[j] = sum;
+    }
+  }
+}
+
+// The top-k of one (row, group) from the importance in imp (one wave).
+template <int NBL>
+__device__ __forceinline__ void topk_part(const DecArgs& a, int64_t row, int64_t g, const float* imp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t p = a.L - a.T + row % a.T;
   int32_t* orow = a.idx + (row * a.G + g) * a.n;
   float* srow = a.score ? a.score + (row * a.G + g) * a.n : nullptr;
   int cj;
@@ -310,7 +324,7 @@ __device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64
   float vals[NBL];
 #pragma unroll
   for (int i = 0; i < NBL; ++i) {
-    const int64_t J = tid + 64 * i;
+    const int64_t J = lane + 64 * i;
     float v = -1.f;
     if (J < nsel) {
       v = imp[a.per * J];
@@ -320,6 +334,16 @@ __device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64
   }
   const int cnt = topk_wave<NBL>(vals, nsel, p / 64, a.flags, (int)a.n, cj, cs);
   topk_write(cnt, cj, cs, (int)a.n, orow, srow);
+}
+
+// Importance (every thread of the workgroup, then a barrier) and the top-k
+// (wave 0).  Threads 64.. return after the barrier.
+template <int DV, int NBL>
+__device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64_t g, int tid, float* imp) {
+  importance_share<DV, NBL>(a, row, g, tid, a.zbuf + (row * a.G + g) * 16 * a.nbp, a.nbp, imp);
+  __syncthreads();
+  if (tid >= 64) return;
+  topk_part<NBL>(a, row, g, imp);
 }
 
 // Log-sum-exp merge of each branch's partial records, gates, output.  With
@@ -356,15 +380,15 @@ __device__ __forceinline__ void merge_body(const DecArgs& a, int64_t row, int64_
     const int h = it / (DV / 4), d = 4 * (it % (DV / 4));
     const int64_t hrow = row * a.H + g * 16 + h;
     f32x4 br[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    // records in groups of 4 loads in flight (few registers: the streaming
-    // phase before sets the budget)
-    for (int w0 = 0; w0 < nwaves; w0 += 4) {
-      f32x4 v[4];
+    // records in groups of 8 loads in flight (the streaming phase before
+    // sets the register budget)
+    for (int w0 = 0; w0 < nwaves; w0 += 8) {
+      f32x4 v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
         if (w0 + i < nwaves) v[i] = *(const f32x4*)(base + (w0 + i) * part_floats<DV>() + h * DV + d);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const int w = w0 + i;
         if (w < nwaves) br[w < nc ? 0 : (w < nc + ns ? 1 : 2)] += v[i] * coef[h][w];
       }
@@ -393,14 +417,14 @@ template <int DQ, int DV, bool WITH_V, int NBL>
 __global__ void __launch_bounds__(256) k_dec_cmpsel(DecArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* imp = (float*)smem;                    // [64 * NBL]
-  float* sM = imp + 64 * NBL;                   // [16]
-  float* sL = sM + 16;                          // [16]
-  uint16_t* vt = (uint16_t*)(sL + 16);          // [4][64 * (DV + 8)] when WITH_V
+  uint16_t* vt = (uint16_t*)(imp + 64 * NBL);   // [4][64 * (DV + 8)] when WITH_V
   const int wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
-  if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, WITH_V>(a, row, g, wave, vt + (WITH_V ? wave * 64 * (DV + 8) : 0));
+  if (wave < a.n_cmp_waves)
+    cmp_wave<DQ, DV, WITH_V>(a, row, g, wave, vt + (WITH_V ? wave * 64 * (DV + 8) : 0),
+                             a.zbuf + (row * a.G + g) * 16 * a.nbp, a.nbp);
   __syncthreads();
-  select_body<DV, NBL>(a, row, g, threadIdx.x, imp, sM, sL);
+  select_body<DV, NBL>(a, row, g, threadIdx.x, imp);
 }
 
 // One workgroup of 4 waves per (row, group): the selected and window blocks,
@@ -415,7 +439,7 @@ __global__ void __launch_bounds__(256) k_dec_attnmerge(DecArgs a) {
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
   sel_wave<DQ, DV>(a, row, g, wave, qf, vt[wave]);
-  win_wave<DQ, DV>(a, row, g, wave, wave, kAttnWaves, qf, vt[wave]);
+  win_wave<DQ, DV>(a, row, g, wave, wave, kAttnWaves, qf, vt[wave], [] {});
   __syncthreads();
   merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
 }
@@ -423,28 +447,41 @@ __global__ void __launch_bounds__(256) k_dec_attnmerge(DecArgs a) {
 // The whole decoding step of one (row, group) in one workgroup: compressed
 // branch, selection, chosen and window blocks, merge -- three barriers, no
 // launch in between, and the (row, group)s of the batch at different phases
-// across the chip.
-template <int DQ, int DV, int NBL, typename TO>
+// across the chip.  ZLDS: the compressed-branch logits stay in LDS (rows of
+// nbp + 4 floats, so the 16 heads' rows start in different banks) instead of
+// going through global memory.
+template <int DQ, int DV, int NBL, bool ZLDS, typename TO>
 __global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* imp = (float*)smem;                          // [64 * NBL]
-  float* sM = imp + 64 * NBL;                         // [16]
-  float* sL = sM + 16;                                // [16]
-  float(*coef)[kMaxRecords] = (float(*)[kMaxRecords])(sL + 16);  // [16][kMaxRecords]
+  float(*coef)[kMaxRecords] = (float(*)[kMaxRecords])(imp + 64 * NBL);  // [16][kMaxRecords]
   float* slse = (float*)(coef + 16);                  // [16]
   uint16_t* vt = (uint16_t*)(slse + 16);              // [4][64 * (DV + 8)]
+  float* zl = (float*)(vt + 4 * 64 * (DV + 8));       // ZLDS: [16][nbp + 4]
   const int wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
   uint16_t* myv = vt + wave * 64 * (DV + 8);
-  if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, true>(a, row, g, wave, myv);
+  float* z = ZLDS ? zl : a.zbuf + (row * a.G + g) * 16 * a.nbp;
+  const int64_t zstride = ZLDS ? a.nbp + 4 : a.nbp;
+  if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, true>(a, row, g, wave, myv, z, zstride);
   __syncthreads();
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
-  // wave 0 finishes the selection (top-k) while waves 1..3 stream the
-  // window, which does not depend on it; wave 0's window record is empty
-  select_body<DV, NBL>(a, row, g, threadIdx.x, imp, sM, sL);
-  if (wave == 0) win_wave<DQ, DV>(a, row, g, 0, 1 << 30, 1, qf, myv);
-  else win_wave<DQ, DV>(a, row, g, wave, wave - 1, kAttnWaves - 1, qf, myv);
+  // every wave computes its share of the importance -- waves 1..3 with
+  // their first window tile's reads in flight -- then one barrier; wave 0
+  // makes the top-k while waves 1..3 stream the rest of the window, which
+  // does not depend on it (wave 0's window record is empty)
+  auto share = [&] {
+    importance_share<DV, NBL>(a, row, g, threadIdx.x, z, zstride, imp);
+    __syncthreads();
+  };
+  if (wave == 0) {
+    share();
+    topk_part<NBL>(a, row, g, imp);
+    win_wave<DQ, DV>(a, row, g, 0, 1 << 30, 1, qf, myv, [] {});
+  } else {
+    win_wave<DQ, DV>(a, row, g, wave, wave - 1, kAttnWaves - 1, qf, myv, share);
+  }
   __syncthreads();  // the chosen blocks are in idx
   sel_wave<DQ, DV>(a, row, g, wave, qf, myv);
   __syncthreads();
@@ -453,14 +490,14 @@ __global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
 
 template <int DQ, int DV, typename TO>
 hipError_t launch_fused(const DecArgs& a, hipStream_t s) {
-  const size_t fixed = (16 + 16 + 16 * kMaxRecords + 16) * 4 + (size_t)4 * 64 * (DV + 8) * 2;
-  if (a.nbp <= 1024) {
-    auto k = k_dec_fused<DQ, DV, 16, TO>;
-    const size_t lds = 64 * 16 * 4 + fixed;
+  const size_t fixed = (16 * kMaxRecords + 16) * 4 + (size_t)4 * 64 * (DV + 8) * 2;
+  if (a.nbp <= 1024) {  // logits in LDS: at most 64 KiB more
+    auto k = k_dec_fused<DQ, DV, 16, true, TO>;
+    const size_t lds = 64 * 16 * 4 + fixed + (size_t)16 * (a.nbp + 4) * 4;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
   } else {
-    auto k = k_dec_fused<DQ, DV, MAX_NB_LANE, TO>;
+    auto k = k_dec_fused<DQ, DV, MAX_NB_LANE, false, TO>;
     const size_t lds = 64 * MAX_NB_LANE * 4 + fixed;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
@@ -473,12 +510,12 @@ hipError_t launch_cmpsel(const DecArgs& a, hipStream_t s) {
   const size_t vbytes = WITH_V ? (size_t)4 * 64 * (DV + 8) * 2 : 0;
   if (a.nbp <= 1024) {
     auto k = k_dec_cmpsel<DQ, DV, WITH_V, 16>;
-    const size_t lds = (64 * 16 + 32) * 4 + vbytes;
+    const size_t lds = 64 * 16 * 4 + vbytes;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
   } else {
     auto k = k_dec_cmpsel<DQ, DV, WITH_V, MAX_NB_LANE>;
-    const size_t lds = (64 * MAX_NB_LANE + 32) * 4 + vbytes;
+    const size_t lds = 64 * MAX_NB_LANE * 4 + vbytes;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
   }
