@@ -53,6 +53,22 @@ __device__ __forceinline__ bool dbetter(float v, int j, float bv, int bj) {
 // [16] maxima (log2 units) and [16] sums.
 template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
 
+// Where a wave writes its partial record: the unnormalised outputs of the 16
+// heads (rows os floats apart) and ml = the 16 maxima, then the 16 sums.
+struct RecLoc {
+  float* o;
+  int64_t os;
+  float* ml;
+};
+
+// Partial record w of (row, group) in global memory.
+template <int DV>
+__device__ __forceinline__ RecLoc grec(const DecArgs& a, int64_t row, int64_t g, int64_t w) {
+  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
+  float* r = a.part + ((row * a.G + g) * nwaves + w) * part_floats<DV>();
+  return RecLoc{r, DV, r + 16 * DV};
+}
+
 // Stream 64-row tiles tile_at(0 .. nt-1) of K [B, N, G, DQ] / V [B, N, G, DV] for
 // one (b, g) and the 16 heads in qf; keep rows where ok(row).  Writes scaled
 // logits to zrow[h * zstride + row] when zrow is given.  Ends by writing the
@@ -65,7 +81,7 @@ template <int DV> constexpr int part_floats() { return 16 * DV + 32; }
 template <int DQ, int DV, bool WITH_V, typename TileAt, typename Ok, typename Pre>
 __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* V, int64_t N, int64_t b, int64_t g,
                                              int64_t G, TileAt tile_at, int nt, Ok ok, const bf16x8 (&qf)[DQ / 32],
-                                             float c, uint16_t* myv, float* zrow, int64_t zstride, float* rec,
+                                             float c, uint16_t* myv, float* zrow, int64_t zstride, RecLoc rec,
                                              Pre pre) {
   constexpr int VS = DV + 8;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -178,10 +194,10 @@ __device__ __forceinline__ void stream_tiles(const uint16_t* K, const uint16_t* 
   if (nt > 0) tile(nt - 1, std::false_type{});
   // o^T: lane holds d = 16*dt + 4*lg + r of head lr
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(rec + lr * DV + 16 * dt + 4 * lg) = o[dt];
+  for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(rec.o + lr * rec.os + 16 * dt + 4 * lg) = o[dt];
   if (lg == 0) {
-    rec[16 * DV + lr] = m == -INFINITY ? -INFINITY : m * c;
-    rec[16 * DV + 16 + lr] = l;
+    rec.ml[lr] = m == -INFINITY ? -INFINITY : m * c;
+    rec.ml[16 + lr] = l;
   }
 }
 
@@ -198,7 +214,7 @@ __device__ __forceinline__ void load_q(const DecArgs& a, int64_t row, int64_t g,
 // n_cmp_waves-th summary tile from its own, logits to zbuf, a partial record.
 template <int DQ, int DV, bool WITH_V>
 __device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t g, int wave, uint16_t* myv,
-                                         float* zrow, int64_t zstride) {
+                                         float* zrow, int64_t zstride, RecLoc rec) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
   int64_t nvis = (p + 1) / a.bs;  // visible summaries
@@ -208,22 +224,18 @@ __device__ __forceinline__ void cmp_wave(const DecArgs& a, int64_t row, int64_t 
   const int nt = ntv > wave ? (int)((ntv - wave + ncw - 1) / ncw) : 0;
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
-  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
-  float* rec = a.part + ((row * a.G + g) * nwaves + wave) * part_floats<DV>();
   stream_tiles<DQ, DV, WITH_V>(a.kc, a.vc, a.nb, b, g, a.G, [&](int i) { return wave + i * ncw; }, nt,
                                [&](int64_t j) { return j < nvis; }, qf, a.scale * kLog2e, myv, zrow, zstride, rec,
                                [] {});
 }
 
 // The chosen blocks of one (row, group) on wave w of kAttnWaves: slots w,
-// w + 4, .. (a record in selected slot w).
+// w + 4, .. (a record at rec).
 template <int DQ, int DV>
 __device__ __forceinline__ void sel_wave(const DecArgs& a, int64_t row, int64_t g, int w, const bf16x8 (&qf)[DQ / 32],
-                                         uint16_t* myv) {
+                                         uint16_t* myv, RecLoc rec) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
-  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
-  float* recs = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves) * part_floats<DV>();
   int sel[kMaxSlotsPerWave];
   int ns = 0;
   if (a.flags & NSA_F_SLC) {
@@ -234,27 +246,24 @@ __device__ __forceinline__ void sel_wave(const DecArgs& a, int64_t row, int64_t 
     }
   }
   stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return sel[i]; }, ns,
-                             [&](int64_t s) { return s <= p; }, qf, a.scale * kLog2e, myv, nullptr, 0,
-                             recs + w * part_floats<DV>(), [] {});
+                             [&](int64_t s) { return s <= p; }, qf, a.scale * kLog2e, myv, nullptr, 0, rec, [] {});
 }
 
 // The window's 64-key tiles first, first + stride, .. of one (row, group)
-// (a record in window slot `slot`; none of them gives an empty record).
+// (a record at rec; none of them gives an empty record).
 // pre(): other work done while the first tile's reads are in flight.
 template <int DQ, int DV, typename Pre>
-__device__ __forceinline__ void win_wave(const DecArgs& a, int64_t row, int64_t g, int slot, int first, int stride,
-                                         const bf16x8 (&qf)[DQ / 32], uint16_t* myv, Pre pre) {
+__device__ __forceinline__ void win_wave(const DecArgs& a, int64_t row, int64_t g, int first, int stride,
+                                         const bf16x8 (&qf)[DQ / 32], uint16_t* myv, RecLoc rec, Pre pre) {
   const int64_t b = row / a.T, t = row % a.T;
   const int64_t p = a.L - a.T + t;
-  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
-  float* recs = a.part + ((row * a.G + g) * nwaves + a.n_cmp_waves + a.n_sel_waves) * part_floats<DV>();
   int64_t lo = p - a.w + 1;
   if (lo < 0) lo = 0;
   const int64_t kb0 = lo / 64, nwt = ((a.flags & NSA_F_WIN) && a.w > 0) ? p / 64 - kb0 + 1 : 0;
   const int nt = nwt > first ? (int)((nwt - first + stride - 1) / stride) : 0;
   stream_tiles<DQ, DV, true>(a.k, a.v, a.L, b, g, a.G, [&](int i) { return (int)(kb0 + first + stride * i); }, nt,
                              [&](int64_t s) { return s <= p && s >= lo; }, qf, a.scale * kLog2e, myv, nullptr, 0,
-                             recs + slot * part_floats<DV>(), pre);
+                             rec, pre);
 }
 
 // The group importance of visible summaries j = tid + 256 i of one (row,
@@ -263,15 +272,13 @@ __device__ __forceinline__ void win_wave(const DecArgs& a, int64_t row, int64_t 
 // no barrier is needed before; imp[j] = sum over heads of exp2(z - M) / L.
 // The caller holds a barrier before imp is read.  NBL: blocks per lane of
 // one wave (nbp <= 64 NBL).
-template <int DV, int NBL>
+template <int DV, int NBL, typename MlOf>
 __device__ __forceinline__ void importance_share(const DecArgs& a, int64_t row, int64_t g, int tid, const float* z,
-                                                 int64_t zstride, float* imp) {
+                                                 int64_t zstride, MlOf ml_of, float* imp) {
   const int lane = tid & 63;
   const int64_t p = a.L - a.T + row % a.T;
   int64_t nvis = (p + 1) / a.bs;  // visible summaries
   if (nvis > a.nb) nvis = a.nb;
-  const int64_t nwaves = a.n_cmp_waves + a.n_sel_waves + a.n_win_waves;
-  const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
   // this thread's logits (z[h * zstride + j]), loaded while the statistics
   // are worked out
   float zv[NBL / 4][16];
@@ -283,10 +290,10 @@ __device__ __forceinline__ void importance_share(const DecArgs& a, int64_t row, 
   }
   float M = -INFINITY, L = 0.f;
   if (lane < 16) {
-    for (int64_t w = 0; w < a.n_cmp_waves; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + lane]);
-    for (int64_t w = 0; w < a.n_cmp_waves; ++w) {
-      const float mw = base[w * part_floats<DV>() + 16 * DV + lane];
-      if (mw != -INFINITY) L = fmaf(exp2f(mw - M), base[w * part_floats<DV>() + 16 * DV + 16 + lane], L);
+    for (int w = 0; w < (int)a.n_cmp_waves; ++w) M = fmaxf(M, ml_of(w)[lane]);
+    for (int w = 0; w < (int)a.n_cmp_waves; ++w) {
+      const float mw = ml_of(w)[lane];
+      if (mw != -INFINITY) L = fmaf(exp2f(mw - M), ml_of(w)[16 + lane], L);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -340,7 +347,8 @@ __device__ __forceinline__ void topk_part(const DecArgs& a, int64_t row, int64_t
 // (wave 0).  Threads 64.. return after the barrier.
 template <int DV, int NBL>
 __device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64_t g, int tid, float* imp) {
-  importance_share<DV, NBL>(a, row, g, tid, a.zbuf + (row * a.G + g) * 16 * a.nbp, a.nbp, imp);
+  importance_share<DV, NBL>(a, row, g, tid, a.zbuf + (row * a.G + g) * 16 * a.nbp, a.nbp,
+                            [&](int w) { return (const float*)grec<DV>(a, row, g, w).ml; }, imp);
   __syncthreads();
   if (tid >= 64) return;
   topk_part<NBL>(a, row, g, imp);
@@ -352,22 +360,22 @@ __device__ __forceinline__ void select_body(const DecArgs& a, int64_t row, int64
 // (it holds a barrier); the 16 x DV/4 output slices are dealt over nthr threads.
 constexpr int kMaxRecords = 32;
 
-template <int DV, typename TO>
+template <int DV, typename TO, typename RecOf>
 __device__ __forceinline__ void merge_body(const DecArgs& a, int64_t row, int64_t g, int tid, int nthr,
-                                           float (*coef)[kMaxRecords], float* slse) {
+                                           float (*coef)[kMaxRecords], float* slse, RecOf rec_of) {
   const int nc = (int)a.n_cmp_waves, ns = (int)a.n_sel_waves, nwaves = nc + ns + (int)a.n_win_waves;
-  const float* base = a.part + (row * a.G + g) * nwaves * part_floats<DV>();
   if (tid < 48) {
     const int hh = tid & 15, br = tid >> 4;  // 0 cmp, 1 sel, 2 win
     const int w0 = br == 0 ? 0 : (br == 1 ? nc : nc + ns), w1 = br == 0 ? nc : (br == 1 ? nc + ns : nwaves);
     float M = -INFINITY;
-    for (int w = w0; w < w1; ++w) M = fmaxf(M, base[w * part_floats<DV>() + 16 * DV + hh]);
+    for (int w = w0; w < w1; ++w) M = fmaxf(M, rec_of(w).ml[hh]);
     float den = 0.f;
     for (int w = w0; w < w1; ++w) {
-      const float mw = base[w * part_floats<DV>() + 16 * DV + hh];
+      const RecLoc r = rec_of(w);
+      const float mw = r.ml[hh];
       const float sc = (M == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - M);
       coef[hh][w] = sc;
-      den = fmaf(sc, base[w * part_floats<DV>() + 16 * DV + 16 + hh], den);
+      den = fmaf(sc, r.ml[16 + hh], den);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     for (int w = w0; w < w1; ++w) coef[hh][w] *= inv;
@@ -386,7 +394,10 @@ __device__ __forceinline__ void merge_body(const DecArgs& a, int64_t row, int64_
       f32x4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (w0 + i < nwaves) v[i] = *(const f32x4*)(base + (w0 + i) * part_floats<DV>() + h * DV + d);
+        if (w0 + i < nwaves) {
+          const RecLoc r = rec_of(w0 + i);
+          v[i] = *(const f32x4*)(r.o + h * r.os + d);
+        }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int w = w0 + i;
@@ -422,7 +433,7 @@ __global__ void __launch_bounds__(256) k_dec_cmpsel(DecArgs a) {
   const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
   if (wave < a.n_cmp_waves)
     cmp_wave<DQ, DV, WITH_V>(a, row, g, wave, vt + (WITH_V ? wave * 64 * (DV + 8) : 0),
-                             a.zbuf + (row * a.G + g) * 16 * a.nbp, a.nbp);
+                             a.zbuf + (row * a.G + g) * 16 * a.nbp, a.nbp, grec<DV>(a, row, g, wave));
   __syncthreads();
   select_body<DV, NBL>(a, row, g, threadIdx.x, imp);
 }
@@ -438,10 +449,11 @@ __global__ void __launch_bounds__(256) k_dec_attnmerge(DecArgs a) {
   const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
-  sel_wave<DQ, DV>(a, row, g, wave, qf, vt[wave]);
-  win_wave<DQ, DV>(a, row, g, wave, wave, kAttnWaves, qf, vt[wave], [] {});
+  const int64_t nc = a.n_cmp_waves, ns = a.n_sel_waves;
+  sel_wave<DQ, DV>(a, row, g, wave, qf, vt[wave], grec<DV>(a, row, g, nc + wave));
+  win_wave<DQ, DV>(a, row, g, wave, kAttnWaves, qf, vt[wave], grec<DV>(a, row, g, nc + ns + wave), [] {});
   __syncthreads();
-  merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
+  merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse, [&](int w) { return grec<DV>(a, row, g, w); });
 }
 
 // The whole decoding step of one (row, group) in one workgroup: compressed
@@ -456,14 +468,24 @@ __global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
   float* imp = (float*)smem;                          // [64 * NBL]
   float(*coef)[kMaxRecords] = (float(*)[kMaxRecords])(imp + 64 * NBL);  // [16][kMaxRecords]
   float* slse = (float*)(coef + 16);                  // [16]
-  uint16_t* vt = (uint16_t*)(slse + 16);              // [4][64 * (DV + 8)]
-  float* zl = (float*)(vt + 4 * 64 * (DV + 8));       // ZLDS: [16][nbp + 4]
+  float* mlr = slse + 16;                             // ZLDS: [kMaxRecords][32] record maxima and sums
+  uint16_t* vt = (uint16_t*)(mlr + kMaxRecords * 32);  // [4][64 * (DV + 8)]
+  // ZLDS: the logits [16][nbp + 4]; after the top-k's barrier the same
+  // space holds the selected and window records' outputs [8][16][DV + 4]
+  float* zl = (float*)(vt + 4 * 64 * (DV + 8));
   const int wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x % a.G, row = blockIdx.x / a.G;
   uint16_t* myv = vt + wave * 64 * (DV + 8);
   float* z = ZLDS ? zl : a.zbuf + (row * a.G + g) * 16 * a.nbp;
   const int64_t zstride = ZLDS ? a.nbp + 4 : a.nbp;
-  if (wave < a.n_cmp_waves) cmp_wave<DQ, DV, true>(a, row, g, wave, myv, z, zstride);
+  const int64_t nc = a.n_cmp_waves, ns = a.n_sel_waves;
+  // record w: compressed-branch outputs in global memory, the rest in LDS
+  auto rec_of = [&](int w) -> RecLoc {
+    if (!ZLDS) return grec<DV>(a, row, g, w);
+    if (w < nc) return RecLoc{grec<DV>(a, row, g, w).o, DV, mlr + 32 * w};
+    return RecLoc{zl + (w - nc) * 16 * (DV + 4), DV + 4, mlr + 32 * w};
+  };
+  if (wave < nc) cmp_wave<DQ, DV, true>(a, row, g, wave, myv, z, zstride, rec_of(wave));
   __syncthreads();
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
@@ -472,28 +494,30 @@ __global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
   // makes the top-k while waves 1..3 stream the rest of the window, which
   // does not depend on it (wave 0's window record is empty)
   auto share = [&] {
-    importance_share<DV, NBL>(a, row, g, threadIdx.x, z, zstride, imp);
+    importance_share<DV, NBL>(a, row, g, threadIdx.x, z, zstride, [&](int w) { return (const float*)rec_of(w).ml; },
+                              imp);
     __syncthreads();
   };
   if (wave == 0) {
     share();
     topk_part<NBL>(a, row, g, imp);
-    win_wave<DQ, DV>(a, row, g, 0, 1 << 30, 1, qf, myv, [] {});
+    win_wave<DQ, DV>(a, row, g, 1 << 30, 1, qf, myv, rec_of(nc + ns), [] {});
   } else {
-    win_wave<DQ, DV>(a, row, g, wave, wave - 1, kAttnWaves - 1, qf, myv, share);
+    win_wave<DQ, DV>(a, row, g, wave - 1, kAttnWaves - 1, qf, myv, rec_of(nc + ns + wave), share);
   }
   __syncthreads();  // the chosen blocks are in idx
-  sel_wave<DQ, DV>(a, row, g, wave, qf, myv);
+  sel_wave<DQ, DV>(a, row, g, wave, qf, myv, rec_of(nc + wave));
   __syncthreads();
-  merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse);
+  merge_body<DV, TO>(a, row, g, threadIdx.x, 256, coef, slse, rec_of);
 }
 
 template <int DQ, int DV, typename TO>
 hipError_t launch_fused(const DecArgs& a, hipStream_t s) {
-  const size_t fixed = (16 * kMaxRecords + 16) * 4 + (size_t)4 * 64 * (DV + 8) * 2;
-  if (a.nbp <= 1024) {  // logits in LDS: at most 64 KiB more
+  const size_t fixed = (16 * kMaxRecords + 16 + kMaxRecords * 32) * 4 + (size_t)4 * 64 * (DV + 8) * 2;
+  if (a.nbp <= 1024) {  // logits, then 8 records, in LDS: at most 66 KiB more
     auto k = k_dec_fused<DQ, DV, 16, true, TO>;
-    const size_t lds = 64 * 16 * 4 + fixed + (size_t)16 * (a.nbp + 4) * 4;
+    const size_t zbytes = (size_t)16 * (a.nbp + 4) * 4, rbytes = (size_t)8 * 16 * (DV + 4) * 4;
+    const size_t lds = 64 * 16 * 4 + fixed + (zbytes > rbytes ? zbytes : rbytes);
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
   } else {
