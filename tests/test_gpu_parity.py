@@ -41,6 +41,9 @@ CASES = [
     ("moba_1m", {}, 8),
     ("nsa_decode_64x64k", dict(batch=6, kv_len=4096 + 17), None),
     ("nsa_decode_64x64k", dict(batch=4, kv_len=4096 + 40, block=32, sel_block=64), None),
+    # more than 1024 summaries (the step kernel keeps its logits in global memory), other head dims
+    ("nsa_decode_64x64k", dict(batch=2, kv_len=40000, block=32, sel_block=64), None),
+    ("nsa_decode_64x64k", dict(batch=3, kv_len=9000, d_qk=128, d_v=64, top_k=12, window=256), None),
 ]
 
 
