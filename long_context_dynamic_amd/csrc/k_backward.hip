@@ -700,6 +700,7 @@ __global__ void __launch_bounds__(64) k_bwd_fill(BwArgs a) {
 //   dv^T += dout^T (gamma P),  dk^T += Q^T dS   (contraction over the 32 head
 //          rows of two tokens: A from LDS by transposing reads)
 enum { KV_WIN = 0, KV_SLC = 1, KV_CMP = 2, KV_STAT = 3 };
+constexpr int kKvWaves = 8;  // waves of the window and compressed key-side workgroups
 
 template <int DQ, int DV>
 struct KvLds {
@@ -708,12 +709,17 @@ struct KvLds {
   uint16_t ds[2][16 * DS];
 };
 
-template <int DQ, int DV, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_bwd_kv(BwArgs a) {
+// NW waves: 16 NW keys per workgroup.  The window and compressed branches
+// run 8 waves (128 keys: each staged token pair serves twice the keys), the
+// listed selected-branch entries 4 (their keys are one 64-token block).
+template <int DQ, int DV, int MODE, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) k_bwd_kv(BwArgs a) {
+  constexpr int NT = 64 * NW;
   constexpr int QS = KvLds<DQ, DV>::QS, DS = KvLds<DQ, DV>::DS;
   constexpr int QC = 16 * DQ / 8, DC = 16 * DV / 8;   // 16-byte chunks of one token's q / dout rows
   constexpr int NCH = 2 * (QC + DC);
-  constexpr int CPT = (NCH + 255) / 256;
+  constexpr int CPT = (NCH + NT - 1) / NT;
+  static_assert(MODE == KV_WIN || MODE == KV_CMP || NW == 4, "listed entries: 4 waves");
   __shared__ __align__(16) KvLds<DQ, DV> sm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int br = MODE == KV_WIN ? BR_WIN : (MODE == KV_CMP ? BR_CMP : BR_SLC);
@@ -726,30 +732,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int32_t* elist = nullptr;  // selected: this chunk's entries
   int64_t chunk_id = 0;
   if (MODE == KV_WIN) {
-    const int64_t ntile = (a.L + 63) / 64;
+    const int64_t ntile = (a.L + 16 * NW - 1) / (16 * NW);
     const int64_t K = blockIdx.x % ntile;
     const int64_t bg = blockIdx.x / ntile;
     g = bg % a.G;
     b = bg / a.G;
-    key0 = K * 64;
-    // tokens whose window [p - w + 1, p] meets [key0, key0 + 63]
-    int64_t plo = key0, phi = key0 + 63 + a.w - 1;
+    key0 = K * 16 * NW;
+    // tokens whose window [p - w + 1, p] meets [key0, key0 + 16 NW - 1]
+    int64_t plo = key0, phi = key0 + 16 * NW - 1 + a.w - 1;
     int64_t tlo = plo - (a.L - a.T), thi = phi - (a.L - a.T);
     if (tlo < 0) tlo = 0;
     if (thi > a.T - 1) thi = a.T - 1;
     tfirst = tlo;
     ntok = thi >= tlo ? thi - tlo + 1 : 0;
   } else if (MODE == KV_CMP) {
+    // NW / 4 consecutive 64-summary tiles J0, J0 + 1, ..: the token range of
+    // the first, which holds every later tile's; wave w writes the partial
+    // rows of tile J0 + w / 4 (tiles past the last are not written)
+    constexpr int TPW = NW / 4;
+    const int64_t nJw = (a.nJ + TPW - 1) / TPW;
     const int64_t c = blockIdx.x % a.nC;
-    const int64_t J = (blockIdx.x / a.nC) % a.nJ;
-    const int64_t bg = blockIdx.x / (a.nC * a.nJ);
+    const int64_t J0 = (blockIdx.x / a.nC) % nJw * TPW;
+    const int64_t bg = blockIdx.x / (a.nC * nJw);
     g = bg % a.G;
     b = bg / a.G;
-    key0 = J * 64;
-    chunk_id = blockIdx.x;
+    key0 = J0 * 64;
+    chunk_id = (bg * a.nJ + J0 + wave / 4) * a.nC + c;
     int64_t lo, hi;
-    cmp_chunk_range(a, J, c, lo, hi);
-    if (hi <= lo) return;  // the reduce skips this chunk by the same rule
+    cmp_chunk_range(a, J0, c, lo, hi);
+    if (hi <= lo) return;  // the reduce skips this chunk by the same rule (for J0 and every later tile)
     tfirst = lo;
     ntok = hi - lo;
   } else {  // KV_SLC, KV_STAT
@@ -808,7 +819,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     const int64_t tt[2] = {token_of(2 * pi), token_of(2 * pi + 1)};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int cc = threadIdx.x + 256 * i;
+      const int cc = threadIdx.x + NT * i;
       u32x4 val = {0u, 0u, 0u, 0u};
       if (cc < NCH) {
         const bool isq = cc < 2 * QC;
@@ -839,7 +850,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   auto stage = [&]() {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int cc = threadIdx.x + 256 * i;
+      const int cc = threadIdx.x + NT * i;
       if (cc < NCH) {
         const bool isq = cc < 2 * QC;
         const int x = isq ? cc : cc - 2 * QC;
@@ -955,7 +966,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(dvr + 16 * dt) = dvt[dt];
   } else {
-    float* prow = (MODE == KV_SLC ? a.part_s : a.part_c) + (chunk_id * 64 + 16 * wave + lr) * (DQ + DV) + 4 * lg;
+    if (MODE == KV_CMP && key0 / 64 + wave / 4 >= a.nJ) return;  // past the last tile
+    float* prow = (MODE == KV_SLC ? a.part_s : a.part_c) + (chunk_id * 64 + 16 * (wave % 4) + lr) * (DQ + DV) + 4 * lg;
 #pragma unroll
     for (int dt = 0; dt < DQ / 16; ++dt) *(f32x4*)(prow + 16 * dt) = dkt[dt] * a.scale;
 #pragma unroll
@@ -1093,7 +1105,7 @@ hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
     k_bwd_fill<<<(unsigned)(P.B * P.G * a.nct), 64, lds, s>>>(a);
     ph.mark();
     // with the training forward's statistics the group launches nothing
-    if (!a.sv_lse) k_bwd_kv<DQ, DV, KV_STAT><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    if (!a.sv_lse) k_bwd_kv<DQ, DV, KV_STAT, 4><<<(unsigned)chunks_max, 256, 0, s>>>(a);
     ph.mark();
   }
   k_bwd_qcw<DQ, DV><<<(unsigned)(P.B * P.G * ((P.T + kQTok - 1) / kQTok)), 64 * kQTok, 0, s>>>(a);
@@ -1101,15 +1113,17 @@ hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
   ph.mark();
   const int64_t ntile = (P.L + 63) / 64;
   if (P.has(NSA_F_WIN) && P.w > 0) {
-    k_bwd_kv<DQ, DV, KV_WIN><<<(unsigned)(P.B * P.G * ntile), 256, 0, s>>>(a);
+    k_bwd_kv<DQ, DV, KV_WIN, kKvWaves><<<(unsigned)(P.B * P.G * ((P.L + 16 * kKvWaves - 1) / (16 * kKvWaves))),
+                                          64 * kKvWaves, 0, s>>>(a);
     ph.mark();
   }
   if (slc) {
-    k_bwd_kv<DQ, DV, KV_SLC><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    k_bwd_kv<DQ, DV, KV_SLC, 4><<<(unsigned)chunks_max, 256, 0, s>>>(a);
     ph.mark();
   }
   if (P.has(NSA_F_CMP) && P.nb > 0) {
-    k_bwd_kv<DQ, DV, KV_CMP><<<(unsigned)(P.B * P.G * a.nJ * a.nC), 256, 0, s>>>(a);
+    k_bwd_kv<DQ, DV, KV_CMP, kKvWaves><<<(unsigned)(P.B * P.G * ((a.nJ + kKvWaves / 4 - 1) / (kKvWaves / 4)) * a.nC),
+                                          64 * kKvWaves, 0, s>>>(a);
     k_bwd_cmpsum<DQ, DV><<<(unsigned)((P.B * P.G * P.nb * (DQ + DV) + 255) / 256), 256, 0, s>>>(a);
     ph.mark();
   }
