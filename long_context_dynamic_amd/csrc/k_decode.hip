@@ -5,13 +5,18 @@
 //
 //   k_dec_fused      one workgroup per (row, group) for the whole step: the
 //                    two phases below back to back, with barriers between;
-//                    waves 1..3 stream the window while wave 0 does the top-k.
+//                    the logits stay in LDS, every wave computes a share of
+//                    the importance (waves 1..3 with their first window tile
+//                    in flight), waves 1..3 stream the window while wave 0
+//                    does the top-k, and the selected and window records
+//                    stay in LDS for the merge.
 //   k_dec_cmpsel     one workgroup per (row, group): 4 waves share out the
 //                    64-summary tiles (compressed-branch logits kept in zbuf
 //                    for the importance, a partial softmax-weighted sum of
 //                    the value summaries per wave); after a barrier the same
-//                    workgroup works out per-head softmax statistics, the
-//                    group importance and the top-k (one wave).
+//                    workgroup works out the group importance (each wave the
+//                    per-head softmax statistics and a share of the blocks)
+//                    and the top-k (one wave).
 //   k_dec_attnmerge  one workgroup per (row, group): 4 waves share out the
 //                    chosen blocks and the window's blocks (an online softmax
 //                    and a record per wave and branch); after a barrier the
