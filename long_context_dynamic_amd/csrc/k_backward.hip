@@ -428,7 +428,9 @@ struct RowStager {  // 64 rows of a [B, N, G, D] tensor, rows clamped to N - 1
   }
 };
 
-template <int DQ, int DV>
+// SAVED: the statistics come from the training forward (a.sv_lse), and the
+// first pass over the tiles is compiled out (fewer live registers).
+template <int DQ, int DV, bool SAVED>
 __global__ void __launch_bounds__(64 * kQTok) k_bwd_qcw(BwArgs a) {
   constexpr int KS = DQ + 16;
   __shared__ __align__(16) uint16_t kt[64 * KS];
@@ -495,7 +497,7 @@ __global__ void __launch_bounds__(64 * kQTok) k_bwd_qcw(BwArgs a) {
     if (!active) khi = -1;
     // statistics (lb: log-sum-exp in log2 units, db: <dout, O_b>) from the
     // training forward, or from a first pass over the tiles
-    const bool saved = a.sv_lse != nullptr;
+    constexpr bool saved = SAVED;
     float m = -INFINITY, l = 0.f, u = 0.f, lb = 0.f, db = 0.f;
     bool any = false;
     if (saved && on && active) {
@@ -1108,7 +1110,9 @@ hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
     if (!a.sv_lse) k_bwd_kv<DQ, DV, KV_STAT, 4><<<(unsigned)chunks_max, 256, 0, s>>>(a);
     ph.mark();
   }
-  k_bwd_qcw<DQ, DV><<<(unsigned)(P.B * P.G * ((P.T + kQTok - 1) / kQTok)), 64 * kQTok, 0, s>>>(a);
+  const unsigned gqcw = (unsigned)(P.B * P.G * ((P.T + kQTok - 1) / kQTok));
+  if (a.sv_lse) k_bwd_qcw<DQ, DV, true><<<gqcw, 64 * kQTok, 0, s>>>(a);
+  else k_bwd_qcw<DQ, DV, false><<<gqcw, 64 * kQTok, 0, s>>>(a);
   if (slc) k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
   ph.mark();
   const int64_t ntile = (P.L + 63) / 64;
