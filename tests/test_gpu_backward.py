@@ -159,3 +159,20 @@ def test_backward_full_size_64k_sampled_rows_and_sums():
     print(f"[bwd] 64k sum dk {rel_k:.2e} of sum |dk|; sum dv off by {rel_v:.2e}", flush=True)
     assert rel_k <= 1e-4
     assert rel_v <= 1e-3
+
+
+@pytest.mark.gpu
+def test_backward_without_dgates_output_matches():
+    """dgates is optional: leaving it out changes nothing else."""
+    name, prob = CASES[1]
+    x = _inputs(prob)
+    idx = _oracle_idx(prob, x)
+    import torch
+    d = {k: nsa.to_device(a, prob) for k, a in x.items() if a is not None}
+    idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    full = nsa.backward(prob, d["q"], d["k"], d["v"], d["gates"], idx_t, d["dout"])
+    part = nsa.backward(prob, d["q"], d["k"], d["v"], d["gates"], idx_t, d["dout"], want_dgates=False)
+    torch.cuda.synchronize()
+    assert part[3] is None
+    for a_, b_ in zip(full[:3], part[:3]):
+        assert torch.equal(a_, b_)
