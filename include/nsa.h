@@ -291,8 +291,9 @@ int32_t nsa_forward_phases(const nsa_params* params, const char** names, int32_t
 /* Workspace bytes that any call above needs for these params (0 if none). */
 size_t nsa_workspace_bytes(const nsa_params* params);
 
-/* Static description of a status code. */
-const char* nsa_status_str(nsa_status status);
+/* Static description of a status code; any int is accepted, values that
+ * are not an nsa_status give "unknown status". */
+const char* nsa_status_str(int status);
 
 #ifdef __cplusplus
 }

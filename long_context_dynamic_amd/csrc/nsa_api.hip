@@ -43,8 +43,10 @@ nsa_status describe(const nsa_params* p, Prob* P) {
   P->flags = p->flags; P->dtype = p->dtype;
   P->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d_qk));
   // element counts must fit the grid: one workgroup per (b, t, g) and per (b, j, g)
-  if (P->B * P->T * P->G >= ((int64_t)1 << 31) || P->B * P->nb * P->G >= ((int64_t)1 << 31))
-    return NSA_ERR_UNSUPPORTED;
+  // (B*T and B*nb fit int64 whatever the int32 fields hold; the products
+  // with G are compared by division so that nothing overflows)
+  const int64_t lim = (((int64_t)1 << 31) - 1) / P->G;
+  if (P->B * P->T > lim || P->B * P->nb > lim) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
@@ -58,7 +60,7 @@ nsa_status hip_status(hipError_t e) { return e == hipSuccess ? NSA_OK : NSA_ERR_
 
 extern "C" {
 
-const char* nsa_status_str(nsa_status s) {
+const char* nsa_status_str(int s) {
   switch (s) {
     case NSA_OK: return "ok";
     case NSA_ERR_INVALID_ARG: return "invalid argument";

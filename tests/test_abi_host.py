@@ -74,6 +74,21 @@ def test_bad_params_are_rejected_before_launch(field, value, code):
     assert nsa.lib().nsa_workspace_bytes(ctypes.byref(p)) == 0
 
 
+def test_huge_sizes_are_unsupported():
+    # every int32 field at its largest: the grid-size checks must not overflow
+    # (run under UndefinedBehaviorSanitizer by test_host_sanitizers.py)
+    big = (1 << 31) - 1
+    for b, t, g in ((big, big, big), (1, big, big), (big, 1, 1), (3, (1 << 30), 1), (1, 1 << 27, 16)):
+        p = _p(BASE)
+        p.batch, p.q_len, p.kv_len, p.n_kv_groups = b, t, t, g
+        p.block, p.sel_block = 4096, 0
+        assert _forward(p) == 2, (b, t, g)
+        assert nsa.lib().nsa_workspace_bytes(ctypes.byref(p)) == 0
+    p = _p(BASE)
+    p.batch, p.q_len, p.kv_len, p.n_kv_groups = 1, 1 << 20, 1 << 20, 1024
+    assert _forward(p) == 3        # 2^30 (b, t, g) rows fit: only the workspace is missing
+
+
 def test_pointer_and_flag_errors():
     lib = nsa.lib()
     p = _p(BASE)
