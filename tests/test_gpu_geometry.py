@@ -1,0 +1,116 @@
+"""Launch-geometry invariance (GPU): a batch of sequences and each of its
+sequences run alone launch different grids (other workgroup counts, another
+spread of work over the XCDs), but every row is computed by the same code in
+the same order, so the results must agree bit for bit.  Checked for the
+forward on each path (generic fp32, matrix-core prefill, MoBA, decode), the
+selection, the training forward's statistics and all four gradients."""
+import pytest
+import torch
+
+from long_context_dynamic_amd import inputs, nsa, workloads
+from tests import gpu_util as U
+from tests.test_gpu_backward import BASE as BW_BASE
+
+pytestmark = pytest.mark.gpu
+
+FWD_CASES = [
+    ("tiny fp32", workloads.get("nsa_tiny_fp32", batch=3, q_len=500, kv_len=700, window=100)),
+    ("prefill bf16", workloads.get("nsa_prefill_8k", batch=3, q_len=900, kv_len=1000, n_groups=2)),
+    ("prefill decoupled", workloads.get("nsa_prefill_8k", batch=2, q_len=700, kv_len=700, block=32, sel_block=64)),
+    ("moba", workloads.get("moba_32k", batch=2, q_len=800, kv_len=2500, n_groups=8)),
+    ("decode", workloads.get("nsa_decode_64x64k", batch=7, kv_len=5000)),
+]
+
+
+def _one(prob, x, b):
+    """Sequence b of a batch as its own problem (contiguous copies of its inputs)."""
+    p1 = dict(prob, batch=1)
+    return p1, {k: (None if a is None else a[b:b + 1].copy()) for k, a in x.items()}
+
+
+def _gates(prob, t):
+    return t.get("gates") if prob["use_cmp"] + prob["use_slc"] + prob["use_win"] > 1 else None
+
+
+def _same(a, b, what):
+    assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), what
+
+
+@pytest.mark.parametrize("name,prob", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_batch_split_is_bit_identical(name, prob):
+    print(f"[case] batch split forward {name}", flush=True)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    out = nsa.forward(prob, t["q"], t["k"], t["v"], _gates(prob, t))
+    kc, _ = nsa.compress(prob, t["k"], t["v"])
+    idx, score = nsa.select_topk(prob, t["q"], kc)
+    torch.cuda.synchronize()
+    for b in range(prob["batch"]):
+        p1, x1 = _one(prob, x, b)
+        t1 = U.upload(x1, p1)
+        o1 = nsa.forward(p1, t1["q"], t1["k"], t1["v"], _gates(p1, t1))
+        kc1, _ = nsa.compress(p1, t1["k"], t1["v"])
+        i1, s1 = nsa.select_topk(p1, t1["q"], kc1)
+        torch.cuda.synchronize()
+        _same(out[b:b + 1], o1, f"out of sequence {b}")
+        _same(kc[b:b + 1], kc1, f"summaries of sequence {b}")
+        _same(idx[b:b + 1], i1, f"selection of sequence {b}")
+        _same(score[b:b + 1], s1, f"scores of sequence {b}")
+
+
+def test_training_batch_split_is_bit_identical():
+    prob = dict(BW_BASE, batch=2, q_len=400, kv_len=520, top_k=6, gate_logits=1)
+    print("[case] batch split training forward + backward", flush=True)
+    x = inputs.generate(prob, want=("q", "k", "v", "gates", "dout"))
+    t = U.upload(x, prob)
+    out, idx, saved = nsa.forward_train(prob, t["q"], t["k"], t["v"], t["gates"])
+    grads = nsa.backward(prob, t["q"], t["k"], t["v"], t["gates"], idx, t["dout"], saved=saved)
+    rec = nsa.backward(prob, t["q"], t["k"], t["v"], t["gates"], idx, t["dout"])
+    lse, o = nsa.saved_views(prob, saved)
+    torch.cuda.synchronize()
+    for b in range(prob["batch"]):
+        p1, x1 = _one(prob, x, b)
+        t1 = U.upload(x1, p1)
+        out1, idx1, saved1 = nsa.forward_train(p1, t1["q"], t1["k"], t1["v"], t1["gates"])
+        g1 = nsa.backward(p1, t1["q"], t1["k"], t1["v"], t1["gates"], idx1, t1["dout"], saved=saved1)
+        r1 = nsa.backward(p1, t1["q"], t1["k"], t1["v"], t1["gates"], idx1, t1["dout"])
+        lse1, o1 = nsa.saved_views(p1, saved1)
+        torch.cuda.synchronize()
+        _same(out[b:b + 1], out1, f"out {b}")
+        _same(idx[b:b + 1], idx1, f"idx {b}")
+        _same(lse[:, b:b + 1], lse1, f"saved lse {b}")
+        _same(o[:, b:b + 1], o1, f"saved O {b}")
+        for nm, g, h in zip(("dq", "dk", "dv", "dgates"), grads, g1):
+            _same(g[b:b + 1], h, f"{nm} from saved statistics, sequence {b}")
+        for nm, g, h in zip(("dq", "dk", "dv", "dgates"), rec, r1):
+            _same(g[b:b + 1], h, f"{nm} recomputed, sequence {b}")
+
+
+SUFFIX_CASES = [
+    ("tiny fp32", workloads.get("nsa_tiny_fp32", q_len=1000, kv_len=1000, window=100), 333),
+    ("prefill bf16", workloads.get("nsa_prefill_8k", q_len=1300, kv_len=1300, n_groups=2), 301),
+    ("moba", workloads.get("moba_32k", q_len=2600, kv_len=2600, n_groups=4), 777),
+]
+
+
+@pytest.mark.parametrize("name,prob,tail", SUFFIX_CASES, ids=[c[0] for c in SUFFIX_CASES])
+def test_queries_at_the_end_match_the_full_prefill(name, prob, tail):
+    """The last `tail` queries asked alone (q_len < kv_len: other workgroup
+    boundaries within the sequence) against the same rows of the full prefill."""
+    print(f"[case] suffix queries {name} tail={tail}", flush=True)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    out = nsa.forward(prob, t["q"], t["k"], t["v"], _gates(prob, t))
+    p1 = dict(prob, q_len=tail)
+    q1 = t["q"][:, -tail:].contiguous()
+    g1 = None if _gates(prob, t) is None else t["gates"][:, -tail:].contiguous()
+    o1 = nsa.forward(p1, q1, t["k"], t["v"], g1)
+    kc, _ = nsa.compress(prob, t["k"], t["v"])
+    idx, _ = nsa.select_topk(prob, t["q"], kc, want_score=False)
+    i1, _ = nsa.select_topk(p1, q1, kc, want_score=False)
+    torch.cuda.synchronize()
+    _same(idx[:, -tail:], i1, "selection")
+    a, b = out[:, -tail:].float(), o1.float()
+    print(f"[suffix] {name}: max |diff| {(a - b).abs().max().item():.3e}, "
+          f"bit-identical rows {(a == b).all(dim=-1).float().mean().item():.3f}", flush=True)
+    _same(out[:, -tail:], o1, "output")
