@@ -120,12 +120,12 @@ __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
   const int64_t cur_max = (a.L - a.T + (t0 + 15 < a.T - 1 ? t0 + 15 : a.T - 1)) / a.bs;
   const int64_t nchunk = (visible_to(tile * kRows + kRows - 1) + 63) / 64;
   Stager<D, D, 256> st;
-  if (nchunk > 0) st.load(a.kc, a.nb, 0, false, nullptr, 0, 0, b, h, a.H, false);
+  if (nchunk > 0) st.load(a.kc, a.nb, 0, nullptr, 0, 0, b, h, a.H, false);
   for (int64_t c = 0; c < nchunk; ++c) {
     __syncthreads();
     st.store(kcs, nullptr, false, false);
     __syncthreads();
-    if (c + 1 < nchunk) st.load(a.kc, a.nb, 64 * (c + 1), false, nullptr, 0, 0, b, h, a.H, false);
+    if (c + 1 < nchunk) st.load(a.kc, a.nb, 64 * (c + 1), nullptr, 0, 0, b, h, a.H, false);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
     const int64_t nt = 4 * c + tt;
@@ -359,12 +359,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     for (int dt = 0; dt < D / 16; ++dt) o[q][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   Stager<D, D, 256> st;
   const int64_t kb0 = j * a.bs, ntl = a.bs / 64;
-  st.load(a.k, a.L, kb0, false, a.vT, a.Lp, kb0, b, h, a.H, true);
+  st.load(a.k, a.L, kb0, a.vT, a.Lp, kb0, b, h, a.H, true);
   for (int64_t i = 0; i < ntl; ++i) {
     __syncthreads();
-    st.store(kt, vt, true, false);
+    st.store(kt, vt, true, true);
     __syncthreads();
-    if (i + 1 < ntl) st.load(a.k, a.L, kb0 + 64 * (i + 1), false, a.vT, a.Lp, kb0 + 64 * (i + 1), b, h, a.H, true);
+    if (i + 1 < ntl) st.load(a.k, a.L, kb0 + 64 * (i + 1), a.vT, a.Lp, kb0 + 64 * (i + 1), b, h, a.H, true);
     if (busy) {
       f32x4 s[2][4];
       qk_tile_T2<D>(kt, qf, s, lr, lg);
@@ -463,12 +463,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int64_t p_wave = TP * pt + 16 * NQ * wave;
   Stager<D, D, 256> st;
   const int64_t kt0 = cur * a.bs / 64, kt1 = p_last / 64;
-  st.load(a.k, a.L, kt0 * 64, false, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
+  st.load(a.k, a.L, kt0 * 64, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
   for (int64_t kb = kt0; kb <= kt1; ++kb) {
     __syncthreads();
-    st.store(kt, vt, true, false);
+    st.store(kt, vt, true, true);
     __syncthreads();
-    if (kb + 1 <= kt1) st.load(a.k, a.L, (kb + 1) * 64, false, a.vT, a.Lp, (kb + 1) * 64, b, h, a.H, true);
+    if (kb + 1 <= kt1) st.load(a.k, a.L, (kb + 1) * 64, a.vT, a.Lp, (kb + 1) * 64, b, h, a.H, true);
     if (kb * 64 > p_wave + 16 * NQ - 1) continue;  // wave-uniform: every key after every row
     f32x4 s[NQ][4];
     if constexpr (NQ == 2) {
@@ -485,7 +485,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (!has_cur[q] || kb * 64 + 16 * mt + 4 * lg + r > p[q]) s[q][mt][r] = -INFINITY;
+            if (!has_cur[q] || kb * 64 + s_key(mt, lg, r) > p[q]) s[q][mt][r] = -INFINITY;
       }
       softmax_step<D>(s[q], m[q], l[q], o[q], c, stale, true);
     }

@@ -180,12 +180,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   Stager<DQ, DV, TQ * 64> st;
   const int64_t ntile_cmp = (nvis_max + 63) / 64;
-  if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, false, a.vcT, a.nbp, 0, b, g, a.G, use_cmp);
+  if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, a.vcT, a.nbp, 0, b, g, a.G, use_cmp);
   for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
-    st.store(kt, vt, use_cmp, false);
+    st.store(kt, vt, use_cmp, true);
     __syncthreads();
-    if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, false, a.vcT, a.nbp, (jt + 1) * 64, b, g, a.G, use_cmp);
+    if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, a.vcT, a.nbp, (jt + 1) * 64, b, g, a.G, use_cmp);
     if (jt * 64 < nvis) {
       f32x4 s[4];
       qk_tile_T<DQ>(kt, qf, s, lr, lg);
@@ -212,12 +212,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     ih[r] = __shfl(inv_l, 4 * lg + r, 64);
   }
   float* my_imp = imp + (int64_t)wave * a.nbp;
-  if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, false, nullptr, 0, 0, b, g, a.G, false);
+  if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, nullptr, 0, 0, b, g, a.G, false);
   for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
     st.store(kt, vt, false, false);
     __syncthreads();
-    if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, false, nullptr, 0, 0, b, g, a.G, false);
+    if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, nullptr, 0, 0, b, g, a.G, false);
     if (jt * 64 < nvis) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -256,12 +256,12 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     int64_t lo = p_first - a.w + 1;
     if (lo < 0) lo = 0;
     const int64_t kb0 = lo / 64, kb1 = p_last / 64;
-    st.load(a.k, a.L, kb0 * 64, false, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
+    st.load(a.k, a.L, kb0 * 64, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
     for (int64_t kb = kb0; kb <= kb1; ++kb) {
       __syncthreads();
-      st.store(kt, vt, true, false);
+      st.store(kt, vt, true, true);
       __syncthreads();
-      if (kb + 1 <= kb1) st.load(a.k, a.L, (kb + 1) * 64, false, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
+      if (kb + 1 <= kb1) st.load(a.k, a.L, (kb + 1) * 64, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
       if (active && kb * 64 <= p && kb * 64 + 63 > p - a.w) {
         f32x4 s[4];
         qk_tile_T<DQ>(kt, qf, s, lr, lg);

@@ -1,34 +1,48 @@
 // nsa_tile.h -- LDS tile machinery shared by the FA-style kernels (internal):
 // a register-prefetching stager for 64-key K / V^T tiles, the 64-key online
 // softmax step with a stale maximum, masks, and the two matrix-op products of
-// one tile.  In an S^T tile, s[mt][r] is key 16*mt + 4*lg + r and lane column
-// lr is one query row (a head of a token, or a token of a head).
+// one tile.  In an S^T tile, s[mt][r] is the key in LDS row 16*mt + 4*lg + r
+// and lane column lr is one query row (a head of a token, or a token of a
+// head).
 #pragma once
 
 #include "nsa_mfma.h"
 
 namespace nsa {
 
-// LDS row strides (bf16 elements).  K tile rows are read 16 bytes per lane
-// with lane l on row l % 16: conflict-free when the row stride is 32 bytes
-// past a multiple of 64 (d + 16 elements for d = 64, 128, 192).  V^T rows
-// are read 8 bytes per lane, lane l on row l % 16, and written 16 bytes per
-// lane the same way: conflict-free at 144 bytes (64 keys + 8).
+// LDS row strides (bf16 elements), from gfx950's measured bank behaviour
+// (counter SQ_LDS_BANK_CONFLICT over strides and lane maps).  16-byte reads
+// with lane l on row l % 16 and 16 bytes per lane group are conflict-free
+// when the row stride is 32 bytes past a multiple of 64: d + 16 elements for
+// K rows of d = 64, 128, 192, and 64 + 16 for V^T rows of a 64-key tile.
+// 16-byte writes of 128 contiguous bytes per 8 lanes are conflict-free at
+// those strides.  (Two 8-byte reads that the compiler pairs into one
+// ds_read2_b64 cost 8 conflict cycles per instruction at a 144-byte stride,
+// which is why the V^T operand is one 16-byte read.)
 template <int D> constexpr int k_lds_stride() { return D + 16; }
-constexpr int kVtStride = 64 + 8;
+constexpr int kVtStride = 64 + 16;
 
-// Within each run of 64 V^T chunks (16 bytes = 8 keys of one dim row; four
-// per 32-key half row) lane l takes chunk 4 * (l % 16) + l / 16, so a wave
-// still reads one contiguous kilobyte and its LDS writes put lane l on row
-// l % 16.
-__device__ __forceinline__ int vt_chunk(int c) { return (c & ~63) | ((c & 15) << 2) | ((c >> 4) & 3); }
+// Permuted key order of a 64-key tile stored with perm = true: LDS row
+// 16*mt + i holds key tile_key(mt, i) = 32*(mt/2) + 8*(i/4) + 4*(mt%2) + i%4.
+// In the S^T tiles mt = 2h and 2h + 1, lane group lg then holds the
+// probabilities of the 8 consecutive keys 32h + 8lg .. 32h + 8lg + 7, so each
+// V^T operand of P.V (keys in natural order) is one 16-byte read.
+__host__ __device__ constexpr int tile_key(int mt, int i) {
+  return 32 * (mt >> 1) + 8 * (i >> 2) + 4 * (mt & 1) + (i & 3);
+}
+__host__ __device__ constexpr int tile_row(int key) {
+  return 16 * (2 * (key >> 5) + ((key >> 2) & 1)) + 4 * ((key >> 3) & 3) + (key & 3);
+}
+// The key of S^T element s[mt][r] of lane group lg in a permuted tile.
+__device__ __forceinline__ int s_key(int mt, int lg, int r) { return 32 * (mt >> 1) + 8 * lg + 4 * (mt & 1) + r; }
 
 // ---------------------------------------------------------------------------
 // Register-prefetching tile stager: load() issues the global reads of one
 // 64-key tile (K rows [row0, row0 + 64) of a [B, Nrows, G, DQ] tensor, rows
 // clamped to Nrows - 1, and optionally V^T columns [col0, col0 + 64) of a
-// [B, G, DV, Np] tensor) into registers; store() writes them to LDS.  The
-// next tile's reads are in flight while the current tile is computed on.
+// tiled [B, G, Np / 32, DV, 32] tensor) into registers; store() writes them
+// to LDS, the K rows in permuted key order when perm is set.  The next
+// tile's reads are in flight while the current tile is computed on.
 template <int DQ, int DV, int NT>
 struct Stager {
   static constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
@@ -36,24 +50,19 @@ struct Stager {
   static constexpr int KPT = (KC + NT - 1) / NT, VPT = (VC + NT - 1) / NT;
   u32x4 kr[KPT], vr[VPT];
 
-  // rows: [B, Nrows, G, DQ], or with group_major one paired-row image of
-  // Nrows (a multiple of 64) rows per (b, g);
-  // colsT: tiled [B, G, Np / 32, DV, 32] (a 64-key tile = two 32-key halves)
-  __device__ __forceinline__ void load(const uint16_t* rows, int64_t Nrows, int64_t row0, bool group_major,
-                                       const uint16_t* colsT, int64_t Np, int64_t col0, int64_t b, int64_t g,
-                                       int64_t G, bool with_v) {
+  // V^T chunk c (16 bytes = 8 keys): row d = c / 8, 32-key half (c % 8) / 4,
+  // keys 8 * (c % 4) ..; 8 lanes cover one 128-byte LDS row, and a wave reads
+  // two contiguous 512-byte runs (one per half).
+  __device__ __forceinline__ void load(const uint16_t* rows, int64_t Nrows, int64_t row0, const uint16_t* colsT,
+                                       int64_t Np, int64_t col0, int64_t b, int64_t g, int64_t G, bool with_v) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = threadIdx.x + i * NT;
       if (KC % NT == 0 || c < KC) {
-        if (group_major) {  // the tile is one contiguous run of the image
-          kr[i] = *(const u32x4*)(rows + ((b * G + g) * Nrows + row0) * DQ + 8 * c);
-        } else {
-          const int r = c / (DQ / 8), c8 = c % (DQ / 8);
-          int64_t row = row0 + r;
-          if (row > Nrows - 1) row = Nrows - 1;
-          kr[i] = *(const u32x4*)(rows + ((b * Nrows + row) * G + g) * DQ + 8 * c8);
-        }
+        const int r = c / (DQ / 8), c8 = c % (DQ / 8);
+        int64_t row = row0 + r;
+        if (row > Nrows - 1) row = Nrows - 1;
+        kr[i] = *(const u32x4*)(rows + ((b * Nrows + row) * G + g) * DQ + 8 * c8);
       }
     }
     if (with_v) {
@@ -61,34 +70,25 @@ struct Stager {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * NT;
-        if (VC % NT == 0 || c < VC) vr[i] = *(const u32x4*)(tile + 8 * vt_chunk(c));
+        const int d = c / 8, h = (c % 8) / 4, j8 = c % 4;
+        if (VC % NT == 0 || c < VC) vr[i] = *(const u32x4*)(tile + (h * DV + d) * 32 + 8 * j8);
       }
     }
   }
-  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, bool with_v, bool group_major) const {
+  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, bool with_v, bool perm) const {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = threadIdx.x + i * NT;
       if (KC % NT == 0 || c < KC) {
-        int r, d;
-        if (group_major) {  // chunk c of the paired-row image: back to (row, dim)
-          const int e = 8 * c, rg = e / (16 * DQ), rem = e % (16 * DQ);
-          const int ks = rem / 512, w8 = (rem % 512) / 64, h = (rem % 64) / 32;
-          r = 16 * rg + 8 * h + w8;
-          d = 32 * ks + (rem % 32);
-        } else {
-          r = c / (DQ / 8);
-          d = 8 * (c % (DQ / 8));
-        }
-        *(u32x4*)(kt + r * KS + d) = kr[i];
+        const int r = c / (DQ / 8), d = 8 * (c % (DQ / 8));
+        *(u32x4*)(kt + (perm ? tile_row(r) : r) * KS + d) = kr[i];
       }
     }
     if (with_v) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * NT;
-        const int cc = vt_chunk(c);  // 16-byte chunk cc: half cc / (4 DV), row d, keys 8 * (cc % 4)
-        const int h = cc / (4 * DV), d = (cc / 4) % DV, j8 = cc % 4;
+        const int d = c / 8, h = (c % 8) / 4, j8 = c % 4;
         if (VC % NT == 0 || c < VC) *(u32x4*)(vt + d * VS + 32 * h + 8 * j8) = vr[i];
       }
     }
@@ -96,8 +96,8 @@ struct Stager {
 };
 
 // One 64-key online-softmax step for one token (16 heads) of one wave.
-// s[mt] holds S^T for keys 16*mt + 4*lg + r (raw dot products, masked ones
-// already -inf); updates the stale maximum m (raw units, raised only by more
+// s[mt] holds S^T for the tile's keys in either order (raw dot products,
+// masked ones already -inf); updates the stale maximum m (raw units, raised only by more
 // than 2^kStaleLog2 in probability), the sum l of head lr, and rescales o
 // when m moves.
 template <int DV>
@@ -131,14 +131,14 @@ __device__ __forceinline__ void softmax_step(f32x4 (&s)[4], float& m, float& l, 
   l += xor_sum16_32(rs);
 }
 
-// Keys (rows of an S^T tile) at or beyond `limit` relative to the tile
-// start are masked: s[mt][r] is key 16*mt + 4*lg + r.
+// Keys of a permuted tile at or beyond `limit` (relative to the tile start)
+// are masked.
 __device__ __forceinline__ void mask_from(f32x4 (&s)[4], int limit, int lg) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (16 * mt + 4 * lg + r >= limit) s[mt][r] = -INFINITY;
+      if (s_key(mt, lg, r) >= limit) s[mt][r] = -INFINITY;
 }
 // ... and keys below `first`.
 __device__ __forceinline__ void mask_below(f32x4 (&s)[4], int first, int lg) {
@@ -146,10 +146,11 @@ __device__ __forceinline__ void mask_below(f32x4 (&s)[4], int first, int lg) {
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (16 * mt + 4 * lg + r < first) s[mt][r] = -INFINITY;
+      if (s_key(mt, lg, r) < first) s[mt][r] = -INFINITY;
 }
 
-// O^T[d, h] += V^T[d, keys] P^T[keys, h] over one 64-key LDS tile.
+// O^T[d, h] += V^T[d, keys] P^T[keys, h] over one 64-key LDS tile whose
+// S^T (pm) came from a permuted K tile.
 template <int DV>
 __device__ __forceinline__ void pv_tile(const uint16_t* vt, const f32x4 (&pm)[4], f32x4 (&o)[DV / 16], int lr,
                                         int lg) {
@@ -158,9 +159,9 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vt, const f32x4 (&pm)[4]
   const bf16x8 p1 = pack8(pm[2], pm[3]);
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) {
-    const uint16_t* row = vt + (16 * dt + lr) * VS;
-    o[dt] = mfma16(ld4x2(row + 4 * lg, row + 16 + 4 * lg), p0, o[dt]);
-    o[dt] = mfma16(ld4x2(row + 32 + 4 * lg, row + 48 + 4 * lg), p1, o[dt]);
+    const uint16_t* row = vt + (16 * dt + lr) * VS + 8 * lg;
+    o[dt] = mfma16(ld8(row), p0, o[dt]);
+    o[dt] = mfma16(ld8(row + 32), p1, o[dt]);
   }
 }
 
@@ -205,9 +206,9 @@ __device__ __forceinline__ void pv_tile2(const uint16_t* vt, const f32x4 (&pm)[2
   const bf16x8 p10 = pack8(pm[1][0], pm[1][1]), p11 = pack8(pm[1][2], pm[1][3]);
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) {
-    const uint16_t* row = vt + (16 * dt + lr) * VS;
-    const bf16x8 v0 = ld4x2(row + 4 * lg, row + 16 + 4 * lg);
-    const bf16x8 v1 = ld4x2(row + 32 + 4 * lg, row + 48 + 4 * lg);
+    const uint16_t* row = vt + (16 * dt + lr) * VS + 8 * lg;
+    const bf16x8 v0 = ld8(row);
+    const bf16x8 v1 = ld8(row + 32);
     o[0][dt] = mfma16(v0, p00, o[0][dt]);
     o[1][dt] = mfma16(v0, p10, o[1][dt]);
     o[0][dt] = mfma16(v1, p01, o[0][dt]);
