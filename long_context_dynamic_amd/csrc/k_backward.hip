@@ -435,7 +435,7 @@ __global__ void __launch_bounds__(64 * kQTok) k_bwd_qcw(BwArgs a) {
   constexpr int KS = DQ + 16;
   __shared__ __align__(16) uint16_t kt[64 * KS];
   __shared__ __align__(16) uint16_t vr[64 * (DV + 16)];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t ntt = (a.T + kQTok - 1) / kQTok;
   const int64_t g = blockIdx.x % a.G;
   const int64_t tile = ntt - 1 - (blockIdx.x / a.G) % ntt;  // longest rows first
@@ -723,7 +723,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int CPT = (NCH + NT - 1) / NT;
   static_assert(MODE == KV_WIN || MODE == KV_CMP || NW == 4, "listed entries: 4 waves");
   __shared__ __align__(16) KvLds<DQ, DV> sm;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int br = MODE == KV_WIN ? BR_WIN : (MODE == KV_CMP ? BR_CMP : BR_SLC);
   constexpr bool LISTED = MODE == KV_SLC || MODE == KV_STAT;
   __shared__ f32x4 red[4][2][16];  // KV_STAT: per wave, token and head: max, sum, sum p.dP

@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) k_mlp_compress(MlpArgs a, int which) {
   constexpr int NTH = DH / 16, NTO = D / 16;
   __shared__ float part[3][16][DH + 4];  // waves 1..3's partial sums
   __shared__ __align__(16) uint16_t hid[16 * HS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const uint16_t* x = which ? a.v : a.k;
   const uint16_t* w1 = which ? a.v_w1 : a.k_w1;
   const uint16_t* b1 = which ? a.v_b1 : a.k_b1;
@@ -110,7 +110,7 @@ constexpr int kGateWS = 64 + 16;  // LDS row stride of a weight slice (16-byte r
 
 __global__ void __launch_bounds__(512) k_gate_proj(GateArgs a) {
   __shared__ __align__(16) uint16_t ws[16 * kGateNT * kGateWS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 128 + 16 * wave;
   int64_t m = m0 + lr;
   if (m > a.M - 1) m = a.M - 1;

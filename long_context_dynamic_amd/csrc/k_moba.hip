@@ -75,7 +75,7 @@ template <int D, int LS, bool SCORES>
 __global__ void __launch_bounds__(256) k_moba_select(MobaArgs a) {
   constexpr int KS = k_lds_stride<D>();
   __shared__ __align__(16) uint16_t kcs[64 * KS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t ntile = (a.T + kRows - 1) / kRows;
   const int64_t h = blockIdx.x % a.H;
   const int64_t tile = (blockIdx.x / a.H) % ntile;
@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int64_t j = bhj % a.nb, h = (bhj / a.nb) % a.H, b = bhj / (a.nb * a.H);
   const int64_t first = a.offsets[bhj] + (int64_t)(w - a.chunk_off[bhj]) * kChunk;
   const int64_t count = a.offsets[bhj + 1] - first;  // entries left in this list
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const bool busy = 32 * wave < count;  // wave-uniform: this wave has rows
   int64_t e[2];
   bf16x8 qf[2][D / 32];
@@ -428,7 +428,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int64_t h = blockIdx.x % a.H;
   const int64_t pt = pt0 + ntile - 1 - (blockIdx.x / a.H) % ntile;  // longest rows first
   const int64_t b = blockIdx.x / (a.H * ntile);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t p_first = TP * pt > P0 ? TP * pt : P0;
   const int64_t p_last = TP * pt + TP - 1 < a.L - 1 ? TP * pt + TP - 1 : a.L - 1;
   const int64_t cur = TP * pt / a.bs;

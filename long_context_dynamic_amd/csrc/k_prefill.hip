@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   uint16_t* vt = kt + 64 * KS;                       // [DV][VS]
   float* imp = (float*)(vt + (FWD ? DV * VS : 0));   // [TQ][nbp]
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
   const int64_t g = blockIdx.x % a.G;
   const int64_t tile = ntiles - 1 - (blockIdx.x / a.G) % ntiles;  // longest rows first
@@ -351,7 +351,7 @@ __device__ __forceinline__ void pv_chunk(const VFrag<DV>& f, f32x4 s0, f32x4 s1,
 
 template <int DQ, int DV, bool FWD, typename TO>
 __global__ void __launch_bounds__(256) k_sel(PfArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   // 4 consecutive tokens of one group per workgroup; each XCD takes a
   // contiguous run of a group's tokens
   const int64_t nq = (a.B * a.T + 3) / 4;

@@ -23,6 +23,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // 16 contiguous bytes (8 bf16) from global or LDS memory.
+// The wave's index in its workgroup, as a value the compiler knows to be
+// uniform across the wave (so that what is derived from it, such as buffer
+// resources, stays in scalar registers instead of per-lane loops).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
 }
