@@ -235,6 +235,16 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
   }
   __syncthreads();
 
+  // the window's first tile is read while the top-k runs
+  int64_t kb0 = 0, kb1 = -1;
+  if (use_win) {
+    int64_t lo = p_first - a.w + 1;
+    if (lo < 0) lo = 0;
+    kb0 = lo / 64;
+    kb1 = p_last / 64;
+    st.load(a.k, a.L, kb0 * 64, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
+  }
+
   // ---- top-k of this token's row (one wave) ----
   if (active) {
     int32_t* orow = a.idx + ((b * a.T + t) * a.G + g) * a.n;
@@ -253,10 +263,6 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     float m2 = -INFINITY, l2 = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int64_t lo = p_first - a.w + 1;
-    if (lo < 0) lo = 0;
-    const int64_t kb0 = lo / 64, kb1 = p_last / 64;
-    st.load(a.k, a.L, kb0 * 64, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
     for (int64_t kb = kb0; kb <= kb1; ++kb) {
       __syncthreads();
       st.store(kt, vt, true, true);

@@ -66,8 +66,8 @@ __device__ __forceinline__ int topk_wave(float (&vals)[NBL], int64_t nvis, int64
 // -1) and their scores to srow (padding -inf) when srow is given.
 __device__ __forceinline__ void topk_write(int cnt, int cj, float cs, int n, int32_t* orow, float* srow) {
   const int lane = threadIdx.x & 63;
-  int rank = 0;
-  for (int k2 = 0; k2 < cnt; ++k2) rank += (__shfl(cj, k2, 64) < cj) ? 1 : 0;
+  int rank = 0;  // lane reads into a scalar register: no LDS round trip per chosen block
+  for (int k2 = 0; k2 < cnt; ++k2) rank += (__builtin_amdgcn_readlane(cj, k2) < cj) ? 1 : 0;
   if (lane < cnt) {
     orow[rank] = cj;
     if (srow) srow[rank] = cs;
