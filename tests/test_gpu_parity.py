@@ -31,6 +31,9 @@ CASES = [
     # a longer ragged prefill checked on every row, and two sequences of one launch
     ("nsa_prefill_8k", dict(q_len=4500, kv_len=4600), None),
     ("nsa_prefill_8k", dict(batch=2, q_len=2100, kv_len=2100, n_groups=2), None),
+    # the largest summary count the matrix-core path takes (2048: the top-k's
+    # 32-values-per-lane form), queries at the end of a 128k cache
+    ("nsa_prefill_8k", dict(q_len=300, kv_len=131072), None),
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
     ("moba_32k", dict(q_len=700, kv_len=3000), None),
     ("moba_32k", dict(batch=2, q_len=1000, kv_len=12000, block=64, top_k=8, d_qk=64, d_v=64, force_first=1), None),
