@@ -34,7 +34,16 @@ __host__ __device__ constexpr int tile_row(int key) {
   return 16 * (2 * (key >> 5) + ((key >> 2) & 1)) + 4 * ((key >> 3) & 3) + (key & 3);
 }
 // The key of S^T element s[mt][r] of lane group lg in a permuted tile.
-__device__ __forceinline__ int s_key(int mt, int lg, int r) { return 32 * (mt >> 1) + 8 * lg + 4 * (mt & 1) + r; }
+__host__ __device__ constexpr int s_key(int mt, int lg, int r) { return 32 * (mt >> 1) + 8 * lg + 4 * (mt & 1) + r; }
+// tile_row inverts tile_key on all 64 rows, and s_key is tile_key of the
+// matrix-op output row 4 * lg + r
+__host__ __device__ constexpr bool tile_perm_ok() {
+  for (int row = 0; row < 64; ++row)
+    if (tile_row(tile_key(row / 16, row % 16)) != row || s_key(row / 16, (row % 16) / 4, row % 4) != tile_key(row / 16, row % 16))
+      return false;
+  return true;
+}
+static_assert(tile_perm_ok(), "tile_row must invert tile_key");
 
 // ---------------------------------------------------------------------------
 // Register-prefetching tile stager: load() issues the global reads of one
