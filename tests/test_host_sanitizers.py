@@ -11,7 +11,6 @@ is kept in _build/asan and redone only when a source or header changes."""
 import concurrent.futures as cf
 import glob
 import os
-import shutil
 import subprocess
 import sys
 
