@@ -31,6 +31,7 @@
  *     q      [B, q_len, H, d_qk]          k     [B, kv_len, G, d_qk]
  *     v      [B, kv_len, G, d_v]          gates [B, q_len, H, 3] (cmp, slc, win)
  *     k_cmp  [B, nb, G, d_qk]             v_cmp [B, nb, G, d_v]   nb = kv_len / block
+ *            (when nb == 0 there is nothing to hold and k_cmp / v_cmp may be NULL)
  *     idx    int32 [B, q_len, G, top_k]   ascending block ids, padded with -1
  *     out    [B, q_len, H, d_v]
  *   Element type: dtype (NSA_BF16 or NSA_F32) for q, k, v, gates, k_cmp,

@@ -20,6 +20,8 @@ constexpr uint32_t kAllFlags = NSA_F_FORCE_FIRST | NSA_F_FORCE_CURRENT | NSA_F_C
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+// an array of n elements: may be NULL when empty (no complete block: no summaries)
+bool arr_ok(const void* p, int64_t n) { return n == 0 ? opt_ok(p) : ptr_ok(p); }
 
 nsa_status describe(const nsa_params* p, Prob* P) {
   if (!p) return NSA_ERR_INVALID_ARG;
@@ -81,7 +83,8 @@ nsa_status nsa_compress(const void* k, const void* v, void* k_cmp, void* v_cmp, 
   Prob P;
   nsa_status st = describe(p, &P);
   if (st != NSA_OK) return st;
-  if (!ptr_ok(k) || !ptr_ok(v) || !ptr_ok(k_cmp) || !ptr_ok(v_cmp)) return NSA_ERR_INVALID_ARG;
+  const int64_t ns = P.B * P.nb * P.G;
+  if (!ptr_ok(k) || !ptr_ok(v) || !arr_ok(k_cmp, ns) || !arr_ok(v_cmp, ns)) return NSA_ERR_INVALID_ARG;
   return hip_status(nsa::launch_pool(P, k, v, k_cmp, v_cmp, (hipStream_t)p->stream));
 }
 
@@ -90,7 +93,8 @@ nsa_status nsa_compress_mlp(const void* k, const void* v, const nsa_mlp_weights*
   Prob P;
   nsa_status st = describe(p, &P);
   if (st != NSA_OK) return st;
-  if (!w || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(k_cmp) || !ptr_ok(v_cmp) || !ptr_ok(w->k_w1) || !ptr_ok(w->k_w2) ||
+  const int64_t ns = P.B * P.nb * P.G;
+  if (!w || !ptr_ok(k) || !ptr_ok(v) || !arr_ok(k_cmp, ns) || !arr_ok(v_cmp, ns) || !ptr_ok(w->k_w1) || !ptr_ok(w->k_w2) ||
       !ptr_ok(w->v_w1) || !ptr_ok(w->v_w2) || !opt_ok(w->k_b1) || !opt_ok(w->k_b2) || !opt_ok(w->v_b1) ||
       !opt_ok(w->v_b2) || w->d_hidden < 1)
     return NSA_ERR_INVALID_ARG;
@@ -135,7 +139,7 @@ nsa_status nsa_select_topk(const void* q, const void* k_cmp, int32_t* idx, float
   Prob P;
   nsa_status st = describe(p, &P);
   if (st != NSA_OK) return st;
-  if (!ptr_ok(q) || !ptr_ok(k_cmp) || !ptr_ok(idx) || !opt_ok(score)) return NSA_ERR_INVALID_ARG;
+  if (!ptr_ok(q) || !arr_ok(k_cmp, P.B * P.nb * P.G) || !ptr_ok(idx) || !opt_ok(score)) return NSA_ERR_INVALID_ARG;
   const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Select, true);
   if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
   return hip_status(nsa::run_select(P, q, k_cmp, idx, score, ws, p->workspace, (hipStream_t)p->stream));

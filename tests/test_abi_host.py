@@ -89,6 +89,16 @@ def test_huge_sizes_are_unsupported():
     assert _forward(p) == 3        # 2^30 (b, t, g) rows fit: only the workspace is missing
 
 
+def test_empty_summary_arrays_may_be_null():
+    # no complete block: the summary arrays are empty, so NULL is accepted
+    # (and nothing is launched); with complete blocks NULL stays invalid
+    lib = nsa.lib()
+    p = _p(workloads.get("nsa_prefill_8k", q_len=40, kv_len=40))
+    assert lib.nsa_compress(FAKE, FAKE, 0, 0, ctypes.byref(p)) == 0
+    assert lib.nsa_compress(FAKE, FAKE, 0, 0, ctypes.byref(_p(BASE))) == 1
+    assert lib.nsa_select_topk(FAKE, 0, FAKE, 0, ctypes.byref(_p(BASE))) == 1
+
+
 def test_pointer_and_flag_errors():
     lib = nsa.lib()
     p = _p(BASE)

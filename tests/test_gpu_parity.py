@@ -34,6 +34,14 @@ CASES = [
     # the largest summary count the matrix-core path takes (2048: the top-k's
     # 32-values-per-lane form), queries at the end of a 128k cache
     ("nsa_prefill_8k", dict(q_len=300, kv_len=131072), None),
+    # degenerate shapes: no complete block (empty compressed branch, only the
+    # partial current block to select), the shortest prefill above the
+    # decoding path, a zero window, a window longer than the sequence
+    ("nsa_prefill_8k", dict(q_len=40, kv_len=40), None),
+    ("nsa_prefill_8k", dict(q_len=9, kv_len=70), None),
+    ("nsa_prefill_8k", dict(q_len=200, kv_len=200, window=0), None),
+    ("nsa_prefill_8k", dict(q_len=300, kv_len=300, window=1000), None),
+    ("nsa_tiny_fp32", dict(q_len=5, kv_len=5), None),
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
     ("moba_32k", dict(q_len=700, kv_len=3000), None),
     ("moba_32k", dict(batch=2, q_len=1000, kv_len=12000, block=64, top_k=8, d_qk=64, d_v=64, force_first=1), None),
