@@ -103,8 +103,9 @@ def pooled(prob, k, v, rounded=True):
     B, T, L, G, hpg, bs, _ = _shapes(prob)
     nb = L // bs
     kk, vv = _widen(k, prob), _widen(v, prob)
-    kc = kk[:, :nb * bs].reshape(B, nb, bs, G, -1).mean(axis=2)
-    vc = vv[:, :nb * bs].reshape(B, nb, bs, G, -1).mean(axis=2)
+    # explicit last dimensions: with no complete block the arrays are empty
+    kc = kk[:, :nb * bs].reshape(B, nb, bs, G, kk.shape[-1]).mean(axis=2)
+    vc = vv[:, :nb * bs].reshape(B, nb, bs, G, vv.shape[-1]).mean(axis=2)
     if rounded:
         kc, vc = _round_store(kc, prob), _round_store(vc, prob)
     return kc, vc

@@ -34,6 +34,7 @@ CASES = [
                                           force_current=0, top_k=5)),
     ("long T=L=4200 G1 top16 w512", dict(BASE, q_len=4200, kv_len=4200, n_groups=1, top_k=16, window=512)),
     ("two sequences T=300 L=450 G2 logits", dict(BASE, batch=2, q_len=300, kv_len=450, top_k=6, gate_logits=1)),
+    ("no complete block T=L=40", dict(BASE, q_len=40, kv_len=40)),
 ]
 
 
