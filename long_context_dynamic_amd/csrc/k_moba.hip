@@ -588,7 +588,9 @@ bool moba_select_ok(const Prob& P) {
 }
 
 bool moba_attend_ok(const Prob& P) {
-  return P.bf16() && P.hpg == 1 && P.sb == P.bs && P.dq == P.dv && (P.dq == 64 || P.dq == 128) &&
+  // nb >= 1: with no complete block there is no list to build (its kernels
+  // would launch empty grids); the generic path takes that case
+  return P.bf16() && P.hpg == 1 && P.sb == P.bs && P.dq == P.dv && (P.dq == 64 || P.dq == 128) && P.nb >= 1 &&
          P.bs % 64 == 0 && P.n >= 1 &&
          P.n <= 8 && P.B * P.T * P.H * P.n < ((int64_t)1 << 31) && P.B * P.H * P.nb < ((int64_t)1 << 30);
 }

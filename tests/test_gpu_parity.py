@@ -43,6 +43,8 @@ CASES = [
     ("nsa_prefill_8k", dict(q_len=300, kv_len=300, window=1000), None),
     ("nsa_tiny_fp32", dict(q_len=5, kv_len=5), None),
     ("nsa_decode_64x64k", dict(batch=3, kv_len=40), None),
+    ("moba_32k", dict(q_len=300, kv_len=300), None),
+    ("moba_32k", dict(q_len=3, kv_len=1000), None),
     ("moba_32k", dict(q_len=2600, kv_len=2600), 160),
     ("moba_32k", dict(q_len=700, kv_len=3000), None),
     ("moba_32k", dict(batch=2, q_len=1000, kv_len=12000, block=64, top_k=8, d_qk=64, d_v=64, force_first=1), None),
