@@ -97,6 +97,12 @@ def test_empty_summary_arrays_may_be_null():
     assert lib.nsa_compress(FAKE, FAKE, 0, 0, ctypes.byref(p)) == 0
     assert lib.nsa_compress(FAKE, FAKE, 0, 0, ctypes.byref(_p(BASE))) == 1
     assert lib.nsa_select_topk(FAKE, 0, FAKE, 0, ctypes.byref(_p(BASE))) == 1
+    w = nsa.MlpWeights()
+    w.d_hidden = 192
+    for n in ("k_w1", "k_w2", "v_w1", "v_w2"):
+        setattr(w, n, FAKE)
+    assert lib.nsa_compress_mlp(FAKE, FAKE, ctypes.byref(w), 0, 0, ctypes.byref(p)) == 0
+    assert lib.nsa_compress_mlp(FAKE, FAKE, ctypes.byref(w), 0, 0, ctypes.byref(_p(BASE))) == 1
 
 
 def test_pointer_and_flag_errors():
