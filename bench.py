@@ -30,6 +30,20 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "NSA fwd tokens/s + % bf16 MFMA peak (64k prefill); decode % HBM peak"
 
 
+# What the pages themselves report for this method, quoted as context: none
+# of it is a measurement of this path or of this chip.
+PAGE_CONTEXT = {
+    "nsa_vs_flashattention_64k": "close to 10x faster than a FlashAttention kernel at 64k tokens, both "
+                                 "written in Triton; hardware, precision and shapes not stated "
+                                 "([P1] s6 'Why Sparse Attention Wins'; [P2] numbers table)",
+    "shorter_sequences": "already faster at 8k-16k, the ratio growing with length; no numbers ([P1] s6, s7)",
+    "decode": "memory-bound, set by the KV bytes read; a speed-up is expected but not quantified ([P1] s6)",
+    "selection_granularity": "NSA: 64-token blocks, top-16; MoBA: 512-token blocks, top-3 ([P1] s7; [P2])",
+    "model_shapes": "4 KV groups, 64 query heads, query head dim 192, hidden size 2560 ([P1] s5; [P2])",
+    "matrix_vs_vector": "half-precision matrix units about 16x the vector ALUs at equal FLOPs, on A100 ([P1] s5)",
+}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -400,11 +414,24 @@ def run_decode(args, torch, nsa, workloads, inputs):
             "phases_ms": {n: round(float(np.median(v)), 4) for n, v in per_phase.items()},
             "roofline": {"kernel": "whole decode step", "bound": "hbm", "achieved": round(achieved, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                         "traffic": None, "algorithmic_bytes_per_step": int(byts)},
+                         "traffic": load_traffic("dec_step", "nsa_decode_64x64k"),
+                         "algorithmic_bytes_per_step": int(byts)},
             "timing": "median of per-step HIP-event times; a 512 MiB read pass between steps evicts the last-level cache"}
 
 
 # -------------------------------------------------------------- cpu oracle --
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 
 def run_cpu_baseline(prob, x, target_s=15.0):
     import oracle
@@ -426,6 +453,7 @@ def run_cpu_baseline(prob, x, target_s=15.0):
     t_rows = timed(rows)
     secs = t_rows + t_pool * n / T
     return {"value": round(n / secs, 2), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n} query rows evenly spaced over the {T}-token sequence (all 64 heads each); "
                       f"pooling of the whole sequence ({t_pool:.2f}s) prorated by {n}/{T}",
             "seconds": round(t_rows + t_pool, 2)}
@@ -553,6 +581,7 @@ def main():
         "algorithmic_tflop": {k: round(v / 1e12, 4) for k, v in fl.items()},
         "forward_mfma_frac": round(f_tot / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
+        "context_from_pages": PAGE_CONTEXT,
     }
     log(f"prefill: {ms:.3f} ms/step, phases {rec['phases_ms']}")
     del x  # host inputs of the 64k workload; made again for the CPU baseline
@@ -563,7 +592,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_extra:
         # MoBA at longer contexts, and the 64k prefill with decoupled block sizes
-        for wl, fn in (("moba_128k", run_moba), ("moba_1m", run_moba), ("nsa_prefill_64k_c32", run_nsa_leg)):
+        for wl, fn in (("nsa_prefill_8k", run_nsa_leg), ("moba_128k", run_moba), ("moba_1m", run_moba),
+                       ("nsa_prefill_64k_c32", run_nsa_leg)):
             rec.setdefault("more_configs", {})[wl] = run_side_leg(args, torch, nsa, workloads, inputs, wl, fn)
             log(f"{wl}: {rec['more_configs'][wl]['ms_per_step']} ms/step")
     if not args.no_backward:

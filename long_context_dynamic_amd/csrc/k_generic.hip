@@ -1,9 +1,8 @@
 // k_generic.hip -- any-shape path of the NSA forward: plain VALU kernels with
-// fp32 arithmetic, one workgroup per (token, KV group).  It covers every
-// shape the ABI accepts (fp32 mode, few heads per group, odd head dims,
-// small blocks) and is the baseline the matrix-core paths are checked
-// against.  Sources: [P1] s4 (three branches, group-summed selection,
-// gating), [P1] s7 and [P5] s13 (MoBA).
+// fp32 arithmetic, one workgroup per (token, KV group).  It takes every
+// shape the ABI accepts that no matrix-core path takes (fp32 mode, few heads
+// per group, odd head dims, small blocks).  Sources: [P1] s4 (three
+// branches, group-summed selection, gating), [P1] s7 and [P5] s13 (MoBA).
 #include <math.h>
 
 #include "nsa_internal.h"

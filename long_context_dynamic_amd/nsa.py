@@ -6,7 +6,9 @@ fallback: if the library is not built, loading fails loudly.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -130,6 +132,19 @@ def params(prob: dict, *, out_f32: bool = False, k_cmp=None, v_cmp=None, workspa
     return p
 
 
+def _on_stream(fn):
+    """Run a wrapper with the caller's stream (keyword `stream`) current, so
+    every tensor it allocates (outputs, workspace) belongs to the stream the
+    library queues its kernels on: the caching allocator then cannot hand
+    that memory to other work while those kernels still use it."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kw)
+    return run
+
+
 def _call(name: str, *args) -> None:
     code = getattr(lib(), name)(*args)
     if code != 0:
@@ -173,6 +188,7 @@ def alloc_workspace(prob: dict, have_cmp: bool = False, device="cuda") -> torch.
     return torch.empty(max(workspace_bytes(prob, have_cmp), 256), dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def compress(prob: dict, k: torch.Tensor, v: torch.Tensor, kc=None, vc=None, stream=None):
     s, dt = _shapes(prob), torch_dtype(prob)
     _check(k, s["k"], dt, "k")
@@ -186,6 +202,7 @@ def compress(prob: dict, k: torch.Tensor, v: torch.Tensor, kc=None, vc=None, str
     return kc, vc
 
 
+@_on_stream
 def select_topk(prob: dict, q: torch.Tensor, kc: torch.Tensor, idx=None, score=None, want_score=True,
                 workspace=None, stream=None):
     s, dt = _shapes(prob), torch_dtype(prob)
@@ -202,6 +219,7 @@ def select_topk(prob: dict, q: torch.Tensor, kc: torch.Tensor, idx=None, score=N
     return idx, score
 
 
+@_on_stream
 def sparse_attn(prob: dict, q, k, v, idx, out=None, lse=None, want_lse=True, out_f32=False,
                 workspace=None, stream=None):
     s, dt = _shapes(prob), torch_dtype(prob)
@@ -230,6 +248,7 @@ def forward_phases(prob: dict, have_cmp: bool = False) -> list:
     return [names[i].decode() for i in range(min(n, 64))]
 
 
+@_on_stream
 def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f32=False,
             workspace=None, stream=None, events=None):
     s, dt = _shapes(prob), torch_dtype(prob)
@@ -272,6 +291,7 @@ def saved_views(prob: dict, saved: torch.Tensor):
     return lse, o
 
 
+@_on_stream
 def forward_train(prob: dict, q, k, v, gates, out=None, idx=None, saved=None, out_f32=False,
                   workspace=None, stream=None, events=None):
     """nsa_forward_train: (out, idx, saved) -- saved is the uint8 statistics buffer."""
@@ -315,6 +335,7 @@ def backward_phases(prob: dict) -> list:
     return [names[i].decode() for i in range(min(n, 64))]
 
 
+@_on_stream
 def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, dgates=None,
              want_dgates=True, workspace=None, stream=None, events=None, saved=None):
     """Gradients of nsa_forward on the selection idx: (dq, dk, dv, dgates), fp32.
@@ -350,6 +371,7 @@ def backward(prob: dict, q, k, v, gates, idx, dout, dq=None, dk=None, dv=None, d
     return dq, dk, dv, dgates
 
 
+@_on_stream
 def compress_mlp(prob: dict, k, v, wk: dict, wv: dict, kc=None, vc=None, stream=None):
     """Learned summaries: wk, wv hold device tensors w1, w2 and optional b1, b2."""
     s, dt = _shapes(prob), torch_dtype(prob)
@@ -378,6 +400,7 @@ def compress_mlp(prob: dict, k, v, wk: dict, wv: dict, kc=None, vc=None, stream=
     return kc, vc
 
 
+@_on_stream
 def gate_proj(prob: dict, x, w, bias=None, gates=None, logits=False, stream=None):
     """gates [B, T, H, 3] = sigmoid(x w^T + bias) (or the logits)."""
     s, dt = _shapes(prob), torch_dtype(prob)

@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
                           "nsa_internal.h"],
     "moba_attn": ["k_moba.hip", "nsa_moba.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
     "moba_own_block": ["k_moba.hip", "nsa_moba.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
+    "dec_step": ["k_decode.hip", "nsa_decode.h", "nsa_topk.h", "nsa_mfma.h", "nsa_internal.h"],
 }
 
 COPY_BYTES = 2 ** 30

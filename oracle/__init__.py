@@ -71,6 +71,7 @@ def _load():
         lib.oracle_select.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, ctypes.c_int64, p, p, p]
         lib.oracle_attend.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, p, p, p,
                                       ctypes.c_int64, p, p, p]
+        lib.oracle_selected_lse.argtypes = [ctypes.POINTER(_Cfg), p, p, p, p, ctypes.c_int64, p]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -169,6 +170,21 @@ def attend(prob: dict, q, k, v, gates, idx, o_cmp=None, rows=None):
                                  _ptr(idx), _ptr(o_cmp), _ptr(rows), len(rows),
                                  _ptr(out), _ptr(oslc), _ptr(owin)), "attend")
     return out, oslc, owin
+
+
+def selected_lse(prob: dict, q, k, idx, rows=None):
+    """Natural log-sum-exp of the selected branch's scaled logits on the
+    GIVEN selection idx [R,G,top_k] (the normaliser of that branch's
+    softmax): [R,H] float64, -inf where the key set is empty."""
+    q, k = _stored(q, prob), _stored(k, prob)
+    rows = _rows(prob, rows)
+    R, H = len(rows), prob["n_groups"] * prob["heads_per_group"]
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(R, prob["n_groups"], prob["top_k"])
+    lse = np.zeros((R, H), dtype=np.float64)
+    c = _cfg(prob)
+    _check(_load().oracle_selected_lse(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(idx), _ptr(rows), len(rows),
+                                       _ptr(lse)), "selected_lse")
+    return lse
 
 
 def forward(prob: dict, q, k, v, gates, rows=None, kc=None, vc=None):

@@ -91,6 +91,68 @@ static double softmax_scale(const oracle_cfg* c) {
   return c->scale != 0.0 ? c->scale : 1.0 / sqrt((double)c->d_qk);
 }
 
+/* Natural log-sum-exp of the selected branch's scaled logits: for each
+ * listed row and head, log sum_s exp(scale * q_h . k_s) over the same key set
+ * as the selected branch of oracle_attend (every position s <= p of the
+ * chosen blocks, [P1] s4), -inf when that set is empty.  The softmax's
+ * normaliser, so that the branch's weights are exp(scale q.k_s - lse).
+ * Taken with the largest logit factored out, so no exp overflows. */
+int oracle_selected_lse(const oracle_cfg* c, const void* q, const void* k, const int32_t* idx,
+                        const int64_t* rows, int64_t nrows, double* lse) {
+  if (!cfg_ok(c)) return ORACLE_BAD_CONFIG;
+  const int64_t T = c->q_len, L = c->kv_len, G = c->n_groups, hpg = c->heads_per_group;
+  const int64_t H = G * hpg, dq = c->d_qk, bs = sel_block(c), n = c->top_k;
+  const double scale = softmax_scale(c);
+  int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t b = rows[r] / T, t = rows[r] % T;
+    const int64_t p = L - T + t;
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n * bs + 1));
+    double* z = (double*)malloc(sizeof(double) * (size_t)(n * bs + 1));
+    if (!keys || !z) {
+      bad = 1;
+      free(keys); free(z);
+      continue;
+    }
+    for (int64_t g = 0; g < G; ++g) {
+      const int32_t* sel = idx + (r * G + g) * n;
+      int64_t nk = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t j = sel[i];
+        if (j < 0) continue;
+        for (int64_t i2 = 0; i2 < i; ++i2)
+          if (sel[i2] == j) bad = 2;
+        if (j * bs > p) { bad = 2; continue; }
+        for (int64_t s = j * bs; s < (j + 1) * bs && s <= p; ++s) keys[nk++] = s;
+      }
+      for (int64_t hh = 0; hh < hpg; ++hh) {
+        const int64_t h = g * hpg + hh;
+        if (nk == 0) {
+          lse[r * H + h] = -INFINITY;
+          continue;
+        }
+        double m = -INFINITY;
+        for (int64_t i = 0; i < nk; ++i) {
+          double dot = 0.0;
+          for (int64_t d = 0; d < dq; ++d)
+            dot += load_elem(q, c->is_bf16, ((b * T + t) * H + h) * dq + d) *
+                   load_elem(k, c->is_bf16, ((b * L + keys[i]) * G + g) * dq + d);
+          z[i] = scale * dot;
+          if (z[i] > m) m = z[i];
+        }
+        double sum = 0.0;
+        for (int64_t i = 0; i < nk; ++i) sum += exp(z[i] - m);
+        lse[r * H + h] = m + log(sum);
+      }
+    }
+    free(keys); free(z);
+  }
+  if (bad == 2) return ORACLE_BAD_SELECTION;
+  return bad ? ORACLE_BAD_CONFIG : ORACLE_OK;
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

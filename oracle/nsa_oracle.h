@@ -74,6 +74,13 @@ int oracle_attend(const oracle_cfg* c, const void* q, const void* k, const void*
                   const int64_t* rows, int64_t nrows,
                   double* out, double* o_slc, double* o_win);
 
+/* Natural log-sum-exp of the selected branch's scaled logits per head,
+ * log sum_s exp(scale q_h . k_s) over oracle_attend's selected key set on
+ * the GIVEN selection idx [nrows, G, top_k]; -inf for an empty set.
+ *   lse [nrows, H].                                                       */
+int oracle_selected_lse(const oracle_cfg* c, const void* q, const void* k, const int32_t* idx,
+                        const int64_t* rows, int64_t nrows, double* lse);
+
 /* Threads the oracle's parallel loops use. */
 int oracle_threads(void);
 

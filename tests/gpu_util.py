@@ -8,6 +8,8 @@ from long_context_dynamic_amd import inputs, nsa
 
 TIE_REL = 1e-4          # near-tie band: |I_j - s_r| <= 1e-4 * s_r
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# a branch's log-sum-exp: fp32 logits of exact bf16 products, fp32 sums
+LSE_ATOL, LSE_RTOL = 1e-4, 1e-4
 
 
 def half_ulp_bf16(x: np.ndarray) -> np.ndarray:

@@ -114,3 +114,19 @@ def test_queries_at_the_end_match_the_full_prefill(name, prob, tail):
     print(f"[suffix] {name}: max |diff| {(a - b).abs().max().item():.3e}, "
           f"bit-identical rows {(a == b).all(dim=-1).float().mean().item():.3f}", flush=True)
     _same(out[:, -tail:], o1, "output")
+
+
+@pytest.mark.parametrize("name,prob", [FWD_CASES[1], FWD_CASES[4]], ids=["prefill bf16", "decode"])
+def test_forward_on_a_side_stream_is_bit_identical(name, prob):
+    """A call queued on another stream (its outputs and workspace allocated
+    on that stream by the binding) gives the same bits as one on the current
+    stream."""
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    a = nsa.forward(prob, t["q"], t["k"], t["v"], _gates(prob, t), out_f32=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    b = nsa.forward(prob, t["q"], t["k"], t["v"], _gates(prob, t), out_f32=True, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    _same(a, b, name)

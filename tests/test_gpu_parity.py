@@ -58,6 +58,11 @@ CASES = [
     # more than 1024 summaries (the step kernel keeps its logits in global memory), other head dims
     ("nsa_decode_64x64k", dict(batch=2, kv_len=40000, block=32, sel_block=64), None),
     ("nsa_decode_64x64k", dict(batch=3, kv_len=9000, d_qk=128, d_v=64, top_k=12, window=256), None),
+    # several new tokens per sequence in one decoding launch: every row has
+    # its own position, visible summaries, current block and window
+    ("nsa_decode_64x64k", dict(batch=2, q_len=5, kv_len=4096 + 17), None),
+    ("nsa_decode_64x64k", dict(batch=3, q_len=3, kv_len=40), None),
+    ("nsa_decode_64x64k", dict(batch=2, q_len=8, kv_len=3000 + 63, block=32, sel_block=64), None),
 ]
 
 
@@ -138,7 +143,14 @@ def test_sparse_attn_on_given_selection(i):
     err = np.abs(got - want).max()
     print(f"max |o_slc - oracle| = {err:.3e}")
     assert err <= U.TOL[prob["dtype"]]
-    assert np.all(np.isfinite(U.gather_rows(lse.cpu().numpy(), prob, sel_rows)))
+    # the branch's log-sum-exp (natural log, -inf for an empty key set)
+    want_lse = oracle.selected_lse(prob, x["q"], x["k"], idx, rows=sel_rows)
+    got_lse = U.gather_rows(lse.cpu().numpy().astype(np.float64), prob, sel_rows)
+    empty = np.isneginf(want_lse)
+    assert np.array_equal(np.isneginf(got_lse), empty)
+    lerr = np.abs(got_lse[~empty] - want_lse[~empty])
+    print(f"max |lse - oracle| = {lerr.max() if lerr.size else 0.0:.3e}")
+    assert np.all(lerr <= U.LSE_ATOL + U.LSE_RTOL * np.abs(want_lse[~empty]))
 
 
 @pytest.mark.parametrize("out_f32", [False, True])
@@ -261,3 +273,24 @@ def test_moba_forward_applies_the_gate():
     want, _, _ = oracle.attend(prob, x["q"], x["k"], x["v"], x["gates"], gsel, None, rows=rows)
     got = U.gather_rows(U.widen_out(out, prob), prob, rows)
     assert np.abs(got - want).max() <= U.TOL[prob["dtype"]]
+
+
+@pytest.mark.parametrize("name,over", [("nsa_decode_64x64k", dict(batch=2, kv_len=5000)),
+                                       ("moba_32k", dict(q_len=3000, kv_len=3000))])
+def test_compress_of_a_growing_cache_keeps_its_summaries(name, over):
+    """A decode cache grows token by token: pooling a prefix of it gives the
+    same bits as the first summaries of pooling the whole of it (a summary
+    depends only on its own block), so summaries can be made once per
+    completed block and kept."""
+    prob = workloads.get(name, **over)
+    x = inputs.generate(prob)
+    t = U.upload(x, prob)
+    kc, vc = nsa.compress(prob, t["k"], t["v"])
+    bs = prob["block"]
+    for L in (bs - 1, bs, 3 * bs + 5, prob["kv_len"] - 1):
+        short = dict(prob, kv_len=L, q_len=min(prob["q_len"], L))
+        kc2, vc2 = nsa.compress(short, t["k"][:, :L].contiguous(), t["v"][:, :L].contiguous())
+        torch.cuda.synchronize()
+        nb = L // bs
+        assert torch.equal(kc2.view(torch.int16), kc[:, :nb].view(torch.int16)), L
+        assert torch.equal(vc2.view(torch.int16), vc[:, :nb].view(torch.int16)), L

@@ -25,6 +25,7 @@ FWD_CASES = [
     ("moba ragged", workloads.get("moba_32k", q_len=700, kv_len=3000)),
     ("decode ragged", workloads.get("nsa_decode_64x64k", batch=5, kv_len=4096 + 17)),
     ("decode long", workloads.get("nsa_decode_64x64k", batch=2, kv_len=40000, block=32, sel_block=64)),
+    ("decode five tokens", workloads.get("nsa_decode_64x64k", batch=2, q_len=5, kv_len=4096 + 17)),
 ]
 
 

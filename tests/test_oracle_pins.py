@@ -9,6 +9,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from long_context_dynamic_amd import inputs
@@ -456,3 +457,75 @@ def test_bad_selection_is_refused():
     idx[:, 0, 1] = 0  # duplicate block
     with pytest.raises(ValueError):
         oracle.attend(prob, x["q"], x["k"], x["v"], x["gates"], idx, np.zeros((32, 1, 4)))
+
+
+# ------------------------------------------ selected-branch log-sum-exp --
+
+@pytest.mark.parametrize("sel_block,dtype", [(0, "f32"), (16, "f32"), (0, "bf16")])
+def test_selected_lse_is_torch_logsumexp_over_the_chosen_keys(sel_block, dtype):
+    # log sum exp of the scaled logits over the chosen blocks' tokens s <= p,
+    # from torch.logsumexp in float64 with the selection as a mask
+    prob = H.problem(q_len=96, kv_len=130, block=8, sel_block=sel_block, top_k=4, n_groups=2,
+                     heads_per_group=2, d_qk=8, d_v=8, window=16, seed=23, dtype=dtype)
+    x = H.make(prob)
+    r = oracle.forward(prob, x["q"], x["k"], x["v"], x["gates"])
+    lse = oracle.selected_lse(prob, x["q"], x["k"], r["idx"])
+    q, k = H.widen(x["q"], prob)[0], H.widen(x["k"], prob)[0]
+    pos = H.positions(prob)
+    blk = np.arange(prob["kv_len"]) // (sel_block or 8)
+    for h in range(4):
+        g = h // 2
+        mask = np.zeros((96, prob["kv_len"]), bool)
+        for t in range(96):
+            chosen = [j for j in r["idx"][t, g] if j >= 0]
+            mask[t] = np.isin(blk, chosen) & (np.arange(prob["kv_len"]) <= pos[t])
+        z = torch.from_numpy(q[:, h]) @ torch.from_numpy(k[:, g]).T * H.default_scale(prob)
+        want = torch.logsumexp(z.masked_fill(~torch.from_numpy(mask), float("-inf")), dim=-1).numpy()
+        np.testing.assert_allclose(lse[:, h], want, atol=1e-12, rtol=1e-13)
+
+
+def test_selected_lse_closed_forms():
+    prob = H.problem(q_len=64, kv_len=64, block=8, top_k=3, n_groups=1, heads_per_group=2,
+                     d_qk=8, d_v=4, window=6, force_first=0, seed=29)
+    x = H.make(prob)
+    T = prob["q_len"]
+    # one key: the current block alone, queried at its first position,
+    # holds only that position; the lse is the query's own scaled logit
+    idx = np.full((T, 1, 3), -1, np.int32)
+    idx[:, 0, 0] = np.arange(T) // 8
+    lse = oracle.selected_lse(prob, x["q"], x["k"], idx)
+    q, k = H.widen(x["q"], prob)[0], H.widen(x["k"], prob)[0]
+    for t in range(0, T, 8):
+        for h in range(2):
+            assert lse[t, h] == pytest.approx(np.dot(q[t, h], k[t, 0]) / np.sqrt(8), abs=1e-13)
+    # q = 0: every logit is 0, the lse is log of the number of keys
+    y = dict(x)
+    y["q"] = np.zeros_like(x["q"])
+    idx2 = np.full((T, 1, 3), -1, np.int32)
+    idx2[:, 0, 0] = 0
+    idx2[:, 0, 1] = np.where(np.arange(T) // 8 > 0, np.arange(T) // 8, -1)
+    lse0 = oracle.selected_lse(prob, y["q"], y["k"], idx2)
+    for t in range(T):
+        nkeys = min(8, t + 1) + (t % 8 + 1 if t >= 8 else 0)
+        np.testing.assert_allclose(lse0[t], np.log(nkeys), atol=1e-14, rtol=0)
+    # an empty key set gives -inf
+    lse_e = oracle.selected_lse(prob, x["q"], x["k"], np.full((T, 1, 3), -1, np.int32))
+    assert np.all(lse_e == -np.inf)
+
+
+def test_selected_lse_has_no_overflow_for_large_logits():
+    # logits in the thousands: exp would overflow without the max factored out
+    prob = H.problem(q_len=16, kv_len=16, block=8, top_k=2, n_groups=1, heads_per_group=1,
+                     d_qk=4, d_v=4, window=4, force_first=0)
+    x = H.make(prob)
+    x["q"] = (x["q"] * 200).astype(np.float32)
+    x["k"] = (x["k"] * 200).astype(np.float32)
+    idx = np.full((16, 1, 2), -1, np.int32)
+    idx[:, 0, 0] = 0
+    idx[8:, 0, 1] = 1
+    lse = oracle.selected_lse(prob, x["q"], x["k"], idx)
+    q, k = H.widen(x["q"], prob)[0, :, 0], H.widen(x["k"], prob)[0, :, 0]
+    for t in range(16):
+        z = q[t] @ k[:t + 1].T / 2.0
+        assert np.isfinite(lse[t, 0])
+        assert lse[t, 0] == pytest.approx(z.max() + np.log(np.exp(z - z.max()).sum()), abs=1e-9)
