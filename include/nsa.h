@@ -45,8 +45,9 @@
  *   Errors: arguments are validated before anything is queued; on any error
  *     nothing is launched and no output is written.  NSA_ERR_HIP reports a
  *     failed launch (hipGetLastError), in which case outputs are undefined.
- *   Thread safety: calls hold no global state and may come from several
- *     threads; calls sharing a workspace must be ordered on one stream.
+ *   Thread safety: calls hold no global state (apart from the fixed scratch
+ *     of nsa_forward_noalloc) and may come from several threads; calls
+ *     sharing a workspace must be ordered on one stream.
  */
 #ifndef NSA_H
 #define NSA_H
@@ -212,6 +213,32 @@ nsa_status nsa_sparse_attn(const void* q, const void* k, const void* v, const in
  */
 nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates,
                        const nsa_params* params, void* out);
+
+/* Bytes of the fixed device scratch that nsa_forward_noalloc works in. */
+#define NSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * nsa_forward without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same operation, arguments, limits and results as
+ * nsa_forward, except that params->workspace and workspace_bytes are ignored:
+ * the scratch is one fixed array of NSA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its device
+ * address is looked up once per device, on the first call there).  The call
+ * allocates and frees nothing.
+ *   Limit: a call whose workspace (nsa_workspace_bytes) exceeds
+ *   NSA_NOALLOC_SCRATCH_BYTES returns NSA_ERR_WORKSPACE before anything is
+ *   queued.  Decoding steps over a caller-held summary cache
+ *   (params->k_cmp / v_cmp) fit, e.g. 64 sequences x 64k tokens; a 64k prefill
+ *   does not.
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps
+ *   whatever the last call left (no result depends on its prior contents).
+ *   Calls that may overlap in time on one GPU (other streams, other threads)
+ *   race on it and must be ordered by the caller.
+ *   NSA_ERR_HIP also when the scratch's device address cannot be obtained.
+ */
+nsa_status nsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gates,
+                               const nsa_params* params, void* out);
 
 /*
  * Training forward: nsa_forward (summaries mean-pooled in the workspace)

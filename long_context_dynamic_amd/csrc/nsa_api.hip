@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "nsa_backward.h"
 #include "nsa_decode.h"
 #include "nsa_internal.h"
@@ -157,26 +159,85 @@ nsa_status nsa_sparse_attn(const void* q, const void* k, const void* v, const in
   return hip_status(nsa::run_sparse_attn(P, q, k, v, idx, out, lse, ws, p->workspace, (hipStream_t)p->stream));
 }
 
-nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates, const nsa_params* p,
-                       void* out) {
-  Prob P;
-  nsa_status st = describe(p, &P);
+}  // extern "C"
+
+namespace {
+
+// Everything nsa_forward and nsa_forward_noalloc check before anything is
+// queued, except the workspace itself.
+nsa_status forward_checks(const void* q, const void* k, const void* v, const void* gates, const nsa_params* p,
+                          const void* out, Prob* P) {
+  nsa_status st = describe(p, P);
   if (st != NSA_OK) return st;
-  const int nbr = n_branches(P.flags);
+  const int nbr = n_branches(P->flags);
   if (nbr == 0 || (gates == nullptr && nbr > 1)) return NSA_ERR_INVALID_ARG;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out) || !opt_ok(gates)) return NSA_ERR_INVALID_ARG;
   if ((p->k_cmp == nullptr) != (p->v_cmp == nullptr) || !opt_ok(p->k_cmp) || !opt_ok(p->v_cmp))
     return NSA_ERR_INVALID_ARG;
-  const bool have_cmp = p->k_cmp != nullptr;
-  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Forward, have_cmp);
-  if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
   if (p->n_phase_events < 0 || (p->n_phase_events > 0 && !p->phase_events)) return NSA_ERR_INVALID_ARG;
+  return NSA_OK;
+}
+
+nsa_status forward_on(const void* q, const void* k, const void* v, const void* gates, const nsa_params* p,
+                      void* out, const Prob& P, const nsa::Workspace& ws, void* base) {
+  const bool have_cmp = p->k_cmp != nullptr;
   nsa::Phases ph;
   ph.ev = p->phase_events;
   ph.n = p->phase_events ? p->n_phase_events : 0;
   return hip_status(nsa::run_forward(P, q, k, v, gates, have_cmp ? p->k_cmp : nullptr,
-                                     have_cmp ? p->v_cmp : nullptr, out, nullptr, nullptr, ws, p->workspace,
+                                     have_cmp ? p->v_cmp : nullptr, out, nullptr, nullptr, ws, base,
                                      (hipStream_t)p->stream, ph));
+}
+
+// ---- the allocation-free forward's scratch ---------------------------------
+// One fixed array per device, the workspace of every nsa_forward_noalloc call
+// on that device.  Its name is only a host-side handle: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device (with
+// that device current) on the first call there, and only that address is
+// ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[NSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of scratch on each device, once looked up
+
+// The current device's scratch address, or NULL when it cannot be had.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status nsa_forward(const void* q, const void* k, const void* v, const void* gates, const nsa_params* p,
+                       void* out) {
+  Prob P;
+  nsa_status st = forward_checks(q, k, v, gates, p, out, &P);
+  if (st != NSA_OK) return st;
+  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Forward, p->k_cmp != nullptr);
+  if (ws.total > 0 && (!ptr_ok(p->workspace) || p->workspace_bytes < ws.total)) return NSA_ERR_WORKSPACE;
+  return forward_on(q, k, v, gates, p, out, P, ws, p->workspace);
+}
+
+nsa_status nsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gates,
+                               const nsa_params* p, void* out) {
+  Prob P;
+  nsa_status st = forward_checks(q, k, v, gates, p, out, &P);
+  if (st != NSA_OK) return st;
+  const nsa::Workspace ws = nsa::plan_workspace(P, nsa::Call::Forward, p->k_cmp != nullptr);
+  if (ws.total > NSA_NOALLOC_SCRATCH_BYTES) return NSA_ERR_WORKSPACE;
+  void* base = device_scratch();
+  if (!base) return NSA_ERR_HIP;
+  return forward_on(q, k, v, gates, p, out, P, ws, base);
 }
 
 // A training forward runs the matrix-core prefill path (its kernels write the

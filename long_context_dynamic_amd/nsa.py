@@ -24,7 +24,9 @@ STATUS = {0: "NSA_OK", 1: "NSA_ERR_INVALID_ARG", 2: "NSA_ERR_UNSUPPORTED", 3: "N
 EXPORTS = ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward",
            "nsa_forward_phases", "nsa_workspace_bytes", "nsa_backward", "nsa_backward_workspace_bytes",
            "nsa_backward_phases", "nsa_compress_mlp", "nsa_gate_proj", "nsa_forward_train",
-           "nsa_train_saved_bytes", "nsa_status_str")
+           "nsa_train_saved_bytes", "nsa_status_str", "nsa_forward_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # NSA_NOALLOC_SCRATCH_BYTES
 
 
 class NsaError(RuntimeError):
@@ -68,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.nsa_select_topk.argtypes = [vp, vp, vp, vp, P]
         L.nsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, vp, P]
         L.nsa_forward.argtypes = [vp, vp, vp, vp, P, vp]
+        L.nsa_forward_noalloc.argtypes = [vp, vp, vp, vp, P, vp]
         L.nsa_workspace_bytes.argtypes = [P]
         L.nsa_workspace_bytes.restype = ctypes.c_size_t
         L.nsa_forward_phases.argtypes = [P, ctypes.POINTER(ctypes.c_char_p), ctypes.c_int32]
@@ -84,7 +87,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_gate_proj.argtypes = [vp, ctypes.c_int32, vp, vp, vp, P]
         L.nsa_status_str.argtypes = [ctypes.c_int]
         L.nsa_status_str.restype = ctypes.c_char_p
-        for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_backward",
+        for name in ("nsa_compress", "nsa_select_topk", "nsa_sparse_attn", "nsa_forward", "nsa_forward_noalloc",
+                     "nsa_backward",
                      "nsa_compress_mlp", "nsa_gate_proj", "nsa_forward_train"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -272,6 +276,25 @@ def forward(prob: dict, q, k, v, gates, out=None, k_cmp=None, v_cmp=None, out_f3
         handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         p.phase_events, p.n_phase_events = handles, len(events)
     _call("nsa_forward", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), ctypes.byref(p),
+          out.data_ptr())
+    return out
+
+
+@_on_stream
+def forward_noalloc(prob: dict, q, k, v, gates, out, k_cmp=None, v_cmp=None, out_f32=False, stream=None):
+    """nsa_forward_noalloc: the forward in the library's fixed device scratch
+    (no workspace); out must be given (nothing is allocated here either)."""
+    s, dt = _shapes(prob), torch_dtype(prob)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, s[name], dt, name)
+    if gates is not None:
+        _check(gates, s["gates"], dt, "gates")
+    if k_cmp is not None:
+        _check(k_cmp, s["kc"], dt, "k_cmp")
+        _check(v_cmp, s["vc"], dt, "v_cmp")
+    _check(out, s["out"], torch.float32 if out_f32 else dt, "out")
+    p = params(prob, out_f32=out_f32, k_cmp=k_cmp, v_cmp=v_cmp, stream=stream)
+    _call("nsa_forward_noalloc", q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(gates), ctypes.byref(p),
           out.data_ptr())
     return out
 

@@ -211,3 +211,24 @@ def test_training_forward_validation():
     B, T, H, dv = BASE["batch"], BASE["q_len"], BASE["n_groups"] * BASE["heads_per_group"], BASE["d_v"]
     lse_bytes = (3 * B * T * H * 4 + 255) // 256 * 256
     assert nsa.train_saved_bytes(BASE) == lse_bytes + 3 * B * T * H * dv * 2
+
+
+def test_noalloc_forward_validates_like_forward_and_refuses_beyond_its_scratch():
+    # the allocation-free forward checks its arguments as nsa_forward does and
+    # refuses a call whose workspace exceeds its fixed scratch, both before
+    # anything touches a device
+    lib = nsa.lib()
+    p = _p(BASE)
+    p.batch = 0
+    assert lib.nsa_forward_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE) == 1
+    big = workloads.get("nsa_prefill_8k")
+    p = _p(big)
+    assert lib.nsa_workspace_bytes(ctypes.byref(p)) > nsa.NOALLOC_SCRATCH_BYTES
+    p.workspace, p.workspace_bytes = FAKE, 1 << 40  # ignored by this call
+    assert lib.nsa_forward_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE) == 3
+
+
+def test_binding_knows_the_noalloc_scratch_size():
+    text = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    m = re.search(r"#define NSA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == nsa.NOALLOC_SCRATCH_BYTES
