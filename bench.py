@@ -146,6 +146,25 @@ def load_traffic(kernel, workload):
     return int(round(rec["traffic_bytes_per_launch"]))
 
 
+def load_counters(kernel, workload):
+    """The committed counter summary of this kernel and workload (matrix-op
+    utilisation and FLOP, VALU busy, waits; mean per dispatch), or None when
+    there is none or the kernel's sources changed since it was taken."""
+    from long_context_dynamic_amd import pmc
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != pmc.source_hash(kernel):
+        log(f"{path}: kernel sources changed since the counters were taken; counters not reported")
+        return None
+    out = {k: round(v, 4) for k, v in rec["counters"].items()}
+    if "executed_over_algorithmic" in rec:
+        out["mfma_flop_executed_over_algorithmic"] = round(rec["executed_over_algorithmic"], 4)
+    return out
+
+
 def roofline(kernel_flops, per_phase, workload):
     dominant = max((k for k in per_phase if k in kernel_flops), key=lambda k: per_phase[k])
     ms = per_phase[dominant]
@@ -153,7 +172,10 @@ def roofline(kernel_flops, per_phase, workload):
     return {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": load_traffic(dominant, workload), "traffic_unit": "HBM bytes per launch",
-            "algorithmic_flop_per_launch": kernel_flops[dominant], "kernel_ms": round(ms, 4)}
+            "algorithmic_flop_per_launch": kernel_flops[dominant], "kernel_ms": round(ms, 4),
+            "counters": load_counters(dominant, workload),
+            "other_kernels_counters": {k: c for k in kernel_flops if k != dominant
+                                       for c in [load_counters(k, workload)] if c is not None}}
 
 
 def prefill_roofline(prob, per_phase, workload):
@@ -464,8 +486,10 @@ def run_cpu_baseline(prob, x, target_s=15.0):
 def run_ceilings(torch):
     """Reference rates measured on this chip: a 1 GiB device copy, and random
     whole 40 KiB block gathers (the selected branch's access pattern: K and V
-    of 64 keys at d 192 / 128) from tables of 160 MiB (fits the 256 MB last-
-    level cache) and 1.25 GiB (does not)."""
+    of 64 keys at d 192 / 128) with ordinary loads from tables of 2.5 MiB
+    (fits each XCD's 4 MB L2), 10 MiB, 40 MiB (one group's K and V at 64k),
+    160 MiB (fits the 256 MB last-level cache) and 1.25 GiB (does not), and
+    with non-temporal loads from 1.25 GiB."""
     import ctypes
     from long_context_dynamic_amd import build as nsa_build
     if not os.path.exists(nsa_build.PROBE_LIB):
@@ -473,7 +497,7 @@ def run_ceilings(torch):
     probe = ctypes.CDLL(nsa_build.PROBE_LIB)
     probe.nsa_probe_gather.restype = ctypes.c_int
     probe.nsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
-                                       ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     res = {}
     a = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -490,10 +514,11 @@ def run_ceilings(torch):
     waves, per_wave = 262144, 4
     out = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
     gen = torch.Generator().manual_seed(0)
-    for nblk, label in ((4096, "160MiB"), (32768, "1280MiB")):
+    for nblk, label, nt in ((64, "2.5MiB", 0), (256, "10MiB", 0), (1024, "40MiB", 0), (4096, "160MiB", 0),
+                            (32768, "1280MiB", 0), (32768, "1280MiB_nontemporal", 1)):
         table = torch.ones(nblk * 40960 // 4, dtype=torch.int32, device="cuda")
         pick = torch.randint(0, nblk, (2 ** 20,), generator=gen, dtype=torch.int32).cuda()
-        args = (table.data_ptr(), pick.data_ptr(), pick.numel(), out.data_ptr(), waves, per_wave, stream)
+        args = (table.data_ptr(), pick.data_ptr(), pick.numel(), out.data_ptr(), waves, per_wave, nt, stream)
         if probe.nsa_probe_gather(*args) != 0:
             raise RuntimeError("gather probe launch failed")
         e0.record()

@@ -8,6 +8,13 @@ KiB per dispatch), each scaled by what the same counter reads for a plain
         --workload nsa_prefill_64k --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --command "..." --out profiles/selected_nsa_prefill_64k_traffic.json
 
+Counters of one kernel (matrix-op utilisation and FLOP, VALU busy, ...)
+from one or more --pmc runs, mean per dispatch:
+
+    python -m long_context_dynamic_amd.pmc counters --kernel k_sel --name selected \\
+        --workload nsa_prefill_64k --runs DIR [DIR ...] --algorithmic-flop 2.644e12 \\
+        --command "..." --out profiles/selected_nsa_prefill_64k_counters.json
+
 Per-kernel durations from a --kernel-trace run (CSV or rocpd database):
 
     python -m long_context_dynamic_amd.pmc trace DIR
@@ -110,6 +117,40 @@ def traffic(args) -> dict:
     }
 
 
+def all_counter_means(run_dir: str) -> dict:
+    """{short kernel name: {counter: mean value per dispatch}} of one --pmc run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    acc = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                k = _short(row["Kernel_Name"])
+                s = acc.setdefault(k, {}).setdefault(row["Counter_Name"], [0.0, 0])
+                s[0] += float(row["Counter_Value"])
+                s[1] += 1
+    return {k: {c: v[0] / v[1] for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def counters(args) -> dict:
+    """One kernel's counters from one or more --pmc runs (mean per dispatch),
+    with the algorithmic FLOP per launch and what the matrix-op count says."""
+    vals = {}
+    for d in args.runs:
+        means = all_counter_means(d)
+        hits = [k for k in means if args.kernel in k]
+        if len(hits) != 1:
+            raise KeyError(f"{len(hits)} kernels match {args.kernel!r} in {d}: {sorted(means)}")
+        vals.update(means[hits[0]])
+    rec = {"kernel": args.name, "kernel_symbol": args.kernel, "workload": args.workload, "counters": vals,
+           "source_hash": source_hash(args.name), "command": args.command}
+    if "MfmaFlopsBF16" in vals and args.algorithmic_flop:
+        rec["algorithmic_flop_per_launch"] = args.algorithmic_flop
+        rec["executed_over_algorithmic"] = vals["MfmaFlopsBF16"] / args.algorithmic_flop
+    return rec
+
+
 def trace_stats(run_dir: str) -> list:
     """[(short name, calls, mean us)] from a --kernel-trace run, longest total first."""
     rows = []
@@ -142,11 +183,19 @@ def main(argv=None):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--command", default="")
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--kernel", required=True, help="substring of the kernel symbol")
+    c.add_argument("--name", required=True, choices=sorted(KERNEL_SOURCES))
+    c.add_argument("--workload", required=True)
+    c.add_argument("--runs", nargs="+", required=True, help="--pmc output directories")
+    c.add_argument("--algorithmic-flop", type=float, default=0.0)
+    c.add_argument("--command", default="")
+    c.add_argument("--out", required=True)
     s = sub.add_parser("trace")
     s.add_argument("dir")
     args = ap.parse_args(argv)
-    if args.cmd == "traffic":
-        rec = traffic(args)
+    if args.cmd in ("traffic", "counters"):
+        rec = traffic(args) if args.cmd == "traffic" else counters(args)
         with open(args.out, "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec, indent=1))

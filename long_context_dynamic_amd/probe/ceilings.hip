@@ -13,6 +13,8 @@ constexpr int kBlockChunks = 2560;  // 40 KiB in 16-byte chunks
 
 // One wave per work item: per_wave blocks table[pick[...]], each read once as
 // 40 chunks of 1 KiB (20 loads in flight per lane), folded into one word.
+// NT: non-temporal loads (kept out of the caches where possible).
+template <bool NT>
 __global__ void __launch_bounds__(256) k_gather(const u32x4* __restrict__ table, const int* __restrict__ pick,
                                                 int npick, unsigned* __restrict__ out, int64_t waves, int per_wave) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -26,7 +28,7 @@ __global__ void __launch_bounds__(256) k_gather(const u32x4* __restrict__ table,
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int k = 0; k < 20; ++k) r[k] = __builtin_nontemporal_load(p + 1280 * h + 64 * k);
+      for (int k = 0; k < 20; ++k) r[k] = NT ? __builtin_nontemporal_load(p + 1280 * h + 64 * k) : p[1280 * h + 64 * k];
 #pragma unroll
       for (int k = 0; k < 20; ++k) acc ^= r[k];
     }
@@ -39,13 +41,17 @@ __global__ void __launch_bounds__(256) k_gather(const u32x4* __restrict__ table,
 extern "C" {
 
 // table: nblocks x 40 KiB (device); pick: npick block ids < nblocks (device);
-// out: waves x 64 words (device).  Queues one launch on stream; returns the
+// out: waves x 64 words (device); nontemporal: 1 for non-temporal loads, 0
+// for ordinary (cached) ones.  Queues one launch on stream; returns the
 // hipError_t of the launch as int.
 int nsa_probe_gather(const void* table, const int* pick, int npick, unsigned* out, int64_t waves, int per_wave,
-                     void* stream) {
+                     int nontemporal, void* stream) {
   if (!table || !pick || !out || npick < 1 || waves < 1 || per_wave < 1) return (int)hipErrorInvalidValue;
-  k_gather<<<(unsigned)((waves + 3) / 4), 256, 0, (hipStream_t)stream>>>((const u32x4*)table, pick, npick, out,
-                                                                          waves, per_wave);
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  if (nontemporal)
+    k_gather<true><<<grid, 256, 0, (hipStream_t)stream>>>((const u32x4*)table, pick, npick, out, waves, per_wave);
+  else
+    k_gather<false><<<grid, 256, 0, (hipStream_t)stream>>>((const u32x4*)table, pick, npick, out, waves, per_wave);
   return (int)hipGetLastError();
 }
 
