@@ -181,7 +181,15 @@ def roofline(kernel_flops, per_phase, workload):
 def prefill_roofline(prob, per_phase, workload):
     fl = algorithmic_flops(prob)
     kernel_flops = {"selected": fl["slc"], "cmp_select_window": fl["cmp"] + fl["win"]}
-    return roofline(kernel_flops, per_phase, workload), fl
+    roof = roofline(kernel_flops, per_phase, workload)
+    # the selected branch is two kernels: the per-stripe partials (the
+    # dominant kernel above) and their merge with the gated sum
+    if "selected_merge" in per_phase:
+        ms = per_phase["selected"] + per_phase["selected_merge"]
+        tf = fl["slc"] / (ms * 1e-3) / 1e12
+        roof["selected_branch"] = {"kernels": ["selected", "selected_merge"], "ms": round(ms, 4),
+                                   "achieved": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return roof, fl
 
 
 def run_moba(args, torch, nsa, workloads, inputs, workload="moba_32k"):

@@ -17,10 +17,13 @@
 //                summaries), group importance (second pass, each head's
 //                probabilities summed), top-k in registers with wave
 //                reductions, window branch, gated partial sum -> fp32 acc.
-//   k_sel        one wave per (token, group): the selected blocks streamed
-//                straight from global memory as contiguous 32-key chunks,
-//                16 heads x 32 keys per matrix op, fp32 online softmax;
-//                epilogue adds the gated result to acc and stores out.
+//   k_sel_part   one wave per (token, group, XCD stripe): the token's
+//                selected blocks that belong to the stripe of its XCD (block
+//                j mod 8) streamed straight from global memory as contiguous
+//                32-key chunks, 16 heads x 32 keys per matrix op, fp32 online
+//                softmax; a normalised partial output and its log-sum-exp.
+//   k_sel_merge  one wave per (token, group): log-sum-exp merge of the
+//                stripes' partials, plus the gated acc; stores out.
 #include <math.h>
 
 #include "nsa_frag.h"
@@ -109,6 +112,40 @@ __global__ void __launch_bounds__(256) k_group_major(const uint16_t* __restrict_
     u32x4 val = {0u, 0u, 0u, 0u};
     if (s0 + r < L) val = *(const u32x4*)(src + ((b * L + s0 + r) * G + g) * D + 8 * c8);
     *(u32x4*)(dst + (b * G + g) * Lp * D + kp_offset(s0 + r, 8 * c8, D)) = val;
+  }
+}
+
+// Fragment-order K image (layout in nsa_frag.h): one workgroup per (b, g,
+// 32-key chunk); each thread writes whole 16-byte pieces in output order,
+// reading the 8 dims of one key row (keys past L give zeros).
+__global__ void __launch_bounds__(256) k_frag_k(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                int64_t L, int64_t nc, int64_t G, int D) {
+  const int64_t c = blockIdx.x % nc, bg = blockIdx.x / nc;
+  const int64_t g = bg % G, b = bg / G;
+  const int npieces = (D / 32) * 2 * 64;
+  uint16_t* out = dst + (bg * nc + c) * 32 * D;
+  for (int P = threadIdx.x; P < npieces; P += 256) {
+    const int l = P & 63, t = (P >> 6) & 1, ks = P >> 7;
+    const int lr = l & 15, lg = l >> 4;
+    const int64_t key = 32 * c + 8 * (lr >> 2) + 4 * t + (lr & 3);
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < L) val = *(const u32x4*)(src + ((b * L + key) * G + g) * D + 32 * ks + 8 * lg);
+    *(u32x4*)(out + 8 * P) = val;
+  }
+}
+
+// Fragment-order V^T image from the tiled V^T [B, G, Lp / 32, D, 32]: a
+// permutation of its 16-byte pieces (one workgroup per (b, g, chunk)).
+__global__ void __launch_bounds__(256) k_frag_v(const uint16_t* __restrict__ vT, uint16_t* __restrict__ dst, int64_t nc,
+                                                int D) {
+  const int64_t c = blockIdx.x % nc, bg = blockIdx.x / nc;
+  const uint16_t* in = vT + (bg * nc + c) * 32 * D;
+  uint16_t* out = dst + (bg * nc + c) * 32 * D;
+  const int npieces = (D / 16) * 64;
+  for (int P = threadIdx.x; P < npieces; P += 256) {
+    const int l = P & 63, dt = P >> 6;
+    const int lr = l & 15, lg = l >> 4;
+    *(u32x4*)(out + 8 * P) = *(const u32x4*)(in + (16 * dt + lr) * 32 + 8 * lg);
   }
 }
 
@@ -355,104 +392,241 @@ __device__ __forceinline__ void pv_chunk(const VFrag<DV>& f, f32x4 s0, f32x4 s1,
   for (int dt = 0; dt < DV / 16; ++dt) o[dt] = mfma16(f.v[dt], pf, o[dt]);
 }
 
-template <int DQ, int DV, bool FWD, typename TO>
-__global__ void __launch_bounds__(256) k_sel(PfArgs a) {
-  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  // 4 consecutive tokens of one group per workgroup; each XCD takes a
-  // contiguous run of a group's tokens
-  const int64_t nq = (a.B * a.T + 3) / 4;
-  const int64_t j = xcd_run(a.G * nq);
-  if (j >= a.G * nq) return;
-  const int64_t g = j / nq;
-  const int64_t tg = (j % nq) * 4 + wave;  // flat (b, t)
-  if (tg >= a.B * a.T) return;
-  const int64_t b = tg / a.T, t = tg % a.T;
-  const int64_t p = a.L - a.T + t;
-  const float c = a.scale * kLog2e;
-  const int64_t h = g * 16 + lr;
-  const int64_t row = (b * a.T + t) * a.H + h;
+// The XCD (0..7) that takes selection block j of a query at position p:
+// blocks are striped over the XCDs (j mod 8), so each XCD's L2 serves one
+// eighth of a group's keys and values -- at most 5 MB for a 64k-token
+// group, which it holds, where the whole group's 40 MB it would not.
+// Block 0, chosen by every query, goes round the XCDs with the query's
+// block (and never to the XCD of the query's own block, also always
+// chosen), so no XCD gets more than its share.
+__device__ __forceinline__ int sel_stripe(int64_t j, int64_t p) {
+  return j > 0 ? (int)(j & 7) : (int)((p / 64 + 4) & 7);
+}
 
-  bf16x8 qf[DQ / 32];
-  {
-    const uint16_t* qr = a.q + row * DQ + 8 * lg;
+// Selected branch, part 1: the chosen blocks of one KV group that lie in
+// one XCD's stripe, streamed straight from global memory as 32-key chunks
+// (16 heads x 32 keys per matrix op, fp32 online softmax), one partial
+// result per (token, group, stripe): the normalised output of the 16 heads
+// (bf16) and its log-sum-exp (log2 units of the scaled logits; -inf when
+// the stripe holds none of the token's blocks).
+//   Workgroup i runs on XCD i % 8 (the dispatcher deals workgroups to the 8
+// XCDs in turn) and takes a tile of 4 * kSelTokPerWave tokens of group
+// i / (8 ntiles): every XCD sweeps the groups one after another, so its L2
+// holds one group's stripe at a time.  Each wave walks kSelTokPerWave
+// tokens (every 4th of the tile); their index rows are staged in LDS once.
+//   The stream is bound by the bytes a wave has in flight (an L2 read under
+// this load takes microseconds), so a token's chunks are read two at a time
+// (40 KiB) and computed on once they are in, two waves per SIMD, one
+// computing while the other waits; the next token's queries are read while
+// the current token is worked on.  K and V come from the fragment-order
+// images (nsa_frag.h): each read instruction fetches 1 KiB in lane order.
+// Partial layout: part_o [(row, group)][stripe][DV / 16][64 lanes][4] (each
+// store instruction writes 512 contiguous bytes), part_l [(row, group)][16
+// heads][8 stripes].
+constexpr int kSelTokPerWave = 16;
+constexpr int kSelMaxTopK = 32;
+
+template <int DQ, int DV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_sel_part(PfArgs a, bool use_slc) {
+  __shared__ int sidx[4][kSelTokPerWave * kSelMaxTopK];
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int x = (int)(blockIdx.x & 7);
+  constexpr int TILE = 4 * kSelTokPerWave;
+  const int64_t BT = a.B * a.T;
+  const int64_t nq = (BT + TILE - 1) / TILE;
+  const int64_t li = blockIdx.x >> 3;
+  if (li >= a.G * nq) return;
+  const int64_t g = li / nq;
+  const int64_t tg0 = (li % nq) * TILE + wave;  // token k of this wave: flat (b, t) = tg0 + 4k
+  if (tg0 >= BT) return;
+  const int ntok = (int)min((int64_t)kSelTokPerWave, (BT - tg0 + 3) / 4);
+  const int n = (int)a.n;
+  const float c = a.scale * kLog2e;
+  const float stale = kStaleLog2 / c;
+  auto tg_of = [&](int k) { return tg0 + 4 * (int64_t)k; };
+  auto write_lse = [&](int64_t rg, float v) {
+    if (lg == 0) a.part_l[(rg * 16 + lr) * 8 + x] = v;
+  };
+
+  // the index rows of the wave's tokens, staged in LDS
+  int* my_idx = sidx[wave];
+  for (int f = lane; f < ntok * n; f += 64) my_idx[f] = a.idx[(tg_of(f / n) * a.G + g) * n + f % n];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+  const uint32_t lofs = 16 * lane;  // fragment-order images: lane l's piece of each operand
+  const int64_t nc = a.Lp / 32;
+  // queries of token k (qf) and of token k + 1 (qn, read while token k is
+  // worked on; the last token's are read twice)
+  bf16x8 qf[DQ / 32], qn[DQ / 32];
+  auto load_q = [&](bf16x8 (&qd)[DQ / 32], int k) {
+    const uint16_t* qr = a.q + (tg_of(k) * a.H + g * 16 + lr) * DQ + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < DQ / 32; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qr + 32 * ks)));
-  }
-  const bool use_slc = !FWD || (a.flags & NSA_F_SLC);
-  // chunk list: lane c describes chunk c = (slot c / 2, half c % 2); n <= 32
-  int64_t kbv = -1;
-  {
-    const int slot = lane >> 1;
-    const int j = slot < a.n ? a.idx[((b * a.T + t) * a.G + g) * a.n + slot] : -1;
-    const int64_t kb = (int64_t)j * 64 + 32 * (lane & 1);
-    if (use_slc && j >= 0 && kb <= p) kbv = kb;
-  }
-  uint64_t pending = __ballot(kbv >= 0);
-  const int nch = __popcll(pending);
-
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[DV / 16];
+      qd[ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qr + 32 * ks)));
+  };
+  load_q(qn, 0);
+  int64_t b = tg0 / a.T, t = tg0 % a.T - 4;  // (b, t) of token k, stepped without divisions
+  for (int k = 0; k < ntok; ++k) {
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kG + (b * a.G + g) * a.Lp * DQ, (uint32_t)(a.Lp * DQ * 2));
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.vT + (b * a.G + g) * a.Lp * DV, (uint32_t)(a.Lp * DV * 2));
-  const uint32_t kofs = 16 * lg, vofs = (lr * 32 + 8 * lg) * 2;
+    for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = qn[ks];
+    t += 4;
+    while (t >= a.T) {
+      t -= a.T;
+      ++b;
+    }
+    const int64_t p = a.L - a.T + t;
+    const int64_t rg = tg_of(k) * a.G + g;
+    // lane c: key base of the token's chunk c (slot c / 2, half c % 2) in this stripe, or -1
+    const int slot = lane >> 1;
+    const int j = slot < n ? my_idx[k * n + slot] : -1;
+    const int kbl = j * 64 + 32 * (lane & 1);
+    const int kbv = (use_slc && j >= 0 && kbl <= p && sel_stripe(j, p) == x) ? kbl : -1;
+    uint64_t pend = __ballot(kbv >= 0);
+    if (!pend) {
+      write_lse(rg, -INFINITY);
+      load_q(qn, k + 1 < ntok ? k + 1 : k);
+      continue;
+    }
+    auto take = [&]() -> int {
+      if (!pend) return -1;
+      const int pos = __ffsll((unsigned long long)pend) - 1;
+      pend &= pend - 1;
+      return __builtin_amdgcn_readlane(kbv, pos);
+    };
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kF + (b * a.G + g) * nc * 32 * DQ, (uint32_t)(nc * 32 * DQ * 2));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.vF + (b * a.G + g) * nc * 32 * DV, (uint32_t)(nc * 32 * DV * 2));
+    const __amdgpu_buffer_rsrc_t kz = make_rsrc(a.kF, 0u), vz = make_rsrc(a.vF, 0u);  // zero records
 
-  // next chunk's key base, -1 once the list is exhausted (its loads then
-  // fall past the end of the buffers: zeros, no memory traffic)
-  auto next_kb = [&]() -> int64_t {
-    if (!pending) return -1;
-    const int pos = __ffsll((unsigned long long)pending) - 1;
-    pending &= pending - 1;
-    return __shfl(kbv, pos, 64);
-  };
-  // two-stage software pipeline: the next chunk's reads are in flight while
-  // this one is computed (unrolled by two: fixed registers, exact waits)
-  const float stale = kStaleLog2 / c;
-  KFrag<DQ> k0, k1;
-  VFrag<DV> v0, v1;
-  auto load = [&](KFrag<DQ>& kf, VFrag<DV>& vf, int64_t kb) {
-    load_k<DQ>(kf, kr, kofs, kb, lr);
-    load_v<DV>(vf, vr, vofs, kb);
-  };
-  auto step = [&](const KFrag<DQ>& kf, const VFrag<DV>& vf, int64_t kb) {
-    f32x4 s0, s1;
-    qk_chunk<DQ>(kf, qf, s0, s1);
-    pv_chunk<DV>(vf, s0, s1, o, m, l, c, stale, kb, p, lg);
-  };
-  if (nch > 0) {
-    int64_t c0 = next_kb(), c1;
-    load(k0, v0, c0);
-    for (int ci = 0; ci < nch; ci += 2) {
-      c1 = next_kb();
-      load(k1, v1, c1);
-      __builtin_amdgcn_sched_barrier(0);
-      step(k0, v0, c0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ci + 1 >= nch) break;
-      c0 = next_kb();
-      load(k0, v0, c0);
-      __builtin_amdgcn_sched_barrier(0);
-      step(k1, v1, c1);
-      __builtin_amdgcn_sched_barrier(0);
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[DV / 16];
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool first = true;
+    do {
+      // a batch of two chunks: both read, then both computed (the second
+      // one's reads land while the first is computed on)
+      const int kb0 = take(), kb1 = take();
+      KFrag<DQ> k0, k1;
+      VFrag<DV> v0, v1;
+      load_k_frag<DQ>(k0, kr, lofs, (uint32_t)(kb0 / 32) * 32 * DQ * 2);
+      load_v_frag<DV>(v0, vr, lofs, (uint32_t)(kb0 / 32) * 32 * DV * 2);
+      load_k_frag<DQ>(k1, kb1 >= 0 ? kr : kz, lofs, kb1 >= 0 ? (uint32_t)(kb1 / 32) * 32 * DQ * 2 : 0u);
+      load_v_frag<DV>(v1, kb1 >= 0 ? vr : vz, lofs, kb1 >= 0 ? (uint32_t)(kb1 / 32) * 32 * DV * 2 : 0u);
+      if (first) load_q(qn, k + 1 < ntok ? k + 1 : k);  // after this batch: its reads are not held up
+      first = false;
+      f32x4 s0, s1;
+      qk_chunk<DQ>(k0, qf, s0, s1);
+      pv_chunk<DV>(v0, s0, s1, o, m, l, c, stale, kb0, p, lg);
+      if (kb1 >= 0) {
+        qk_chunk<DQ>(k1, qf, s0, s1);
+        pv_chunk<DV>(v1, s0, s1, o, m, l, c, stale, kb1, p, lg);
+      }
+    } while (pend);
+
+    // every chunk holds a key <= p, so l > 0
+    const float inv_l = 1.f / l;
+    uint16_t* orow = a.part_o + (rg * 8 + x) * 16 * DV + 4 * lane;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) store4<uint16_t>(orow + 256 * dt, o[dt] * inv_l);
+    write_lse(rg, m * c + __log2f(l));
+  }
+}
+
+// Stores of 4 values that leave whole cache lines to the L2 to assemble
+// (ordinary write-back stores: non-temporal ones of 32-byte pieces would go
+// to memory as partial-line writes).
+template <typename TO> __device__ __forceinline__ void store4_wb(TO* p, f32x4 v);
+template <> __device__ __forceinline__ void store4_wb<float>(float* p, f32x4 v) { *(f32x4*)p = v; }
+template <> __device__ __forceinline__ void store4_wb<uint16_t>(uint16_t* p, f32x4 v) {
+  *(u32x2*)p = u32x2{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                     (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+}
+
+// Selected branch, part 2: the stripes' partial results of one (token,
+// group) merged by log-sum-exp (their weights are 2^(lse_x - lse), lse the
+// log-sum-exp of all of them: one softmax over the union of the chosen
+// blocks).  FWD: out = acc + gate * the selected branch (the gated sum of all
+// three branches; the training forward also keeps the branch's log-sum-exp
+// and output); else out = the selected branch and lse its natural
+// log-sum-exp.  Two waves per (token, group), each with half of the dims:
+// lane (lr, lg) takes dims 16 dt + 4 lg .. + 3 of head lr, the layout the
+// partials were written in.  Every read of the wave is issued before any is
+// used (the log-sum-exps, all 8 stripes' partials, acc), so one memory
+// latency per wave; a stripe without blocks has weight 0 and its (stale)
+// partial is discarded by a select, never multiplied.
+template <int DV, bool FWD, typename TO>
+__global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
+  constexpr int ND = DV / 32;  // 16-dim column blocks per wave
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + wave;  // (row, group, half)
+  if (wv >= 2 * a.B * a.T * a.G) return;
+  const int64_t rg = wv >> 1;
+  const int hv = (int)(wv & 1);
+  const int64_t tg = rg / a.G, g = rg % a.G;
+  const int64_t row = tg * a.H + g * 16 + lr;  // (b, t, head)
+
+  const f32x4* lp = (const f32x4*)(a.part_l + (rg * 16 + lr) * 8);
+  const f32x4 l0 = lp[0], l1 = lp[1];
+  u32x2 raw[8][ND];
+  const uint16_t* pbase = a.part_o + (rg * 8 * (DV / 16) + hv * ND) * 256 + 4 * lane;
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+      raw[x][i] = __builtin_nontemporal_load((const u32x2*)(pbase + ((int64_t)x * (DV / 16) + i) * 256));
+  f32x4 accv[ND];
+  if (FWD) {
+    const float* arow = a.acc + row * DV + 16 * hv * ND + 4 * lg;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) accv[i] = __builtin_nontemporal_load((const f32x4*)(arow + 16 * i));
+  }
+
+  const float lx[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+  float M = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) M = fmaxf(M, lx[x]);
+  float W = 0.f, w[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    w[x] = lx[x] == -INFINITY ? 0.f : fast_exp2(lx[x] - M);
+    W += w[x];
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const float wx = w[x] * inv;
+    const bool on = w[x] > 0.f;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const u32x2 u = raw[x][i];
+      const f32x4 v = {bf16_to_f32((uint16_t)u[0]), bf16_to_f32((uint16_t)(u[0] >> 16)),
+                       bf16_to_f32((uint16_t)u[1]), bf16_to_f32((uint16_t)(u[1] >> 16))};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[i][e] += on ? v[e] * wx : 0.f;
     }
   }
-
-  const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  TO* orow = (TO*)a.out + row * DV + 4 * lg;
+  const float lse_nat = W > 0.f ? (M + __log2f(W)) * 0.69314718055994531f : -INFINITY;
+  const int64_t dofs = row * DV + 16 * hv * ND + 4 * lg;
+  TO* orow = (TO*)a.out + dofs;
   if (FWD) {
-    float g1 = 0.f;
-    if (a.flags & NSA_F_SLC) g1 = gate_of(a, row, 1) * inv_l;
-    if (a.sv_lse) save_branch<DV>(a, 1, row, use_slc && l > 0.f, m * a.scale + logf(l), o, inv_l, lg);
-    const float* arow = a.acc + row * DV + 4 * lg;
+    const float g1 = (a.flags & NSA_F_SLC) ? gate_of(a, row, 1) : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt)
-      store4<TO>(orow + 16 * dt, __builtin_nontemporal_load((const f32x4*)(arow + 16 * dt)) + o[dt] * g1);
+    for (int i = 0; i < ND; ++i) store4_wb<TO>(orow + 16 * i, accv[i] + o[i] * g1);
+    if (a.sv_lse) {
+      const int64_t nrow = a.B * a.T * a.H;
+      if (lg == 0 && hv == 0) a.sv_lse[nrow + row] = lse_nat;
+      uint16_t* srow = a.sv_o + nrow * DV + dofs;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) store4_wb<uint16_t>(srow + 16 * i, o[i]);
+    }
   } else {
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) store4<TO>(orow + 16 * dt, o[dt] * inv_l);
-    if (a.lse && lg == 0) a.lse[row] = l > 0.f ? m * a.scale + logf(l) : -INFINITY;
+    for (int i = 0; i < ND; ++i) store4_wb<TO>(orow + 16 * i, o[i]);
+    if (a.lse && lg == 0 && hv == 0) a.lse[row] = lse_nat;
   }
 }
 
@@ -474,14 +648,19 @@ hipError_t launch_cmpwin_t(const PfArgs& a, bool fwd, hipStream_t s) {
 }
 
 template <int DQ, int DV>
-hipError_t launch_sel_t(const PfArgs& a, bool fwd, bool out_f32, hipStream_t s) {
-  const unsigned grid = xcd_grid(a.G * ((a.B * a.T + 3) / 4));
+hipError_t launch_sel_t(const PfArgs& a, bool fwd, bool out_f32, hipStream_t s, Phases* ph) {
+  const unsigned grid = (unsigned)(8 * a.G * ((a.B * a.T + 4 * kSelTokPerWave - 1) / (4 * kSelTokPerWave)));
+  k_sel_part<DQ, DV><<<grid, 256, 0, s>>>(a, !fwd || (a.flags & NSA_F_SLC));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ph) ph->mark();
+  const unsigned mgrid = (unsigned)((2 * a.B * a.T * a.G + 3) / 4);
   if (fwd) {
-    if (out_f32) k_sel<DQ, DV, true, float><<<grid, 256, 0, s>>>(a);
-    else k_sel<DQ, DV, true, uint16_t><<<grid, 256, 0, s>>>(a);
+    if (out_f32) k_sel_merge<DV, true, float><<<mgrid, 256, 0, s>>>(a);
+    else k_sel_merge<DV, true, uint16_t><<<mgrid, 256, 0, s>>>(a);
   } else {
-    if (out_f32) k_sel<DQ, DV, false, float><<<grid, 256, 0, s>>>(a);
-    else k_sel<DQ, DV, false, uint16_t><<<grid, 256, 0, s>>>(a);
+    if (out_f32) k_sel_merge<DV, false, float><<<mgrid, 256, 0, s>>>(a);
+    else k_sel_merge<DV, false, uint16_t><<<mgrid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -494,6 +673,25 @@ bool prefill_fast_ok(const Prob& P) {
          (P.dq == 64 || P.dq == 128 || P.dq == 192) && (P.dv == 64 || P.dv == 128) && nbp <= 64 * MAX_NB_LANE &&
          P.n <= 32;
 }
+
+hipError_t launch_frag_k(const void* k, void* kF, int64_t B, int64_t L, int64_t G, int D, hipStream_t s) {
+  const int64_t nc = (L + 63) / 64 * 2;
+  const unsigned grid = (unsigned)(B * G * nc);
+  if (grid == 0) return hipSuccess;
+  k_frag_k<<<grid, 256, 0, s>>>((const uint16_t*)k, (uint16_t*)kF, L, nc, G, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_frag_v(const void* vT, void* vF, int64_t B, int64_t L, int64_t G, int D, hipStream_t s) {
+  const int64_t nc = (L + 63) / 64 * 2;
+  const unsigned grid = (unsigned)(B * G * nc);
+  if (grid == 0) return hipSuccess;
+  k_frag_v<<<grid, 256, 0, s>>>((const uint16_t*)vT, (uint16_t*)vF, nc, D);
+  return hipGetLastError();
+}
+
+size_t sel_part_o_bytes(const Prob& P) { return (size_t)(P.B * P.T * P.G) * 8 * 16 * (size_t)P.dv * 2; }
+size_t sel_part_l_bytes(const Prob& P) { return (size_t)(P.B * P.T * P.G) * 16 * 8 * 4; }
 
 hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, int64_t G, int D, hipStream_t s) {
   const int64_t Lp = (L + 63) / 64 * 64;
@@ -523,8 +721,8 @@ hipError_t launch_cmpwin(const Prob& P, const PfArgs& a, bool fwd, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_sel(const Prob& P, const PfArgs& a, bool fwd, bool out_f32, hipStream_t s) {
-#define CALL_SEL(DQ, DV) launch_sel_t<DQ, DV>(a, fwd, out_f32, s)
+hipError_t launch_sel(const Prob& P, const PfArgs& a, bool fwd, bool out_f32, hipStream_t s, Phases* ph) {
+#define CALL_SEL(DQ, DV) launch_sel_t<DQ, DV>(a, fwd, out_f32, s, ph)
   if (P.dq == 192 && P.dv == 128) return CALL_SEL(192, 128);
   if (P.dq == 128 && P.dv == 128) return CALL_SEL(128, 128);
   if (P.dq == 64 && P.dv == 64) return CALL_SEL(64, 64);

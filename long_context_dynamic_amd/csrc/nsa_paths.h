@@ -13,10 +13,13 @@ struct Workspace {
   size_t kc = 0, vc = 0;  // block summaries, when the caller gives none
   size_t idx = 0;         // int32 [B, T, G, top_k]
   size_t ocmp = 0;        // fp32 [B, T, H, d_v] compressed-branch output
-  size_t kG = 0;          // keys per group, paired-row image [B, G, round_up(L, 64), d_qk]
+  size_t kG = 0;          // keys per group, fragment-order image [B, G, round_up(L, 64), d_qk]
+  size_t vF = 0;          // values per group, fragment-order image [B, G, round_up(L, 64), d_v]
   size_t vT = 0;          // values, tiled [B, G, round_up(L, 64) / 32, d_v, 32]
   size_t vcT = 0;         // value summaries, tiled [B, G, round_up(nb, 64) / 32, d_v, 32]
   size_t acc = 0;         // fp32 [B, T, H, d_v] gated compressed + window sum
+  size_t sel_o = 0;       // bf16 [B, T, G, 8, 16, d_v] selected branch per XCD stripe
+  size_t sel_l = 0;       // fp32 [B, T, G, 16, 8]      its log-sum-exps
   size_t zbuf = 0;        // decoding: fp32 [B*T, G, 16, round_up(nb, 64)] logits
   size_t part = 0;        // decoding, MoBA: partial attention records
   size_t counts = 0;      // MoBA: int32 [B, H, nb] entries per (b, h, block)

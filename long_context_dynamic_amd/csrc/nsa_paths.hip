@@ -89,6 +89,9 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     } else if (fast) {
       w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
       w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+      w.vF = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+      w.sel_o = take(sel_part_o_bytes(P));
+      w.sel_l = take(sel_part_l_bytes(P));
     }
     w.total = off;
     return w;
@@ -107,8 +110,11 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
   } else if (fast) {
     w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
     w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+    w.vF = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
     w.vcT = take((size_t)(P.B * P.G * P.dv * pad64(P.nb)) * 2);
     w.acc = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
+    w.sel_o = take(sel_part_o_bytes(P));
+    w.sel_l = take(sel_part_l_bytes(P));
   } else if (P.has(NSA_F_CMP)) {
     w.ocmp = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
   }
@@ -140,9 +146,11 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
   } else if (prefill_fast_ok(P)) {
     list[n++] = "transpose_vc";
     list[n++] = "transpose_v";
-    list[n++] = "group_major_k";
+    list[n++] = "fragment_v";
+    list[n++] = "fragment_k";
     list[n++] = "cmp_select_window";
     list[n++] = "selected";
+    list[n++] = "selected_merge";
   } else {
     list[n++] = "select_generic";
     list[n++] = "attend_generic";
@@ -200,18 +208,23 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
   if (prefill_fast_ok(P)) {
     PfArgs a = pf_args(S);
     uint16_t* vT = at<uint16_t>(base, ws.vT);
-    uint16_t* kG = at<uint16_t>(base, ws.kG);
+    uint16_t* vF = at<uint16_t>(base, ws.vF);
+    uint16_t* kF = at<uint16_t>(base, ws.kG);
     hipError_t e = launch_transpose(v, vT, P.B, P.L, a.Lp, P.G, (int)P.dv, s);
     if (e != hipSuccess) return e;
-    if ((e = launch_group_major(k, kG, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
+    if ((e = launch_frag_v(vT, vF, P.B, P.L, P.G, (int)P.dv, s)) != hipSuccess) return e;
+    if ((e = launch_frag_k(k, kF, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
-    a.kG = kG;
+    a.kF = kF;
     a.vT = vT;
+    a.vF = vF;
     a.idx = (int32_t*)idx;
     a.out = out;
     a.lse = lse;
-    return launch_sel(P, a, false, P.has(NSA_F_OUT_F32), s);
+    a.part_o = at<uint16_t>(base, ws.sel_o);
+    a.part_l = at<float>(base, ws.sel_l);
+    return launch_sel(P, a, false, P.has(NSA_F_OUT_F32), s, nullptr);
   }
   if (moba_attend_ok(P)) {
     MobaArgs a = moba_args(S);
@@ -268,17 +281,23 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     ph.mark();
     if ((e = launch_transpose(v, vT, P.B, P.L, a.Lp, P.G, (int)P.dv, s)) != hipSuccess) return e;
     ph.mark();
-    uint16_t* kG = at<uint16_t>(base, ws.kG);
-    if ((e = launch_group_major(k, kG, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
+    uint16_t* vF = at<uint16_t>(base, ws.vF);
+    if ((e = launch_frag_v(vT, vF, P.B, P.L, P.G, (int)P.dv, s)) != hipSuccess) return e;
+    ph.mark();
+    uint16_t* kF = at<uint16_t>(base, ws.kG);
+    if ((e = launch_frag_k(k, kF, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
     ph.mark();
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
-    a.kG = kG;
+    a.kF = kF;
     a.vT = vT;
+    a.vF = vF;
     a.kc = (const uint16_t*)kc;
     a.vcT = vcT;
     a.gates = (const uint16_t*)gates;
     a.acc = at<float>(base, ws.acc);
+    a.part_o = at<uint16_t>(base, ws.sel_o);
+    a.part_l = at<float>(base, ws.sel_l);
     a.idx = idx;
     a.out = out;
     if (saved) {
@@ -287,7 +306,7 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     }
     if ((e = launch_cmpwin(P, a, true, s)) != hipSuccess) return e;
     ph.mark();
-    if ((e = launch_sel(P, a, true, P.has(NSA_F_OUT_F32), s)) != hipSuccess) return e;
+    if ((e = launch_sel(P, a, true, P.has(NSA_F_OUT_F32), s, &ph)) != hipSuccess) return e;
     ph.mark();
     return ph.err;
   }

@@ -31,7 +31,7 @@ def _run_pair(prob, with_cmp):
 @pytest.mark.parametrize("name,big,small,with_cmp", [
     ("decode", dict(batch=64, kv_len=65536), dict(batch=5, kv_len=4096 + 17), True),
     ("decode, summaries in scratch", dict(batch=4, kv_len=20000), dict(batch=2, q_len=3, kv_len=3000), False),
-    ("prefill", dict(q_len=1500, kv_len=1600), dict(q_len=700, kv_len=700), False),
+    ("prefill", dict(q_len=300, kv_len=400), dict(q_len=120, kv_len=120), False),
 ])
 def test_noalloc_matches_forward_on_two_calls(name, big, small, with_cmp):
     base = "nsa_decode_64x64k" if name.startswith("decode") else "nsa_prefill_8k"
