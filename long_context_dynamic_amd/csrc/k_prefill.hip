@@ -35,7 +35,7 @@
 namespace nsa {
 namespace {
 
-constexpr int TQ = 8;             // tokens (waves) per k_cmpwin workgroup
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int MAX_NB_LANE = 32;   // pooled blocks per lane in the top-k: nb <= 2048
 
 __device__ __forceinline__ float gate_of(const PfArgs& a, int64_t row, int branch) {
@@ -173,49 +173,78 @@ __device__ __forceinline__ void topk_row(const float* imp, int64_t per, int64_t 
   topk_write(cnt, cj, cs, n, orow, srow);
 }
 
+// S^T of one 64-key LDS tile for the TW tokens of a wave: each K fragment
+// read from LDS feeds the matrix ops of all of them.
+template <int DQ, int TW>
+__device__ __forceinline__ void qk_tiles(const uint16_t* kt, const bf16x8 (&qf)[TW][DQ / 32], f32x4 (&s)[TW][4],
+                                         int lr, int lg) {
+  if constexpr (TW == 2) qk_tile_T2<DQ>(kt, qf, s, lr, lg);
+  else qk_tile_T<DQ>(kt, qf[0], s[0], lr, lg);
+}
+template <int DV, int TW>
+__device__ __forceinline__ void pv_tiles(const uint16_t* vt, const f32x4 (&s)[TW][4], f32x4 (&o)[TW][DV / 16],
+                                         int lr, int lg) {
+  if constexpr (TW == 2) pv_tile2<DV>(vt, s, o, lr, lg);
+  else pv_tile<DV>(vt, s[0], o[0], lr, lg);
+}
+
 // ---------------------------------------------------------------------------
-template <int DQ, int DV, bool FWD>
-__global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
+// One workgroup of 8 waves per (tile of 8 TW consecutive tokens, KV group);
+// wave w takes tokens w, w + 8, .. of the tile (TW of them), so the K and V
+// tiles staged in LDS feed 8 TW tokens and every fragment a wave reads from
+// LDS feeds TW tokens' matrix ops.  A token past the end computes on the
+// tile's last row and stores nothing.
+template <int DQ, int DV, bool FWD, int TW>
+__global__ void __launch_bounds__(512) k_cmpwin(PfArgs a) {
   constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
+  constexpr int TQW = 8 * TW;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* kt = (uint16_t*)smem_raw;                // [64][KS]
   uint16_t* vt = kt + 64 * KS;                       // [DV][VS]
-  float* imp = (float*)(vt + (FWD ? DV * VS : 0));   // [TQ][nbp]
+  float* imp = (float*)(vt + (FWD ? DV * VS : 0));   // [TQW][nbp]
 
   const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int64_t ntiles = (a.T + TQ - 1) / TQ;
+  const int64_t ntiles = (a.T + TQW - 1) / TQW;
   const int64_t g = blockIdx.x % a.G;
   const int64_t tile = ntiles - 1 - (blockIdx.x / a.G) % ntiles;  // longest rows first
   const int64_t b = blockIdx.x / (a.G * ntiles);
-  const int64_t t = tile * TQ + wave;
-  const bool active = t < a.T;
-  const int64_t t_last = (tile * TQ + TQ - 1 < a.T - 1) ? tile * TQ + TQ - 1 : a.T - 1;
-  const int64_t p = a.L - a.T + (active ? t : t_last);
-  const int64_t p_first = a.L - a.T + tile * TQ, p_last = a.L - a.T + t_last;
-  int64_t nvis = active ? (p + 1) / a.bs : 0;  // visible summaries
-  if (nvis > a.nb) nvis = a.nb;
+  const int64_t t_last = (tile * TQW + TQW - 1 < a.T - 1) ? tile * TQW + TQW - 1 : a.T - 1;
+  const int64_t p_first = a.L - a.T + tile * TQW, p_last = a.L - a.T + t_last;
   int64_t nvis_max = (p_last + 1) / a.bs;
   if (nvis_max > a.nb) nvis_max = a.nb;
   const float c = a.scale * kLog2e;
   const float stale = kStaleLog2 / c;
-  const int64_t h = g * 16 + lr;
-  const int64_t row = (b * a.T + (active ? t : t_last)) * a.H + h;
   const bool use_cmp = FWD && (a.flags & NSA_F_CMP);
   const bool use_win = FWD && (a.flags & NSA_F_WIN) && a.w > 0;
 
-  bf16x8 qf[DQ / 32];
-  {
-    const uint16_t* qr = a.q + row * DQ + 8 * lg;
+  bool active[TW];
+  int64_t t[TW], p[TW], nvis[TW], row[TW];
+  bf16x8 qf[TW][DQ / 32];
 #pragma unroll
-    for (int ks = 0; ks < DQ / 32; ++ks) qf[ks] = ld8(qr + 32 * ks);
+  for (int i = 0; i < TW; ++i) {
+    t[i] = tile * TQW + wave + 8 * i;
+    active[i] = t[i] < a.T;
+    const int64_t tt = active[i] ? t[i] : t_last;
+    p[i] = a.L - a.T + tt;
+    nvis[i] = active[i] ? (p[i] + 1) / a.bs : 0;  // visible summaries
+    if (nvis[i] > a.nb) nvis[i] = a.nb;
+    row[i] = (b * a.T + tt) * a.H + g * 16 + lr;
+    const uint16_t* qr = a.q + row[i] * DQ + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < DQ / 32; ++ks) qf[i][ks] = ld8(qr + 32 * ks);
   }
 
   // ---- pass 1: compressed branch, softmax statistics (+ its output) ----
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[DV / 16];
+  float m[TW], l[TW];
+  f32x4 o[TW][DV / 16];
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Stager<DQ, DV, TQ * 64> st;
+  for (int i = 0; i < TW; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  Stager<DQ, DV, 512> st;
   const int64_t ntile_cmp = (nvis_max + 63) / 64;
   if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, a.vcT, a.nbp, 0, b, g, a.G, use_cmp);
   for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
@@ -223,50 +252,76 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     st.store(kt, vt, use_cmp, true);
     __syncthreads();
     if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, a.vcT, a.nbp, (jt + 1) * 64, b, g, a.G, use_cmp);
-    if (jt * 64 < nvis) {
-      f32x4 s[4];
-      qk_tile_T<DQ>(kt, qf, s, lr, lg);
-      if (jt * 64 + 64 > nvis) mask_from(s, (int)(nvis - jt * 64), lg);
-      softmax_step<DV>(s, m, l, o, c, stale, use_cmp);
-      if (use_cmp) pv_tile<DV>(vt, s, o, lr, lg);
+    if (jt * 64 < nvis[TW - 1] || jt * 64 < nvis[0]) {
+      f32x4 s[TW][4];
+      qk_tiles<DQ, TW>(kt, qf, s, lr, lg);
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        if (jt * 64 < nvis[i]) {
+          if (jt * 64 + 64 > nvis[i]) mask_from(s[i], (int)(nvis[i] - jt * 64), lg);
+          softmax_step<DV>(s[i], m[i], l[i], o[i], c, stale, use_cmp);
+        } else {  // no visible key here: probabilities 0
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) s[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      if (use_cmp) pv_tiles<DV, TW>(vt, s, o, lr, lg);
     }
   }
-  const float inv_l = l > 0.f ? 1.f / l : 0.f;
-
-  f32x4 fin[DV / 16];
-  if (FWD) {
-    const float g0 = use_cmp ? gate_of(a, row, 0) * inv_l : 0.f;
+  float inv_l[TW];
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) fin[dt] = o[dt] * g0;
-    if (a.sv_lse && active) save_branch<DV>(a, 0, row, use_cmp && l > 0.f, m * a.scale + logf(l), o, inv_l, lg);
+  for (int i = 0; i < TW; ++i) inv_l[i] = l[i] > 0.f ? 1.f / l[i] : 0.f;
+
+  // the gated compressed branch goes to acc now (the window branch adds to
+  // it at the end): the registers are needed for the window's state
+  if (FWD) {
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      if (!active[i]) continue;
+      const float g0 = use_cmp ? gate_of(a, row[i], 0) * inv_l[i] : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(a.acc + row[i] * DV + 16 * dt + 4 * lg) = o[i][dt] * g0;
+      if (a.sv_lse)
+        save_branch<DV>(a, 0, row[i], use_cmp && l[i] > 0.f, m[i] * a.scale + logf(l[i]), o[i], inv_l[i], lg);
+    }
   }
 
   // ---- pass 2: importance of each visible block, summed over the heads ----
-  float mh[4], ih[4];  // per head 4*lg + r: m * c and 1 / l
+  float mh[TW][4], ih[TW][4];  // per head 4*lg + r: m * c and 1 / l
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mh[r] = __shfl(m * c, 4 * lg + r, 64);
-    ih[r] = __shfl(inv_l, 4 * lg + r, 64);
-  }
-  float* my_imp = imp + (int64_t)wave * a.nbp;
+  for (int i = 0; i < TW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mh[i][r] = __shfl(m[i] * c, 4 * lg + r, 64);
+      ih[i][r] = __shfl(inv_l[i], 4 * lg + r, 64);
+    }
   if (ntile_cmp > 0) st.load(a.kc, a.nb, 0, nullptr, 0, 0, b, g, a.G, false);
   for (int64_t jt = 0; jt < ntile_cmp; ++jt) {
     __syncthreads();
     st.store(kt, vt, false, false);
     __syncthreads();
     if (jt + 1 < ntile_cmp) st.load(a.kc, a.nb, (jt + 1) * 64, nullptr, 0, 0, b, g, a.G, false);
-    if (jt * 64 < nvis) {
+    if (jt * 64 < nvis[TW - 1] || jt * 64 < nvis[0]) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        f32x4 s[TW];
 #pragma unroll
-        for (int ks = 0; ks < DQ / 32; ++ks) s = mfma16(qf[ks], ld8(kt + (16 * nt + lr) * KS + 8 * lg + 32 * ks), s);
-        float v = 0.f;
+        for (int i = 0; i < TW; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v = fmaf(fast_exp2(fmaf(s[r], c, -mh[r])), ih[r], v);
-        v = xor_sum16_32(v);
+        for (int ks = 0; ks < DQ / 32; ++ks) {
+          const bf16x8 kf = ld8(kt + (16 * nt + lr) * KS + 8 * lg + 32 * ks);
+#pragma unroll
+          for (int i = 0; i < TW; ++i) s[i] = mfma16(qf[i][ks], kf, s[i]);
+        }
         const int64_t blk = jt * 64 + 16 * nt + lr;
-        if (lg == 0 && blk < nvis) my_imp[blk] = v;
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          float v = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v = fmaf(fast_exp2(fmaf(s[i][r], c, -mh[i][r])), ih[i][r], v);
+          v = xor_sum16_32(v);
+          if (lg == 0 && blk < nvis[i]) imp[(int64_t)(wave + 8 * i) * a.nbp + blk] = v;
+        }
       }
     }
   }
@@ -282,49 +337,77 @@ __global__ void __launch_bounds__(TQ * 64) k_cmpwin(PfArgs a) {
     st.load(a.k, a.L, kb0 * 64, a.vT, a.Lp, kb0 * 64, b, g, a.G, true);
   }
 
-  // ---- top-k of this token's row (one wave) ----
-  if (active) {
-    int32_t* orow = a.idx + ((b * a.T + t) * a.G + g) * a.n;
-    float* srow = a.score ? a.score + ((b * a.T + t) * a.G + g) * a.n : nullptr;
+  // ---- top-k of each token's row (one wave per row) ----
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    if (!active[i]) continue;
+    const float* my_imp = imp + (int64_t)(wave + 8 * i) * a.nbp;
+    int32_t* orow = a.idx + ((b * a.T + t[i]) * a.G + g) * a.n;
+    float* srow = a.score ? a.score + ((b * a.T + t[i]) * a.G + g) * a.n : nullptr;
     // 64-token selection blocks, complete ones are candidates
-    int64_t nsel = (p + 1) / 64;
+    int64_t nsel = (p[i] + 1) / 64;
     if (nsel > a.nbs) nsel = a.nbs;
-    if (a.nbs <= 1024) topk_row<16>(my_imp, a.per, nsel, p / 64, a.flags, (int)a.n, orow, srow);
-    else topk_row<MAX_NB_LANE>(my_imp, a.per, nsel, p / 64, a.flags, (int)a.n, orow, srow);
+    if (a.nbs <= 1024) topk_row<16>(my_imp, a.per, nsel, p[i] / 64, a.flags, (int)a.n, orow, srow);
+    else topk_row<MAX_NB_LANE>(my_imp, a.per, nsel, p[i] / 64, a.flags, (int)a.n, orow, srow);
   }
 
   if (!FWD) return;
 
   // ---- window branch: keys p - w < s <= p, FA-style over the tile ----
   if (use_win) {
-    float m2 = -INFINITY, l2 = 0.f;
+    float m2[TW], l2[TW];
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < TW; ++i) {
+      m2[i] = -INFINITY;
+      l2[i] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int64_t kb = kb0; kb <= kb1; ++kb) {
       __syncthreads();
       st.store(kt, vt, true, true);
       __syncthreads();
       if (kb + 1 <= kb1) st.load(a.k, a.L, (kb + 1) * 64, a.vT, a.Lp, (kb + 1) * 64, b, g, a.G, true);
-      if (active && kb * 64 <= p && kb * 64 + 63 > p - a.w) {
-        f32x4 s[4];
-        qk_tile_T<DQ>(kt, qf, s, lr, lg);
-        if (kb * 64 + 63 > p) mask_from(s, (int)(p + 1 - kb * 64), lg);
-        if (kb * 64 <= p - a.w) mask_below(s, (int)(p - a.w + 1 - kb * 64), lg);
-        softmax_step<DV>(s, m2, l2, o, c, stale, true);
-        pv_tile<DV>(vt, s, o, lr, lg);
+      bool on[TW], any = false;
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        on[i] = active[i] && kb * 64 <= p[i] && kb * 64 + 63 > p[i] - a.w;
+        any = any || on[i];
+      }
+      if (any) {
+        f32x4 s[TW][4];
+        qk_tiles<DQ, TW>(kt, qf, s, lr, lg);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          if (on[i]) {
+            if (kb * 64 + 63 > p[i]) mask_from(s[i], (int)(p[i] + 1 - kb * 64), lg);
+            if (kb * 64 <= p[i] - a.w) mask_below(s[i], (int)(p[i] - a.w + 1 - kb * 64), lg);
+            softmax_step<DV>(s[i], m2[i], l2[i], o[i], c, stale, true);
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) s[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        pv_tiles<DV, TW>(vt, s, o, lr, lg);
       }
     }
-    const float g2 = gate_of(a, row, 2) * (l2 > 0.f ? 1.f / l2 : 0.f);
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) fin[dt] += o[dt] * g2;
-    if (a.sv_lse && active) save_branch<DV>(a, 2, row, l2 > 0.f, m2 * a.scale + logf(l2), o, 1.f / l2, lg);
-  } else if (FWD && a.sv_lse && active) {
-    save_branch<DV>(a, 2, row, false, 0.f, o, 0.f, lg);
-  }
-
-  if (active) {
+    for (int i = 0; i < TW; ++i) {
+      if (!active[i]) continue;
+      const float g2 = gate_of(a, row[i], 2) * (l2[i] > 0.f ? 1.f / l2[i] : 0.f);
+      f32x4* arow = (f32x4*)(a.acc + row[i] * DV + 4 * lg);  // written by this lane above
+      f32x4 prev[DV / 16];
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(a.acc + row * DV + 16 * dt + 4 * lg) = fin[dt];
+      for (int dt = 0; dt < DV / 16; ++dt) prev[dt] = arow[4 * dt];
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) arow[4 * dt] = prev[dt] + o[i][dt] * g2;
+      if (a.sv_lse)
+        save_branch<DV>(a, 2, row[i], l2[i] > 0.f, m2[i] * a.scale + logf(l2[i]), o[i], 1.f / l2[i], lg);
+    }
+  } else if (a.sv_lse) {
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+      if (active[i]) save_branch<DV>(a, 2, row[i], false, 0.f, o[i], 0.f, lg);
   }
 }
 
@@ -630,21 +713,30 @@ __global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
   }
 }
 
+template <int DQ, int DV, int TW>
+hipError_t launch_cmpwin_tw(const PfArgs& a, bool fwd, size_t lds, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.B * a.G * ((a.T + 8 * TW - 1) / (8 * TW)));
+  if (fwd) {
+    auto kern = k_cmpwin<DQ, DV, true, TW>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    kern<<<grid, 512, lds, s>>>(a);
+  } else {
+    auto kern = k_cmpwin<DQ, DV, false, TW>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    kern<<<grid, 512, lds, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+// Two tokens per wave where the 16 rows of block importances fit the LDS
+// beside the K / V tiles, else one.
 template <int DQ, int DV>
 hipError_t launch_cmpwin_t(const PfArgs& a, bool fwd, hipStream_t s) {
   constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
-  const size_t lds = sizeof(uint16_t) * (64 * KS + (fwd ? DV * VS : 0)) + sizeof(float) * TQ * a.nbp;
-  const unsigned grid = (unsigned)(a.B * a.G * ((a.T + TQ - 1) / TQ));
-  if (fwd) {
-    auto kern = k_cmpwin<DQ, DV, true>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, TQ * 64, lds, s>>>(a);
-  } else {
-    auto kern = k_cmpwin<DQ, DV, false>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, TQ * 64, lds, s>>>(a);
-  }
-  return hipGetLastError();
+  const size_t tiles = sizeof(uint16_t) * (64 * KS + (fwd ? DV * VS : 0));
+  const size_t lds2 = tiles + sizeof(float) * 16 * a.nbp;
+  if (lds2 <= kLdsBytes) return launch_cmpwin_tw<DQ, DV, 2>(a, fwd, lds2, s);
+  return launch_cmpwin_tw<DQ, DV, 1>(a, fwd, tiles + sizeof(float) * 8 * a.nbp, s);
 }
 
 template <int DQ, int DV>
