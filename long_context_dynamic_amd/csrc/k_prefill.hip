@@ -512,15 +512,46 @@ constexpr int kSelMaxTopK = 32;
 template <int DQ, int DV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_sel_part(PfArgs a, bool use_slc) {
   __shared__ int sidx[4][kSelTokPerWave * kSelMaxTopK];
+  __shared__ __align__(16) uint16_t sblk[64 * (DQ + DV)];  // the staged block: K chunks, then V chunks
   const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int x = (int)(blockIdx.x & 7);
   constexpr int TILE = 4 * kSelTokPerWave;
   const int64_t BT = a.B * a.T;
   const int64_t nq = (BT + TILE - 1) / TILE;
   const int64_t li = blockIdx.x >> 3;
-  if (li >= a.G * nq) return;
+  if (li >= a.G * nq) return;  // the whole workgroup
   const int64_t g = li / nq;
-  const int64_t tg0 = (li % nq) * TILE + wave;  // token k of this wave: flat (b, t) = tg0 + 4k
+  const int64_t nc = a.Lp / 32;
+
+  // The block every token of the tile chooses that falls in this stripe --
+  // the query's own block (stripe j mod 8) or block 0 (stripe of the own
+  // block + 4), taken from the tile's first token -- is read once into LDS
+  // and served from there to every token that chose it (same batch row).
+  const int64_t tf = (li % nq) * TILE;
+  const int64_t bs0 = tf / a.T;
+  const int64_t cb0 = (a.L - a.T + tf % a.T) / 64;
+  int64_t stage_j = -1;
+  if (use_slc) stage_j = (cb0 > 0 && x == (int)(cb0 & 7)) ? cb0 : (x == (int)((cb0 + 4) & 7) ? 0 : -1);
+  if (stage_j >= 0) {
+    const uint16_t* ks = a.kF + ((bs0 * a.G + g) * nc + 2 * stage_j) * 32 * DQ;
+    const uint16_t* vs = a.vF + ((bs0 * a.G + g) * nc + 2 * stage_j) * 32 * DV;
+    constexpr int NK = 64 * DQ / 8, NV = 64 * DV / 8;  // 16-byte pieces
+    u32x4 r[(NK + NV + 255) / 256];
+#pragma unroll
+    for (int i = 0; i < (NK + NV + 255) / 256; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      if (c < NK) r[i] = *(const u32x4*)(ks + 8 * c);
+      else if (c < NK + NV) r[i] = *(const u32x4*)(vs + 8 * (c - NK));
+    }
+#pragma unroll
+    for (int i = 0; i < (NK + NV + 255) / 256; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      if (c < NK + NV) *(u32x4*)(sblk + 8 * c) = r[i];
+    }
+  }
+  __syncthreads();
+
+  const int64_t tg0 = tf + wave;  // token k of this wave: flat (b, t) = tg0 + 4k
   if (tg0 >= BT) return;
   const int ntok = (int)min((int64_t)kSelTokPerWave, (BT - tg0 + 3) / 4);
   const int n = (int)a.n;
@@ -538,7 +569,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
   const uint32_t lofs = 16 * lane;  // fragment-order images: lane l's piece of each operand
-  const int64_t nc = a.Lp / 32;
   // queries of token k (qf) and of token k + 1 (qn, read while token k is
   // worked on; the last token's are read twice)
   bf16x8 qf[DQ / 32], qn[DQ / 32];
@@ -565,8 +595,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int j = slot < n ? my_idx[k * n + slot] : -1;
     const int kbl = j * 64 + 32 * (lane & 1);
     const int kbv = (use_slc && j >= 0 && kbl <= p && sel_stripe(j, p) == x) ? kbl : -1;
-    uint64_t pend = __ballot(kbv >= 0);
-    if (!pend) {
+    const bool stg = kbv >= 0 && j == stage_j && b == bs0;  // served from LDS
+    uint64_t pend = __ballot(kbv >= 0 && !stg);
+    const uint64_t sm = __ballot(stg);  // lanes 2s, 2s + 1 of the staged block's slot s
+    if (!pend && !sm) {
       write_lse(rg, -INFINITY);
       load_q(qn, k + 1 < ntok ? k + 1 : k);
       continue;
@@ -586,7 +618,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool first = true;
-    do {
+    while (pend) {
       // a batch of two chunks: both read, then both computed (the second
       // one's reads land while the first is computed on)
       const int kb0 = take(), kb1 = take();
@@ -605,7 +637,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         qk_chunk<DQ>(k1, qf, s0, s1);
         pv_chunk<DV>(v1, s0, s1, o, m, l, c, stale, kb1, p, lg);
       }
-    } while (pend);
+    }
+    if (first) load_q(qn, k + 1 < ntok ? k + 1 : k);
+    // the staged block's chunks (its first one always holds a key <= p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (!(sm & (h ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull))) continue;
+      const uint16_t* kl = sblk + h * 32 * DQ + 8 * lane;
+      const uint16_t* vl = sblk + 64 * DQ + h * 32 * DV + 8 * lane;
+      KFrag<DQ> kf;
+      VFrag<DV> vf;
+#pragma unroll
+      for (int ks = 0; ks < DQ / 32; ++ks) {
+        kf.k0[ks] = *(const bf16x8*)(kl + (2 * ks) * 512);
+        kf.k1[ks] = *(const bf16x8*)(kl + (2 * ks + 1) * 512);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) vf.v[dt] = *(const bf16x8*)(vl + dt * 512);
+      f32x4 s0, s1;
+      qk_chunk<DQ>(kf, qf, s0, s1);
+      pv_chunk<DV>(vf, s0, s1, o, m, l, c, stale, stage_j * 64 + 32 * h, p, lg);
+    }
 
     // every chunk holds a key <= p, so l > 0
     const float inv_l = 1.f / l;
