@@ -12,8 +12,11 @@ namespace nsa {
 // here.  Afterwards lane k < the returned count holds the k-th chosen block
 // in cj and its score in cs (+inf for forced blocks), forced ones first, the
 // rest by falling importance.  Each round finds the largest remaining value
-// and the lowest block id holding it with two cross-lane reductions; only
-// the winning lane rescans its own candidates.
+// and the lowest block id holding it with two cross-lane reductions.  Every
+// lane keeps its best and second-best candidates in the order (importance
+// falling, block id rising); the winning lane moves its second-best up, and
+// only a lane that wins while its second-best is unknown rescans its
+// candidates (for the best one after the block it gave last).
 template <int NBL>
 __device__ __forceinline__ int topk_wave(float (&vals)[NBL], int64_t nvis, int64_t cur, uint32_t flags, int n,
                                          int& cj, float& cs) {
@@ -39,24 +42,45 @@ __device__ __forceinline__ int topk_wave(float (&vals)[NBL], int64_t nvis, int64
   cs = -INFINITY;
   if (lane == 0 && f0 >= 0) { cj = f0; cs = INFINITY; }
   if (lane == 1 && f1 >= 0) { cj = f1; cs = INFINITY; }
-  // this lane's best remaining candidate (first index wins ties)
-  float bv = -1.f;
-  int bi = 0;
+  // this lane's best and second-best candidates (strict comparisons over a
+  // rising index: of equal values the lower index ranks first)
+  float bv = -1.f, bv2 = -1.f;
+  int bi = 0, bi2 = 0;
 #pragma unroll
-  for (int i = 0; i < NBL; ++i)
-    if (vals[i] > bv) { bv = vals[i]; bi = i; }
+  for (int i = 0; i < NBL; ++i) {
+    const float v = vals[i];
+    const bool top = v > bv, second = !top && v > bv2;
+    bv2 = top ? bv : (second ? v : bv2);
+    bi2 = top ? bi : (second ? i : bi2);
+    bv = top ? v : bv;
+    bi = top ? i : bi;
+  }
+  bool known2 = true;  // bv2 / bi2 hold the lane's second-best
   for (int round = 0; round < r_take; ++round) {
     const float M = wave_allmax(bv);
     const int J = wave_allmin_u(bv == M ? lane + 64 * bi : 0x7fffffff);
     if (lane == nf + round) { cj = J; cs = M; }
-    if (lane == (J & 63)) {
+    const bool win = lane == (J & 63);
+    const bool rescan = __builtin_amdgcn_readlane((int)(win && !known2), J & 63);
+    if (rescan) {
+      // the winner's best candidate after (M, its index): the lane's
+      // candidates in order below it
+      if (win) {
+        const float lv = bv;
+        const int li = bi;
+        bv = -1.f;
+        bi = 0;
 #pragma unroll
-      for (int i = 0; i < NBL; ++i) vals[i] = i == (J >> 6) ? -1.f : vals[i];
-      bv = -1.f;
-      bi = 0;
-#pragma unroll
-      for (int i = 0; i < NBL; ++i)
-        if (vals[i] > bv) { bv = vals[i]; bi = i; }
+        for (int i = 0; i < NBL; ++i) {
+          const float v = vals[i];
+          const bool after = v < lv || (v == lv && i > li);
+          if (after && v > bv) { bv = v; bi = i; }
+        }
+      }
+    } else if (win) {
+      bv = bv2;
+      bi = bi2;
+      known2 = false;
     }
   }
   return nf + r_take;
