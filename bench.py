@@ -174,8 +174,10 @@ def roofline(kernel_flops, per_phase, workload):
             "traffic": load_traffic(dominant, workload), "traffic_unit": "HBM bytes per launch",
             "algorithmic_flop_per_launch": kernel_flops[dominant], "kernel_ms": round(ms, 4),
             "counters": load_counters(dominant, workload),
-            "other_kernels_counters": {k: c for k in kernel_flops if k != dominant
-                                       for c in [load_counters(k, workload)] if c is not None}}
+            "other_kernels_counters": {k: c for k in list(kernel_flops) + ["selected_merge"] if k != dominant
+                                       for c in [load_counters(k, workload)] if c is not None},
+            "other_kernels_traffic": {k: t for k in list(kernel_flops) + ["selected_merge"] if k != dominant
+                                      for t in [load_traffic(k, workload)] if t is not None}}
 
 
 def prefill_roofline(prob, per_phase, workload):
@@ -445,7 +447,9 @@ def run_decode(args, torch, nsa, workloads, inputs):
             "roofline": {"kernel": "whole decode step", "bound": "hbm", "achieved": round(achieved, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("dec_step", "nsa_decode_64x64k"),
-                         "algorithmic_bytes_per_step": int(byts)},
+                         "traffic_unit": "HBM bytes per launch",
+                         "algorithmic_bytes_per_step": int(byts),
+                         "counters": load_counters("dec_step", "nsa_decode_64x64k")},
             "timing": "median of per-step HIP-event times; a 512 MiB read pass between steps evicts the last-level cache"}
 
 
@@ -498,14 +502,7 @@ def run_ceilings(torch):
     (fits each XCD's 4 MB L2), 10 MiB, 40 MiB (one group's K and V at 64k),
     160 MiB (fits the 256 MB last-level cache) and 1.25 GiB (does not), and
     with non-temporal loads from 1.25 GiB."""
-    import ctypes
-    from long_context_dynamic_amd import build as nsa_build
-    if not os.path.exists(nsa_build.PROBE_LIB):
-        raise RuntimeError(f"{nsa_build.PROBE_LIB} is not built (python -m long_context_dynamic_amd.build)")
-    probe = ctypes.CDLL(nsa_build.PROBE_LIB)
-    probe.nsa_probe_gather.restype = ctypes.c_int
-    probe.nsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
-                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe = _probe_lib()
     res = {}
     a = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -539,6 +536,43 @@ def run_ceilings(torch):
     return res
 
 
+GATHER_CAL = {"blocks": 32768, "waves": 262144, "per_wave": 4}  # 1.25 GiB table: read from HBM
+
+
+def _probe_lib():
+    import ctypes
+    from long_context_dynamic_amd import build as nsa_build
+    if not os.path.exists(nsa_build.PROBE_LIB):
+        raise RuntimeError(f"{nsa_build.PROBE_LIB} is not built (python -m long_context_dynamic_amd.build)")
+    probe = ctypes.CDLL(nsa_build.PROBE_LIB)
+    probe.nsa_probe_gather.restype = ctypes.c_int
+    probe.nsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return probe
+
+
+def run_gather_calibration(torch, launches):
+    """Launches of the read-only block gather over a 1.25 GiB table (larger
+    than the last-level cache): a kernel whose HBM read bytes are known
+    (waves x blocks per wave x 40 KiB, nothing written but 256 bytes per
+    wave) and whose access pattern is the selected branch's and the decode's
+    -- whole 40 KiB blocks at random -- so its FETCH_SIZE counter calibrates
+    theirs.  Returns the bytes read per launch."""
+    probe = _probe_lib()
+    c = GATHER_CAL
+    table = torch.ones(c["blocks"] * 40960 // 4, dtype=torch.int32, device="cuda")
+    gen = torch.Generator().manual_seed(0)
+    pick = torch.randint(0, c["blocks"], (2 ** 20,), generator=gen, dtype=torch.int32).cuda()
+    out = torch.empty(c["waves"] * 64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(max(1, launches)):
+        if probe.nsa_probe_gather(table.data_ptr(), pick.data_ptr(), pick.numel(), out.data_ptr(), c["waves"],
+                                  c["per_wave"], 0, stream) != 0:
+            raise RuntimeError("gather probe launch failed")
+    torch.cuda.synchronize()
+    return c["waves"] * c["per_wave"] * 40960
+
+
 # ------------------------------------------------------- profiling legs --
 
 def run_only(args, torch, nsa, workloads, inputs):
@@ -546,6 +580,8 @@ def run_only(args, torch, nsa, workloads, inputs):
     device copy whose byte counters calibrate the others'."""
     if args.only == "ceilings":
         log(f"ceilings {run_ceilings(torch)}")
+    elif args.only == "gather":
+        log(f"gathered {run_gather_calibration(torch, args.steps)} bytes per launch")
     elif args.only == "copy":
         a = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
@@ -581,7 +617,8 @@ def main():
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip MoBA 128k/1M and the decoupled-block 64k legs")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceilings", "backward", "learned"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "gather", "ceilings", "backward", "learned"],
+                    default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()
     if args.gpus != 1:

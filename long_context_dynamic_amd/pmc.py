@@ -1,11 +1,14 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
 HBM traffic of a kernel from two counter runs (FETCH_SIZE, then WRITE_SIZE,
-KiB per dispatch), each scaled by what the same counter reads for a plain
-1 GiB device copy (whose true traffic is 1 GiB read + 1 GiB written):
+KiB per dispatch), each scaled by what the same counter reads for a kernel
+of known traffic: WRITE_SIZE by a plain 1 GiB device copy (1 GiB written),
+FETCH_SIZE by the read-only block gather of bench.py's gather leg (known
+bytes, the selected branch's and the decode's access pattern) or, without
+one, by the copy (1 GiB read):
 
-    python -m long_context_dynamic_amd.pmc traffic --kernel k_sel --name selected \\
-        --workload nsa_prefill_64k --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
+    python -m long_context_dynamic_amd.pmc traffic --kernel k_sel_part --name selected \\
+        --workload nsa_prefill_64k --fetch DIR --write DIR --gather-fetch DIR --copy-write DIR \\
         --command "..." --out profiles/selected_nsa_prefill_64k_traffic.json
 
 Counters of one kernel (matrix-op utilisation and FLOP, VALU busy, ...)
@@ -41,6 +44,8 @@ CSRC = os.path.join(PKG, "csrc")
 KERNEL_SOURCES = {
     "selected": ["k_prefill.hip", "nsa_prefill.h", "nsa_frag.h", "nsa_tile.h", "nsa_topk.h", "nsa_mfma.h",
                  "nsa_internal.h"],
+    "selected_merge": ["k_prefill.hip", "nsa_prefill.h", "nsa_frag.h", "nsa_tile.h", "nsa_topk.h", "nsa_mfma.h",
+                       "nsa_internal.h"],
     "cmp_select_window": ["k_prefill.hip", "nsa_prefill.h", "nsa_frag.h", "nsa_tile.h", "nsa_topk.h", "nsa_mfma.h",
                           "nsa_internal.h"],
     "moba_attn": ["k_moba.hip", "nsa_moba.h", "nsa_tile.h", "nsa_mfma.h", "nsa_internal.h"],
@@ -97,13 +102,26 @@ def _copy_value(means: dict) -> float:
     return max(hits)
 
 
+# the gather leg of bench.py: 262144 waves x 4 blocks x 40 KiB per launch
+GATHER_BYTES = 262144 * 4 * 40960
+
+
 def traffic(args) -> dict:
     f_k = _pick(counter_means(args.fetch, "FETCH_SIZE"), args.kernel)
     w_k = _pick(counter_means(args.write, "WRITE_SIZE"), args.kernel)
-    f_c = _copy_value(counter_means(args.copy_fetch, "FETCH_SIZE"))
     w_c = _copy_value(counter_means(args.copy_write, "WRITE_SIZE"))
-    fetch_scale = COPY_BYTES / (f_c * 1024.0)
     write_scale = COPY_BYTES / (w_c * 1024.0)
+    if args.gather_fetch:
+        f_c = _pick(counter_means(args.gather_fetch, "FETCH_SIZE"), "k_gather")
+        fetch_scale = GATHER_BYTES / (f_c * 1024.0)
+        cal = {"fetch": "read-only 40 KiB block gather over 1.25 GiB", "FETCH_SIZE_kib": f_c,
+               "fetch_bytes": GATHER_BYTES}
+    else:
+        f_c = _copy_value(counter_means(args.copy_fetch, "FETCH_SIZE"))
+        fetch_scale = COPY_BYTES / (f_c * 1024.0)
+        cal = {"fetch": "1 GiB device copy", "FETCH_SIZE_kib": f_c, "fetch_bytes": COPY_BYTES}
+    cal.update({"fetch_scale": fetch_scale, "write": "1 GiB device copy", "WRITE_SIZE_kib": w_c,
+                "write_bytes": COPY_BYTES, "write_scale": write_scale})
     fetch = f_k * 1024.0 * fetch_scale
     write = w_k * 1024.0 * write_scale
     return {
@@ -111,8 +129,7 @@ def traffic(args) -> dict:
         "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
         "traffic_bytes_per_launch": fetch + write,
         "raw_kib_per_dispatch": {"FETCH_SIZE": f_k, "WRITE_SIZE": w_k},
-        "copy_calibration": {"FETCH_SIZE_kib": f_c, "WRITE_SIZE_kib": w_c, "fetch_scale": fetch_scale,
-                             "write_scale": write_scale, "copy_bytes": COPY_BYTES},
+        "calibration": cal,
         "source_hash": source_hash(args.name), "command": args.command,
     }
 
@@ -179,8 +196,12 @@ def main(argv=None):
     t.add_argument("--kernel", required=True, help="substring of the kernel symbol")
     t.add_argument("--name", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
-    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+    for k in ("fetch", "write", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--gather-fetch", dest="gather_fetch", default=None,
+                   help="FETCH_SIZE run of bench.py --only gather (calibrates FETCH_SIZE)")
+    t.add_argument("--copy-fetch", dest="copy_fetch", default=None,
+                   help="FETCH_SIZE run of bench.py --only copy (used without --gather-fetch)")
     t.add_argument("--command", default="")
     t.add_argument("--out", required=True)
     c = sub.add_parser("counters")
