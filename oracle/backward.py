@@ -257,6 +257,74 @@ def backward(prob, q, k, v, gates, idx, dout, rounded=True):
     return dq, dk, dvv, dgates
 
 
+def _branch_magnitudes(qh, doh, K, V, gb, c):
+    """The terms of _branch_grads taken in absolute value: for every entry of
+    a gradient, the sum of |term| over the products that form it, with the
+    softmax gradient dS bounded by P (|dP| + |gamma D|).  A rounding of
+    relative size u in any factor of a term moves the entry by at most u
+    times this magnitude."""
+    P = _softmax_rows(c * qh @ K.T)
+    O = P @ V
+    D = np.sum(doh * O, axis=1)
+    dP = gb * (doh @ V.T)
+    AS = P * (np.abs(dP) + np.abs(gb * D[:, None]))
+    return (c * AS @ np.abs(K), c * AS.T @ np.abs(qh), P.T @ np.abs(gb * doh),
+            np.sum(np.abs(doh) * (P @ np.abs(V)), axis=1))
+
+
+def backward_magnitudes(prob, q, k, v, gates, idx, dout, rounded=True):
+    """Per-entry magnitudes of the gradients (the shapes of backward's):
+    each entry's sum of absolute values of the terms that backward adds up,
+    accumulated over the branches and key sets exactly as backward does.
+    Tests bound the error of a bf16-operand, fp32-accumulated gradient
+    entry by a small multiple of 2^-9 times its magnitude."""
+    B, T, L, G, hpg, bs, sb = _shapes(prob)
+    H, dqk, dv = G * hpg, prob["d_qk"], prob["d_v"]
+    nb = L // bs
+    c = _scale(prob)
+    qq, kk, vv = _widen(q, prob), _widen(k, prob), _widen(v, prob)
+    do = _widen(dout, prob).reshape(B, T, H, dv)
+    kc, vc = pooled(prob, k, v, rounded)
+    gam, dsig = _gamma(prob, gates)
+    on = _branches(prob)
+    aq = np.zeros((B, T, H, dqk))
+    ak = np.zeros((B, L, G, dqk))
+    av = np.zeros((B, L, G, dv))
+    akc = np.zeros((B, nb, G, dqk))
+    avc = np.zeros((B, nb, G, dv))
+    ag = np.zeros((B, T, H, 3))
+    for b in range(B):
+        for t in range(T):
+            for g in range(G):
+                hs = slice(g * hpg, (g + 1) * hpg)
+                sets = key_sets(prob, idx, b, t, g)
+                for br in on:
+                    s_ids = sets[br]
+                    if len(s_ids) == 0:
+                        continue
+                    K = kc[b, s_ids, g] if br == 0 else kk[b, s_ids, g]
+                    V = vc[b, s_ids, g] if br == 0 else vv[b, s_ids, g]
+                    mq, mK, mV, mg = _branch_magnitudes(qq[b, t, hs], do[b, t, hs], K, V,
+                                                        gam[b, t, hs, br][:, None], c)
+                    ag[b, t, hs, br] = mg
+                    aq[b, t, hs] += mq
+                    if br == 0:
+                        akc[b, s_ids, g] += mK
+                        avc[b, s_ids, g] += mV
+                    else:
+                        np.add.at(ak, (b, s_ids, g), mK)
+                        np.add.at(av, (b, s_ids, g), mV)
+    ak[:, :nb * bs] += np.repeat(akc, bs, axis=1) / bs
+    av[:, :nb * bs] += np.repeat(avc, bs, axis=1) / bs
+    agates = None
+    if gates is not None:
+        agates = ag * np.abs(dsig)
+        for br in range(3):
+            if br not in on:
+                agates[..., br] = 0.0
+    return aq, ak, av, agates
+
+
 def query_grads(prob, q, k, v, gates, idx, dout, rows, kc=None, vc=None):
     """dq [R, H, d_qk] and dgates [R, H, 3] (or None) of the listed flat rows
     b * T + t alone -- the query-side terms of backward(), which depend on

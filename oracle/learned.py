@@ -59,10 +59,11 @@ def mlp_rows(X, w1, b1, w2, b2):
     return y
 
 
-def compress(prob, k, v, wk, wv):
+def compress(prob, k, v, wk, wv, exact=False):
     """Learned block summaries kc [B, nb, G, d_qk], vc [B, nb, G, d_v] in the
-    storage type.  wk, wv: dicts with w1 [dh, block * d], b1 [dh] or None,
-    w2 [d, dh], b2 [d] or None (arrays in the storage type or float64)."""
+    storage type (exact: float64, before that rounding).  wk, wv: dicts with
+    w1 [dh, block * d], b1 [dh] or None, w2 [d, dh], b2 [d] or None (arrays
+    in the storage type or float64)."""
     dt = prob["dtype"]
     B, L, G, bs = prob["batch"], prob["kv_len"], prob["n_groups"], prob["block"]
     nb = L // bs
@@ -73,7 +74,7 @@ def compress(prob, k, v, wk, wv):
         blocks = xx[:, :nb * bs].reshape(B, nb, bs, G, d).transpose(0, 1, 3, 2, 4).reshape(B * nb * G, bs * d)
         W = {n: (None if w.get(n) is None else _widen(w[n], dt)) for n in ("w1", "b1", "w2", "b2")}
         y = mlp_rows(blocks, W["w1"], W["b1"], W["w2"], W["b2"]).reshape(B, nb, G, d)
-        out.append(_round_store(y, dt))
+        out.append(y if exact else _round_store(y, dt))
     return out[0], out[1]
 
 
@@ -87,3 +88,25 @@ def gate_proj(x, w, b, dtype, logits=False):
     if not logits:
         z = 1.0 / (1.0 + np.exp(-z))
     return z.reshape(*xx.shape[:-1], -1, 3)
+
+
+# ---- per-entry error bound of the gate projection (what the tests allow
+# between gate_proj and a GPU's bf16-operand, fp32-accumulated result) ----
+# Products of bf16 values are exact in fp32; a sum of n of them accumulated
+# in fp32 in any order is within n 2^-24 times the sum of the products'
+# absolute values of the exact sum (the worst case); the sigmoid's slope is
+# at most 1/4.
+
+_U32 = 2.0 ** -24
+
+
+def gate_proj_error_bound(x, w, b, dtype, logits=False):
+    """Per-entry bound (float64, gate_proj's shape, before the final rounding
+    to the storage type) on |GPU - exact|."""
+    xx, ww = _widen(x, dtype), _widen(w, dtype)
+    n = xx.shape[-1]
+    a = np.abs(xx) @ np.abs(ww).T
+    if b is not None:
+        a = a + np.abs(_widen(b, dtype))
+    bound = (n + 1) * _U32 * a * (1.0 if logits else 0.25)
+    return bound.reshape(*xx.shape[:-1], -1, 3)

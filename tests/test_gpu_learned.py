@@ -1,9 +1,16 @@
 """GPU parity of the learned block compression (nsa_compress_mlp) and the gate
 projection (nsa_gate_proj) against the fp64 oracle (oracle/learned.py), with
-seeded random-initialised weights.  Tolerance: the output bound of the
-forward (2e-2 on the fp32-accumulated value) plus half a bf16 step of the
-stored result; the compression's hidden layer is rounded to bf16 once (a
-relative 2^-9 on each hidden value, far inside the bound at these scales).
+seeded random-initialised weights.
+  Gate projection, entry by entry: the oracle's bound for bf16 operands with
+fp32 accumulation (gate_proj_error_bound: n 2^-24 times the sum of the
+absolute products, times the sigmoid's slope of at most 1/4), half a bf16
+step of the stored result and 1e-6 for the device's exponential -- about
+one bf16 step at the gates' scale.
+  Compression: the forward's output bound (2e-2 on the fp32-accumulated
+value) plus half a bf16 step of the stored result; its hidden layer is
+rounded to bf16 once, a relative 2^-9 on each hidden value whose effect on
+an output is 2^-9 times the sum of |w2| |hidden| over the hidden width, well
+inside that bound at these scales.
 """
 import numpy as np
 import pytest
@@ -12,7 +19,8 @@ from oracle import learned as LR
 from long_context_dynamic_amd import inputs, nsa, workloads
 from tests import gpu_util as U
 
-TOL = 2e-2
+TOL = 2e-2      # the compression's output bound
+EXP_TOL = 1e-6  # the device exponential in the sigmoid
 
 MLP_CASES = [
     ("8k shape T=L=1000 G2 dh192", dict(workloads.get("nsa_prefill_8k"), q_len=1000, kv_len=1000, n_groups=2), 192, True),
@@ -26,12 +34,13 @@ def _dev(a, prob):
     return None if a is None else nsa.to_device(a, prob)
 
 
-def _close(got_bits, ref_bits, prob, what):
-    got = U.widen_out(got_bits, prob) if not isinstance(got_bits, np.ndarray) else got_bits
-    ref = inputs.bf16_bits_to_f32(ref_bits).astype(np.float64) if ref_bits.dtype == np.uint16 else ref_bits
-    tol = TOL + U.half_ulp_bf16(ref)
+def _close(got, ref, bound, what):
+    """got: the device result widened to float64; ref: the exact value (before
+    any rounding); bound: the accumulation bound per entry."""
+    tol = bound + U.half_ulp_bf16(np.maximum(np.abs(ref), np.abs(got))) + EXP_TOL
     err = np.abs(got - ref)
-    print(f"[learned] {what}: max err {err.max():.3g} max |ref| {np.abs(ref).max():.3g}", flush=True)
+    print(f"[learned] {what}: max err {err.max():.3g} max |ref| {np.abs(ref).max():.3g} "
+          f"worst err/tol {(err / tol).max():.3f}", flush=True)
     assert np.all(err <= tol), what
 
 
@@ -42,12 +51,13 @@ def test_compress_mlp_matches_oracle(i):
     print(f"[case] compress_mlp {name}", flush=True)
     x = inputs.generate(prob, want=("k", "v"))
     w = inputs.learned_weights(prob, dh, seed=i, bias=bias)
-    rk, rv = LR.compress(prob, x["k"], x["v"], w["k"], w["v"])
+    rk, rv = LR.compress(prob, x["k"], x["v"], w["k"], w["v"], exact=True)
+    bk = bv = TOL
     wk = {n: _dev(a, prob) for n, a in w["k"].items()}
     wv = {n: _dev(a, prob) for n, a in w["v"].items()}
     kc, vc = nsa.compress_mlp(prob, _dev(x["k"], prob), _dev(x["v"], prob), wk, wv)
-    _close(kc, rk, prob, f"{name} k_cmp")
-    _close(vc, rv, prob, f"{name} v_cmp")
+    _close(U.widen_out(kc, prob), rk, bk, f"{name} k_cmp")
+    _close(U.widen_out(vc, prob), rv, bv, f"{name} v_cmp")
 
 
 GATE_CASES = [
@@ -65,5 +75,6 @@ def test_gate_projection_matches_oracle(i):
     print(f"[case] gate_proj {name}", flush=True)
     w = inputs.learned_weights(prob, 64, d_model=dm, seed=10 + i)
     ref = LR.gate_proj(w["x"], w["gate_w"], w["gate_b"], prob["dtype"], logits=logits)
+    bound = LR.gate_proj_error_bound(w["x"], w["gate_w"], w["gate_b"], prob["dtype"], logits=logits)
     got = nsa.gate_proj(prob, _dev(w["x"], prob), _dev(w["gate_w"], prob), _dev(w["gate_b"], prob), logits=logits)
-    _close(U.widen_out(got, prob), ref, prob, f"{name} gates")
+    _close(U.widen_out(got, prob), ref, bound, f"{name} gates")

@@ -228,3 +228,33 @@ def test_branch_lse_single_key_and_disabled_branches():
             assert abs(lse[2, 0, t, h] - want) <= 1e-12 * max(1.0, abs(want))
     assert np.all(np.isneginf(lse[0]))            # compressed branch off
     assert np.all(np.isfinite(lse[1]))            # the forced current block is never empty
+
+
+@pytest.mark.parametrize("gate_logits", [0, 1])
+def test_gradient_magnitudes_bound_the_gradients(gate_logits):
+    """|sum of terms| <= sum of |terms|: every gradient entry lies within its
+    magnitude (the basis of the element-wise GPU tolerance)."""
+    prob = _tiny(gate_logits=gate_logits)
+    q, k, v, gates, dout = _inputs64(prob, seed=7)
+    idx = _selection(prob, q, k, v)
+    grads = BW.backward(prob, q, k, v, gates, idx, dout, rounded=False)
+    mags = BW.backward_magnitudes(prob, q, k, v, gates, idx, dout, rounded=False)
+    for name, g, a in zip(("dq", "dk", "dv", "dgates"), grads, mags):
+        assert g.shape == a.shape, name
+        assert np.all(a >= 0), name
+        assert np.all(np.abs(g) <= a * (1 + 1e-12) + 1e-300), name
+
+
+def test_gradient_magnitudes_equal_the_gradients_when_no_term_cancels():
+    """With v, dout and the gates non-negative, every term of dv and of
+    dgates (softmax weights times non-negative values) is non-negative, so
+    their magnitudes are the gradients themselves; a dropped term or a wrong
+    weight in the magnitudes would show here."""
+    prob = _tiny()
+    q, k, v, gates, dout = _inputs64(prob, seed=9)
+    v, dout = np.abs(v), np.abs(dout)
+    idx = _selection(prob, q, k, v)
+    _, _, dv, dg = BW.backward(prob, q, k, v, gates, idx, dout, rounded=False)
+    _, _, av, ag = BW.backward_magnitudes(prob, q, k, v, gates, idx, dout, rounded=False)
+    np.testing.assert_allclose(av, dv, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(ag, dg, rtol=1e-12, atol=1e-300)

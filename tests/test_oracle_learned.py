@@ -103,3 +103,22 @@ def test_gate_projection_of_zero_weights_is_one_half():
     x = np.ones((1, 3, 8), dtype=np.float32)
     g = LR.gate_proj(x, np.zeros((6, 8), dtype=np.float32), None, "f32")
     assert np.all(g == 0.5)
+
+
+
+def test_gate_bound_covers_an_fp32_evaluation_and_is_tight():
+    """The gate projection's per-entry bound holds for an independent
+    bf16-operand, fp32 evaluation (numpy float32 sums) and stays under half
+    a bf16 step of the gates, so the GPU tolerance is about one bf16 step,
+    not a loose constant."""
+    from long_context_dynamic_amd import inputs, workloads
+    prob = dict(workloads.get("nsa_prefill_8k"), q_len=256, kv_len=256)
+    w = inputs.learned_weights(prob, 64, seed=2, d_model=2560)
+    f32 = lambda a: LR._widen(a, "bf16").astype(np.float32)
+    for logits in (False, True):
+        exact = LR.gate_proj(w["x"], w["gate_w"], w["gate_b"], "bf16", logits=logits)
+        bound = LR.gate_proj_error_bound(w["x"], w["gate_w"], w["gate_b"], "bf16", logits=logits)
+        z = (f32(w["x"]) @ f32(w["gate_w"]).T + f32(w["gate_b"])).astype(np.float64)
+        got = z if logits else 1.0 / (1.0 + np.exp(-z))
+        assert np.all(np.abs(got.reshape(exact.shape) - exact) <= bound)
+        assert bound.max() < 2.0 ** -9 * max(np.abs(exact).max(), 1.0)
