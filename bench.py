@@ -453,6 +453,53 @@ def run_decode(args, torch, nsa, workloads, inputs):
             "timing": "median of per-step HIP-event times; a 512 MiB read pass between steps evicts the last-level cache"}
 
 
+def run_decode_variants(args, torch, nsa, workloads):
+    """Where the decode step's time goes, from the public call alone: the
+    64 x 64k step with branches switched off by their flags, at other batch
+    sizes and cache lengths (seeded normal inputs; kernel time by HIP events,
+    the last-level cache flushed before each step).  Printed, not part of
+    the JSON line."""
+    base = workloads.get("nsa_decode_64x64k")
+    flush = torch.ones(128 * 2 ** 20, dtype=torch.int32, device="cuda")
+
+    def timed(prob, steps):
+        B, L, G, dq, dv = prob["batch"], prob["kv_len"], prob["n_groups"], prob["d_qk"], prob["d_v"]
+        H = workloads.n_heads(prob)
+        gen = torch.Generator(device="cuda").manual_seed(0)
+        q = torch.randn((B, 1, H, dq), generator=gen, device="cuda").to(torch.bfloat16)
+        k = torch.randn((B, L, G, dq), generator=gen, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, L, G, dv), generator=gen, device="cuda").to(torch.bfloat16)
+        gates = torch.rand((B, 1, H, 3), generator=gen, device="cuda").to(torch.bfloat16)
+        kc, vc = nsa.compress(prob, k, v)
+        ws = nsa.alloc_workspace(prob, have_cmp=True)
+        out = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device="cuda")
+        ts = []
+        for i in range(steps + 3):
+            flush.max()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nsa.forward(prob, q, k, v, gates, out=out, k_cmp=kc, v_cmp=vc, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        del q, k, v, kc, vc, ws, out
+        torch.cuda.empty_cache()
+        return round(float(np.median(ts)), 1)
+
+    res = {}
+    for label, kw in (("full", {}), ("no window", {"use_win": 0}), ("no selected", {"use_slc": 0}),
+                      ("compressed only", {"use_win": 0, "use_slc": 0}), ("batch 32", {"batch": 32}),
+                      ("batch 128", {"batch": 128}), ("top-4", {"top_k": 4}), ("top-8", {"top_k": 8})):
+        res[label] = timed(dict(base, **kw), args.steps)
+        log(f"decode {label}: {res[label]} us")
+    for L in (16384, 32768, 131072):
+        res[f"kv_len {L}"] = timed(dict(base, kv_len=L), args.steps)
+        res[f"kv_len {L} compressed only"] = timed(dict(base, kv_len=L, use_win=0, use_slc=0), args.steps)
+        log(f"decode kv_len {L}: {res[f'kv_len {L}']} us, compressed only {res[f'kv_len {L} compressed only']} us")
+    return res
+
+
 # -------------------------------------------------------------- cpu oracle --
 
 def cpu_model():
@@ -580,6 +627,8 @@ def run_only(args, torch, nsa, workloads, inputs):
     device copy whose byte counters calibrate the others'."""
     if args.only == "ceilings":
         log(f"ceilings {run_ceilings(torch)}")
+    elif args.only == "decode_variants":
+        log(f"decode variants (us) {run_decode_variants(args, torch, nsa, workloads)}")
     elif args.only == "gather":
         log(f"gathered {run_gather_calibration(torch, args.steps)} bytes per launch")
     elif args.only == "copy":
@@ -617,7 +666,8 @@ def main():
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip MoBA 128k/1M and the decoupled-block 64k legs")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "gather", "ceilings", "backward", "learned"],
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_variants", "copy", "gather", "ceilings",
+                                       "backward", "learned"],
                     default=None,
                     help="profiling runs: one leg only, no JSON contract line")
     args = ap.parse_args()

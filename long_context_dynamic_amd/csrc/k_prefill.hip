@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(256) k_frag_k(const uint16_t* __restrict__ src
   const int64_t c = blockIdx.x % nc, bg = blockIdx.x / nc;
   const int64_t g = bg % G, b = bg / G;
   const int npieces = (D / 32) * 2 * 64;
-  uint16_t* out = dst + (bg * nc + c) * 32 * D;
+  uint16_t* out = dst + (bg * nc + c) * frag_chunk(D);
   for (int P = threadIdx.x; P < npieces; P += 256) {
     const int l = P & 63, t = (P >> 6) & 1, ks = P >> 7;
     const int lr = l & 15, lg = l >> 4;
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) k_frag_v(const uint16_t* __restrict__ vT,
                                                 int D) {
   const int64_t c = blockIdx.x % nc, bg = blockIdx.x / nc;
   const uint16_t* in = vT + (bg * nc + c) * 32 * D;
-  uint16_t* out = dst + (bg * nc + c) * 32 * D;
+  uint16_t* out = dst + (bg * nc + c) * frag_chunk(D);
   const int npieces = (D / 16) * 64;
   for (int P = threadIdx.x; P < npieces; P += 256) {
     const int l = P & 63, dt = P >> 6;
@@ -533,15 +533,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   int64_t stage_j = -1;
   if (use_slc) stage_j = (cb0 > 0 && x == (int)(cb0 & 7)) ? cb0 : (x == (int)((cb0 + 4) & 7) ? 0 : -1);
   if (stage_j >= 0) {
-    const uint16_t* ks = a.kF + ((bs0 * a.G + g) * nc + 2 * stage_j) * 32 * DQ;
-    const uint16_t* vs = a.vF + ((bs0 * a.G + g) * nc + 2 * stage_j) * 32 * DV;
-    constexpr int NK = 64 * DQ / 8, NV = 64 * DV / 8;  // 16-byte pieces
+    const uint16_t* ks = a.kF + ((bs0 * a.G + g) * nc + 2 * stage_j) * frag_chunk(DQ);
+    const uint16_t* vs = a.vF + ((bs0 * a.G + g) * nc + 2 * stage_j) * frag_chunk(DV);
+    constexpr int NK = 64 * DQ / 8, NV = 64 * DV / 8;  // 16-byte pieces (two chunks each)
     u32x4 r[(NK + NV + 255) / 256];
 #pragma unroll
     for (int i = 0; i < (NK + NV + 255) / 256; ++i) {
       const int c = (int)threadIdx.x + 256 * i;
-      if (c < NK) r[i] = *(const u32x4*)(ks + 8 * c);
-      else if (c < NK + NV) r[i] = *(const u32x4*)(vs + 8 * (c - NK));
+      if (c < NK) r[i] = *(const u32x4*)(ks + (c / (NK / 2)) * frag_chunk(DQ) + 8 * (c % (NK / 2)));
+      else if (c < NK + NV)
+        r[i] = *(const u32x4*)(vs + ((c - NK) / (NV / 2)) * frag_chunk(DV) + 8 * ((c - NK) % (NV / 2)));
     }
 #pragma unroll
     for (int i = 0; i < (NK + NV + 255) / 256; ++i) {
@@ -595,9 +596,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int j = slot < n ? my_idx[k * n + slot] : -1;
     const int kbl = j * 64 + 32 * (lane & 1);
     const int kbv = (use_slc && j >= 0 && kbl <= p && sel_stripe(j, p) == x) ? kbl : -1;
-    const bool stg = kbv >= 0 && j == stage_j && b == bs0;  // served from LDS
-    uint64_t pend = __ballot(kbv >= 0 && !stg);
-    const uint64_t sm = __ballot(stg);  // lanes 2s, 2s + 1 of the staged block's slot s
+    // The block this stripe stages for a tile that starts at this token (its
+    // own block, or block 0 in the stripe four on) has its chunks computed
+    // after all others -- from LDS when this workgroup staged it -- so the
+    // order of the sums, and the result, does not depend on where tiles
+    // start (a batch row run alone gives bit-identical outputs).
+    const int64_t cbp = p / 64;
+    const int64_t spec = (cbp > 0 && x == (int)(cbp & 7)) ? cbp : (x == (int)((cbp + 4) & 7) ? 0 : -1);
+    const bool from_lds = spec == stage_j && b == bs0;
+    const bool last_blk = kbv >= 0 && j == spec;
+    uint64_t pend = __ballot(kbv >= 0 && !last_blk);
+    const uint64_t sm = __ballot(last_blk);  // lanes 2s, 2s + 1 of that block's slot s
     if (!pend && !sm) {
       write_lse(rg, -INFINITY);
       load_q(qn, k + 1 < ntok ? k + 1 : k);
@@ -609,8 +618,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       pend &= pend - 1;
       return __builtin_amdgcn_readlane(kbv, pos);
     };
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kF + (b * a.G + g) * nc * 32 * DQ, (uint32_t)(nc * 32 * DQ * 2));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.vF + (b * a.G + g) * nc * 32 * DV, (uint32_t)(nc * 32 * DV * 2));
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc(a.kF + (b * a.G + g) * nc * frag_chunk(DQ), (uint32_t)(nc * frag_chunk(DQ) * 2));
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc(a.vF + (b * a.G + g) * nc * frag_chunk(DV), (uint32_t)(nc * frag_chunk(DV) * 2));
     const __amdgpu_buffer_rsrc_t kz = make_rsrc(a.kF, 0u), vz = make_rsrc(a.vF, 0u);  // zero records
 
     float m = -INFINITY, l = 0.f;
@@ -624,10 +635,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int kb0 = take(), kb1 = take();
       KFrag<DQ> k0, k1;
       VFrag<DV> v0, v1;
-      load_k_frag<DQ>(k0, kr, lofs, (uint32_t)(kb0 / 32) * 32 * DQ * 2);
-      load_v_frag<DV>(v0, vr, lofs, (uint32_t)(kb0 / 32) * 32 * DV * 2);
-      load_k_frag<DQ>(k1, kb1 >= 0 ? kr : kz, lofs, kb1 >= 0 ? (uint32_t)(kb1 / 32) * 32 * DQ * 2 : 0u);
-      load_v_frag<DV>(v1, kb1 >= 0 ? vr : vz, lofs, kb1 >= 0 ? (uint32_t)(kb1 / 32) * 32 * DV * 2 : 0u);
+      load_k_frag<DQ>(k0, kr, lofs, (uint32_t)((kb0 / 32) * frag_chunk(DQ) * 2));
+      load_v_frag<DV>(v0, vr, lofs, (uint32_t)((kb0 / 32) * frag_chunk(DV) * 2));
+      load_k_frag<DQ>(k1, kb1 >= 0 ? kr : kz, lofs, kb1 >= 0 ? (uint32_t)((kb1 / 32) * frag_chunk(DQ) * 2) : 0u);
+      load_v_frag<DV>(v1, kb1 >= 0 ? vr : vz, lofs, kb1 >= 0 ? (uint32_t)((kb1 / 32) * frag_chunk(DV) * 2) : 0u);
       if (first) load_q(qn, k + 1 < ntok ? k + 1 : k);  // after this batch: its reads are not held up
       first = false;
       f32x4 s0, s1;
@@ -639,24 +650,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if (first) load_q(qn, k + 1 < ntok ? k + 1 : k);
-    // the staged block's chunks (its first one always holds a key <= p)
+    // that block's chunks last (its first one holds a key <= p)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (!(sm & (h ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull))) continue;
-      const uint16_t* kl = sblk + h * 32 * DQ + 8 * lane;
-      const uint16_t* vl = sblk + 64 * DQ + h * 32 * DV + 8 * lane;
       KFrag<DQ> kf;
       VFrag<DV> vf;
+      if (from_lds) {
+        const uint16_t* kl = sblk + h * 32 * DQ + 8 * lane;
+        const uint16_t* vl = sblk + 64 * DQ + h * 32 * DV + 8 * lane;
 #pragma unroll
-      for (int ks = 0; ks < DQ / 32; ++ks) {
-        kf.k0[ks] = *(const bf16x8*)(kl + (2 * ks) * 512);
-        kf.k1[ks] = *(const bf16x8*)(kl + (2 * ks + 1) * 512);
+        for (int ks = 0; ks < DQ / 32; ++ks) {
+          kf.k0[ks] = *(const bf16x8*)(kl + (2 * ks) * 512);
+          kf.k1[ks] = *(const bf16x8*)(kl + (2 * ks + 1) * 512);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DV / 16; ++dt) vf.v[dt] = *(const bf16x8*)(vl + dt * 512);
+      } else {
+        load_k_frag<DQ>(kf, kr, lofs, (uint32_t)((2 * spec + h) * frag_chunk(DQ) * 2));
+        load_v_frag<DV>(vf, vr, lofs, (uint32_t)((2 * spec + h) * frag_chunk(DV) * 2));
       }
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) vf.v[dt] = *(const bf16x8*)(vl + dt * 512);
       f32x4 s0, s1;
       qk_chunk<DQ>(kf, qf, s0, s1);
-      pv_chunk<DV>(vf, s0, s1, o, m, l, c, stale, stage_j * 64 + 32 * h, p, lg);
+      pv_chunk<DV>(vf, s0, s1, o, m, l, c, stale, spec * 64 + 32 * h, p, lg);
     }
 
     // every chunk holds a key <= p, so l > 0

@@ -87,6 +87,8 @@ __device__ __forceinline__ void load_v_u(VFrag<DV>& f, __amdgpu_buffer_rsrc_t vr
 //     (lr = l % 16, lg = l / 16: the interleaved key order of KFrag);
 //   vF [B, G, Lp / 32][DV / 16][64][8]: piece (dt, l) of chunk c holds
 //     V[32 c + 8 lg .. + 7][16 dt + lr] (keys along the piece).
+// Consecutive chunks are frag_chunk(D) = 32 D elements apart.
+__host__ __device__ constexpr int64_t frag_chunk(int D) { return 32 * (int64_t)D; }
 template <int DQ>
 __device__ __forceinline__ void load_k_frag(KFrag<DQ>& f, __amdgpu_buffer_rsrc_t kr, uint32_t lofs, uint32_t cofs) {
 #pragma unroll

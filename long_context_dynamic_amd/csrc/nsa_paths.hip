@@ -5,6 +5,7 @@
 
 #include <functional>
 #include "nsa_decode.h"
+#include "nsa_frag.h"
 #include "nsa_moba.h"
 #include "nsa_prefill.h"
 
@@ -14,6 +15,10 @@ namespace {
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t elem_bytes(const Prob& P) { return P.bf16() ? 2 : 4; }
 int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
+// a fragment-order image (nsa_frag.h): pad64(L) / 32 chunks per (b, g)
+size_t frag_image_bytes(const Prob& P, int64_t D) {
+  return (size_t)(P.B * P.G * (pad64(P.L) / 32) * frag_chunk((int)D)) * 2;
+}
 
 template <typename T> T* at(void* base, size_t off) { return (T*)((char*)base + off); }
 
@@ -87,9 +92,9 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     } else if (dec) {
       w.part = take(decode_part_bytes(P));
     } else if (fast) {
-      w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
+      w.kG = take(frag_image_bytes(P, P.dq));
       w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
-      w.vF = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+      w.vF = take(frag_image_bytes(P, P.dv));
       w.sel_o = take(sel_part_o_bytes(P));
       w.sel_l = take(sel_part_l_bytes(P));
     }
@@ -108,9 +113,9 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     w.zbuf = take(zbytes);
     w.part = take(decode_part_bytes(P));
   } else if (fast) {
-    w.kG = take((size_t)(P.B * P.G * pad64(P.L) * P.dq) * 2);
+    w.kG = take(frag_image_bytes(P, P.dq));
     w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
-    w.vF = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
+    w.vF = take(frag_image_bytes(P, P.dv));
     w.vcT = take((size_t)(P.B * P.G * P.dv * pad64(P.nb)) * 2);
     w.acc = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
     w.sel_o = take(sel_part_o_bytes(P));
