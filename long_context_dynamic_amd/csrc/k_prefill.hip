@@ -149,6 +149,21 @@ __global__ void __launch_bounds__(256) k_frag_v(const uint16_t* __restrict__ vT,
   }
 }
 
+// Fragment-order image of the queries: piece (ks, lane l) of row r and
+// group g holds q[r, 16 g + l % 16, 32 ks + 8 (l / 16) .. + 7], the lane
+// layout of the matrix op's query operand (one thread per 16-byte piece).
+__global__ void __launch_bounds__(256) k_frag_q(const uint16_t* __restrict__ q, uint16_t* __restrict__ qF, int64_t n,
+                                                int D) {
+  const int64_t P = (int64_t)blockIdx.x * 256 + threadIdx.x;  // piece: (row, group, ks, lane)
+  if (P >= n) return;
+  const int l = (int)(P & 63);
+  const int64_t rest = P >> 6;
+  const int nks = D / 32;
+  const int ks = (int)(rest % nks);
+  const int64_t rg = rest / nks;  // row * G + g: the 16 heads of (row, g) are rows 16 rg .. of q
+  *(u32x4*)(qF + 8 * P) = *(const u32x4*)(q + (16 * rg + (l & 15)) * D + 32 * ks + 8 * (l >> 4));
+}
+
 // Top-k of one token's selection blocks (one wave): block J < nsel has the
 // importance imp[per * J] + .. + imp[per * J + per - 1] (its summaries);
 // written sorted to orow / srow.
@@ -232,6 +247,13 @@ __global__ void __launch_bounds__(512) k_cmpwin(PfArgs a) {
     const uint16_t* qr = a.q + row[i] * DQ + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < DQ / 32; ++ks) qf[i][ks] = ld8(qr + 32 * ks);
+    // the selected branch reads the queries in this lane order (1 KiB per
+    // operand in lane order, coalesced) from the fragment-order image
+    if (FWD && a.qF && active[i]) {
+      uint16_t* qo = a.qF + ((b * a.T + t[i]) * a.G + g) * 16 * DQ + 8 * lane;
+#pragma unroll
+      for (int ks = 0; ks < DQ / 32; ++ks) *(bf16x8*)(qo + 512 * ks) = qf[i][ks];
+    }
   }
 
   // ---- pass 1: compressed branch, softmax statistics (+ its output) ----
@@ -573,11 +595,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // queries of token k (qf) and of token k + 1 (qn, read while token k is
   // worked on; the last token's are read twice)
   bf16x8 qf[DQ / 32], qn[DQ / 32];
-  auto load_q = [&](bf16x8 (&qd)[DQ / 32], int k) {
-    const uint16_t* qr = a.q + (tg_of(k) * a.H + g * 16 + lr) * DQ + 8 * lg;
+  auto load_q = [&](bf16x8 (&qd)[DQ / 32], int k) {  // from the fragment-order image: 1 KiB per load
+    const uint16_t* qr = a.qF + (tg_of(k) * a.G + g) * 16 * DQ + 8 * lane;
 #pragma unroll
     for (int ks = 0; ks < DQ / 32; ++ks)
-      qd[ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qr + 32 * ks)));
+      qd[ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qr + 512 * ks)));
   };
   load_q(qn, 0);
   int64_t b = tg0 / a.T, t = tg0 % a.T - 4;  // (b, t) of token k, stepped without divisions
@@ -839,6 +861,13 @@ hipError_t launch_frag_k(const void* k, void* kF, int64_t B, int64_t L, int64_t 
   const unsigned grid = (unsigned)(B * G * nc);
   if (grid == 0) return hipSuccess;
   k_frag_k<<<grid, 256, 0, s>>>((const uint16_t*)k, (uint16_t*)kF, L, nc, G, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_frag_q(const void* q, void* qF, int64_t R, int64_t G, int D, hipStream_t s) {
+  const int64_t n = R * G * (D / 32) * 64;  // 16-byte pieces
+  if (n == 0) return hipSuccess;
+  k_frag_q<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)q, (uint16_t*)qF, n, D);
   return hipGetLastError();
 }
 

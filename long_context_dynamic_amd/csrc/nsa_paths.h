@@ -15,6 +15,7 @@ struct Workspace {
   size_t ocmp = 0;        // fp32 [B, T, H, d_v] compressed-branch output
   size_t kG = 0;          // keys per group, fragment-order image [B, G, round_up(L, 64), d_qk]
   size_t vF = 0;          // values per group, fragment-order image [B, G, round_up(L, 64), d_v]
+  size_t qF = 0;          // queries, fragment-order image [B, T, G, d_qk / 32, 64, 8]
   size_t vT = 0;          // values, tiled [B, G, round_up(L, 64) / 32, d_v, 32]
   size_t vcT = 0;         // value summaries, tiled [B, G, round_up(nb, 64) / 32, d_v, 32]
   size_t acc = 0;         // fp32 [B, T, H, d_v] gated compressed + window sum

@@ -95,6 +95,7 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
       w.kG = take(frag_image_bytes(P, P.dq));
       w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
       w.vF = take(frag_image_bytes(P, P.dv));
+      w.qF = take((size_t)(P.B * P.T * P.H * P.dq) * 2);
       w.sel_o = take(sel_part_o_bytes(P));
       w.sel_l = take(sel_part_l_bytes(P));
     }
@@ -116,6 +117,7 @@ Workspace plan_workspace(const Prob& P, Call call, bool have_cmp) {
     w.kG = take(frag_image_bytes(P, P.dq));
     w.vT = take((size_t)(P.B * P.G * P.dv * pad64(P.L)) * 2);
     w.vF = take(frag_image_bytes(P, P.dv));
+    w.qF = take((size_t)(P.B * P.T * P.H * P.dq) * 2);
     w.vcT = take((size_t)(P.B * P.G * P.dv * pad64(P.nb)) * 2);
     w.acc = take((size_t)(P.B * P.T * P.H * P.dv) * sizeof(float));
     w.sel_o = take(sel_part_o_bytes(P));
@@ -219,6 +221,8 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
     if (e != hipSuccess) return e;
     if ((e = launch_frag_v(vT, vF, P.B, P.L, P.G, (int)P.dv, s)) != hipSuccess) return e;
     if ((e = launch_frag_k(k, kF, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
+    a.qF = at<uint16_t>(base, ws.qF);
+    if ((e = launch_frag_q(q, a.qF, P.B * P.T, P.G, (int)P.dq, s)) != hipSuccess) return e;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.kF = kF;
@@ -293,6 +297,7 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
     if ((e = launch_frag_k(k, kF, P.B, P.L, P.G, (int)P.dq, s)) != hipSuccess) return e;
     ph.mark();
     a.q = (const uint16_t*)q;
+    a.qF = at<uint16_t>(base, ws.qF);  // written by the compressed/window kernel
     a.k = (const uint16_t*)k;
     a.kF = kF;
     a.vT = vT;

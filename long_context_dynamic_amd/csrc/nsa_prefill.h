@@ -9,6 +9,8 @@ namespace nsa {
 
 struct PfArgs {
   const uint16_t* q;      // [B, T, H, DQ]
+  uint16_t* qF;           // [B, T, G, DQ / 32, 64, 8] queries in fragment order (nsa_frag.h); the
+                          // compressed/window kernel writes it, the selected branch reads it
   const uint16_t* k;      // [B, L, G, DQ]
   const uint16_t* kF;     // [B, G, Lp / 32, DQ / 32, 2, 64, 8] keys in fragment order (nsa_frag.h)
   const uint16_t* vT;     // [B, G, Lp / 32, DV, 32]  values, tiled and key-contiguous
@@ -40,6 +42,8 @@ hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, 
 // Fragment-order images of K (from K [B, L, G, D]) and of V (from the tiled
 // V^T), Lp = round_up(L, 64) keys each.
 hipError_t launch_frag_k(const void* k, void* kF, int64_t B, int64_t L, int64_t G, int D, hipStream_t s);
+// Fragment-order image of the queries (q [R, G * 16, D] -> [R, G, D / 32, 64, 8]).
+hipError_t launch_frag_q(const void* q, void* qF, int64_t R, int64_t G, int D, hipStream_t s);
 hipError_t launch_frag_v(const void* vT, void* vF, int64_t B, int64_t L, int64_t G, int D, hipStream_t s);
 hipError_t launch_transpose(const void* src, void* dst, int64_t B, int64_t N, int64_t Np, int64_t G, int D,
                             hipStream_t s);
