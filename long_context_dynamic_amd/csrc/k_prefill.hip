@@ -44,6 +44,15 @@ __device__ __forceinline__ float gate_of(const PfArgs& a, int64_t row, int branc
   return (a.flags & NSA_F_GATE_LOGITS) ? sigmoid(x) : x;
 }
 
+// The gated compressed + window partial sum of (row = b T + t, group g) in
+// fragment order: 16-dim block dt of the 16 heads is 1 KiB, lane (lr, lg)'s
+// 4 floats (dims 16 dt + 4 lg .. + 3 of head lr, the matrix op's output
+// layout) at float offset 4 lane, so its writes and the merge's reads are
+// 1 KiB contiguous per instruction.
+__device__ __forceinline__ float* acc_frag(const PfArgs& a, int64_t row, int64_t g, int dt, int DV) {
+  return a.acc + ((row * a.G + g) * (DV / 16) + dt) * 256;
+}
+
 // Training forward: branch br's natural log-sum-exp of the scaled logits
 // (-inf when the branch is off or its key set empty) and its normalised
 // output in bf16, for head lr of the row; o^T holds dims 16*dt + 4*lg + r.
@@ -302,7 +311,7 @@ __global__ void __launch_bounds__(512) k_cmpwin(PfArgs a) {
       if (!active[i]) continue;
       const float g0 = use_cmp ? gate_of(a, row[i], 0) * inv_l[i] : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(a.acc + row[i] * DV + 16 * dt + 4 * lg) = o[i][dt] * g0;
+      for (int dt = 0; dt < DV / 16; ++dt) *(f32x4*)(acc_frag(a, b * a.T + t[i], g, dt, DV) + 4 * lane) = o[i][dt] * g0;
       if (a.sv_lse)
         save_branch<DV>(a, 0, row[i], use_cmp && l[i] > 0.f, m[i] * a.scale + logf(l[i]), o[i], inv_l[i], lg);
     }
@@ -417,12 +426,12 @@ __global__ void __launch_bounds__(512) k_cmpwin(PfArgs a) {
     for (int i = 0; i < TW; ++i) {
       if (!active[i]) continue;
       const float g2 = gate_of(a, row[i], 2) * (l2[i] > 0.f ? 1.f / l2[i] : 0.f);
-      f32x4* arow = (f32x4*)(a.acc + row[i] * DV + 4 * lg);  // written by this lane above
+      f32x4* arow = (f32x4*)(acc_frag(a, b * a.T + t[i], g, 0, DV) + 4 * lane);  // written by this lane above
       f32x4 prev[DV / 16];
 #pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) prev[dt] = arow[4 * dt];
+      for (int dt = 0; dt < DV / 16; ++dt) prev[dt] = arow[64 * dt];
 #pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) arow[4 * dt] = prev[dt] + o[i][dt] * g2;
+      for (int dt = 0; dt < DV / 16; ++dt) arow[64 * dt] = prev[dt] + o[i][dt] * g2;
       if (a.sv_lse)
         save_branch<DV>(a, 2, row[i], l2[i] > 0.f, m2[i] * a.scale + logf(l2[i]), o[i], 1.f / l2[i], lg);
     }
@@ -750,9 +759,9 @@ __global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
       raw[x][i] = __builtin_nontemporal_load((const u32x2*)(pbase + ((int64_t)x * (DV / 16) + i) * 256));
   f32x4 accv[ND];
   if (FWD) {
-    const float* arow = a.acc + row * DV + 16 * hv * ND + 4 * lg;
+    const float* arow = acc_frag(a, tg, g, hv * ND, DV) + 4 * lane;
 #pragma unroll
-    for (int i = 0; i < ND; ++i) accv[i] = __builtin_nontemporal_load((const f32x4*)(arow + 16 * i));
+    for (int i = 0; i < ND; ++i) accv[i] = __builtin_nontemporal_load((const f32x4*)(arow + 256 * i));
   }
 
   const float lx[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
