@@ -11,9 +11,10 @@
 // and the compressed branch's key/value gradients reach each token of block
 // j as dk_cmp_j / 64.  The work splits by which side owns the sums:
 //
-//   images     paired-row copies of k, v and of the summaries and tiled V^T
-//              copies, so that the global matrix-op operands below are
-//              contiguous 16-byte reads.
+//   images     fragment-order copies of k, v and of the summaries (each
+//              matrix-op operand 1 KiB in lane order, nsa_frag.h) and tiled
+//              V^T copies, so that the global matrix-op operands below are
+//              contiguous reads.
 //   k_bwd_qcw  compressed and window branches from the query side: one
 //              workgroup per 8 tokens of a group, one wave per token (16
 //              heads as the matrix N), the 64-key tiles of K and V rows
@@ -217,7 +218,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
   for (int ks = 0; ks < DV / 32; ++ks) df[ks] = ld8(a.dout + row * DV + 8 * lg + 32 * ks);
 
-  const uint32_t kofs = 16 * lg, tofs = (lr * 32 + 8 * lg) * 2;
+  const uint32_t tofs = (lr * 32 + 8 * lg) * 2;
   const int64_t bg = b * a.G + g;
   auto rs = [&](const uint16_t* base, int64_t rows, int D) {
     return make_rsrc(base + bg * rows * D, (uint32_t)(rows * D * 2));
@@ -296,7 +297,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     for (int64_t kb = it.pop(); kb >= 0; kb = it.pop()) {
       KFrag<DQ> kf;
       VFrag<DV> vf;
-      load_k<DQ>(kf, kr, kofs, kb, lr);
+      load_k_frag<DQ>(kf, kr, 16 * lane, (uint32_t)(kb / 32) * 32 * DQ * 2);
       load_v<DV>(vf, vr, tofs, kb);
       f32x4 s0, s1;
       qk_chunk_b<DQ>(kf, qf, s0, s1);
@@ -359,8 +360,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     for (int64_t kb = it.pop(); kb >= 0; kb = it.pop()) {
       KFrag<DQ> kf;
       KFrag<DV> vf;
-      load_k<DQ>(kf, kr, kofs, kb, lr);
-      load_k<DV>(vf, vgr, kofs, kb, lr);
+      load_k_frag<DQ>(kf, kr, 16 * lane, (uint32_t)(kb / 32) * 32 * DQ * 2);
+      load_k_frag<DV>(vf, vgr, 16 * lane, (uint32_t)(kb / 32) * 32 * DV * 2);
       // the K fragments, back to rows (key - kb) of the wave's LDS tile, so
       // that K^T operands come out of transposing reads
       {
@@ -1217,12 +1218,12 @@ hipError_t run_backward(const Prob& P, const void* q, const void* k, const void*
   hipError_t e = launch_pool(P, k, v, kc, vc, s);
   if (e != hipSuccess) return e;
   const int64_t B = P.B, G = P.G;
-  if ((e = launch_group_major(k, (void*)a.kG, B, P.L, G, (int)P.dq, s)) != hipSuccess) return e;
-  if ((e = launch_group_major(v, (void*)a.vG, B, P.L, G, (int)P.dv, s)) != hipSuccess) return e;
+  if ((e = launch_frag_k(k, (void*)a.kG, B, P.L, G, (int)P.dq, s)) != hipSuccess) return e;
+  if ((e = launch_frag_k(v, (void*)a.vG, B, P.L, G, (int)P.dv, s)) != hipSuccess) return e;
   if ((e = launch_transpose(v, (void*)a.vT, B, P.L, a.Lp, G, (int)P.dv, s)) != hipSuccess) return e;
   if (P.nb > 0) {
-    if ((e = launch_group_major(kc, (void*)a.kcG, B, P.nb, G, (int)P.dq, s)) != hipSuccess) return e;
-    if ((e = launch_group_major(vc, (void*)a.vcG, B, P.nb, G, (int)P.dv, s)) != hipSuccess) return e;
+    if ((e = launch_frag_k(kc, (void*)a.kcG, B, P.nb, G, (int)P.dq, s)) != hipSuccess) return e;
+    if ((e = launch_frag_k(vc, (void*)a.vcG, B, P.nb, G, (int)P.dv, s)) != hipSuccess) return e;
     if ((e = launch_transpose(vc, (void*)a.vcT, B, P.nb, a.nbp, G, (int)P.dv, s)) != hipSuccess) return e;
   }
   ph.mark();

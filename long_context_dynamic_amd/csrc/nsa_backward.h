@@ -16,7 +16,7 @@ struct BwArgs {
   const uint16_t* dout;   // [B, T, H, DV]
   const uint16_t* kc;     // [B, nb, G, DQ] block summaries
   const uint16_t* vc;     // [B, nb, G, DV]
-  const uint16_t* kG;     // paired-row images [B, G, Lp, D] of k, v
+  const uint16_t* kG;     // fragment-order images [B, G, Lp / 32, D / 32, 2, 64, 8] of k, v (nsa_frag.h)
   const uint16_t* vG;
   const uint16_t* vT;     // tiled transpose [B, G, Lp / 32, DV, 32] of v
   const uint16_t* kcG;    // the same three images of the summaries (nbp rows)
