@@ -1102,37 +1102,35 @@ hipError_t launch_t(const Prob& P, BwArgs& a, hipStream_t s, Phases& ph) {
   const int64_t chunks_max = (ne + kListChunk - 1) / kListChunk + nl;  // surplus workgroups exit at once
   if (slc) {
     const size_t lds = (size_t)a.nbk * 4;
-    k_bwd_count<<<(unsigned)(P.B * P.G * a.nct), kCountTok, lds, s>>>(a);
-    k_bwd_colscan<<<(unsigned)((nl + 255) / 256), 256, 0, s>>>(a);
-    k_bwd_scan<<<1, 1024, 0, s>>>(a, nl);
-    k_bwd_fill<<<(unsigned)(P.B * P.G * a.nct), 64, lds, s>>>(a);
+    launch("k_bwd_count", k_bwd_count, (unsigned)(P.B * P.G * a.nct), kCountTok, lds, s, a);
+    launch("k_bwd_colscan", k_bwd_colscan, (unsigned)((nl + 255) / 256), 256, 0, s, a);
+    launch("k_bwd_scan", k_bwd_scan, 1, 1024, 0, s, a, nl);
+    launch("k_bwd_fill", k_bwd_fill, (unsigned)(P.B * P.G * a.nct), 64, lds, s, a);
     ph.mark();
     // with the training forward's statistics the group launches nothing
-    if (!a.sv_lse) k_bwd_kv<DQ, DV, KV_STAT, 4><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    if (!a.sv_lse) launch("k_bwd_kv<DQ, DV, KV_STAT, 4>", k_bwd_kv<DQ, DV, KV_STAT, 4>, (unsigned)chunks_max, 256, 0, s, a);
     ph.mark();
   }
   const unsigned gqcw = (unsigned)(P.B * P.G * ((P.T + kQTok - 1) / kQTok));
-  if (a.sv_lse) k_bwd_qcw<DQ, DV, true><<<gqcw, 64 * kQTok, 0, s>>>(a);
-  else k_bwd_qcw<DQ, DV, false><<<gqcw, 64 * kQTok, 0, s>>>(a);
-  if (slc) k_bwd_q<DQ, DV><<<gq, 256, 0, s>>>(a);
+  if (a.sv_lse) launch("k_bwd_qcw<DQ, DV, true>", k_bwd_qcw<DQ, DV, true>, gqcw, 64 * kQTok, 0, s, a);
+  else launch("k_bwd_qcw<DQ, DV, false>", k_bwd_qcw<DQ, DV, false>, gqcw, 64 * kQTok, 0, s, a);
+  if (slc) launch("k_bwd_q<DQ, DV>", k_bwd_q<DQ, DV>, gq, 256, 0, s, a);
   ph.mark();
   const int64_t ntile = (P.L + 63) / 64;
   if (P.has(NSA_F_WIN) && P.w > 0) {
-    k_bwd_kv<DQ, DV, KV_WIN, kKvWaves><<<(unsigned)(P.B * P.G * ((P.L + 16 * kKvWaves - 1) / (16 * kKvWaves))),
-                                          64 * kKvWaves, 0, s>>>(a);
+    launch("k_bwd_kv<DQ, DV, KV_WIN, kKvWaves>", k_bwd_kv<DQ, DV, KV_WIN, kKvWaves>, (unsigned)(P.B * P.G * ((P.L + 16 * kKvWaves - 1) / (16 * kKvWaves))), 64 * kKvWaves, 0, s, a);
     ph.mark();
   }
   if (slc) {
-    k_bwd_kv<DQ, DV, KV_SLC, 4><<<(unsigned)chunks_max, 256, 0, s>>>(a);
+    launch("k_bwd_kv<DQ, DV, KV_SLC, 4>", k_bwd_kv<DQ, DV, KV_SLC, 4>, (unsigned)chunks_max, 256, 0, s, a);
     ph.mark();
   }
   if (P.has(NSA_F_CMP) && P.nb > 0) {
-    k_bwd_kv<DQ, DV, KV_CMP, kKvWaves><<<(unsigned)(P.B * P.G * ((a.nJ + kKvWaves / 4 - 1) / (kKvWaves / 4)) * a.nC),
-                                          64 * kKvWaves, 0, s>>>(a);
-    k_bwd_cmpsum<DQ, DV><<<(unsigned)((P.B * P.G * P.nb * (DQ + DV) + 255) / 256), 256, 0, s>>>(a);
+    launch("k_bwd_kv<DQ, DV, KV_CMP, kKvWaves>", k_bwd_kv<DQ, DV, KV_CMP, kKvWaves>, (unsigned)(P.B * P.G * ((a.nJ + kKvWaves / 4 - 1) / (kKvWaves / 4)) * a.nC), 64 * kKvWaves, 0, s, a);
+    launch("k_bwd_cmpsum<DQ, DV>", k_bwd_cmpsum<DQ, DV>, (unsigned)((P.B * P.G * P.nb * (DQ + DV) + 255) / 256), 256, 0, s, a);
     ph.mark();
   }
-  k_bwd_reduce<DQ, DV><<<(unsigned)(P.B * P.G * ntile * kReduceSlices), 256, 0, s>>>(a);
+  launch("k_bwd_reduce<DQ, DV>", k_bwd_reduce<DQ, DV>, (unsigned)(P.B * P.G * ntile * kReduceSlices), 256, 0, s, a);
   ph.mark();
   return ph.err != hipSuccess ? ph.err : hipGetLastError();
 }

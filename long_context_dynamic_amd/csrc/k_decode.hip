@@ -524,12 +524,12 @@ hipError_t launch_fused(const DecArgs& a, hipStream_t s) {
     const size_t zbytes = (size_t)16 * (a.nbp + 4) * 4, rbytes = (size_t)8 * 16 * (DV + 4) * 4;
     const size_t lds = 64 * 16 * 4 + fixed + (zbytes > rbytes ? zbytes : rbytes);
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+    launch("k_dec_fused<DQ, DV, 16, true, TO>", k, (unsigned)(a.R * a.G), 256, lds, s, a);
   } else {
     auto k = k_dec_fused<DQ, DV, MAX_NB_LANE, false, TO>;
     const size_t lds = 64 * MAX_NB_LANE * 4 + fixed;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+    launch("k_dec_fused<DQ, DV, MAX_NB_LANE, false, TO>", k, (unsigned)(a.R * a.G), 256, lds, s, a);
   }
   return hipGetLastError();
 }
@@ -541,12 +541,12 @@ hipError_t launch_cmpsel(const DecArgs& a, hipStream_t s) {
     auto k = k_dec_cmpsel<DQ, DV, WITH_V, 16>;
     const size_t lds = 64 * 16 * 4 + vbytes;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+    launch("k_dec_cmpsel<DQ, DV, WITH_V, 16>", k, (unsigned)(a.R * a.G), 256, lds, s, a);
   } else {
     auto k = k_dec_cmpsel<DQ, DV, WITH_V, MAX_NB_LANE>;
     const size_t lds = 64 * MAX_NB_LANE * 4 + vbytes;
     (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k<<<(unsigned)(a.R * a.G), 256, lds, s>>>(a);
+    launch("k_dec_cmpsel<DQ, DV, WITH_V, MAX_NB_LANE>", k, (unsigned)(a.R * a.G), 256, lds, s, a);
   }
   return hipGetLastError();
 }
@@ -561,8 +561,8 @@ hipError_t run_t(const DecArgs& a, int mode, bool out_f32, hipStream_t s, Phases
   } else if (mode == 1) {
     e = out_f32 ? launch_fused<DQ, DV, float>(a, s) : launch_fused<DQ, DV, uint16_t>(a, s);
   } else {
-    if (out_f32) k_dec_attnmerge<DQ, DV, float><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
-    else k_dec_attnmerge<DQ, DV, uint16_t><<<(unsigned)(a.R * a.G), 256, 0, s>>>(a);
+    if (out_f32) launch("k_dec_attnmerge<DQ, DV, float>", k_dec_attnmerge<DQ, DV, float>, (unsigned)(a.R * a.G), 256, 0, s, a);
+    else launch("k_dec_attnmerge<DQ, DV, uint16_t>", k_dec_attnmerge<DQ, DV, uint16_t>, (unsigned)(a.R * a.G), 256, 0, s, a);
     e = hipGetLastError();
   }
   if (ph) ph->mark();

@@ -319,11 +319,11 @@ hipError_t launch_select_generic(const Prob& P, const void* q, const void* kc, c
   if (P.bf16()) {
     auto kern = k_select_generic<uint16_t>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, kThreads, lds, s>>>((const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, idx, score, ocmp, a);
+    launch("k_select_generic<uint16_t>", kern, grid, kThreads, lds, s, (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, idx, score, ocmp, a);
   } else {
     auto kern = k_select_generic<float>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, kThreads, lds, s>>>((const float*)q, (const float*)kc, (const float*)vc, idx, score, ocmp, a);
+    launch("k_select_generic<float>", kern, grid, kThreads, lds, s, (const float*)q, (const float*)kc, (const float*)vc, idx, score, ocmp, a);
   }
   return hipGetLastError();
 }
@@ -341,7 +341,7 @@ hipError_t launch_attend_generic(const Prob& P, const void* q, const void* k, co
   do {                                                                                               \
     auto kern = k_attend_generic<TI, TO>;                                                            \
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);    \
-    kern<<<grid, kThreads, lds, s>>>((const TI*)q, (const TI*)k, (const TI*)v, (const TI*)gates, idx, \
+    launch("k_attend_generic<TI, TO>", kern, grid, kThreads, lds, s, (const TI*)q, (const TI*)k, (const TI*)v, (const TI*)gates, idx, \
                                      ocmp, (TO*)out, lse, a, cap);                                   \
   } while (0)
   if (P.bf16()) {

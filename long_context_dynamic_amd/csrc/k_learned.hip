@@ -174,10 +174,10 @@ template <int D>
 hipError_t launch_mlp_d(const MlpArgs& a, int which, int DH, hipStream_t s) {
   const unsigned grid = (unsigned)((a.B * a.nb * a.G + 15) / 16);
   switch (DH) {
-    case 64: k_mlp_compress<D, 64><<<grid, 256, 0, s>>>(a, which); break;
-    case 128: k_mlp_compress<D, 128><<<grid, 256, 0, s>>>(a, which); break;
-    case 192: k_mlp_compress<D, 192><<<grid, 256, 0, s>>>(a, which); break;
-    case 256: k_mlp_compress<D, 256><<<grid, 256, 0, s>>>(a, which); break;
+    case 64: launch("k_mlp_compress<D, 64>", k_mlp_compress<D, 64>, grid, 256, 0, s, a, which); break;
+    case 128: launch("k_mlp_compress<D, 128>", k_mlp_compress<D, 128>, grid, 256, 0, s, a, which); break;
+    case 192: launch("k_mlp_compress<D, 192>", k_mlp_compress<D, 192>, grid, 256, 0, s, a, which); break;
+    case 256: launch("k_mlp_compress<D, 256>", k_mlp_compress<D, 256>, grid, 256, 0, s, a, which); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -215,7 +215,7 @@ hipError_t launch_mlp_compress(const Prob& P, const MlpArgs& a, hipStream_t s) {
 hipError_t launch_gate_proj(const GateArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.M + 127) / 128);
   if (grid == 0) return hipSuccess;
-  k_gate_proj<<<grid, 512, 0, s>>>(a);
+  launch("k_gate_proj", k_gate_proj, grid, 512, 0, s, a);
   return hipGetLastError();
 }
 

@@ -13,11 +13,11 @@
 //   k_moba_count / k_moba_scan / k_moba_fill
 //                  list, for every (head, block), the (token, slot) entries
 //                  that chose it (the current block excluded).
-//   k_moba_attn    one workgroup per 64 listed entries of one (head, block):
+//   k_moba_attn    one workgroup per 128 listed entries of one (head, block):
 //                  the block's K and V^T tiles are staged through LDS once and
-//                  shared by the 64 gathered queries; writes a (max, sum,
+//                  shared by the 128 gathered queries; writes a (max, sum,
 //                  output) partial per entry.
-//   k_moba_diag    one workgroup per (head, 64-token tile): causal attention
+//   k_moba_diag    one workgroup per (head, 128-token tile): causal attention
 //                  over the query's own block, then the log-sum-exp merge with
 //                  the entries' partials, output.
 #include <math.h>
@@ -33,6 +33,8 @@ constexpr int kRows = 64;    // tokens per selection workgroup (4 waves x 16)
 constexpr int kChunk = 128;  // listed entries per attention workgroup (4 waves x 2 x 16)
 constexpr int kCountTok = 256;  // tokens per list-counting workgroup
 constexpr int kXcds = 8;     // the chip's compute dies, each with its own L2
+constexpr int kMaxN = 8;     // most blocks one token selects on this path
+constexpr int kRecBatch = 4; // partial records whose values one merge step loads together
 
 // Partial record of one entry (16-byte aligned): the normalised output o / l
 // as D fp16 values scaled by 2^-ex so that all lie in (-1, 1) (a relative
@@ -326,18 +328,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int32_t run = (int32_t)(blockIdx.x / kXcds);
   const int32_t w = (int32_t)(blockIdx.x % kXcds) * per + run;
   if (run >= per || w >= total) return;
-  // the (b, h, block) list this chunk belongs to
+  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  // the (b, h, block) list this chunk belongs to: the last list whose first
+  // chunk is <= w, by a 64-way search (each lane tests one point of the
+  // interval, so a round costs one load latency; 2 rounds for 4096 lists)
   int64_t lo = 0, hi = nl;  // chunk_off[lo] <= w < chunk_off[hi]
   while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) / 2;
-    if (a.chunk_off[mid] <= w) lo = mid;
-    else hi = mid;
+    const int64_t step = (hi - lo + 63) / 64, pos = lo + lane * step;
+    const bool le = pos < hi && a.chunk_off[pos] <= w;  // a prefix of the lanes, lane 0 always
+    lo += (int64_t)(__popcll(__ballot(le)) - 1) * step;
+    hi = lo + step < hi ? lo + step : hi;
   }
   const int64_t bhj = lo;
   const int64_t j = bhj % a.nb, h = (bhj / a.nb) % a.H, b = bhj / (a.nb * a.H);
   const int64_t first = a.offsets[bhj] + (int64_t)(w - a.chunk_off[bhj]) * kChunk;
   const int64_t count = a.offsets[bhj + 1] - first;  // entries left in this list
-  const int wave = wave_id(), lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const bool busy = 32 * wave < count;  // wave-uniform: this wave has rows
   int64_t e[2];
   bf16x8 qf[2][D / 32];
@@ -432,8 +437,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int64_t p_first = TP * pt > P0 ? TP * pt : P0;
   const int64_t p_last = TP * pt + TP - 1 < a.L - 1 ? TP * pt + TP - 1 : a.L - 1;
   const int64_t cur = TP * pt / a.bs;
+  // the first K / V tile is requested before anything else
+  Stager<D, D, 256> st;
+  const int64_t kt0 = cur * a.bs / 64, kt1 = p_last / 64;
+  st.load(a.k, a.L, kt0 * 64, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
   int64_t p[NQ], t[NQ];
   bool valid[NQ], has_cur[NQ];
+  uint32_t earlier[NQ];  // bit i: the token's slot i holds a block before its own
   bf16x8 qf[NQ][D / 32];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -441,13 +451,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     valid[q] = pl >= P0 && pl < a.L;
     p[q] = valid[q] ? pl : p_last;  // out-of-range lanes shadow the last row
     t[q] = p[q] - P0;
-    // does this token's selection hold its own block?
+    // the token's selection (at most kMaxN slots, all loads in flight together)
     const int32_t* irow = a.idx + ((b * a.T + t[q]) * a.H + h) * a.n;
-    has_cur[q] = false;
-    for (int i = 0; i < a.n; ++i) has_cur[q] |= (irow[i] == cur);
+    int32_t sel[kMaxN];
+#pragma unroll
+    for (int i = 0; i < kMaxN; ++i) sel[i] = i < a.n ? irow[i] : -1;
     const uint16_t* qr = a.q + ((b * a.T + t[q]) * a.H + h) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qf[q][ks] = ld8(qr + 32 * ks);
+    has_cur[q] = false;
+    earlier[q] = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxN; ++i) {
+      has_cur[q] |= (sel[i] == cur);
+      if (sel[i] >= 0 && sel[i] < cur) earlier[q] |= 1u << i;
+    }
   }
   const float c = a.scale * kLog2e, stale = kStaleLog2 / c;
   float m[NQ], l[NQ];
@@ -461,9 +479,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   }
   // the wave's first row: tiles that start after it have nothing for it
   const int64_t p_wave = TP * pt + 16 * NQ * wave;
-  Stager<D, D, 256> st;
-  const int64_t kt0 = cur * a.bs / 64, kt1 = p_last / 64;
-  st.load(a.k, a.L, kt0 * 64, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
   for (int64_t kb = kt0; kb <= kt1; ++kb) {
     __syncthreads();
     st.store(kt, vt, true, true);
@@ -498,32 +513,45 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     if (!valid[q]) continue;
-    const int32_t* irow = a.idx + ((b * a.T + t[q]) * a.H + h) * a.n;
-    // merge with the partials of the earlier chosen blocks (log2 units)
+    // merge with the partials of the earlier chosen blocks (log2 units); the
+    // records' tails are loaded together, then their values, a few at a time
     const bool own = has_cur[q] && l[q] > 0.f;  // a row without its own block ran on -inf only
     const char* prow = (const char*)a.part + ((b * a.T + t[q]) * a.H + h) * a.n * rec_bytes<D>();
+    f32x4 tail[kMaxN];
+#pragma unroll
+    for (int i = 0; i < kMaxN; ++i)
+      tail[i] = (earlier[q] >> i) & 1 ? *(const f32x4*)(prow + i * rec_bytes<D>() + 2 * D)
+                                      : f32x4{-INFINITY, 0.f, 0.f, 0.f};
     float M = own ? m[q] * c : -INFINITY;
-    for (int i = 0; i < a.n; ++i) {
-      const int j = irow[i];
-      if (j >= 0 && j < cur) M = fmaxf(M, *(const float*)(prow + i * rec_bytes<D>() + 2 * D));
-    }
+#pragma unroll
+    for (int i = 0; i < kMaxN; ++i) M = fmaxf(M, tail[i][0]);
     const float wd = own ? exp2f(m[q] * c - M) : 0.f;
     float den = own ? wd * l[q] : 0.f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] = own ? o[q][dt] * wd : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < a.n; ++i) {
-      const int j = irow[i];
-      if (j < 0 || j >= cur) continue;
-      const char* rec = prow + i * rec_bytes<D>();
-      const float* tail = (const float*)(rec + 2 * D);
-      const float ws = exp2f(tail[0] - M) * tail[1];  // the record's weight: its share of the softmax mass
-      den += ws;
-      const float f = ws * ldexpf(1.f, (int)tail[2]);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f16x4 hv = __builtin_bit_cast(f16x4, *(const u32x2*)(rec + 2 * (16 * dt + 4 * lg)));
-        acc[dt] += f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]} * f;
+    for (int i0 = 0; i0 < kMaxN; i0 += kRecBatch) {
+      if (!(earlier[q] >> i0)) break;  // no later slot holds an earlier block
+      u32x2 hv[kRecBatch][D / 16];
+#pragma unroll
+      for (int i = i0; i < i0 + kRecBatch; ++i)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          hv[i - i0][dt] = (earlier[q] >> i) & 1
+                               ? *(const u32x2*)(prow + i * rec_bytes<D>() + 2 * (16 * dt + 4 * lg))
+                               : u32x2{0u, 0u};
+#pragma unroll
+      for (int i = i0; i < i0 + kRecBatch; ++i) {
+        // the record's weight: its share of the softmax mass (0 for unused slots)
+        const float ws = (earlier[q] >> i) & 1 ? exp2f(tail[i][0] - M) * tail[i][1] : 0.f;
+        den += ws;
+        const float f = ws * ldexpf(1.f, (int)tail[i][2]);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const f16x4 x = __builtin_bit_cast(f16x4, hv[i - i0][dt]);
+          acc[dt] += f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]} * f;
+        }
       }
     }
     float g = den > 0.f ? 1.f / den : 0.f;
@@ -546,35 +574,35 @@ hipError_t run_select_t(const MobaArgs& a, hipStream_t s) {
   // list length per lane: the most candidates one token takes
   const int64_t nf_min = (a.flags & (NSA_F_FORCE_FIRST | NSA_F_FORCE_CURRENT)) ? 1 : 0;
   const int64_t need = a.n - nf_min;
-  if (need <= 2) k_moba_select<D, 2, SCORES><<<grid, 256, 0, s>>>(a);
-  else if (need <= 4) k_moba_select<D, 4, SCORES><<<grid, 256, 0, s>>>(a);
-  else k_moba_select<D, 8, SCORES><<<grid, 256, 0, s>>>(a);
+  if (need <= 2) launch("k_moba_select<D, 2, SCORES>", k_moba_select<D, 2, SCORES>, grid, 256, 0, s, a);
+  else if (need <= 4) launch("k_moba_select<D, 4, SCORES>", k_moba_select<D, 4, SCORES>, grid, 256, 0, s, a);
+  else launch("k_moba_select<D, 8, SCORES>", k_moba_select<D, 8, SCORES>, grid, 256, 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t run_attend_t(const MobaArgs& a, bool out_f32, hipStream_t s, Phases* ph) {
   const int64_t ne = a.B * a.T * a.H * a.n, nl = a.B * a.H * a.nb;
-  k_moba_zero<<<(unsigned)((nl + 255) / 256), 256, 0, s>>>(a.counts, nl);
+  launch("k_moba_zero", k_moba_zero, (unsigned)((nl + 255) / 256), 256, 0, s, a.counts, nl);
   const unsigned gcount = (unsigned)(a.B * a.H * ((a.T + kCountTok - 1) / kCountTok));
-  k_moba_count<<<gcount, kCountTok, (size_t)a.nb * sizeof(int32_t), s>>>(a);
-  k_moba_scan<<<1, 1024, 0, s>>>(a);
-  k_moba_fill<<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(a);
+  launch("k_moba_count", k_moba_count, gcount, kCountTok, (size_t)a.nb * sizeof(int32_t), s, a);
+  launch("k_moba_scan", k_moba_scan, 1, 1024, 0, s, a);
+  launch("k_moba_fill", k_moba_fill, (unsigned)((ne + 255) / 256), 256, 0, s, a);
   if (ph) ph->mark();
   // an upper bound of the chunk count, in whole runs of 8; surplus
   // workgroups exit at once
   const int64_t chunks_max = (ne + kChunk - 1) / kChunk + nl;
   const unsigned gattn = (unsigned)((chunks_max + kXcds - 1) / kXcds * kXcds);
-  k_moba_attn<D><<<gattn, 256, 0, s>>>(a);
+  launch("k_moba_attn<D>", k_moba_attn<D>, gattn, 256, 0, s, a);
   if (ph) ph->mark();
   if (a.bs % 128 == 0) {
     const unsigned gdiag = (unsigned)(a.B * a.H * ((a.L - 1) / 128 - (a.L - a.T) / 128 + 1));
-    if (out_f32) k_moba_diag<D, 2, float><<<gdiag, 256, 0, s>>>(a);
-    else k_moba_diag<D, 2, uint16_t><<<gdiag, 256, 0, s>>>(a);
+    if (out_f32) launch("k_moba_diag<D, 2, float>", k_moba_diag<D, 2, float>, gdiag, 256, 0, s, a);
+    else launch("k_moba_diag<D, 2, uint16_t>", k_moba_diag<D, 2, uint16_t>, gdiag, 256, 0, s, a);
   } else {
     const unsigned gdiag = (unsigned)(a.B * a.H * ((a.L - 1) / 64 - (a.L - a.T) / 64 + 1));
-    if (out_f32) k_moba_diag<D, 1, float><<<gdiag, 256, 0, s>>>(a);
-    else k_moba_diag<D, 1, uint16_t><<<gdiag, 256, 0, s>>>(a);
+    if (out_f32) launch("k_moba_diag<D, 1, float>", k_moba_diag<D, 1, float>, gdiag, 256, 0, s, a);
+    else launch("k_moba_diag<D, 1, uint16_t>", k_moba_diag<D, 1, uint16_t>, gdiag, 256, 0, s, a);
   }
   if (ph) ph->mark();
   return hipGetLastError();
@@ -592,7 +620,7 @@ bool moba_attend_ok(const Prob& P) {
   // would launch empty grids); the generic path takes that case
   return P.bf16() && P.hpg == 1 && P.sb == P.bs && P.dq == P.dv && (P.dq == 64 || P.dq == 128) && P.nb >= 1 &&
          P.bs % 64 == 0 && P.n >= 1 &&
-         P.n <= 8 && P.B * P.T * P.H * P.n < ((int64_t)1 << 31) && P.B * P.H * P.nb < ((int64_t)1 << 30);
+         P.n <= kMaxN && P.B * P.T * P.H * P.n < ((int64_t)1 << 31) && P.B * P.H * P.nb < ((int64_t)1 << 30);
 }
 
 bool moba_ok(const Prob& P) {

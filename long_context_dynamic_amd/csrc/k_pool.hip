@@ -100,18 +100,18 @@ hipError_t launch_pool(const Prob& P, const void* k, const void* v, void* kc, vo
     const int64_t threads = rows * (P.dq + (vc ? P.dv : 0)) / ve;
     const unsigned grid = (unsigned)((threads + 255) / 256);
     if (P.bf16())
-      k_pool_vec<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc,
+      launch("k_pool_vec<uint16_t>", k_pool_vec<uint16_t>, grid, 256, 0, s, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc,
                                                 (uint16_t*)vc, P.L, P.G, P.dq, P.dv, P.bs, P.nb, rows);
     else
-      k_pool_vec<float><<<grid, 256, 0, s>>>((const float*)k, (const float*)v, (float*)kc, (float*)vc, P.L, P.G,
+      launch("k_pool_vec<float>", k_pool_vec<float>, grid, 256, 0, s, (const float*)k, (const float*)v, (float*)kc, (float*)vc, P.L, P.G,
                                              P.dq, P.dv, P.bs, P.nb, rows);
     return hipGetLastError();
   }
   if (P.bf16())
-    k_pool<uint16_t><<<dim3((unsigned)rows), dim3(256), 0, s>>>(
+    launch("k_pool<uint16_t>", k_pool<uint16_t>, dim3((unsigned)rows), dim3(256), 0, s,
         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc, (uint16_t*)vc, P.L, P.G, P.dq, P.dv, P.bs, P.nb);
   else
-    k_pool<float><<<dim3((unsigned)rows), dim3(256), 0, s>>>(
+    launch("k_pool<float>", k_pool<float>, dim3((unsigned)rows), dim3(256), 0, s,
         (const float*)k, (const float*)v, (float*)kc, (float*)vc, P.L, P.G, P.dq, P.dv, P.bs, P.nb);
   return hipGetLastError();
 }

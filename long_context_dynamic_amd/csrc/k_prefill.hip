@@ -818,11 +818,11 @@ hipError_t launch_cmpwin_tw(const PfArgs& a, bool fwd, size_t lds, hipStream_t s
   if (fwd) {
     auto kern = k_cmpwin<DQ, DV, true, TW>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, 512, lds, s>>>(a);
+    launch("k_cmpwin<DQ, DV, true, TW>", kern, grid, 512, lds, s, a);
   } else {
     auto kern = k_cmpwin<DQ, DV, false, TW>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kern<<<grid, 512, lds, s>>>(a);
+    launch("k_cmpwin<DQ, DV, false, TW>", kern, grid, 512, lds, s, a);
   }
   return hipGetLastError();
 }
@@ -841,17 +841,17 @@ hipError_t launch_cmpwin_t(const PfArgs& a, bool fwd, hipStream_t s) {
 template <int DQ, int DV>
 hipError_t launch_sel_t(const PfArgs& a, bool fwd, bool out_f32, hipStream_t s, Phases* ph) {
   const unsigned grid = (unsigned)(8 * a.G * ((a.B * a.T + 4 * kSelTokPerWave - 1) / (4 * kSelTokPerWave)));
-  k_sel_part<DQ, DV><<<grid, 256, 0, s>>>(a, !fwd || (a.flags & NSA_F_SLC));
+  launch("k_sel_part<DQ, DV>", k_sel_part<DQ, DV>, grid, 256, 0, s, a, !fwd || (a.flags & NSA_F_SLC));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ph) ph->mark();
   const unsigned mgrid = (unsigned)((2 * a.B * a.T * a.G + 3) / 4);
   if (fwd) {
-    if (out_f32) k_sel_merge<DV, true, float><<<mgrid, 256, 0, s>>>(a);
-    else k_sel_merge<DV, true, uint16_t><<<mgrid, 256, 0, s>>>(a);
+    if (out_f32) launch("k_sel_merge<DV, true, float>", k_sel_merge<DV, true, float>, mgrid, 256, 0, s, a);
+    else launch("k_sel_merge<DV, true, uint16_t>", k_sel_merge<DV, true, uint16_t>, mgrid, 256, 0, s, a);
   } else {
-    if (out_f32) k_sel_merge<DV, false, float><<<mgrid, 256, 0, s>>>(a);
-    else k_sel_merge<DV, false, uint16_t><<<mgrid, 256, 0, s>>>(a);
+    if (out_f32) launch("k_sel_merge<DV, false, float>", k_sel_merge<DV, false, float>, mgrid, 256, 0, s, a);
+    else launch("k_sel_merge<DV, false, uint16_t>", k_sel_merge<DV, false, uint16_t>, mgrid, 256, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -869,14 +869,14 @@ hipError_t launch_frag_k(const void* k, void* kF, int64_t B, int64_t L, int64_t 
   const int64_t nc = (L + 63) / 64 * 2;
   const unsigned grid = (unsigned)(B * G * nc);
   if (grid == 0) return hipSuccess;
-  k_frag_k<<<grid, 256, 0, s>>>((const uint16_t*)k, (uint16_t*)kF, L, nc, G, D);
+  launch("k_frag_k", k_frag_k, grid, 256, 0, s, (const uint16_t*)k, (uint16_t*)kF, L, nc, G, D);
   return hipGetLastError();
 }
 
 hipError_t launch_frag_q(const void* q, void* qF, int64_t R, int64_t G, int D, hipStream_t s) {
   const int64_t n = R * G * (D / 32) * 64;  // 16-byte pieces
   if (n == 0) return hipSuccess;
-  k_frag_q<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const uint16_t*)q, (uint16_t*)qF, n, D);
+  launch("k_frag_q", k_frag_q, (unsigned)((n + 255) / 256), 256, 0, s, (const uint16_t*)q, (uint16_t*)qF, n, D);
   return hipGetLastError();
 }
 
@@ -884,7 +884,7 @@ hipError_t launch_frag_v(const void* vT, void* vF, int64_t B, int64_t L, int64_t
   const int64_t nc = (L + 63) / 64 * 2;
   const unsigned grid = (unsigned)(B * G * nc);
   if (grid == 0) return hipSuccess;
-  k_frag_v<<<grid, 256, 0, s>>>((const uint16_t*)vT, (uint16_t*)vF, nc, D);
+  launch("k_frag_v", k_frag_v, grid, 256, 0, s, (const uint16_t*)vT, (uint16_t*)vF, nc, D);
   return hipGetLastError();
 }
 
@@ -895,7 +895,7 @@ hipError_t launch_group_major(const void* src, void* dst, int64_t B, int64_t L, 
   const int64_t Lp = (L + 63) / 64 * 64;
   const unsigned grid = (unsigned)(B * (Lp / 64));
   if (grid == 0) return hipSuccess;
-  k_group_major<<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, L, Lp, G, D);
+  launch("k_group_major", k_group_major, grid, 256, 0, s, (const uint16_t*)src, (uint16_t*)dst, L, Lp, G, D);
   return hipGetLastError();
 }
 
@@ -903,7 +903,7 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t B, int64_t N, in
                             hipStream_t s) {
   const unsigned grid = (unsigned)(B * G * (Np / 64));
   if (grid == 0) return hipSuccess;
-  k_transpose<<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, N, Np, G, D);
+  launch("k_transpose", k_transpose, grid, 256, 0, s, (const uint16_t*)src, (uint16_t*)dst, N, Np, G, D);
   return hipGetLastError();
 }
 

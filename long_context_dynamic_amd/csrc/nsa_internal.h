@@ -5,10 +5,27 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "nsa.h"
 
 namespace nsa {
+
+// ---- launch logging: with NSA_LOG set (and not "0") in the environment,
+// every kernel launch prints its name, grid, block and dynamic LDS to
+// stderr (read at each launch, so it can be switched at run time) ----
+inline bool log_on() {
+  const char* e = getenv("NSA_LOG");
+  return e && *e && !(e[0] == '0' && e[1] == 0);
+}
+template <typename K, typename... A>
+inline void launch(const char* name, K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, A... args) {
+  if (log_on())
+    fprintf(stderr, "[nsa] %s grid %u x %u block %u lds %zu\n", name, grid.x, grid.y, block.x, lds);
+  kern<<<grid, block, lds, s>>>(args...);
+}
+
 
 // Problem sizes widened to 64 bits, plus derived quantities.
 struct Prob {

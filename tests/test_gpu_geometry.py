@@ -130,3 +130,33 @@ def test_forward_on_a_side_stream_is_bit_identical(name, prob):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     _same(a, b, name)
+
+
+def test_launch_log_prints_each_kernel_and_its_grid(capfd, monkeypatch):
+    """With NSA_LOG=1 every launch prints its kernel, grid, block and LDS to
+    stderr; unset, nothing is printed."""
+    prob = FWD_CASES[1][1]
+    print("[case] launch log on the bf16 prefill", flush=True)
+    t = U.upload(inputs.generate(prob), prob)
+    monkeypatch.delenv("NSA_LOG", raising=False)
+    nsa.forward(prob, t["q"], t["k"], t["v"], _gates(prob, t))
+    torch.cuda.synchronize()
+    assert "[nsa]" not in capfd.readouterr().err
+    monkeypatch.setenv("NSA_LOG", "1")
+    nsa.forward(prob, t["q"], t["k"], t["v"], _gates(prob, t))
+    torch.cuda.synchronize()
+    monkeypatch.delenv("NSA_LOG")
+    lines = [l.split() for l in capfd.readouterr().err.splitlines() if l.startswith("[nsa] ")]
+    assert lines, "no launch lines"
+    grids = {}
+    for l in lines:
+        # [nsa] NAME grid X x Y block N lds M  (NAME may hold spaces)
+        assert (l[-8], l[-6], l[-4], l[-2]) == ("grid", "x", "block", "lds"), l
+        name = " ".join(l[1:-8])
+        grids.setdefault(name.split("<")[0], []).append((int(l[-7]), int(l[-1])))
+    B, T, G = prob["batch"], prob["q_len"], prob["n_groups"]
+    assert grids["k_sel_merge"] == [((2 * B * T * G + 3) // 4, 0)]
+    (g_sel, lds_sel), = grids["k_sel_part"]
+    assert g_sel % (8 * G) == 0 and lds_sel == 0
+    (g_cw, lds_cw), = grids["k_cmpwin"]
+    assert g_cw in (B * G * -(-T // 8), B * G * -(-T // 16)) and 0 < lds_cw <= 160 * 1024
