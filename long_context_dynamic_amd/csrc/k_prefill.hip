@@ -447,6 +447,14 @@ template <typename TO> __device__ __forceinline__ void store4(TO* p, f32x4 v);
 // outputs are written once and never re-read here: non-temporal stores keep
 // them from evicting the K/V tiles that other tokens re-use
 template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 v) { __builtin_nontemporal_store(v, (f32x4*)p); }
+// two blocks of 4 values as one 16-byte piece of bf16
+__device__ __forceinline__ void store8_nt(uint16_t* p, f32x4 a, f32x4 b) {
+  const u32x4 w = {(uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16),
+                   (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16),
+                   (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16),
+                   (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16)};
+  __builtin_nontemporal_store(w, (u32x4*)p);
+}
 template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
   u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
              (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
@@ -534,9 +542,11 @@ __device__ __forceinline__ int sel_stripe(int64_t j, int64_t p) {
 // computing while the other waits; the next token's queries are read while
 // the current token is worked on.  K and V come from the fragment-order
 // images (nsa_frag.h): each read instruction fetches 1 KiB in lane order.
-// Partial layout: part_o [(row, group)][stripe][DV / 16][64 lanes][4] (each
-// store instruction writes 512 contiguous bytes), part_l [(row, group)][16
-// heads][8 stripes].
+// Partial layout: part_o [(row, group)][stripe][DV / 32][64 lanes][8]: lane
+// (lr, lg)'s 16 bytes of pair q hold dims 32 q + 4 lg .. + 3 and 32 q + 16 +
+// 4 lg .. + 3 of head lr (its output blocks 2 q and 2 q + 1), so each store
+// and each of the merge's loads moves 1 KiB contiguous; part_l [(row,
+// group)][16 heads][8 stripes].
 constexpr int kSelTokPerWave = 16;
 constexpr int kSelMaxTopK = 32;
 
@@ -708,9 +718,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // every chunk holds a key <= p, so l > 0
     const float inv_l = 1.f / l;
-    uint16_t* orow = a.part_o + (rg * 8 + x) * 16 * DV + 4 * lane;
+    uint16_t* orow = a.part_o + (rg * 8 + x) * 16 * DV + 8 * lane;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) store4<uint16_t>(orow + 256 * dt, o[dt] * inv_l);
+    for (int q = 0; q < DV / 32; ++q) store8_nt(orow + 512 * q, o[2 * q] * inv_l, o[2 * q + 1] * inv_l);
     write_lse(rg, m * c + __log2f(l));
   }
 }
@@ -750,13 +760,13 @@ __global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
 
   const f32x4* lp = (const f32x4*)(a.part_l + (rg * 16 + lr) * 8);
   const f32x4 l0 = lp[0], l1 = lp[1];
-  u32x2 raw[8][ND];
-  const uint16_t* pbase = a.part_o + (rg * 8 * (DV / 16) + hv * ND) * 256 + 4 * lane;
+  u32x4 raw[8][ND / 2];  // pair j: this half's output blocks 2 j and 2 j + 1
+  const uint16_t* pbase = a.part_o + (rg * 8 * (DV / 32) + hv * (ND / 2)) * 512 + 8 * lane;
 #pragma unroll
   for (int x = 0; x < 8; ++x)
 #pragma unroll
-    for (int i = 0; i < ND; ++i)
-      raw[x][i] = __builtin_nontemporal_load((const u32x2*)(pbase + ((int64_t)x * (DV / 16) + i) * 256));
+    for (int j = 0; j < ND / 2; ++j)
+      raw[x][j] = __builtin_nontemporal_load((const u32x4*)(pbase + ((int64_t)x * (DV / 32) + j) * 512));
   f32x4 accv[ND];
   if (FWD) {
     const float* arow = acc_frag(a, tg, g, hv * ND, DV) + 4 * lane;
@@ -784,9 +794,9 @@ __global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
     const bool on = w[x] > 0.f;
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
-      const u32x2 u = raw[x][i];
-      const f32x4 v = {bf16_to_f32((uint16_t)u[0]), bf16_to_f32((uint16_t)(u[0] >> 16)),
-                       bf16_to_f32((uint16_t)u[1]), bf16_to_f32((uint16_t)(u[1] >> 16))};
+      const uint32_t u0 = raw[x][i / 2][2 * (i % 2)], u1 = raw[x][i / 2][2 * (i % 2) + 1];
+      const f32x4 v = {bf16_to_f32((uint16_t)u0), bf16_to_f32((uint16_t)(u0 >> 16)),
+                       bf16_to_f32((uint16_t)u1), bf16_to_f32((uint16_t)(u1 >> 16))};
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[i][e] += on ? v[e] * wx : 0.f;
     }

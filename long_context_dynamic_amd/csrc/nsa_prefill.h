@@ -19,7 +19,7 @@ struct PfArgs {
   const uint16_t* vcT;    // [B, G, nbp / 32, DV, 32]  value summaries, tiled likewise
   const uint16_t* gates;  // [B, T, H, 3] or NULL
   float* acc;             // [B, T, G, DV / 16, 64, 4] gated compressed + window partial sum, fragment order
-  uint16_t* part_o;       // [B, T, G, 8, 16, DV] selected branch per XCD stripe: normalised output (bf16)
+  uint16_t* part_o;       // [B, T, G, 8, DV / 32, 64, 8] selected branch per XCD stripe: normalised output (bf16), in the matrix op's lane order
   float* part_l;          // [B, T, G, 16, 8]      ... and its log-sum-exp (log2 units, -inf when empty)
   int32_t* idx;           // [B, T, G, n]
   float* score;           // [B, T, G, n] or NULL
