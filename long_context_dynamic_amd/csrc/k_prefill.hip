@@ -743,10 +743,10 @@ template <> __device__ __forceinline__ void store4_wb<uint16_t>(uint16_t* p, f32
 // and output); else out = the selected branch and lse its natural
 // log-sum-exp.  Two waves per (token, group), each with half of the dims:
 // lane (lr, lg) takes dims 16 dt + 4 lg .. + 3 of head lr, the layout the
-// partials were written in.  Every read of the wave is issued before any is
-// used (the log-sum-exps, all 8 stripes' partials, acc), so one memory
-// latency per wave; a stripe without blocks has weight 0 and its (stale)
-// partial is discarded by a select, never multiplied.
+// partials were written in.  The wave reads the log-sum-exps and acc, then
+// all partials of the stripes that hold chosen blocks at once (two memory
+// latencies per wave); a stripe without blocks has weight 0 and its partial
+// is neither read nor multiplied.
 template <int DV, bool FWD, typename TO>
 __global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
   constexpr int ND = DV / 32;  // 16-dim column blocks per wave
@@ -760,21 +760,24 @@ __global__ void __launch_bounds__(256) k_sel_merge(PfArgs a) {
 
   const f32x4* lp = (const f32x4*)(a.part_l + (rg * 16 + lr) * 8);
   const f32x4 l0 = lp[0], l1 = lp[1];
-  u32x4 raw[8][ND / 2];  // pair j: this half's output blocks 2 j and 2 j + 1
-  const uint16_t* pbase = a.part_o + (rg * 8 * (DV / 32) + hv * (ND / 2)) * 512 + 8 * lane;
-#pragma unroll
-  for (int x = 0; x < 8; ++x)
-#pragma unroll
-    for (int j = 0; j < ND / 2; ++j)
-      raw[x][j] = __builtin_nontemporal_load((const u32x4*)(pbase + ((int64_t)x * (DV / 32) + j) * 512));
   f32x4 accv[ND];
   if (FWD) {
     const float* arow = acc_frag(a, tg, g, hv * ND, DV) + 4 * lane;
 #pragma unroll
     for (int i = 0; i < ND; ++i) accv[i] = __builtin_nontemporal_load((const f32x4*)(arow + 256 * i));
   }
-
   const float lx[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+  // the partials of the stripes that hold chosen blocks (an empty stripe's
+  // log-sum-exp is -inf for all 16 heads: the wave skips its loads)
+  u32x4 raw[8][ND / 2];  // pair j: this half's output blocks 2 j and 2 j + 1
+  const uint16_t* pbase = a.part_o + (rg * 8 * (DV / 32) + hv * (ND / 2)) * 512 + 8 * lane;
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int j = 0; j < ND / 2; ++j)
+      raw[x][j] = lx[x] == -INFINITY
+                      ? u32x4{0u, 0u, 0u, 0u}
+                      : __builtin_nontemporal_load((const u32x4*)(pbase + ((int64_t)x * (DV / 32) + j) * 512));
   float M = -INFINITY;
 #pragma unroll
   for (int x = 0; x < 8; ++x) M = fmaxf(M, lx[x]);
