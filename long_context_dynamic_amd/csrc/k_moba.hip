@@ -14,7 +14,8 @@
 //                  list, for every (head, block), the (token, slot) entries
 //                  that chose it (the current block excluded).
 //   k_moba_attn    one workgroup per 128 listed entries of one (head, block):
-//                  the block's K and V^T tiles are staged through LDS once and
+//                  the block's K and V tiles are staged through LDS once (V as
+//                  rows, read back transposed by ds_read_b64_tr_b16) and
 //                  shared by the 128 gathered queries; writes a (max, sum,
 //                  output) partial per entry.
 //   k_moba_diag    one workgroup per (head, 128-token tile): causal attention
@@ -321,7 +322,7 @@ __global__ void k_moba_fill(MobaArgs a) {
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_moba_attn(MobaArgs a) {
   __shared__ __align__(16) uint16_t kt[64 * k_lds_stride<D>()];
-  __shared__ __align__(16) uint16_t vt[D * kVtStride];
+  __shared__ __align__(16) uint16_t vt[64 * v_row_stride<D>()];  // V rows of the tile, read back transposed
   const int64_t nl = a.B * a.H * a.nb;
   const int32_t total = a.chunk_off[nl];
   const int32_t per = (total + kXcds - 1) / kXcds;
@@ -362,20 +363,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[q][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Stager<D, D, 256> st;
+  Stager<D, D, 256, true> st;
   const int64_t kb0 = j * a.bs, ntl = a.bs / 64;
-  st.load(a.k, a.L, kb0, a.vT, a.Lp, kb0, b, h, a.H, true);
+  st.load(a.k, a.L, kb0, a.v, a.Lp, kb0, b, h, a.H, true);
   for (int64_t i = 0; i < ntl; ++i) {
     __syncthreads();
     st.store(kt, vt, true, true);
     __syncthreads();
-    if (i + 1 < ntl) st.load(a.k, a.L, kb0 + 64 * (i + 1), a.vT, a.Lp, kb0 + 64 * (i + 1), b, h, a.H, true);
+    if (i + 1 < ntl) st.load(a.k, a.L, kb0 + 64 * (i + 1), a.v, a.Lp, kb0 + 64 * (i + 1), b, h, a.H, true);
     if (busy) {
       f32x4 s[2][4];
       qk_tile_T2<D>(kt, qf, s, lr, lg);
       softmax_step<D>(s[0], m[0], l[0], o[0], c, stale, true);
       softmax_step<D>(s[1], m[1], l[1], o[1], c, stale, true);
-      pv_tile2<D>(vt, s, o, lr, lg);
+      pv_tile2_rows<D>(vt, s, o, lr, lg);
     }
   }
 #pragma unroll
@@ -426,7 +427,7 @@ template <> __device__ __forceinline__ void mstore4<uint16_t>(uint16_t* p, f32x4
 template <int D, int NQ, typename TO>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_moba_diag(MobaArgs a) {
   __shared__ __align__(16) uint16_t kt[64 * k_lds_stride<D>()];
-  __shared__ __align__(16) uint16_t vt[D * kVtStride];
+  __shared__ __align__(16) uint16_t vt[64 * v_row_stride<D>()];  // V rows of the tile, read back transposed
   constexpr int TP = 64 * NQ;
   const int64_t P0 = a.L - a.T;  // position of token 0
   const int64_t pt0 = P0 / TP, ntile = (a.L - 1) / TP - pt0 + 1;
@@ -438,9 +439,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
   const int64_t p_last = TP * pt + TP - 1 < a.L - 1 ? TP * pt + TP - 1 : a.L - 1;
   const int64_t cur = TP * pt / a.bs;
   // the first K / V tile is requested before anything else
-  Stager<D, D, 256> st;
+  Stager<D, D, 256, true> st;
   const int64_t kt0 = cur * a.bs / 64, kt1 = p_last / 64;
-  st.load(a.k, a.L, kt0 * 64, a.vT, a.Lp, kt0 * 64, b, h, a.H, true);
+  st.load(a.k, a.L, kt0 * 64, a.v, a.Lp, kt0 * 64, b, h, a.H, true);
   int64_t p[NQ], t[NQ];
   bool valid[NQ], has_cur[NQ];
   uint32_t earlier[NQ];  // bit i: the token's slot i holds a block before its own
@@ -483,7 +484,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     __syncthreads();
     st.store(kt, vt, true, true);
     __syncthreads();
-    if (kb + 1 <= kt1) st.load(a.k, a.L, (kb + 1) * 64, a.vT, a.Lp, (kb + 1) * 64, b, h, a.H, true);
+    if (kb + 1 <= kt1) st.load(a.k, a.L, (kb + 1) * 64, a.v, a.Lp, (kb + 1) * 64, b, h, a.H, true);
     if (kb * 64 > p_wave + 16 * NQ - 1) continue;  // wave-uniform: every key after every row
     f32x4 s[NQ][4];
     if constexpr (NQ == 2) {
@@ -505,9 +506,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
       softmax_step<D>(s[q], m[q], l[q], o[q], c, stale, true);
     }
     if constexpr (NQ == 2) {
-      pv_tile2<D>(vt, s, o, lr, lg);
+      pv_tile2_rows<D>(vt, s, o, lr, lg);
     } else {
-      pv_tile<D>(vt, s[0], o[0], lr, lg);
+      pv_tile_rows<D>(vt, s[0], o[0], lr, lg);
     }
   }
 #pragma unroll

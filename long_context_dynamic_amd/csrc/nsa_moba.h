@@ -10,7 +10,7 @@ namespace nsa {
 struct MobaArgs {
   const uint16_t* q;      // [B, T, H, D]
   const uint16_t* k;      // [B, L, H, D]
-  const uint16_t* vT;     // [B, H, Lp / 32, D, 32]  values, tiled and key-contiguous
+  const uint16_t* v;      // [B, L, H, D]
   const uint16_t* kc;     // [B, nb, H, D]  mean keys of the blocks
   const uint16_t* gates;  // [B, T, H, 3] or NULL (slot 1 scales the output)
   int32_t* idx;           // [B, T, H, n]
@@ -29,7 +29,7 @@ struct MobaArgs {
 };
 
 // Shapes the MoBA kernels take: bf16, one head per group; selection:
-// d_qk in {64, 128}, 1 <= nb <= 256, 1 <= top_k <= 8; attention: d_qk = d_v,
+// d_qk in {64, 128}, nb >= 1, 1 <= top_k <= 8; attention: d_qk = d_v,
 // blocks a multiple of 64 long, top_k <= 8; the forward pass: both, and the
 // selected branch alone.
 bool moba_select_ok(const Prob& P);

@@ -50,7 +50,6 @@ MobaArgs moba_args(const Prob& P) {
 // The MoBA attention stage: entry lists and partial records.
 void take_moba(const Prob& P, Workspace& w, const std::function<size_t(size_t)>& take) {
   const size_t ne = (size_t)(P.B * P.T * P.H * P.n), nl = (size_t)(P.B * P.H * P.nb);
-  w.vT = take((size_t)(P.B * P.H * P.dv * pad64(P.L)) * 2);
   w.counts = take(nl * sizeof(int32_t));
   w.pos = take(ne * sizeof(int32_t));
   w.offsets = take((nl + 1) * sizeof(int32_t));
@@ -60,7 +59,6 @@ void take_moba(const Prob& P, Workspace& w, const std::function<size_t(size_t)>&
 }
 
 void set_moba_ws(MobaArgs& a, const Workspace& ws, void* base) {
-  a.vT = at<uint16_t>(base, ws.vT);
   a.counts = at<int32_t>(base, ws.counts);
   a.pos = at<int32_t>(base, ws.pos);
   a.offsets = at<int32_t>(base, ws.offsets);
@@ -145,7 +143,6 @@ int forward_phase_names(const Prob& P, bool have_cmp, const char** names, int ma
   if (decode_ok(P)) {
     list[n++] = "dec_step";
   } else if (moba_ok(P)) {
-    list[n++] = "transpose_v";
     list[n++] = "moba_select";
     list[n++] = "moba_lists";
     list[n++] = "moba_attn";
@@ -238,8 +235,7 @@ hipError_t run_sparse_attn(const Prob& P, const void* q, const void* k, const vo
   if (moba_attend_ok(P)) {
     MobaArgs a = moba_args(S);
     set_moba_ws(a, ws, base);
-    hipError_t e = launch_transpose(v, (void*)a.vT, P.B, P.L, a.Lp, P.H, (int)P.dv, s);
-    if (e != hipSuccess) return e;
+    a.v = (const uint16_t*)v;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.idx = (int32_t*)idx;
@@ -323,8 +319,7 @@ hipError_t run_forward(const Prob& P, const void* q, const void* k, const void* 
   if (moba) {
     MobaArgs a = moba_args(P);
     set_moba_ws(a, ws, base);
-    if ((e = launch_transpose(v, (void*)a.vT, P.B, P.L, a.Lp, P.H, (int)P.dv, s)) != hipSuccess) return e;
-    ph.mark();
+    a.v = (const uint16_t*)v;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.kc = (const uint16_t*)kc;

@@ -21,6 +21,9 @@ namespace nsa {
 // which is why the V^T operand is one 16-byte read.)
 template <int D> constexpr int k_lds_stride() { return D + 16; }
 constexpr int kVtStride = 64 + 16;
+// Row-major V tiles (keys x d) read back transposed (ld_vt_pair): rows of
+// d + 8 elements, as the decoding kernels use.
+template <int D> constexpr int v_row_stride() { return D + 8; }
 
 // Permuted key order of a 64-key tile stored with perm = true: LDS row
 // 16*mt + i holds key tile_key(mt, i) = 32*(mt/2) + 8*(i/4) + 4*(mt%2) + i%4.
@@ -49,12 +52,14 @@ static_assert(tile_perm_ok(), "tile_row must invert tile_key");
 // Register-prefetching tile stager: load() issues the global reads of one
 // 64-key tile (K rows [row0, row0 + 64) of a [B, Nrows, G, DQ] tensor, rows
 // clamped to Nrows - 1, and optionally V^T columns [col0, col0 + 64) of a
-// tiled [B, G, Np / 32, DV, 32] tensor) into registers; store() writes them
-// to LDS, the K rows in permuted key order when perm is set.  The next
-// tile's reads are in flight while the current tile is computed on.
-template <int DQ, int DV, int NT>
+// tiled [B, G, Np / 32, DV, 32] tensor, or with VROWS the V rows [col0,
+// col0 + 64) of a [B, Nrows, G, DV] tensor, clamped the same way) into
+// registers; store() writes them to LDS, the K rows in permuted key order
+// when perm is set, V rows in key order (row stride v_row_stride<DV>).  The
+// next tile's reads are in flight while the current tile is computed on.
+template <int DQ, int DV, int NT, bool VROWS = false>
 struct Stager {
-  static constexpr int KS = k_lds_stride<DQ>(), VS = kVtStride;
+  static constexpr int KS = k_lds_stride<DQ>(), VS = VROWS ? v_row_stride<DV>() : kVtStride;
   static constexpr int KC = 64 * DQ / 8, VC = DV * 8;
   static constexpr int KPT = (KC + NT - 1) / NT, VPT = (VC + NT - 1) / NT;
   u32x4 kr[KPT], vr[VPT];
@@ -74,7 +79,18 @@ struct Stager {
         kr[i] = *(const u32x4*)(rows + ((b * Nrows + row) * G + g) * DQ + 8 * c8);
       }
     }
-    if (with_v) {
+    if (with_v && VROWS) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (VC % NT == 0 || c < VC) {
+          const int r = c / (DV / 8), c8 = c % (DV / 8);
+          int64_t row = col0 + r;
+          if (row > Nrows - 1) row = Nrows - 1;
+          vr[i] = *(const u32x4*)(colsT + ((b * Nrows + row) * G + g) * DV + 8 * c8);
+        }
+      }
+    } else if (with_v) {
       const uint16_t* tile = colsT + ((b * G + g) * (Np / 64) + col0 / 64) * DV * 64;
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
@@ -93,7 +109,13 @@ struct Stager {
         *(u32x4*)(kt + (perm ? tile_row(r) : r) * KS + d) = kr[i];
       }
     }
-    if (with_v) {
+    if (with_v && VROWS) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (VC % NT == 0 || c < VC) *(u32x4*)(vt + (c / (DV / 8)) * VS + 8 * (c % (DV / 8))) = vr[i];
+      }
+    } else if (with_v) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * NT;
@@ -218,6 +240,38 @@ __device__ __forceinline__ void pv_tile2(const uint16_t* vt, const f32x4 (&pm)[2
     const uint16_t* row = vt + (16 * dt + lr) * VS + 8 * lg;
     const bf16x8 v0 = ld8(row);
     const bf16x8 v1 = ld8(row + 32);
+    o[0][dt] = mfma16(v0, p00, o[0][dt]);
+    o[1][dt] = mfma16(v0, p10, o[1][dt]);
+    o[0][dt] = mfma16(v1, p01, o[0][dt]);
+    o[1][dt] = mfma16(v1, p11, o[1][dt]);
+  }
+}
+
+// The same two products over a row-major V tile (keys in natural order,
+// row stride v_row_stride<DV>): each V^T operand (keys 8 lg .. + 7, and 32
+// on, of column 16 dt + lr) is two transposing 8-byte reads.
+template <int DV>
+__device__ __forceinline__ void pv_tile_rows(const uint16_t* vr, const f32x4 (&pm)[4], f32x4 (&o)[DV / 16], int lr,
+                                             int lg) {
+  constexpr int VS = v_row_stride<DV>();
+  const bf16x8 p0 = pack8(pm[0], pm[1]);
+  const bf16x8 p1 = pack8(pm[2], pm[3]);
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) {
+    o[dt] = mfma16(ld_vt_pair(vr, 8 * lg, 8 * lg + 4, 16 * dt, VS, lr), p0, o[dt]);
+    o[dt] = mfma16(ld_vt_pair(vr, 32 + 8 * lg, 36 + 8 * lg, 16 * dt, VS, lr), p1, o[dt]);
+  }
+}
+template <int DV>
+__device__ __forceinline__ void pv_tile2_rows(const uint16_t* vr, const f32x4 (&pm)[2][4], f32x4 (&o)[2][DV / 16],
+                                              int lr, int lg) {
+  constexpr int VS = v_row_stride<DV>();
+  const bf16x8 p00 = pack8(pm[0][0], pm[0][1]), p01 = pack8(pm[0][2], pm[0][3]);
+  const bf16x8 p10 = pack8(pm[1][0], pm[1][1]), p11 = pack8(pm[1][2], pm[1][3]);
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) {
+    const bf16x8 v0 = ld_vt_pair(vr, 8 * lg, 8 * lg + 4, 16 * dt, VS, lr);
+    const bf16x8 v1 = ld_vt_pair(vr, 32 + 8 * lg, 36 + 8 * lg, 16 * dt, VS, lr);
     o[0][dt] = mfma16(v0, p00, o[0][dt]);
     o[1][dt] = mfma16(v0, p10, o[1][dt]);
     o[0][dt] = mfma16(v1, p01, o[0][dt]);
