@@ -22,6 +22,12 @@ Per-kernel durations from a --kernel-trace run (CSV or rocpd database):
 
     python -m long_context_dynamic_amd.pmc trace DIR
 
+All passes of bench.py legs at once (rocprofv3 started as a child process
+for each pass, the summaries written to profiles/, each leg's kernel-trace
+table printed):
+
+    python -m long_context_dynamic_amd.pmc collect --legs prefill moba decode --dir gpurun_out/prof
+
 The traffic summary records a hash of the kernel's sources; bench.py reports
 the traffic only while the sources still hash the same.
 """
@@ -189,6 +195,107 @@ def trace_stats(run_dir: str) -> list:
     return sorted(((n, c, t / c) for n, (c, t) in agg.items()), key=lambda x: -x[1] * x[2])
 
 
+# ------------------------------------------------------------- collection --
+# The rocprofv3 passes behind the committed summaries, per bench.py leg:
+# FETCH_SIZE and WRITE_SIZE runs, counter sets that each fit the hardware's
+# per-block limits (at most 8 SQ, 4 TCC, 4 TCP, 2 TA, 2 GRBM), a kernel
+# trace.  Algorithmic FLOP per launch are bench.py's counts for the
+# workload (selected: 2.644e12, compressed + window: 2.742e12 at 64k;
+# MoBA 32k: 5.369e11 listed blocks, 1.377e11 own block).
+PREFILL_SETS = (["MfmaUtil", "MfmaFlopsBF16", "VALUBusy", "SQ_WAIT_INST_ANY", "SQ_WAVES"],
+                ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"],
+                ["TA_BUSY_avr", "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TCC_READ_REQ_sum", "TCC_HIT_sum", "TCC_MISS_sum",
+                 "GRBM_GUI_ACTIVE"])
+DECODE_SETS = (["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                "SQ_INSTS_VMEM_RD", "SQ_INSTS_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+               ["TA_BUSY_avr", "TCP_TCC_READ_REQ_sum", "TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE"])
+LEGS = {
+    "prefill": {"workload": "nsa_prefill_64k", "args": ["--only", "prefill", "--workload", "nsa_prefill_64k"],
+                "kernels": [("selected", "k_sel_part<192, 128>", 2.644089e12), ("selected_merge", "k_sel_merge", 0.0),
+                            ("cmp_select_window", "k_cmpwin<192, 128, true", 2.742e12)],
+                "sets": PREFILL_SETS, "trace_steps": 5},
+    "moba": {"workload": "moba_32k", "args": ["--only", "prefill", "--workload", "moba_32k"],
+             "kernels": [("moba_attn", "k_moba_attn", 5.36870912e11), ("moba_own_block", "k_moba_diag", 1.37707e11)],
+             "sets": PREFILL_SETS, "trace_steps": 5},
+    "decode": {"workload": "nsa_decode_64x64k", "args": ["--only", "decode"],
+               "kernels": [("dec_step", "k_dec_fused", 0.0)], "sets": DECODE_SETS, "trace_steps": 10},
+}
+
+
+def _run_pass(repo, out_dir, name, prof_args, bench_args, limit):
+    """One rocprofv3 pass over bench.py (the program itself after --), in
+    /tmp, killed with its process group after limit seconds.  Returns the
+    command as recorded in the summaries."""
+    import signal
+    import subprocess
+    import time
+    d = os.path.join(out_dir, name)
+    cmd = ["rocprofv3"] + prof_args + ["-d", d, "-o", "run", "--output-format", "csv", "--",
+                                        "python3", os.path.join(repo, "bench.py")] + bench_args
+    env = dict(os.environ, TMPDIR="/tmp")
+    t0 = time.time()
+    print(f"[pmc] {name}: {' '.join(cmd)}", flush=True)
+    p = subprocess.Popen(cmd, cwd="/tmp", env=env, start_new_session=True,
+                         stdout=open(d + ".log", "w"), stderr=subprocess.STDOUT)
+    try:
+        rc = p.wait(timeout=limit)
+    except subprocess.TimeoutExpired:
+        os.killpg(p.pid, signal.SIGKILL)
+        p.wait()
+        raise RuntimeError(f"{name}: killed after {limit} s (log {d}.log)")
+    if rc != 0 and not glob.glob(os.path.join(d, "**", "*.csv"), recursive=True):
+        raise RuntimeError(f"{name}: rocprofv3 exited {rc} with no results (log {d}.log)")
+    print(f"[pmc] {name}: done in {time.time() - t0:.0f} s (rc {rc})", flush=True)
+    return "cd /tmp && export TMPDIR=/tmp; " + " ".join(cmd).replace(repo, "$REPO")
+
+
+def collect(args) -> None:
+    """Runs the passes of the named legs into args.dir and writes their
+    traffic and counter summaries to args.profiles; prints each leg's
+    kernel-trace table."""
+    repo = os.path.dirname(PKG)
+    os.makedirs(args.dir, exist_ok=True)
+    lim = args.limit
+    cal_f = _run_pass(repo, args.dir, "FETCH_SIZE_gather", ["--pmc", "FETCH_SIZE"],
+                      ["--only", "gather", "--steps", "2", "--warmup", "1"], lim)
+    cal_w = _run_pass(repo, args.dir, "WRITE_SIZE_copy", ["--pmc", "WRITE_SIZE"],
+                      ["--only", "copy", "--steps", "2", "--warmup", "1"], lim)
+    for leg in args.legs:
+        L = LEGS[leg]
+        wl = L["workload"]
+        steps = ["--steps", "2", "--warmup", "1"]
+        cf = _run_pass(repo, args.dir, f"FETCH_SIZE_{leg}", ["--pmc", "FETCH_SIZE"], L["args"] + steps, lim)
+        cw = _run_pass(repo, args.dir, f"WRITE_SIZE_{leg}", ["--pmc", "WRITE_SIZE"], L["args"] + steps, lim)
+        tcmd = "; ".join([cf, cw, cal_f, cal_w])
+        runs, ccmds = [], []
+        for i, s in enumerate(L["sets"]):
+            name = f"ctr_{leg}{i + 1}"
+            ccmds.append(_run_pass(repo, args.dir, name, ["--pmc"] + s,
+                                   L["args"] + ["--steps", "1", "--warmup", "1"], lim))
+            runs.append(os.path.join(args.dir, name))
+        trace_dir = f"trace_{leg}"
+        _run_pass(repo, args.dir, trace_dir, ["--kernel-trace", "--stats"],
+                  L["args"] + ["--steps", str(L["trace_steps"]), "--warmup", "2"], lim)
+        for name, sym, flop in L["kernels"]:
+            ns = argparse.Namespace(kernel=sym, name=name, workload=wl, command=tcmd,
+                                    fetch=os.path.join(args.dir, f"FETCH_SIZE_{leg}"),
+                                    write=os.path.join(args.dir, f"WRITE_SIZE_{leg}"),
+                                    gather_fetch=os.path.join(args.dir, "FETCH_SIZE_gather"), copy_fetch=None,
+                                    copy_write=os.path.join(args.dir, "WRITE_SIZE_copy"))
+            with open(os.path.join(args.profiles, f"{name}_{wl}_traffic.json"), "w") as fh:
+                json.dump(traffic(ns), fh, indent=1)
+            ns = argparse.Namespace(kernel=sym, name=name, workload=wl, runs=runs, algorithmic_flop=flop,
+                                    command="; ".join(ccmds))
+            with open(os.path.join(args.profiles, f"{name}_{wl}_counters.json"), "w") as fh:
+                json.dump(counters(ns), fh, indent=1)
+            print(f"[pmc] wrote {name}_{wl} traffic and counters", flush=True)
+        print(f"[pmc] kernel trace of {leg} ({wl}):\n| kernel | calls | avg us |\n|---|---|---|")
+        for n, c, us in trace_stats(os.path.join(args.dir, trace_dir)):
+            print(f"| {n} | {c} | {us:.1f} |")
+        sys.stdout.flush()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -214,7 +321,14 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     s = sub.add_parser("trace")
     s.add_argument("dir")
+    r = sub.add_parser("collect", help="run the rocprofv3 passes of bench.py legs and write their summaries")
+    r.add_argument("--legs", nargs="+", choices=sorted(LEGS), required=True)
+    r.add_argument("--dir", required=True, help="directory for the raw rocprofv3 output")
+    r.add_argument("--profiles", default=os.path.join(os.path.dirname(PKG), "profiles"))
+    r.add_argument("--limit", type=int, default=240, help="seconds per pass before it is killed")
     args = ap.parse_args(argv)
+    if args.cmd == "collect":
+        return collect(args)
     if args.cmd in ("traffic", "counters"):
         rec = traffic(args) if args.cmd == "traffic" else counters(args)
         with open(args.out, "w") as fh:
