@@ -366,7 +366,18 @@ __device__ __forceinline__ void topk_part(const DecArgs& a, int64_t row, int64_t
     }
     vals[i] = v;
   }
-  const int cnt = topk_wave<NBL>(vals, nsel, p / 64, a.flags, (int)a.n, cj, cs);
+  int cnt;
+  if constexpr (NBL <= 16) {
+    int nf;
+    cnt = topk_wave_keys<NBL>(vals, nsel, p / 64, a.flags, (int)a.n, cj, nf);
+    cs = INFINITY;  // forced blocks
+    if (srow && lane >= nf && lane < cnt) {
+      cs = imp[a.per * cj];
+      for (int64_t k = 1; k < a.per; ++k) cs += imp[a.per * cj + k];
+    }
+  } else {
+    cnt = topk_wave<NBL>(vals, nsel, p / 64, a.flags, (int)a.n, cj, cs);
+  }
   topk_write(cnt, cj, cs, (int)a.n, orow, srow);
   if (lsel) {  // the same list, ascending, for the workgroup's own use
     int rank = 0;

@@ -191,9 +191,19 @@ __device__ __forceinline__ void topk_row(const float* imp, int64_t per, int64_t 
     }
     vals[i] = v;
   }
-  int cj;
+  int cj, cnt;
   float cs;
-  const int cnt = topk_wave<NBL>(vals, nsel, cur, flags, n, cj, cs);
+  if constexpr (NBL <= 16) {
+    int nf;
+    cnt = topk_wave_keys<NBL>(vals, nsel, cur, flags, n, cj, nf);
+    cs = INFINITY;  // forced blocks
+    if (srow && lane >= nf && lane < cnt) {
+      cs = imp[per * cj];
+      for (int64_t k = 1; k < per; ++k) cs += imp[per * cj + k];
+    }
+  } else {
+    cnt = topk_wave<NBL>(vals, nsel, cur, flags, n, cj, cs);
+  }
   topk_write(cnt, cj, cs, n, orow, srow);
 }
 

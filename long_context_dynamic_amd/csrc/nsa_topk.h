@@ -86,6 +86,89 @@ __device__ __forceinline__ int topk_wave(float (&vals)[NBL], int64_t nvis, int64
   return nf + r_take;
 }
 
+// Maximum of unsigned values over all 64 lanes, returned in every lane.
+__device__ __forceinline__ unsigned wave_allmax_u32(unsigned x) {
+  x = max(x, (unsigned)dpp_i<kDppXor1>((int)x));
+  x = max(x, (unsigned)dpp_i<kDppXor2>((int)x));
+  x = max(x, (unsigned)dpp_i<kDppHalfMirror>((int)x));
+  x = max(x, (unsigned)dpp_i<kDppMirror>((int)x));
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((unsigned)r[0], (unsigned)r[1]);
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((unsigned)r[0], (unsigned)r[1]);
+}
+
+// The same selection as topk_wave for at most 1024 blocks (NBL <= 16), one
+// cross-lane reduction per round: each candidate is one 32-bit key, its
+// importance's exponent and top 14 mantissa bits (plus one, so every
+// candidate's key is above the 0 of the non-candidates) over 10 bits of
+// 1023 - block id, so a larger key means a larger importance and, among
+// importances that agree to 2^-14 relative, the lower block id.  Keys are
+// distinct; each lane keeps its best and second-best and rescans (below
+// the key it gave last) only when it wins with its second-best unknown.
+// Returns the count; lane k < count holds the k-th chosen block in cj
+// (forced ones first, in lanes 0 .. nforced - 1).
+template <int NBL>
+__device__ __forceinline__ int topk_wave_keys(const float (&vals)[NBL], int64_t nvis, int64_t cur, uint32_t flags,
+                                              int n, int& cj, int& nforced) {
+  static_assert(NBL <= 16, "10 bits of block id");
+  const int lane = threadIdx.x & 63;
+  const bool first = flags & NSA_F_FORCE_FIRST;
+  const bool current = (flags & NSA_F_FORCE_CURRENT) && !(first && cur == 0);
+  const int f0 = first ? 0 : (current ? (int)cur : -1);
+  const int f1 = (first && current) ? (int)cur : -1;
+  const int nf = (f0 >= 0) + (f1 >= 0);
+  int ncand = (int)nvis;
+  if (f0 >= 0 && f0 < nvis) --ncand;
+  if (f1 >= 0 && f1 < nvis) --ncand;
+  unsigned kv[NBL];
+  unsigned b1 = 0u, b2 = 0u;  // this lane's best and second-best key
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int j = lane + 64 * i;
+    const float v = vals[i];
+    const bool cand = j < nvis && j != f0 && j != f1 && v >= 0.f;
+    const unsigned k = cand ? ((((unsigned)__float_as_uint(v) >> 9) + 1u) << 10) | (unsigned)(1023 - j) : 0u;
+    kv[i] = k;
+    b2 = k > b1 ? b1 : max(b2, k);
+    b1 = max(b1, k);
+  }
+  const int r_take = (n - nf) < ncand ? (n - nf) : ncand;
+  cj = -1;
+  if (lane == 0 && f0 >= 0) cj = f0;
+  if (lane == 1 && f1 >= 0) cj = f1;
+  bool known2 = true;
+  int taken = 0;
+  for (int round = 0; round < r_take; ++round) {
+    const unsigned M = (unsigned)__builtin_amdgcn_readfirstlane((int)wave_allmax_u32(b1));
+    if (M == 0u) break;  // no candidate left (only with non-finite importances)
+    ++taken;
+    const int J = 1023 - (int)(M & 1023u), wl = J & 63;
+    if (lane == nf + round) cj = J;
+    const bool win = lane == wl;
+    if (__builtin_amdgcn_readlane((int)known2, wl)) {
+      if (win) {
+        b1 = b2;
+        known2 = false;
+      }
+    } else if (win) {
+      // the winner's best and second-best keys below M
+      unsigned c1 = 0u, c2 = 0u;
+#pragma unroll
+      for (int i = 0; i < NBL; ++i) {
+        const unsigned k = kv[i] < M ? kv[i] : 0u;
+        c2 = k > c1 ? c1 : max(c2, k);
+        c1 = max(c1, k);
+      }
+      b1 = c1;
+      b2 = c2;
+      known2 = true;
+    }
+  }
+  nforced = nf;
+  return nf + taken;
+}
+
 // Writes the chosen blocks of topk_wave ascending to orow[0 .. n) (padding
 // -1) and their scores to srow (padding -inf) when srow is given.
 __device__ __forceinline__ void topk_write(int cnt, int cj, float cs, int n, int32_t* orow, float* srow) {
