@@ -294,3 +294,37 @@ def test_compress_of_a_growing_cache_keeps_its_summaries(name, over):
         nb = L // bs
         assert torch.equal(kc2.view(torch.int16), kc[:, :nb].view(torch.int16)), L
         assert torch.equal(vc2.view(torch.int16), vc[:, :nb].view(torch.int16)), L
+
+
+@pytest.mark.parametrize("name,over", [("nsa_prefill_8k", dict(q_len=700, kv_len=1100)),
+                                       ("nsa_decode_64x64k", dict(batch=3, kv_len=5000))])
+def test_exact_ties_pick_the_lower_block_ids(name, over):
+    """Every block's keys repeated from one of the first four blocks: blocks
+    with the same keys have the same summary, so their importances are
+    exactly equal in the oracle and on the GPU, and the selection must take
+    the lower block ids among them (reading R6).  The near-tie band would
+    accept either order, so each (row, group) whose four distinct
+    importances are more than 1e-4 apart is compared with the oracle's
+    selection exactly."""
+    prob = workloads.get(name, **over)
+    x = inputs.generate(prob)
+    bs, nb = prob["block"], prob["kv_len"] // prob["block"]
+    for j in range(4, nb):
+        x["k"][:, j * bs:(j + 1) * bs] = x["k"][:, (j % 4) * bs:(j % 4 + 1) * bs]
+    t = U.upload(x, prob)
+    rows = np.arange(prob["batch"] * prob["q_len"])
+    kc, vc = oracle.pool(prob, x["k"], x["v"])
+    idx, imp, _ = oracle.select(prob, x["q"], kc, vc, rows=rows, want_cmp=False)
+    gidx, _ = nsa.select_topk(prob, t["q"], nsa.to_device(kc, prob))
+    got = U.gather_rows(gidx.cpu().numpy(), prob, rows)
+    exact = 0
+    for ri in range(len(rows)):
+        for g in range(prob["n_groups"]):
+            v = np.sort(imp[ri, g][:4][np.isfinite(imp[ri, g][:4])])
+            if len(v) > 1 and np.min(np.diff(v) / v[1:]) <= U.TIE_REL:
+                continue
+            np.testing.assert_array_equal(got[ri, g], idx[ri, g], err_msg=f"row {rows[ri]} group {g}")
+            exact += 1
+    U.check_selection(prob, rows, got, idx, imp)
+    print(f"{exact} of {len(rows) * prob['n_groups']} (row, group) pairs compared exactly")
+    assert exact >= 0.9 * len(rows) * prob["n_groups"]
