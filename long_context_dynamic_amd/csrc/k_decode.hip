@@ -356,15 +356,24 @@ __device__ __forceinline__ void topk_part(const DecArgs& a, int64_t row, int64_t
   int64_t nsel = (p + 1) / 64;
   if (nsel > a.nbs) nsel = a.nbs;
   float vals[NBL];
+  if (a.per == 1 && nsel > 0) {
+    // one summary per selection block: every lane's reads in flight together
+    // (blocks past nsel read the last visible one and are then masked)
 #pragma unroll
-  for (int i = 0; i < NBL; ++i) {
-    const int64_t J = lane + 64 * i;
-    float v = -1.f;
-    if (J < nsel) {
-      v = imp[a.per * J];
-      for (int64_t k = 1; k < a.per; ++k) v += imp[a.per * J + k];
+    for (int i = 0; i < NBL; ++i) vals[i] = imp[min(lane + 64 * i, (int)nsel - 1)];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) vals[i] = lane + 64 * i < nsel ? vals[i] : -1.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const int64_t J = lane + 64 * i;
+      float v = -1.f;
+      if (J < nsel) {
+        v = imp[a.per * J];
+        for (int64_t k = 1; k < a.per; ++k) v += imp[a.per * J + k];
+      }
+      vals[i] = v;
     }
-    vals[i] = v;
   }
   int cnt;
   if constexpr (NBL <= 16) {

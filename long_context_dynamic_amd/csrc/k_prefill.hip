@@ -181,15 +181,24 @@ __device__ __forceinline__ void topk_row(const float* imp, int64_t per, int64_t 
                                          int n, int32_t* orow, float* srow) {
   const int lane = threadIdx.x & 63;
   float vals[NBL];
+  if (per == 1 && nsel > 0) {
+    // one summary per selection block: every lane's reads in flight together
+    // (blocks past nsel read the last visible one and are then masked)
 #pragma unroll
-  for (int i = 0; i < NBL; ++i) {
-    const int64_t j = lane + 64 * i;
-    float v = -1.f;
-    if (j < nsel) {
-      v = imp[per * j];
-      for (int64_t k = 1; k < per; ++k) v += imp[per * j + k];
+    for (int i = 0; i < NBL; ++i) vals[i] = imp[min(lane + 64 * i, (int)nsel - 1)];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) vals[i] = lane + 64 * i < nsel ? vals[i] : -1.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const int64_t j = lane + 64 * i;
+      float v = -1.f;
+      if (j < nsel) {
+        v = imp[per * j];
+        for (int64_t k = 1; k < per; ++k) v += imp[per * j + k];
+      }
+      vals[i] = v;
     }
-    vals[i] = v;
   }
   int cj, cnt;
   float cs;

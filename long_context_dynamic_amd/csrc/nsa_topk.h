@@ -137,21 +137,16 @@ __device__ __forceinline__ int topk_wave_keys(const float (&vals)[NBL], int64_t 
   cj = -1;
   if (lane == 0 && f0 >= 0) cj = f0;
   if (lane == 1 && f1 >= 0) cj = f1;
+  // Every step stays in the vector unit (the reduction leaves the maximum in
+  // every lane): no scalar round trip per round.  Only the winning lane can
+  // take the rescan branch, which the wave skips when it does not.
   bool known2 = true;
-  int taken = 0;
   for (int round = 0; round < r_take; ++round) {
-    const unsigned M = (unsigned)__builtin_amdgcn_readfirstlane((int)wave_allmax_u32(b1));
-    if (M == 0u) break;  // no candidate left (only with non-finite importances)
-    ++taken;
-    const int J = 1023 - (int)(M & 1023u), wl = J & 63;
-    if (lane == nf + round) cj = J;
-    const bool win = lane == wl;
-    if (__builtin_amdgcn_readlane((int)known2, wl)) {
-      if (win) {
-        b1 = b2;
-        known2 = false;
-      }
-    } else if (win) {
+    const unsigned M = wave_allmax_u32(b1);
+    const int J = 1023 - (int)(M & 1023u);
+    if (lane == nf + round && M != 0u) cj = J;  // M == 0: no candidate left (non-finite importances)
+    const bool win = lane == (J & 63) && M != 0u;
+    if (win && !known2) {
       // the winner's best and second-best keys below M
       unsigned c1 = 0u, c2 = 0u;
 #pragma unroll
@@ -163,8 +158,12 @@ __device__ __forceinline__ int topk_wave_keys(const float (&vals)[NBL], int64_t 
       b1 = c1;
       b2 = c2;
       known2 = true;
+    } else if (win) {
+      b1 = b2;
+      known2 = false;
     }
   }
+  const int taken = __popcll(__ballot(lane >= nf && lane < nf + r_take && cj >= 0));
   nforced = nf;
   return nf + taken;
 }
