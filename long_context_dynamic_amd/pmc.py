@@ -26,7 +26,7 @@ All passes of bench.py legs at once (rocprofv3 started as a child process
 for each pass, the summaries written to profiles/, each leg's kernel-trace
 table printed):
 
-    python -m long_context_dynamic_amd.pmc collect --legs prefill moba decode --dir gpurun_out/prof
+    python -m long_context_dynamic_amd.pmc collect --legs prefill moba decode --dir prof_out
 
 The traffic summary records a hash of the kernel's sources; bench.py reports
 the traffic only while the sources still hash the same.
