@@ -6,10 +6,10 @@
 //   k_dec_fused      one workgroup per (row, group) for the whole step: the
 //                    two phases below back to back, with barriers between;
 //                    the logits stay in LDS, every wave computes a share of
-//                    the importance with its first window tile in flight,
-//                    all four waves stream the window (wave 0 the fewest
-//                    tiles, after its top-k), and the selected and window
-//                    records stay in LDS for the merge.
+//                    the importance (waves 1..3 with their first window tile
+//                    in flight), waves 1..3 stream the window while wave 0
+//                    does the top-k, and the selected and window records
+//                    stay in LDS for the merge.
 //   k_dec_cmpsel     one workgroup per (row, group): 4 waves share out the
 //                    64-summary tiles (compressed-branch logits kept in zbuf
 //                    for the importance, a partial softmax-weighted sum of
@@ -645,26 +645,22 @@ __global__ void __launch_bounds__(256) k_dec_fused(DecArgs a) {
   __syncthreads();  // the compressed-branch records (global memory) and logits are complete
   bf16x8 qf[DQ / 32];
   load_q<DQ>(a, row, g, qf);
-  // every wave computes its share of the importance with its first window
-  // tile's reads in flight, which the LDS-only barrier leaves in flight;
-  // then wave 0 makes the top-k while the others go on with the window,
-  // which does not depend on it
+  // every wave computes its share of the importance -- waves 1..3 with
+  // their first window tile's reads in flight, which the LDS-only barrier
+  // leaves in flight -- then wave 0 makes the top-k while waves 1..3 stream
+  // the rest of the window, which does not depend on it (wave 0's window
+  // record is empty)
   auto share = [&] {
     importance_share<DV, NBL>(a, row, g, threadIdx.x, z, zstride, [&](int w) { return (const float*)rec_of(w).ml; },
                               imp);
     lds_barrier();
   };
-  // the window's tiles are dealt over all four waves (tile i to wave
-  // (i + 1) % 4, so wave 0, which also makes the top-k, gets the fewest);
-  // wave 0 makes the top-k with its own first window tile in flight
-  const int wfirst = (wave + kAttnWaves - 1) % kAttnWaves;
   if (wave == 0) {
-    win_wave<DQ, DV>(a, row, g, wfirst, kAttnWaves, qf, myv, rec_of(nc + ns + wave), [&] {
-      share();
-      topk_part<NBL>(a, row, g, imp, lsel);
-    });
+    share();
+    topk_part<NBL>(a, row, g, imp, lsel);
+    win_wave<DQ, DV>(a, row, g, 1 << 30, 1, qf, myv, rec_of(nc + ns), [] {});
   } else {
-    win_wave<DQ, DV>(a, row, g, wfirst, kAttnWaves, qf, myv, rec_of(nc + ns + wave), share);
+    win_wave<DQ, DV>(a, row, g, wave - 1, kAttnWaves - 1, qf, myv, rec_of(nc + ns + wave), share);
   }
   lds_barrier();  // the chosen blocks are in lsel
   sel_wave<DQ, DV>(a, row, g, wave, lsel, qf, myv, rec_of(nc + wave));
